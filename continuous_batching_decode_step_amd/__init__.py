@@ -1,0 +1,311 @@
+"""Python binding of libcbd.so, the batched decode step for MI355X (gfx950).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+behind the C-ABI of ``include/cbd.h``; the names here mirror it.  PyTorch is
+used for device memory and streams.  There is no CPU fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcbd.so")
+
+CBD_F32, CBD_BF16, CBD_Q8_0 = 0, 1, 2
+ERRORS = {
+    -1: "CBD_E_ARG", -2: "CBD_E_DUP_LANE", -3: "CBD_E_LANE_NOT_LIVE", -4: "CBD_E_POS_MISMATCH",
+    -5: "CBD_E_KV_FULL", -6: "CBD_E_TOKEN", -7: "CBD_E_NO_FREE_LANE", -8: "CBD_E_HIP",
+    -9: "CBD_E_WORKSPACE", -10: "CBD_E_UNSUPPORTED",
+}
+# Every symbol include/cbd.h declares.
+SYMBOLS = [
+    "cbd_version", "cbd_last_error", "cbd_model_create", "cbd_model_destroy", "cbd_arena_bytes",
+    "cbd_arena_create", "cbd_arena_destroy", "cbd_lane_alloc", "cbd_lane_clear", "cbd_lane_evict",
+    "cbd_lane_length", "cbd_arena_used_bytes", "cbd_arena_live_lanes", "cbd_workspace_bytes",
+    "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
+]
+
+
+class CbdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+        self.name = ERRORS.get(code, "?")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int), ("n_layers", ctypes.c_int), ("n_heads", ctypes.c_int),
+                ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("ffn_dim", ctypes.c_int),
+                ("vocab", ctypes.c_int), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("tied_embeddings", ctypes.c_int), ("wtype", ctypes.c_int)]
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("embed", _Matrix), ("lm_head", _Matrix), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", ctypes.POINTER(ctypes.c_void_p)), ("ffn_norm", ctypes.POINTER(ctypes.c_void_p)),
+                ("w_qkv", ctypes.POINTER(_Matrix)), ("w_o", ctypes.POINTER(_Matrix)),
+                ("w_gu", ctypes.POINTER(_Matrix)), ("w_down", ctypes.POINTER(_Matrix))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcbd.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libcbd.so is not built (%s); run continuous_batching_decode_step_amd/build.py"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        L.cbd_version.restype = ctypes.c_char_p
+        L.cbd_last_error.restype = ctypes.c_char_p
+        L.cbd_model_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Weights), ctypes.POINTER(vp)]
+        L.cbd_model_destroy.argtypes = [vp]
+        L.cbd_model_destroy.restype = None
+        L.cbd_arena_bytes.argtypes = [ctypes.POINTER(Config), i32, i32]
+        L.cbd_arena_bytes.restype = sz
+        L.cbd_arena_create.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(vp)]
+        L.cbd_arena_destroy.argtypes = [vp]
+        L.cbd_arena_destroy.restype = None
+        L.cbd_lane_alloc.argtypes = [vp, pi32]
+        L.cbd_lane_clear.argtypes = [vp, i32]
+        L.cbd_lane_evict.argtypes = [vp, i32]
+        L.cbd_lane_length.argtypes = [vp, i32]
+        L.cbd_arena_used_bytes.argtypes = [vp]
+        L.cbd_arena_used_bytes.restype = sz
+        L.cbd_arena_live_lanes.argtypes = [vp]
+        L.cbd_workspace_bytes.argtypes = [vp, i32, i32]
+        L.cbd_workspace_bytes.restype = sz
+        L.cbd_decode_step_batch.argtypes = [vp, vp, i32, pi32, pi32, pi32, vp, vp, vp, sz, vp]
+        L.cbd_decode_step.argtypes = [vp, vp, i32, pi32, ctypes.c_int32, vp, vp, vp, sz, vp]
+        L.cbd_lane_kv_export.argtypes = [vp, i32, vp, vp, vp]
+        L.cbd_lane_kv_import.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.cbd_set_variant.argtypes = [vp, i32]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise CbdError(rc, lib().cbd_last_error().decode())
+    return rc
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a torch tensor (or an int / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _pi32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def config_of(cfg) -> Config:
+    """C config from any object with the fields of a model shape (d, n_layers, ...)."""
+    return Config(cfg.d, cfg.n_layers, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab,
+                  cfg.rms_eps, cfg.rope_theta, int(cfg.tied), int(cfg.wtype))
+
+
+# ---- device weights -------------------------------------------------------------
+
+@dataclass
+class DeviceMatrix:
+    data: "object"                    # torch tensor [N, K] (float32 / int16 bf16 bits / int8)
+    scale: Optional["object"] = None  # torch int16 tensor of binary16 bits [N, K/32] (Q8_0)
+
+
+@dataclass
+class DeviceWeights:
+    embed: DeviceMatrix
+    lm_head: Optional[DeviceMatrix]
+    final_norm: "object"
+    attn_norm: List["object"]
+    ffn_norm: List["object"]
+    w_qkv: List[DeviceMatrix]
+    w_o: List[DeviceMatrix]
+    w_gu: List[DeviceMatrix]
+    w_down: List[DeviceMatrix]
+
+    def nbytes(self) -> int:
+        n = 0
+        for m in [self.embed, self.lm_head] + self.w_qkv + self.w_o + self.w_gu + self.w_down:
+            if m is not None:
+                n += m.data.numel() * m.data.element_size()
+                if m.scale is not None:
+                    n += m.scale.numel() * m.scale.element_size()
+        return n
+
+
+def upload_weights(W, device="cuda") -> DeviceWeights:
+    """Copy host weight arrays (numpy, in the layout of include/cbd.h) to device tensors."""
+    import torch
+
+    def t(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    def m(x):
+        return None if x is None else DeviceMatrix(t(x.data), None if x.scale is None else t(x.scale))
+
+    return DeviceWeights(embed=m(W.embed), lm_head=m(W.lm_head), final_norm=t(W.final_norm),
+                         attn_norm=[t(a) for a in W.attn_norm], ffn_norm=[t(a) for a in W.ffn_norm],
+                         w_qkv=[m(x) for x in W.w_qkv], w_o=[m(x) for x in W.w_o], w_gu=[m(x) for x in W.w_gu],
+                         w_down=[m(x) for x in W.w_down])
+
+
+# ---- objects ------------------------------------------------------------------------
+
+class Model:
+    """cbd_model over device weights (kept referenced by this object)."""
+
+    def __init__(self, cfg, weights: DeviceWeights):
+        self.cfg = cfg
+        self.weights = weights
+        self._c = config_of(cfg)
+        L = cfg.n_layers
+        mat = lambda x: _Matrix(_ptr(x.data), _ptr(x.scale)) if x is not None else _Matrix(None, None)
+        self._attn = (ctypes.c_void_p * L)(*[_ptr(a) for a in weights.attn_norm])
+        self._ffn = (ctypes.c_void_p * L)(*[_ptr(a) for a in weights.ffn_norm])
+        self._qkv = (_Matrix * L)(*[mat(x) for x in weights.w_qkv])
+        self._o = (_Matrix * L)(*[mat(x) for x in weights.w_o])
+        self._gu = (_Matrix * L)(*[mat(x) for x in weights.w_gu])
+        self._down = (_Matrix * L)(*[mat(x) for x in weights.w_down])
+        self._w = _Weights(mat(weights.embed), mat(weights.lm_head), _ptr(weights.final_norm),
+                           ctypes.cast(self._attn, ctypes.POINTER(ctypes.c_void_p)),
+                           ctypes.cast(self._ffn, ctypes.POINTER(ctypes.c_void_p)),
+                           self._qkv, self._o, self._gu, self._down)
+        h = ctypes.c_void_p()
+        _check(lib().cbd_model_create(ctypes.byref(self._c), ctypes.byref(self._w), ctypes.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().cbd_model_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, max_batch: int, max_seq: int) -> int:
+        return lib().cbd_workspace_bytes(self.h, max_batch, max_seq)
+
+    def set_variant(self, variant: int):
+        _check(lib().cbd_set_variant(self.h, variant))
+
+    def decode_step_batch(self, arena: "Arena", lanes: Sequence[int], positions: np.ndarray, tokens,
+                          logits, argmax=None, workspace=None, workspace_bytes: Optional[int] = None,
+                          stream=None) -> None:
+        """positions: np.int32 array, advanced in place on success."""
+        ln = _i32(lanes)
+        assert isinstance(positions, np.ndarray) and positions.dtype == np.int32 and positions.flags["C_CONTIGUOUS"]
+        tk = _i32(tokens)
+        B = len(ln)
+        assert len(positions) == B and len(tk) == B
+        wsb = workspace_bytes if workspace_bytes is not None else (
+            0 if workspace is None else workspace.numel() * workspace.element_size())
+        _check(lib().cbd_decode_step_batch(self.h, arena.h, B, _pi32(ln), _pi32(positions), _pi32(tk),
+                                           _ptr(logits), _ptr(argmax), _ptr(workspace), wsb, _stream(stream)))
+
+    def decode_step(self, arena: "Arena", lane: int, position: np.ndarray, token: int, logits, argmax=None,
+                    workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+        """position: np.int32 array of one element, advanced in place on success."""
+        assert isinstance(position, np.ndarray) and position.dtype == np.int32 and position.size == 1
+        wsb = workspace_bytes if workspace_bytes is not None else (
+            0 if workspace is None else workspace.numel() * workspace.element_size())
+        _check(lib().cbd_decode_step(self.h, arena.h, lane, _pi32(position), int(token), _ptr(logits),
+                                     _ptr(argmax), _ptr(workspace), wsb, _stream(stream)))
+
+
+def arena_bytes(cfg, n_lanes: int, max_seq: int) -> int:
+    c = config_of(cfg)
+    return lib().cbd_arena_bytes(ctypes.byref(c), n_lanes, max_seq)
+
+
+class Arena:
+    """cbd_arena over caller-owned device memory (kept referenced by this object)."""
+
+    def __init__(self, model: Model, n_lanes: int, max_seq: int, dev_mem, dev_bytes: Optional[int] = None):
+        self.model = model
+        self.n_lanes = n_lanes
+        self.max_seq = max_seq
+        self.mem = dev_mem
+        nbytes = dev_bytes if dev_bytes is not None else dev_mem.numel() * dev_mem.element_size()
+        h = ctypes.c_void_p()
+        _check(lib().cbd_arena_create(model.h, n_lanes, max_seq, _ptr(dev_mem), nbytes, ctypes.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().cbd_arena_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def lane_alloc(self) -> int:
+        out = ctypes.c_int32()
+        _check(lib().cbd_lane_alloc(self.h, ctypes.byref(out)))
+        return out.value
+
+    def lane_clear(self, lane: int):
+        _check(lib().cbd_lane_clear(self.h, lane))
+
+    def lane_evict(self, lane: int):
+        _check(lib().cbd_lane_evict(self.h, lane))
+
+    def lane_length(self, lane: int) -> int:
+        return _check(lib().cbd_lane_length(self.h, lane))
+
+    @property
+    def used_bytes(self) -> int:
+        return lib().cbd_arena_used_bytes(self.h)
+
+    @property
+    def live_lanes(self) -> int:
+        return lib().cbd_arena_live_lanes(self.h)
+
+    def kv_export(self, lane: int, k_dst, v_dst, stream=None):
+        _check(lib().cbd_lane_kv_export(self.h, lane, _ptr(k_dst), _ptr(v_dst), _stream(stream)))
+
+    def kv_import(self, lane: int, length: int, k_src, v_src, stream=None):
+        _check(lib().cbd_lane_kv_import(self.h, lane, length, _ptr(k_src), _ptr(v_src), _stream(stream)))

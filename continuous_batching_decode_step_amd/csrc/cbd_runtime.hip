@@ -1,0 +1,553 @@
+// Host runtime of the C-ABI in include/cbd.h: model and arena objects,
+// host-side validation (all of it before any GPU work, so a failed call
+// changes nothing), the workspace layout and the per-step launch sequence.
+//
+// Step = embed + first RMSNorm, then per layer: QKV projection, attention
+// (rotary, in-place KV append, ragged split-K), O projection + residual,
+// RMSNorm, gate|up projection + SwiGLU, down projection + residual, RMSNorm;
+// then the LM head with per-lane greedy argmax.  Every projection runs once
+// over the [B, d] panel of the step ("MODEL-BATCHING-RESULTS — multi-user
+// batched decode, measured", section "The lever").
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/cbd.h"
+#include "cbd_internal.h"
+
+using namespace cbd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(CBD_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int TARGET_WAVES = 2048;  // split-K is chosen so a B=1 step has this many waves
+constexpr int MIN_KS = 256;         // but no split shorter than this many elements
+constexpr int NSLOT = 4;            // pinned staging slots for per-step metadata
+
+struct Plan {
+  int N, Nraw, K, S, Ks, nRB;
+};
+
+Plan make_plan(int N, int Nraw, int K, int kstep, int rows_per_rb) {
+  Plan p;
+  p.N = N;
+  p.Nraw = Nraw;
+  p.K = K;
+  p.nRB = (N + rows_per_rb - 1) / rows_per_rb;
+  int S = (TARGET_WAVES + p.nRB - 1) / p.nRB;
+  S = std::max(1, std::min(S, K / MIN_KS));
+  int Ks = (K + S - 1) / S;
+  Ks = (Ks + kstep - 1) / kstep * kstep;
+  p.Ks = Ks;
+  p.S = (K + Ks - 1) / Ks;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct cbd_model {
+  cbd_config c;
+  int wt;
+  int q_dim, kv_dim, n_qkv, G, actb, kvb, pl, kstep;
+  cbd_matrix embed, head;
+  const float* final_norm;
+  std::vector<const float*> attn_norm, ffn_norm;
+  std::vector<cbd_matrix> qkv, o, gu, down;
+  Plan p_qkv, p_o, p_gu, p_down, p_head;
+  int variant = 0;
+  // pinned staging for per-step metadata
+  void* slot[NSLOT] = {};
+  size_t slot_bytes[NSLOT] = {};
+  hipEvent_t ev[NSLOT] = {};
+  bool ev_live[NSLOT] = {};
+  int next_slot = 0;
+  // the workspace whose counters are known to be zero
+  const void* ws_ready = nullptr;
+  size_t ws_ready_bytes = 0;
+  int ws_ready_seq = 0;
+};
+
+struct cbd_arena {
+  cbd_model* m;
+  int n_lanes, max_seq;
+  char* base;
+  size_t bytes;
+  long long lane_stride;  // elements per lane in each of the K and V regions
+  size_t region_bytes;
+  std::vector<uint8_t> live;
+  std::vector<int> len;
+};
+
+namespace {
+
+struct WsLayout {
+  size_t cnt_gemm, n_cnt_gemm, cnt_attn, n_cnt_attn, meta, x, xn, qkv, o, a, part, amax, rope, apart, total;
+  int maxB, MS;
+};
+
+WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
+  WsLayout L{};
+  const cbd_config& c = m->c;
+  L.maxB = maxB;
+  L.MS = (max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const Plan* plans[] = {&m->p_qkv, &m->p_o, &m->p_gu, &m->p_down, &m->p_head};
+  size_t ncg = (size_t)(maxB + TILE - 1) / TILE;
+  size_t ncnt = 0, npart = 0;
+  for (const Plan* p : plans) {
+    ncnt = std::max(ncnt, (size_t)p->nRB * ncg);
+    if (p->S > 1) npart = std::max(npart, (size_t)p->S * maxB * p->Nraw);
+  }
+  L.n_cnt_gemm = ncnt;
+  L.n_cnt_attn = (size_t)maxB * c.n_kv_heads;
+  L.cnt_gemm = take(4 * L.n_cnt_gemm);
+  L.cnt_attn = take(4 * L.n_cnt_attn);
+  L.meta = take(4 * ((size_t)3 * maxB + (size_t)2 * maxB * L.MS));
+  L.x = take(4 * (size_t)maxB * c.d_model);
+  L.xn = take((size_t)m->actb * maxB * c.d_model);
+  L.qkv = take(4 * (size_t)maxB * m->n_qkv);
+  L.o = take((size_t)m->actb * maxB * m->q_dim);
+  L.a = take((size_t)m->actb * maxB * c.ffn_dim);
+  L.part = take(4 * npart);
+  L.amax = take(8 * (size_t)m->p_head.nRB * maxB);
+  L.rope = take(8 * (size_t)maxB * (c.head_dim / 2));
+  L.apart = take(4 * (size_t)maxB * L.MS * c.n_kv_heads * m->G * (c.head_dim + 2));
+  L.total = off;
+  return L;
+}
+
+int max_batch_for(const cbd_model* m, int max_seq, size_t bytes) {
+  if (layout(m, 1, max_seq).total > bytes) return 0;
+  int lo = 1, hi = 1 << 16;
+  while (lo < hi) {
+    int mid = lo + (hi - lo + 1) / 2;
+    if (layout(m, mid, max_seq).total <= bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_matrix(const cbd_matrix& mt, int wt, const char* name) {
+  if (!mt.data) return fail(CBD_E_ARG, "weight %s: null data pointer", name);
+  if (!aligned16(mt.data)) return fail(CBD_E_ARG, "weight %s: data not 16-byte aligned", name);
+  if (wt == WT_Q8 && !mt.scale) return fail(CBD_E_ARG, "weight %s: Q8_0 needs a scale plane", name);
+  return CBD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cbd_version(void) { return "cbd 0.1 gfx950"; }
+
+const char* cbd_last_error(void) { return g_err.c_str(); }
+
+int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** out) {
+  if (!cfg || !w || !out) return fail(CBD_E_ARG, "null argument");
+  const cbd_config& c = *cfg;
+  if (c.d_model <= 0 || c.n_layers <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.ffn_dim <= 0 || c.vocab <= 0)
+    return fail(CBD_E_ARG, "non-positive model dimension");
+  if (c.wtype < CBD_F32 || c.wtype > CBD_Q8_0) return fail(CBD_E_ARG, "unknown wtype %d", c.wtype);
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(CBD_E_ARG, "bad rms_eps or rope_theta");
+  if (c.n_heads % c.n_kv_heads != 0 || c.n_heads / c.n_kv_heads > 8)
+    return fail(CBD_E_UNSUPPORTED, "n_heads / n_kv_heads must be an integer <= 8");
+  if (c.head_dim != 16 && c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(CBD_E_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", c.head_dim);
+  const int pl = c.wtype == CBD_F32 ? 4 : (c.wtype == CBD_BF16 ? 8 : 32);
+  const int qd = c.n_heads * c.head_dim;
+  if (c.d_model % pl || c.ffn_dim % pl || qd % pl)
+    return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and n_heads*head_dim must be multiples of %d", pl);
+  if (!w->final_norm || !w->attn_norm || !w->ffn_norm || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down)
+    return fail(CBD_E_ARG, "null weight pointer array");
+  int rc;
+  if ((rc = check_matrix(w->embed, c.wtype, "embed"))) return rc;
+  if (!c.tied_embeddings && (rc = check_matrix(w->lm_head, c.wtype, "lm_head"))) return rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!w->attn_norm[l] || !w->ffn_norm[l]) return fail(CBD_E_ARG, "layer %d: null norm gain", l);
+    if ((rc = check_matrix(w->w_qkv[l], c.wtype, "w_qkv"))) return rc;
+    if ((rc = check_matrix(w->w_o[l], c.wtype, "w_o"))) return rc;
+    if ((rc = check_matrix(w->w_gu[l], c.wtype, "w_gu"))) return rc;
+    if ((rc = check_matrix(w->w_down[l], c.wtype, "w_down"))) return rc;
+  }
+  cbd_model* m = new cbd_model();
+  m->c = c;
+  m->wt = c.wtype;
+  m->q_dim = qd;
+  m->kv_dim = c.n_kv_heads * c.head_dim;
+  m->n_qkv = qd + 2 * m->kv_dim;
+  m->G = c.n_heads / c.n_kv_heads;
+  m->actb = c.wtype == CBD_F32 ? 4 : 2;
+  m->kvb = c.wtype == CBD_BF16 ? 2 : 4;
+  m->pl = pl == 32 ? 8 : pl;
+  m->kstep = c.wtype == CBD_F32 ? 16 : 32;
+  m->embed = w->embed;
+  m->head = c.tied_embeddings ? w->embed : w->lm_head;
+  m->final_norm = w->final_norm;
+  for (int l = 0; l < c.n_layers; ++l) {
+    m->attn_norm.push_back(w->attn_norm[l]);
+    m->ffn_norm.push_back(w->ffn_norm[l]);
+    m->qkv.push_back(w->w_qkv[l]);
+    m->o.push_back(w->w_o[l]);
+    m->gu.push_back(w->w_gu[l]);
+    m->down.push_back(w->w_down[l]);
+  }
+  const int rows = TILE * GEMM_R;
+  m->p_qkv = make_plan(m->n_qkv, m->n_qkv, c.d_model, m->kstep, rows);
+  m->p_o = make_plan(c.d_model, c.d_model, qd, m->kstep, rows);
+  m->p_gu = make_plan(c.ffn_dim, 2 * c.ffn_dim, c.d_model, m->kstep, rows / 2);
+  m->p_down = make_plan(c.d_model, c.d_model, c.ffn_dim, m->kstep, rows);
+  m->p_head = make_plan(c.vocab, c.vocab, c.d_model, m->kstep, rows);
+  *out = m;
+  return CBD_OK;
+}
+
+void cbd_model_destroy(cbd_model* m) {
+  if (!m) return;
+  for (int i = 0; i < NSLOT; ++i) {
+    if (m->ev[i]) {
+      (void)hipEventSynchronize(m->ev[i]);
+      (void)hipEventDestroy(m->ev[i]);
+    }
+    if (m->slot[i]) (void)hipHostFree(m->slot[i]);
+  }
+  delete m;
+}
+
+size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq) {
+  if (!cfg || n_lanes <= 0 || max_seq <= 0 || cfg->n_layers <= 0 || cfg->n_kv_heads <= 0 || cfg->head_dim <= 0)
+    return 0;
+  const size_t kvb = cfg->wtype == CBD_BF16 ? 2 : 4;
+  return 2 * (size_t)n_lanes * cfg->n_layers * cfg->n_kv_heads * (size_t)max_seq * cfg->head_dim * kvb;
+}
+
+int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes, cbd_arena** out) {
+  if (!m || !out || !dev_mem) return fail(CBD_E_ARG, "null argument");
+  if (n_lanes <= 0 || max_seq <= 0) return fail(CBD_E_ARG, "n_lanes and max_seq must be positive");
+  if ((uintptr_t)dev_mem & 255u) return fail(CBD_E_ARG, "arena memory must be 256-byte aligned");
+  const size_t need = cbd_arena_bytes(&m->c, n_lanes, max_seq);
+  if (dev_bytes < need) return fail(CBD_E_ARG, "arena needs %zu bytes, got %zu", need, dev_bytes);
+  cbd_arena* a = new cbd_arena();
+  a->m = m;
+  a->n_lanes = n_lanes;
+  a->max_seq = max_seq;
+  a->base = (char*)dev_mem;
+  a->bytes = dev_bytes;
+  a->lane_stride = (long long)m->c.n_layers * m->c.n_kv_heads * max_seq * m->c.head_dim;
+  a->region_bytes = need / 2;
+  a->live.assign(n_lanes, 0);
+  a->len.assign(n_lanes, 0);
+  *out = a;
+  return CBD_OK;
+}
+
+void cbd_arena_destroy(cbd_arena* a) { delete a; }
+
+int cbd_lane_alloc(cbd_arena* a, int* lane) {
+  if (!a || !lane) return fail(CBD_E_ARG, "null argument");
+  for (int i = 0; i < a->n_lanes; ++i)
+    if (!a->live[i]) {
+      a->live[i] = 1;
+      a->len[i] = 0;
+      *lane = i;
+      return CBD_OK;
+    }
+  return fail(CBD_E_NO_FREE_LANE, "all %d lanes are live", a->n_lanes);
+}
+
+static int check_lane(const cbd_arena* a, int lane) {
+  if (!a) return fail(CBD_E_ARG, "null arena");
+  if (lane < 0 || lane >= a->n_lanes) return fail(CBD_E_ARG, "lane %d outside [0, %d)", lane, a->n_lanes);
+  if (!a->live[lane]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", lane);
+  return CBD_OK;
+}
+
+int cbd_lane_clear(cbd_arena* a, int lane) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  a->len[lane] = 0;
+  return CBD_OK;
+}
+
+int cbd_lane_evict(cbd_arena* a, int lane) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  a->live[lane] = 0;
+  a->len[lane] = 0;
+  return CBD_OK;
+}
+
+int cbd_lane_length(const cbd_arena* a, int lane) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  return a->len[lane];
+}
+
+size_t cbd_arena_used_bytes(const cbd_arena* a) {
+  if (!a) return 0;
+  const cbd_config& c = a->m->c;
+  const size_t per_tok = 2 * (size_t)c.n_layers * c.n_kv_heads * c.head_dim * a->m->kvb;
+  size_t n = 0;
+  for (int i = 0; i < a->n_lanes; ++i)
+    if (a->live[i]) n += (size_t)a->len[i] * per_tok;
+  return n;
+}
+
+int cbd_arena_live_lanes(const cbd_arena* a) {
+  if (!a) return 0;
+  int n = 0;
+  for (uint8_t v : a->live) n += v;
+  return n;
+}
+
+size_t cbd_workspace_bytes(const cbd_model* m, int max_batch, int max_seq) {
+  if (!m || max_batch <= 0 || max_seq <= 0) return 0;
+  return layout(m, max_batch, max_seq).total;
+}
+
+int cbd_set_variant(cbd_model* m, int variant) {
+  if (!m || variant < 0 || variant > 1) return fail(CBD_E_ARG, "variant must be 0 or 1");
+  m->variant = variant;
+  return CBD_OK;
+}
+
+static int run_gemm(cbd_model* m, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
+                    void* act_out, char* ws, const WsLayout& L, hipStream_t st) {
+  GemmArgs g{};
+  g.W = W.data;
+  g.Ws = (const uint16_t*)W.scale;
+  g.X = X;
+  g.N = p.N;
+  g.Nraw = p.Nraw;
+  g.K = p.K;
+  g.B = B;
+  g.S = p.S;
+  g.Ks = p.Ks;
+  g.nRB = p.nRB;
+  const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  g.nCG = (B + TILE * C - 1) / (TILE * C);
+  g.out = out;
+  g.act_out = act_out;
+  g.part = (float*)(ws + L.part);
+  g.cnt = (unsigned*)(ws + L.cnt_gemm);
+  g.amax = (float2*)(ws + L.amax);
+  const int n_waves = g.nRB * g.S * g.nCG;
+  HIP_TRY(launch_gemm(m->wt, epi, C, g, n_waves, st));
+  return CBD_OK;
+}
+
+int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!m || !a || !lanes || !positions || !tokens || !logits) return fail(CBD_E_ARG, "null argument");
+  if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
+  if (B < 1) return fail(CBD_E_ARG, "B = %d < 1", B);
+  const cbd_config& c = m->c;
+  // lanes: range, liveness, distinctness; positions; tokens
+  std::vector<uint8_t> seen(a->n_lanes, 0);
+  for (int b = 0; b < B; ++b) {
+    const int ln = lanes[b];
+    if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", b, ln, a->n_lanes);
+    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
+    seen[ln] = 1;
+    if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
+    if (positions[b] != a->len[ln])
+      return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", b, positions[b], ln,
+                  a->len[ln]);
+    if (positions[b] >= a->max_seq)
+      return fail(CBD_E_KV_FULL, "lane %d is full (%d of %d slots)", ln, positions[b], a->max_seq);
+    if (tokens[b] < 0 || tokens[b] >= c.vocab)
+      return fail(CBD_E_TOKEN, "tokens[%d] = %d outside [0, %d)", b, tokens[b], c.vocab);
+  }
+  if (!workspace) return fail(CBD_E_WORKSPACE, "null workspace");
+  if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
+  if (maxB < B)
+    return fail(CBD_E_WORKSPACE, "workspace of %zu bytes holds %d lanes, step has %d (need %zu)", workspace_bytes,
+                maxB, B, cbd_workspace_bytes(m, B, a->max_seq));
+  const WsLayout L = layout(m, maxB, a->max_seq);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  // Counters must be zero; every kernel that uses them leaves them zero.
+  if (m->ws_ready != workspace || m->ws_ready_bytes != workspace_bytes || m->ws_ready_seq != a->max_seq) {
+    HIP_TRY(launch_fill_u32((unsigned*)(ws + L.cnt_gemm), (L.cnt_attn - L.cnt_gemm) / 4 + L.n_cnt_attn, 0u, st));
+    m->ws_ready = workspace;
+    m->ws_ready_bytes = workspace_bytes;
+    m->ws_ready_seq = a->max_seq;
+  }
+
+  // Per-step metadata: lanes, positions, tokens, attention work items (b, split).
+  std::vector<int32_t> meta;
+  meta.reserve((size_t)3 * B + 2 * (size_t)B * L.MS);
+  meta.insert(meta.end(), lanes, lanes + B);
+  meta.insert(meta.end(), positions, positions + B);
+  meta.insert(meta.end(), tokens, tokens + B);
+  int n_items = 0;
+  for (int b = 0; b < B; ++b) {
+    const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
+    for (int s = 0; s < ns; ++s) {
+      meta.push_back(b);
+      meta.push_back(s);
+      ++n_items;
+    }
+  }
+  const size_t meta_bytes = meta.size() * 4;
+  const int si = m->next_slot;
+  m->next_slot = (si + 1) % NSLOT;
+  if (m->ev_live[si]) HIP_TRY(hipEventSynchronize(m->ev[si]));
+  if (m->slot_bytes[si] < meta_bytes) {
+    if (m->slot[si]) HIP_TRY(hipHostFree(m->slot[si]));
+    m->slot[si] = nullptr;
+    m->slot_bytes[si] = 0;
+    const size_t cap = std::max(meta_bytes, (size_t)65536);
+    HIP_TRY(hipHostMalloc(&m->slot[si], cap, hipHostMallocDefault));
+    m->slot_bytes[si] = cap;
+  }
+  if (!m->ev[si]) HIP_TRY(hipEventCreateWithFlags(&m->ev[si], hipEventDisableTiming));
+  memcpy(m->slot[si], meta.data(), meta_bytes);
+  int32_t* dmeta = (int32_t*)(ws + L.meta);
+  HIP_TRY(hipMemcpyAsync(dmeta, m->slot[si], meta_bytes, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(m->ev[si], st));
+  m->ev_live[si] = true;
+  const int* d_lanes = dmeta;
+  const int* d_pos = dmeta + B;
+  const int* d_tok = dmeta + 2 * B;
+  const int* d_items = dmeta + 3 * B;
+
+  float* x = (float*)(ws + L.x);
+  void* xn = ws + L.xn;
+  float* qkv = (float*)(ws + L.qkv);
+  void* o = ws + L.o;
+  void* act = ws + L.a;
+  float2* rope = (float2*)(ws + L.rope);
+  const int d = c.d_model;
+
+  HIP_TRY(launch_embed_norm(m->wt, m->embed.data, (const uint16_t*)m->embed.scale, d_tok, d_pos, B, d, c.head_dim,
+                            c.rope_theta, c.rms_eps, m->attn_norm[0], x, xn, rope, st));
+  AttnArgs at{};
+  at.qkv = qkv;
+  at.kslab = a->base;
+  at.vslab = a->base + a->region_bytes;
+  at.lane_stride = a->lane_stride;
+  at.max_seq = a->max_seq;
+  at.B = B;
+  at.lanes = d_lanes;
+  at.pos = d_pos;
+  at.items = d_items;
+  at.n_items = n_items;
+  at.max_splits = L.MS;
+  at.Hq = c.n_heads;
+  at.Hkv = c.n_kv_heads;
+  at.G = m->G;
+  at.Nqkv = m->n_qkv;
+  at.rope = rope;
+  at.part = (float*)(ws + L.apart);
+  at.cnt = (unsigned*)(ws + L.cnt_attn);
+  at.out = o;
+  int rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    if ((rc = run_gemm(m, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
+    at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
+    HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
+    if ((rc = run_gemm(m, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
+    HIP_TRY(launch_rmsnorm(m->wt, x, m->ffn_norm[l], B, d, c.rms_eps, xn, st));
+    if ((rc = run_gemm(m, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
+    if ((rc = run_gemm(m, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
+    const float* g_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
+    HIP_TRY(launch_rmsnorm(m->wt, x, g_next, B, d, c.rms_eps, xn, st));
+  }
+  if ((rc = run_gemm(m, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
+  if (argmax) HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+
+  for (int b = 0; b < B; ++b) {
+    positions[b] += 1;
+    a->len[lanes[b]] += 1;
+  }
+  return CBD_OK;
+}
+
+int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int32_t token, float* logits,
+                    int32_t* argmax, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!position) return fail(CBD_E_ARG, "null position");
+  const int32_t ln = lane, tok = token;
+  return cbd_decode_step_batch(m, a, 1, &ln, position, &tok, logits, argmax, workspace, workspace_bytes, stream);
+}
+
+int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  if (!k_dst || !v_dst) return fail(CBD_E_ARG, "null destination");
+  const cbd_config& c = a->m->c;
+  const int len = a->len[lane];
+  hipStream_t st = (hipStream_t)stream;
+  if (len > 0) {
+    const size_t kvb = a->m->kvb;
+    const size_t width = (size_t)len * c.head_dim * kvb;
+    const size_t spitch = (size_t)a->max_seq * c.head_dim * kvb;
+    const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
+    const size_t off = (size_t)lane * a->lane_stride * kvb;
+    HIP_TRY(hipMemcpy2DAsync(k_dst, width, a->base + off, spitch, width, rows, hipMemcpyDefault, st));
+    HIP_TRY(hipMemcpy2DAsync(v_dst, width, a->base + a->region_bytes + off, spitch, width, rows, hipMemcpyDefault,
+                             st));
+  }
+  HIP_TRY(hipStreamSynchronize(st));
+  return CBD_OK;
+}
+
+int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, const void* v_src, void* stream) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  if (length < 0) return fail(CBD_E_ARG, "negative length");
+  if (length > a->max_seq) return fail(CBD_E_KV_FULL, "length %d exceeds max_seq %d", length, a->max_seq);
+  if (length > 0 && (!k_src || !v_src)) return fail(CBD_E_ARG, "null source");
+  const cbd_config& c = a->m->c;
+  hipStream_t st = (hipStream_t)stream;
+  if (length > 0) {
+    const size_t kvb = a->m->kvb;
+    const size_t width = (size_t)length * c.head_dim * kvb;
+    const size_t dpitch = (size_t)a->max_seq * c.head_dim * kvb;
+    const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
+    const size_t off = (size_t)lane * a->lane_stride * kvb;
+    HIP_TRY(hipMemcpy2DAsync(a->base + off, dpitch, k_src, width, width, rows, hipMemcpyDefault, st));
+    HIP_TRY(hipMemcpy2DAsync(a->base + a->region_bytes + off, dpitch, v_src, width, width, rows, hipMemcpyDefault,
+                             st));
+  }
+  HIP_TRY(hipStreamSynchronize(st));
+  a->len[lane] = length;
+  return CBD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,197 @@
+/*
+ * cbd — the batched decode step of a dense Llama decoder on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * One call of cbd_decode_step_batch advances B independent sequences
+ * ("lanes") by one token each.  The operation is the multi-user batched
+ * decode of "MODEL-BATCHING-RESULTS — multi-user batched decode, measured"
+ * (section "The lever"): one decode token per user is stacked into a [B, d]
+ * panel, each of the seven projections (q, k, v, o, gate, up, down) and the
+ * LM head runs once over that panel so every weight byte is read once for the
+ * whole batch, and attention stays per user over that user's own KV cache and
+ * length, with no mixing between users.  Its interface follows the primitive
+ * of "Fat-station continuous batching" (section "The capture"): per-lane KV
+ * caches, per-lane positions and one input token per lane in, logits for every
+ * lane out, positions advanced.  Lanes live in a fixed arena allocated once at
+ * capacity and bounded by a maximum sequence length (same page, "Components",
+ * items 1 and 4); a lane is cleared for reuse by the next job and released
+ * when its job completes, after which its KV usage is zero ("DGR-012",
+ * section "Summary", bounded memory).
+ *
+ * Conventions
+ *  - All functions return 0 (CBD_OK) on success or a negative CBD_E_* code;
+ *    cbd_last_error() gives a message for the calling thread's last failure.
+ *  - Every check runs on the host before any GPU work is enqueued, so a call
+ *    that fails changes nothing (arena, positions and device memory untouched).
+ *  - Device pointers are plain HIP device addresses (e.g. a torch tensor's
+ *    data_ptr()).  The caller owns all device memory: weights, the arena, the
+ *    workspace and the outputs.  The library borrows it and never frees it.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Steps are asynchronous on that stream; results are valid once it syncs.
+ *  - One host thread drives a given model and arena at a time.
+ *
+ * Number formats: f32 is IEEE binary32; bf16 is the upper 16 bits of a
+ * binary32 (round to nearest even when produced); Q8_0 stores a weight matrix
+ * [N, K] as two planes: int8 q [N, K] and binary16 scales [N, K/32], one per
+ * block of 32 consecutive elements along K, value = q * scale.
+ */
+#ifndef CBD_H
+#define CBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CBD_OK 0
+#define CBD_E_ARG (-1)           /* bad argument: null pointer, size or config out of range */
+#define CBD_E_DUP_LANE (-2)      /* the same lane appears twice in one step */
+#define CBD_E_LANE_NOT_LIVE (-3) /* lane not allocated, or already evicted (a cache miss) */
+#define CBD_E_POS_MISMATCH (-4)  /* positions[b] differs from the lane's KV length */
+#define CBD_E_KV_FULL (-5)       /* positions[b] == max_seq: no slot left in the lane */
+#define CBD_E_TOKEN (-6)         /* token id outside [0, vocab) */
+#define CBD_E_NO_FREE_LANE (-7)  /* every lane of the arena is live */
+#define CBD_E_HIP (-8)           /* a HIP runtime call failed */
+#define CBD_E_WORKSPACE (-9)     /* workspace null or smaller than cbd_workspace_bytes() */
+#define CBD_E_UNSUPPORTED (-10)  /* model shape outside what the kernels are built for */
+
+/* Weight storage type; also fixes the activation and KV formats:
+ *  CBD_F32  - f32 weights, f32 projection inputs, f32 KV.
+ *  CBD_BF16 - bf16 weights, bf16 projection inputs and KV, f32 accumulation,
+ *             f32 residual stream, norm statistics, softmax and logits.
+ *  CBD_Q8_0 - Q8_0 weights, binary16 projection inputs, f32 KV.            */
+typedef enum { CBD_F32 = 0, CBD_BF16 = 1, CBD_Q8_0 = 2 } cbd_wtype;
+
+/* Model shape.  Requirements: n_heads % n_kv_heads == 0 and
+ * n_heads / n_kv_heads <= 8; head_dim in {16, 32, 64, 128}; d_model and
+ * ffn_dim multiples of 4 (f32), 8 (bf16) or 32 (Q8_0); n_heads*head_dim a
+ * multiple of the same. */
+typedef struct {
+  int d_model, n_layers, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps;    /* RMSNorm epsilon, e.g. 1e-5 */
+  float rope_theta; /* rotary base, e.g. 10000 */
+  int tied_embeddings; /* nonzero: the LM head is the embedding matrix */
+  int wtype;           /* cbd_wtype */
+} cbd_config;
+
+/* One weight matrix [N, K], row-major, K contiguous, rows 16-byte aligned.
+ * data: f32, bf16 or int8 (Q8_0) device pointer; scale: binary16 [N, K/32]
+ * device pointer for Q8_0, NULL otherwise. */
+typedef struct {
+  const void* data;
+  const void* scale;
+} cbd_matrix;
+
+/* Weights (device memory, borrowed for the model's lifetime).  The pointer
+ * arrays themselves are host arrays of n_layers entries, copied at create.
+ *  embed      [vocab, d]
+ *  lm_head    [vocab, d] (ignored when tied_embeddings)
+ *  final_norm, attn_norm[l], ffn_norm[l]  f32 [d] RMSNorm gains
+ *  w_qkv[l]   [(n_heads + 2 n_kv_heads) * head_dim, d]: query rows, key rows, value rows
+ *  w_o[l]     [d, n_heads * head_dim]
+ *  w_gu[l]    [2 ffn, d]: gate rows, then up rows
+ *  w_down[l]  [d, ffn]                                                        */
+typedef struct {
+  cbd_matrix embed;
+  cbd_matrix lm_head;
+  const float* final_norm;
+  const float* const* attn_norm;
+  const float* const* ffn_norm;
+  const cbd_matrix* w_qkv;
+  const cbd_matrix* w_o;
+  const cbd_matrix* w_gu;
+  const cbd_matrix* w_down;
+} cbd_weights;
+
+typedef struct cbd_model cbd_model;
+typedef struct cbd_arena cbd_arena;
+
+/* Library version string. */
+const char* cbd_version(void);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* cbd_last_error(void);
+
+/* Validate the shape, copy the config and the weight pointer arrays.  No GPU
+ * work happens here.  Errors: CBD_E_ARG (null or inconsistent), CBD_E_UNSUPPORTED. */
+int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** out);
+void cbd_model_destroy(cbd_model* m);
+
+/* Device bytes an arena of n_lanes lanes of max_seq positions needs:
+ * K and V slabs [n_lanes][n_layers][n_kv_heads][max_seq][head_dim] each, in
+ * the KV format of the model's wtype.  Returns 0 for invalid arguments. */
+size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq);
+
+/* Create a lane arena over caller-owned device memory dev_mem of dev_bytes
+ * (>= cbd_arena_bytes) bytes, 256-byte aligned.  All lanes start free.
+ * Errors: CBD_E_ARG. */
+int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes,
+                     cbd_arena** out);
+void cbd_arena_destroy(cbd_arena* a);
+
+/* Reserve the lowest free lane; its length is 0.  Errors: CBD_E_NO_FREE_LANE. */
+int cbd_lane_alloc(cbd_arena* a, int* lane);
+/* Length := 0, reservation kept (reuse by the next job).  Errors: CBD_E_ARG,
+ * CBD_E_LANE_NOT_LIVE. */
+int cbd_lane_clear(cbd_arena* a, int lane);
+/* Release the lane: its usage drops to zero, and stepping it is an error
+ * until it is allocated again.  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE. */
+int cbd_lane_evict(cbd_arena* a, int lane);
+/* KV length of a live lane (>= 0), or a negative error code. */
+int cbd_lane_length(const cbd_arena* a, int lane);
+/* Sum over live lanes of length * KV bytes per token (all layers, K and V). */
+size_t cbd_arena_used_bytes(const cbd_arena* a);
+/* Number of live lanes. */
+int cbd_arena_live_lanes(const cbd_arena* a);
+
+/* Device bytes of the workspace a step of up to max_batch lanes of an arena
+ * of max_seq positions needs (activations, split partials, counters,
+ * per-step metadata).  Returns 0 for invalid arguments. */
+size_t cbd_workspace_bytes(const cbd_model* m, int max_batch, int max_seq);
+
+/* One decode step over B lanes (1 <= B <= the max_batch the workspace was
+ * sized for).  Host inputs: lanes[B] (distinct live lanes), positions[B]
+ * (in/out: must equal each lane's KV length on entry; each is incremented on
+ * success), tokens[B] (ids in [0, vocab)).  Device outputs: logits [B, vocab]
+ * f32 (required) and argmax [B] int32 (optional, NULL to skip; lowest index
+ * wins ties).  Lane b's token is embedded, written into the lane's KV slot
+ * positions[b] of every layer, attends over slots [0, positions[b]] of its own
+ * lane only, and its logits land in row b.  workspace: device memory of
+ * workspace_bytes >= cbd_workspace_bytes(m, B, arena max_seq), used by one
+ * model at a time; the library keeps counters in it that it clears on first
+ * use of each workspace address.
+ * Errors: CBD_E_ARG, CBD_E_DUP_LANE, CBD_E_LANE_NOT_LIVE, CBD_E_POS_MISMATCH,
+ * CBD_E_KV_FULL, CBD_E_TOKEN, CBD_E_WORKSPACE, CBD_E_HIP. */
+int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* The same step for one lane (B = 1): position in/out, logits [vocab]. */
+int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int32_t token, float* logits,
+                    int32_t* argmax, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Copy a live lane's KV out: k_dst, v_dst (host or device, hipMemcpy default
+ * kind) receive [n_layers][n_kv_heads][length][head_dim] in the KV format.
+ * Synchronous with respect to `stream`.  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE,
+ * CBD_E_HIP. */
+int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream);
+
+/* Load a live lane's KV from k_src, v_src laid out as in export, with
+ * `length` positions (<= max_seq), and set its length.  Keys are taken as
+ * already rotated.  Synchronous with respect to `stream`.
+ * Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL, CBD_E_HIP. */
+int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, const void* v_src, void* stream);
+
+/* Projection kernel family for steps of this model: 0 = automatic by batch
+ * width, 1 = weight-streaming split-K tiles at every width.  Every family
+ * computes each output with the same chunked reduction, so the choice changes
+ * speed only, never a bit of the result.  Errors: CBD_E_ARG. */
+int cbd_set_variant(cbd_model* m, int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBD_H */

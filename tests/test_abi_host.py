@@ -1,0 +1,170 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/cbd.h
+declares, validates models, arenas and steps, and keeps lane accounting —
+without any GPU call (fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import continuous_batching_decode_step_amd as cbd
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(cbd.LIB_PATH):
+        from continuous_batching_decode_step_amd import build
+        build.build()
+    cbd.lib()
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "cbd.h")).read()
+    declared = set(re.findall(r"\b(cbd_[a-z0-9_]+)\s*\(", hdr))
+    assert declared == set(cbd.SYMBOLS)
+    L = cbd.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert cbd.lib().cbd_version().decode().startswith("cbd")
+
+
+FAKE = 1 << 24  # a 256-byte aligned address that is never dereferenced on the host
+
+
+def fake_weights(cfg):
+    fm = lambda: cbd.DeviceMatrix(FAKE, FAKE if cfg.wtype == synth.WTYPE_Q8_0 else None)
+    L = cfg.n_layers
+    return cbd.DeviceWeights(embed=fm(), lm_head=None if cfg.tied else fm(), final_norm=FAKE,
+                             attn_norm=[FAKE] * L, ffn_norm=[FAKE] * L, w_qkv=[fm() for _ in range(L)],
+                             w_o=[fm() for _ in range(L)], w_gu=[fm() for _ in range(L)],
+                             w_down=[fm() for _ in range(L)])
+
+
+class _P:  # DeviceMatrix holding raw ints
+    pass
+
+
+def test_model_create_validates_shapes():
+    for cfg in (synth.TINY, synth.SMOL135M, synth.SMOL135M_Q8, synth.MISTRAL7B):
+        m = cbd.Model(cfg, fake_weights(cfg))
+        m.close()
+    from dataclasses import replace
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Model(replace(synth.TINY, head_dim=24), fake_weights(synth.TINY))
+    assert e.value.name == "CBD_E_UNSUPPORTED"
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Model(replace(synth.TINY, n_kv_heads=3), fake_weights(synth.TINY))
+    assert e.value.name == "CBD_E_UNSUPPORTED"
+    with pytest.raises(cbd.CbdError) as e:  # Q8_0 needs K % 32 == 0 (ffn 172)
+        cbd.Model(synth.TINY.with_wtype(synth.WTYPE_Q8_0), fake_weights(synth.TINY.with_wtype(synth.WTYPE_Q8_0)))
+    assert e.value.name == "CBD_E_UNSUPPORTED"
+    w = fake_weights(synth.TINY)
+    w.w_o[1] = cbd.DeviceMatrix(FAKE + 8)  # misaligned rows
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Model(synth.TINY, w)
+    assert e.value.name == "CBD_E_ARG"
+    wq = fake_weights(synth.SMOL135M_Q8)
+    wq.w_gu[0] = cbd.DeviceMatrix(FAKE, None)  # Q8_0 without scales
+    with pytest.raises(cbd.CbdError):
+        cbd.Model(synth.SMOL135M_Q8, wq)
+
+
+def test_arena_bytes_per_token():
+    # K and V, every layer and KV head: 2 * L * Hkv * hd * bytes per token per lane
+    assert cbd.arena_bytes(synth.MISTRAL7B, 1, 1) == 131072
+    assert cbd.arena_bytes(synth.SMOL135M, 1, 1) == 46080
+    assert cbd.arena_bytes(synth.TINY, 3, 10) == 3 * 10 * 1024
+    assert cbd.arena_bytes(synth.TINY, 0, 10) == 0
+
+
+def make_model_arena(cfg=synth.TINY, n_lanes=4, max_seq=8):
+    m = cbd.Model(cfg, fake_weights(cfg))
+    a = cbd.Arena(m, n_lanes, max_seq, FAKE, cbd.arena_bytes(cfg, n_lanes, max_seq))
+    return m, a
+
+
+def test_lane_alloc_clear_evict_and_usage_returns_to_zero():
+    m, a = make_model_arena()
+    lanes = [a.lane_alloc() for _ in range(4)]
+    assert lanes == [0, 1, 2, 3] and a.live_lanes == 4
+    with pytest.raises(cbd.CbdError) as e:
+        a.lane_alloc()
+    assert e.value.name == "CBD_E_NO_FREE_LANE"
+    assert a.used_bytes == 0
+    a.lane_evict(2)
+    with pytest.raises(cbd.CbdError) as e:
+        a.lane_length(2)
+    assert e.value.name == "CBD_E_LANE_NOT_LIVE"
+    with pytest.raises(cbd.CbdError) as e:
+        a.lane_clear(2)
+    assert e.value.name == "CBD_E_LANE_NOT_LIVE"
+    assert a.lane_alloc() == 2  # lowest free lane is reused
+    for l in lanes:
+        a.lane_evict(l)
+    assert a.live_lanes == 0 and a.used_bytes == 0
+    with pytest.raises(cbd.CbdError) as e:
+        a.lane_evict(9)
+    assert e.value.name == "CBD_E_ARG"
+
+
+def test_arena_create_rejects_small_or_misaligned_memory():
+    m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
+    need = cbd.arena_bytes(synth.TINY, 2, 8)
+    with pytest.raises(cbd.CbdError):
+        cbd.Arena(m, 2, 8, FAKE, need - 1)
+    with pytest.raises(cbd.CbdError):
+        cbd.Arena(m, 2, 8, FAKE + 64, need)
+
+
+def step_err(m, a, lanes, pos, toks, ws=FAKE, wsb=None, logits=FAKE):
+    pos = np.array(pos, np.int32)
+    before = pos.copy()
+    lens = {l: a.lane_length(l) for l in range(a.n_lanes) if _live(a, l)}
+    wsb = m.workspace_bytes(max(1, len(lanes)), a.max_seq) if wsb is None else wsb
+    with pytest.raises(cbd.CbdError) as e:
+        m.decode_step_batch(a, lanes, pos, toks, logits, None, ws, wsb, stream=0)
+    # a failed call changes nothing
+    assert np.array_equal(pos, before)
+    assert lens == {l: a.lane_length(l) for l in range(a.n_lanes) if _live(a, l)}
+    return e.value.name
+
+
+def _live(a, l):
+    try:
+        a.lane_length(l)
+        return True
+    except cbd.CbdError:
+        return False
+
+
+def test_step_validation_errors_change_nothing():
+    m, a = make_model_arena()
+    l0, l1, l2 = a.lane_alloc(), a.lane_alloc(), a.lane_alloc()
+    a.lane_evict(l2)
+    assert step_err(m, a, [l0, l0], [0, 0], [1, 2]) == "CBD_E_DUP_LANE"
+    assert step_err(m, a, [l0, l2], [0, 0], [1, 2]) == "CBD_E_LANE_NOT_LIVE"
+    assert step_err(m, a, [l0, 7], [0, 0], [1, 2]) == "CBD_E_ARG"
+    assert step_err(m, a, [l0, l1], [0, 1], [1, 2]) == "CBD_E_POS_MISMATCH"
+    assert step_err(m, a, [l0, l1], [0, 0], [1, 256]) == "CBD_E_TOKEN"
+    assert step_err(m, a, [l0, l1], [0, 0], [-1, 2]) == "CBD_E_TOKEN"
+    assert step_err(m, a, [], [], []) == "CBD_E_ARG"
+    assert step_err(m, a, [l0, l1], [0, 0], [1, 2], ws=0) == "CBD_E_WORKSPACE"
+    small = m.workspace_bytes(1, a.max_seq)
+    assert step_err(m, a, [l0, l1], [0, 0], [1, 2], wsb=small) == "CBD_E_WORKSPACE"
+    assert step_err(m, a, [l0, l1], [0, 0], [1, 2], logits=0) == "CBD_E_ARG"
+
+
+def test_workspace_grows_with_batch_and_context():
+    m = cbd.Model(synth.MISTRAL7B, fake_weights(synth.MISTRAL7B))
+    w1 = m.workspace_bytes(1, 4097)
+    w8 = m.workspace_bytes(8, 4097)
+    assert 0 < w1 < w8 < m.workspace_bytes(64, 4097)
+    assert m.workspace_bytes(8, 512) < w8
+    assert m.workspace_bytes(0, 10) == 0
+    with pytest.raises(cbd.CbdError):
+        m.set_variant(5)
+    m.set_variant(1)

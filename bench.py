@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched decode step on one MI355X: aggregate decode tokens/s
+versus batch width B, with the step's and the dominant kernel's fraction of
+the HBM roofline, and the CPU oracle timed beside it.
+
+Workload (default): the Mistral-7B shape in bf16 (d=4096, 32 layers, 32 query
+/ 8 KV heads of 128, FFN 14336, vocab 32000) with seeded synthetic weights
+N(0, 0.02); 64 lanes whose KV lengths are uniform in [128, 4096] (seed 2),
+holding synthetic post-rotary K/V ~ N(0, 1) (seed 3); one decode step over the
+first B lanes, one new token per lane (seed 1).  Each timed step rewrites the
+same slot of every lane (the lanes are rolled back to their lengths before
+each step), so every step does the same work.  Inputs are resident in HBM
+before timing starts.
+
+Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batches", default="1,2,4,8,16,32,64", help="B sweep; the last is the headline B")
+    ap.add_argument("--lanes", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import continuous_batching_decode_step_amd as cbd
+    from continuous_batching_decode_step_amd import roofline as rf
+    from continuous_batching_decode_step_amd.driver import Engine
+
+    cbd.lib()  # fail loudly if the HIP library is missing
+    cfg = synth.MISTRAL7B
+    batches = [int(x) for x in args.batches.split(",")]
+    n_lanes = max(args.lanes, max(batches))
+    t0 = time.time()
+    W = synth.make_weights(cfg)
+    log("weights generated in %.1fs" % (time.time() - t0))
+    dw = cbd.upload_weights(W)
+    lens = synth.kv_lengths(n_lanes)  # U[128, 4096]
+    toks = synth.step_tokens(cfg, n_lanes)
+    max_seq = int(lens.max()) + 1
+    eng = Engine(cfg, dw, n_lanes, max_seq, max_batch=max(batches))
+    lanes = [eng.arena.lane_alloc() for _ in range(n_lanes)]
+    keep_kv = {}
+    t0 = time.time()
+    for b in range(n_lanes):
+        k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
+        eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
+        if b < 8 and not args.no_cpu_baseline:
+            keep_kv[b] = (k, v)
+    torch.cuda.synchronize()
+    log("KV of %d lanes generated and loaded in %.1fs" % (n_lanes, time.time() - t0))
+
+    def step(B):
+        for b in range(B):
+            eng.arena.lane_truncate(lanes[b], int(lens[b]))
+        pos = lens[:B].astype(np.int32).copy()
+        eng.step(lanes[:B], pos, toks[:B])
+
+    stream = torch.cuda.current_stream()
+    sweep = []
+    headline = None
+    for B in batches:
+        for _ in range(args.warmup):
+            step(B)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step(B)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms = e0.elapsed_time(e1) / args.steps
+        pos = [int(x) for x in lens[:B]]
+        t_roof = rf.roofline_time_s(cfg, pos)
+        # per-kernel durations: a second pass with events around every launch
+        eng.model.profile_reset()
+        eng.model.profile_enable(True)
+        for _ in range(args.steps):
+            step(B)
+        torch.cuda.synchronize()
+        prof = eng.model.profile_read()
+        eng.model.profile_enable(False)
+        per = rf.per_class_summary(cfg, prof, pos)
+        row = {"B": B, "tok_s": B / (ms * 1e-3), "ms_per_step": ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+               "step_alg_GB": rf.step_bytes(cfg, pos) / 1e9, "roofline_tok_s": B / t_roof,
+               "roofline_frac": t_roof / (ms * 1e-3),
+               "kernels": {k: {"avg_us": round(v["avg_us"], 2), "share": round(v["total_ms"] / max(
+                   1e-9, sum(x["total_ms"] for x in per.values())), 4),
+                   "GBs": None if v["achieved_GBs"] is None else round(v["achieved_GBs"], 1)}
+                   for k, v in per.items()}}
+        sweep.append(row)
+        log("B=%3d  %8.1f tok/s  %.3f ms/step  roofline %.3f  %s" % (
+            B, row["tok_s"], ms, row["roofline_frac"],
+            " ".join("%s=%.1fus/%sGB/s" % (k, v["avg_us"], v["GBs"]) for k, v in row["kernels"].items())))
+        headline = (B, ms, per, pos)
+
+    B, ms, per, pos = headline
+    dom = max((k for k in per if per[k]["alg_bytes"] > 0), key=lambda k: per[k]["total_ms"])
+    d = per[dom]
+    achieved = d["achieved_GBs"]
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / rf.HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+            "alg_bytes_per_launch": d["alg_bytes"], "avg_launch_us": round(d["avg_us"], 2),
+            "launches": d["launches"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        M = oracle.Model(W)
+        done, t_cpu = 0, 0.0
+        for b in sorted(keep_kv):
+            k, v = keep_kv[b]
+            lane = M.lane(int(lens[b]) + 1)
+            lane.set_kv(synth.bf16_to_f32(k), synth.bf16_to_f32(v))
+            t1 = time.perf_counter()
+            M.step(lane, int(toks[b]))
+            t_cpu += time.perf_counter() - t1
+            done += 1
+            del lane
+            if t_cpu >= args.cpu_seconds:
+                break
+        cpu = {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d lane-steps of the same workload (lanes 0..%d at their KV lengths, one decode step "
+                         "each, serial f32 oracle on bf16 weights), %.1f s" % (done, done - 1, t_cpu)}
+        log("cpu oracle: %s" % cpu)
+
+    out = {
+        "metric": "aggregate decode tokens/s vs batch B; % HBM roofline",
+        "value": round(B / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mistral-7b-shape bf16 decode step, ragged KV lengths U[128,4096] (seed 2), "
+                               "one token per lane", "batch": B, "lanes": n_lanes, "d": cfg.d,
+                   "layers": cfg.n_layers, "heads": "%d/%d" % (cfg.n_heads, cfg.n_kv_heads),
+                   "head_dim": cfg.head_dim, "ffn": cfg.ffn, "vocab": cfg.vocab,
+                   "mean_kv_len": float(np.mean(lens[:B])), "parallelism": "single GPU"},
+        "step_roofline_frac": round(sweep[-1]["roofline_frac"], 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -29,6 +29,8 @@ SYMBOLS = [
     "cbd_arena_create", "cbd_arena_destroy", "cbd_lane_alloc", "cbd_lane_clear", "cbd_lane_evict",
     "cbd_lane_length", "cbd_arena_used_bytes", "cbd_arena_live_lanes", "cbd_workspace_bytes",
     "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
+    "cbd_lane_truncate", "cbd_profile_enable", "cbd_profile_reset", "cbd_profile_read", "cbd_profile_classes",
+    "cbd_profile_class_name",
 ]
 
 
@@ -94,6 +96,13 @@ def lib():
         L.cbd_lane_kv_export.argtypes = [vp, i32, vp, vp, vp]
         L.cbd_lane_kv_import.argtypes = [vp, i32, i32, vp, vp, vp]
         L.cbd_set_variant.argtypes = [vp, i32]
+        L.cbd_lane_truncate.argtypes = [vp, i32, i32]
+        L.cbd_profile_enable.argtypes = [vp, i32]
+        L.cbd_profile_reset.argtypes = [vp]
+        L.cbd_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)]
+        L.cbd_profile_classes.argtypes = []
+        L.cbd_profile_class_name.argtypes = [i32]
+        L.cbd_profile_class_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -229,6 +238,21 @@ class Model:
     def set_variant(self, variant: int):
         _check(lib().cbd_set_variant(self.h, variant))
 
+    def profile_enable(self, on: bool = True):
+        _check(lib().cbd_profile_enable(self.h, int(on)))
+
+    def profile_reset(self):
+        _check(lib().cbd_profile_reset(self.h))
+
+    def profile_read(self) -> dict:
+        """{class name: (total ms, launches)} since the last reset."""
+        out = {}
+        for c in range(lib().cbd_profile_classes()):
+            ms, n = ctypes.c_double(), ctypes.c_longlong()
+            _check(lib().cbd_profile_read(self.h, c, ctypes.byref(ms), ctypes.byref(n)))
+            out[lib().cbd_profile_class_name(c).decode()] = (ms.value, n.value)
+        return out
+
     def decode_step_batch(self, arena: "Arena", lanes: Sequence[int], positions: np.ndarray, tokens,
                           logits, argmax=None, workspace=None, workspace_bytes: Optional[int] = None,
                           stream=None) -> None:
@@ -292,6 +316,9 @@ class Arena:
 
     def lane_evict(self, lane: int):
         _check(lib().cbd_lane_evict(self.h, lane))
+
+    def lane_truncate(self, lane: int, length: int):
+        _check(lib().cbd_lane_truncate(self.h, lane, length))
 
     def lane_length(self, lane: int) -> int:
         return _check(lib().cbd_lane_length(self.h, lane))

@@ -85,6 +85,12 @@ struct cbd_model {
   hipEvent_t ev[NSLOT] = {};
   bool ev_live[NSLOT] = {};
   int next_slot = 0;
+  // per-kernel-class timing
+  bool prof = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> pending;
+  double prof_ms[16] = {};
+  long long prof_n[16] = {};
   // the workspace whose counters are known to be zero
   const void* ws_ready = nullptr;
   size_t ws_ready_bytes = 0;
@@ -167,6 +173,59 @@ int check_matrix(const cbd_matrix& mt, int wt, const char* name) {
   return CBD_OK;
 }
 
+const char* const kClassNames[] = {"meta_copy", "embed_norm", "gemm_qkv", "attention", "gemm_o",
+                                   "rmsnorm",   "gemm_gu",    "gemm_down", "gemm_head", "argmax"};
+enum { P_META, P_EMBED, P_QKV, P_ATTN, P_O, P_NORM, P_GU, P_DOWN, P_HEAD, P_ARGMAX, P_N };
+
+hipEvent_t take_event(cbd_model* m) {
+  if (!m->ev_pool.empty()) {
+    hipEvent_t e = m->ev_pool.back();
+    m->ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Fold finished event pairs into the per-class totals (all of them if `all`).
+int drain_profile(cbd_model* m, bool all) {
+  size_t keep_from = 0;
+  const size_t n = m->pending.size();
+  const size_t upto = all ? n : (n > 2048 ? n - 1024 : 0);
+  for (size_t i = 0; i < upto; ++i) {
+    auto& pr = m->pending[i];
+    HIP_TRY(hipEventSynchronize(pr.second.second));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, pr.second.first, pr.second.second));
+    m->prof_ms[pr.first] += ms;
+    m->prof_n[pr.first] += 1;
+    m->ev_pool.push_back(pr.second.first);
+    m->ev_pool.push_back(pr.second.second);
+    keep_from = i + 1;
+  }
+  m->pending.erase(m->pending.begin(), m->pending.begin() + keep_from);
+  return CBD_OK;
+}
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+  cbd_model* m;
+  int cls;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(cbd_model* m_, int cls_, hipStream_t st_) : m(m_), cls(cls_), st(st_) {
+    if (m->prof && (a = take_event(m))) (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEvent_t b = take_event(m);
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    m->pending.push_back({cls, {a, b}});
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +295,8 @@ int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** ou
 
 void cbd_model_destroy(cbd_model* m) {
   if (!m) return;
+  (void)drain_profile(m, true);
+  for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   for (int i = 0; i < NSLOT; ++i) {
     if (m->ev[i]) {
       (void)hipEventSynchronize(m->ev[i]);
@@ -337,13 +398,52 @@ size_t cbd_workspace_bytes(const cbd_model* m, int max_batch, int max_seq) {
   return layout(m, max_batch, max_seq).total;
 }
 
+int cbd_lane_truncate(cbd_arena* a, int lane, int length) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  if (length < 0 || length > a->len[lane])
+    return fail(CBD_E_ARG, "length %d outside [0, %d] for lane %d", length, a->len[lane], lane);
+  a->len[lane] = length;
+  return CBD_OK;
+}
+
+int cbd_profile_enable(cbd_model* m, int enable) {
+  if (!m) return fail(CBD_E_ARG, "null model");
+  m->prof = enable != 0;
+  return CBD_OK;
+}
+
+int cbd_profile_reset(cbd_model* m) {
+  if (!m) return fail(CBD_E_ARG, "null model");
+  int rc = drain_profile(m, true);
+  if (rc) return rc;
+  for (int i = 0; i < 16; ++i) {
+    m->prof_ms[i] = 0.0;
+    m->prof_n[i] = 0;
+  }
+  return CBD_OK;
+}
+
+int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launches) {
+  if (!m || !total_ms || !launches || cls < 0 || cls >= P_N) return fail(CBD_E_ARG, "bad argument");
+  int rc = drain_profile(m, true);
+  if (rc) return rc;
+  *total_ms = m->prof_ms[cls];
+  *launches = m->prof_n[cls];
+  return CBD_OK;
+}
+
+int cbd_profile_classes(void) { return P_N; }
+
+const char* cbd_profile_class_name(int cls) { return cls >= 0 && cls < P_N ? kClassNames[cls] : nullptr; }
+
 int cbd_set_variant(cbd_model* m, int variant) {
   if (!m || variant < 0 || variant > 1) return fail(CBD_E_ARG, "variant must be 0 or 1");
   m->variant = variant;
   return CBD_OK;
 }
 
-static int run_gemm(cbd_model* m, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
+static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
                     void* act_out, char* ws, const WsLayout& L, hipStream_t st) {
   GemmArgs g{};
   g.W = W.data;
@@ -364,6 +464,7 @@ static int run_gemm(cbd_model* m, const Plan& p, int epi, const cbd_matrix& W, c
   g.cnt = (unsigned*)(ws + L.cnt_gemm);
   g.amax = (float2*)(ws + L.amax);
   const int n_waves = g.nRB * g.S * g.nCG;
+  ProfScope ps(m, cls, st);
   HIP_TRY(launch_gemm(m->wt, epi, C, g, n_waves, st));
   return CBD_OK;
 }
@@ -439,7 +540,10 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   if (!m->ev[si]) HIP_TRY(hipEventCreateWithFlags(&m->ev[si], hipEventDisableTiming));
   memcpy(m->slot[si], meta.data(), meta_bytes);
   int32_t* dmeta = (int32_t*)(ws + L.meta);
-  HIP_TRY(hipMemcpyAsync(dmeta, m->slot[si], meta_bytes, hipMemcpyHostToDevice, st));
+  {
+    ProfScope ps(m, P_META, st);
+    HIP_TRY(hipMemcpyAsync(dmeta, m->slot[si], meta_bytes, hipMemcpyHostToDevice, st));
+  }
   HIP_TRY(hipEventRecord(m->ev[si], st));
   m->ev_live[si] = true;
   const int* d_lanes = dmeta;
@@ -455,8 +559,11 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   float2* rope = (float2*)(ws + L.rope);
   const int d = c.d_model;
 
-  HIP_TRY(launch_embed_norm(m->wt, m->embed.data, (const uint16_t*)m->embed.scale, d_tok, d_pos, B, d, c.head_dim,
-                            c.rope_theta, c.rms_eps, m->attn_norm[0], x, xn, rope, st));
+  {
+    ProfScope ps(m, P_EMBED, st);
+    HIP_TRY(launch_embed_norm(m->wt, m->embed.data, (const uint16_t*)m->embed.scale, d_tok, d_pos, B, d, c.head_dim,
+                              c.rope_theta, c.rms_eps, m->attn_norm[0], x, xn, rope, st));
+  }
   AttnArgs at{};
   at.qkv = qkv;
   at.kslab = a->base;
@@ -479,18 +586,31 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   at.out = o;
   int rc;
   for (int l = 0; l < c.n_layers; ++l) {
-    if ((rc = run_gemm(m, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
+    if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
     at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
-    HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
-    if ((rc = run_gemm(m, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
-    HIP_TRY(launch_rmsnorm(m->wt, x, m->ffn_norm[l], B, d, c.rms_eps, xn, st));
-    if ((rc = run_gemm(m, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
-    if ((rc = run_gemm(m, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
+    {
+      ProfScope ps(m, P_ATTN, st);
+      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
+    }
+    if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
+    {
+      ProfScope ps(m, P_NORM, st);
+      HIP_TRY(launch_rmsnorm(m->wt, x, m->ffn_norm[l], B, d, c.rms_eps, xn, st));
+    }
+    if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
+    if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
     const float* g_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
-    HIP_TRY(launch_rmsnorm(m->wt, x, g_next, B, d, c.rms_eps, xn, st));
+    {
+      ProfScope ps(m, P_NORM, st);
+      HIP_TRY(launch_rmsnorm(m->wt, x, g_next, B, d, c.rms_eps, xn, st));
+    }
   }
-  if ((rc = run_gemm(m, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
-  if (argmax) HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
+  if (argmax) {
+    ProfScope ps(m, P_ARGMAX, st);
+    HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+  }
+  if (m->prof && (rc = drain_profile(m, false))) return rc;
 
   for (int b = 0; b < B; ++b) {
     positions[b] += 1;

@@ -184,6 +184,26 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
  * Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL, CBD_E_HIP. */
 int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, const void* v_src, void* stream);
 
+/* Keep only the first `length` positions of a live lane (0 <= length <= its
+ * current length); later slots become free and are rewritten by the next
+ * steps.  Host bookkeeping only, no GPU work.  Lets a caller roll a lane back
+ * (e.g. replay the same step).  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE. */
+int cbd_lane_truncate(cbd_arena* a, int lane, int length);
+
+/* Per-kernel timing for measurement.  While enabled, every step brackets each
+ * kernel launch with HIP events on the step's stream and attributes the
+ * elapsed GPU time to a kernel class (see cbd_profile_class_name).  The event
+ * records add small gaps between kernels, so time the throughput of a step
+ * with profiling disabled.  cbd_profile_read synchronizes on the recorded
+ * events and returns the accumulated milliseconds and launch count of one
+ * class since the last reset.  Errors: CBD_E_ARG, CBD_E_HIP. */
+int cbd_profile_enable(cbd_model* m, int enable);
+int cbd_profile_reset(cbd_model* m);
+int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launches);
+/* Number of kernel classes, and the name of class `cls` (NULL if out of range). */
+int cbd_profile_classes(void);
+const char* cbd_profile_class_name(int cls);
+
 /* Projection kernel family for steps of this model: 0 = automatic by batch
  * width, 1 = weight-streaming split-K tiles at every width.  Every family
  * computes each output with the same chunked reduction, so the choice changes

@@ -307,6 +307,11 @@ def prompt_tokens(cfg: ModelConfig, lane: int, length: int, seed: int = SEED_TOK
     return uniform_int(seed, lane, length, 0, cfg.vocab - 1)
 
 
+def step_tokens(cfg: ModelConfig, n_lanes: int, seed: int = SEED_TOKENS) -> np.ndarray:
+    """One input token per lane for a single decode step, uniform in [0, vocab) (stream 999)."""
+    return uniform_int(seed, 999, n_lanes, 0, cfg.vocab - 1)
+
+
 def kv_lengths(n_lanes: int, lo: int = 128, hi: int = 4096, seed: int = SEED_LENGTHS) -> np.ndarray:
     """Per-lane KV lengths uniform in [lo, hi] (stream 0, element = lane)."""
     return uniform_int(seed, 0, n_lanes, lo, hi)

@@ -50,6 +50,14 @@
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2 };
 
+/* Accumulator of every sum (dot products, sums of squares, softmax sums, the
+ * weighted value sum): the sums are computed exactly up to double rounding and
+ * rounded to f32 where the definition stores a value. */
+#ifndef ORC_ACC
+#define ORC_ACC double
+#endif
+typedef ORC_ACC acc_t;
+
 typedef struct {
   int d, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab;
   float rms_eps, rope_theta;
@@ -136,12 +144,13 @@ static inline float wval(const orc_mat* W, int wtype, int64_t K, int64_t r, int6
   return q * orc_f16_to_f32(W->scale[r * (K / 32) + i / 32]);
 }
 
-/* The one dot product every projection uses: sum_{i=0}^{K-1} W[r][i] * x[i],
- * accumulated in ascending i, each product and sum rounded to f32. */
+/* The one dot product every projection uses: sum_{i=0}^{K-1} W[r][i] * x[i]
+ * in ascending i, products and sum in the accumulator type, the result
+ * rounded to f32. */
 static float dot_row(const orc_mat* W, int wtype, int64_t K, int64_t r, const float* x) {
-  float acc = 0.0f;
-  for (int64_t i = 0; i < K; ++i) acc += wval(W, wtype, K, r, i) * x[i];
-  return acc;
+  acc_t acc = 0;
+  for (int64_t i = 0; i < K; ++i) acc += (acc_t)wval(W, wtype, K, r, i) * (acc_t)x[i];
+  return (float)acc;
 }
 
 /* ---- pieces, exported so tests can pin them one by one ------------------- */
@@ -153,11 +162,12 @@ void orc_matvec(const orc_mat* W, int wtype, int row0, int nrows, int K, const f
 }
 
 /* out_i = (x_i * r) * g_i with r = 1 / sqrt(mean(x^2) + eps); the sum of
- * squares runs in ascending i. */
+ * squares runs in ascending i in the accumulator type; the mean is rounded to
+ * f32 and r computed in f32. */
 void orc_rmsnorm(const float* x, const float* g, int n, float eps, float* out) {
-  float ss = 0.0f;
-  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
-  float ms = ss / (float)n;
+  acc_t ss = 0;
+  for (int i = 0; i < n; ++i) ss += (acc_t)x[i] * (acc_t)x[i];
+  float ms = (float)(ss / (acc_t)n);
   float r = 1.0f / sqrtf(ms + eps);
   for (int i = 0; i < n; ++i) out[i] = (x[i] * r) * g[i];
 }
@@ -199,26 +209,28 @@ void orc_attention(const float* q, const float* Kc, const float* Vc, int64_t kv_
     int g = h / grp;
     const float* qh = q + (int64_t)h * hd;
     float* sc = (float*)malloc(sizeof(float) * (size_t)n_keys);
+    acc_t* oa = (acc_t*)malloc(sizeof(acc_t) * (size_t)hd);
     float m = -INFINITY;
     for (int t = 0; t < n_keys; ++t) {
       const float* kt = Kc + (int64_t)t * kv_stride + (int64_t)g * hd;
-      float dot = 0.0f;
-      for (int i = 0; i < hd; ++i) dot += qh[i] * kt[i];
-      sc[t] = dot * inv;
+      acc_t dot = 0;
+      for (int i = 0; i < hd; ++i) dot += (acc_t)qh[i] * (acc_t)kt[i];
+      sc[t] = (float)dot * inv;
       if (sc[t] > m) m = sc[t];
     }
-    float Z = 0.0f;
+    acc_t Z = 0;
     for (int t = 0; t < n_keys; ++t) {
       sc[t] = expf(sc[t] - m);
       Z += sc[t];
     }
-    float* oh = out + (int64_t)h * hd;
-    for (int i = 0; i < hd; ++i) oh[i] = 0.0f;
+    for (int i = 0; i < hd; ++i) oa[i] = 0;
     for (int t = 0; t < n_keys; ++t) {
       const float* vt = Vc + (int64_t)t * kv_stride + (int64_t)g * hd;
-      for (int i = 0; i < hd; ++i) oh[i] += sc[t] * vt[i];
+      for (int i = 0; i < hd; ++i) oa[i] += (acc_t)sc[t] * (acc_t)vt[i];
     }
-    for (int i = 0; i < hd; ++i) oh[i] = oh[i] / Z;
+    float* oh = out + (int64_t)h * hd;
+    for (int i = 0; i < hd; ++i) oh[i] = (float)(oa[i] / Z);
+    free(oa);
     free(sc);
   }
 }

@@ -30,7 +30,7 @@ SYMBOLS = [
     "cbd_lane_length", "cbd_arena_used_bytes", "cbd_arena_live_lanes", "cbd_workspace_bytes",
     "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
     "cbd_lane_truncate", "cbd_profile_enable", "cbd_profile_reset", "cbd_profile_read", "cbd_profile_classes",
-    "cbd_profile_class_name",
+    "cbd_profile_class_name", "cbd_set_graph_replay",
 ]
 
 
@@ -97,6 +97,7 @@ def lib():
         L.cbd_lane_kv_import.argtypes = [vp, i32, i32, vp, vp, vp]
         L.cbd_set_variant.argtypes = [vp, i32]
         L.cbd_lane_truncate.argtypes = [vp, i32, i32]
+        L.cbd_set_graph_replay.argtypes = [vp, i32]
         L.cbd_profile_enable.argtypes = [vp, i32]
         L.cbd_profile_reset.argtypes = [vp]
         L.cbd_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)]
@@ -237,6 +238,9 @@ class Model:
 
     def set_variant(self, variant: int):
         _check(lib().cbd_set_variant(self.h, variant))
+
+    def set_graph_replay(self, on: bool = True):
+        _check(lib().cbd_set_graph_replay(self.h, int(on)))
 
     def profile_enable(self, on: bool = True):
         _check(lib().cbd_profile_enable(self.h, int(on)))

@@ -6,30 +6,329 @@
 // (layer, KV head) in the arena, so there is no padding and no mask: a lane at
 // position p reads slots [0, p] and writes slot p.
 //
-// One workgroup handles (lane, KV head, split of ATTN_SPLIT keys) for the
-// whole group of query heads sharing that KV head, so each K/V row is read
-// once per group.  The workgroup that owns slot p rotates the new key at p
-// (the same position as the queries, "parallel-slots.md", trap 2 of
-// "S1b decode: design traps"), rounds it to the KV format, writes it into the
-// slab in place and uses the rounded value.  Splits combine by the usual
-// max-rescaled sum, done by the last workgroup of the lane/head to finish (an
-// agent-scope counter) in split order, so the result is fixed by the lane's
-// position alone.
+// Work item = (lane, KV head, chunk of ATTN_SPLIT = 64 keys), one workgroup of
+// one wave, so a single lane's keys spread over many CUs.  Inside the wave, 16
+// lanes share one key row: lane
+// (r, c) = (lane / 16, lane % 16) holds dims [c*D, c*D + D) of key 4*it + r
+// for it = 0..15, D = hd / 16, so every load instruction reads 4 whole rows
+// (coalesced 16-byte loads for hd = 128 bf16 and hd = 64 f32).  The group's
+// query heads (all heads sharing the KV head) are scored together, so each K
+// and V row is read once per group.  Scores are f32 dot products of the
+// rotated f32 query with the stored keys; a reduce-scatter across the 16
+// lanes of a row leaves lane (r, c) with the score of key 4c + r.  Softmax
+// statistics and the value sum are exact f32 per chunk; chunks meet in a
+// second, small kernel that rescales by each chunk's max and sums them in
+// chunk order.  Chunk size is a constant, so a lane's result depends on its
+// own position only, never on B or on other lanes.
+//
+// The workgroup whose chunk holds slot p rotates the new key at p (the same
+// position as the queries: "parallel-slots.md", "S1b decode: design traps",
+// trap 2), rounds K and V to the KV format, writes them in place, and uses
+// the rounded values for key p.
 #include "cbd_internal.h"
 
 namespace cbd {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int MAXG = 8;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline uint16_t f2bf_a(float f) {
   unsigned u = __builtin_bit_cast(unsigned, f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-__device__ inline float bf2f(uint16_t h) { return __builtin_bit_cast(float, (unsigned)h << 16); }
+__device__ inline float bf2f(unsigned h16) { return __builtin_bit_cast(float, h16 << 16); }
+
+// D consecutive KV elements (D = hd/16) of one key as loaded (raw words), and
+// their f32 values.  Loading and converting are separate so that a whole
+// batch of loads can be issued before the first one is waited for.
+template <int D, bool BF>
+struct KVRaw {
+  static constexpr int BYTES = D * (BF ? 2 : 4);
+  static constexpr int NW = BYTES >= 4 ? BYTES / 4 : 1;
+  unsigned w[NW];
+};
+
+template <int D, bool BF>
+__device__ inline KVRaw<D, BF> load_raw(const void* base, long long off) {
+  KVRaw<D, BF> r;
+  constexpr int BYTES = KVRaw<D, BF>::BYTES;
+  const char* p = (const char*)base + off * (BF ? 2 : 4);
+  if constexpr (BYTES >= 16) {
+#pragma unroll
+    for (int h = 0; h < BYTES / 16; ++h) {
+      const u32x4 v = *((const u32x4*)p + h);
+      r.w[4 * h] = v.x;
+      r.w[4 * h + 1] = v.y;
+      r.w[4 * h + 2] = v.z;
+      r.w[4 * h + 3] = v.w;
+    }
+  } else if constexpr (BYTES == 8) {
+    const u32x2 v = *(const u32x2*)p;
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+  } else if constexpr (BYTES == 4) {
+    r.w[0] = *(const unsigned*)p;
+  } else {
+    r.w[0] = *(const uint16_t*)p;
+  }
+  return r;
+}
+
+// x := (x & keep) | (n & take), word by word: keeps the loaded key, or puts
+// the new one in its place, or zeroes it, without branches.
+template <int D, bool BF>
+__device__ inline void raw_select(KVRaw<D, BF>& x, unsigned keep, unsigned take, const KVRaw<D, BF>& n) {
+#pragma unroll
+  for (int i = 0; i < KVRaw<D, BF>::NW; ++i) x.w[i] = (x.w[i] & keep) | (n.w[i] & take);
+}
+
+template <int D, bool BF>
+__device__ inline void raw_to_f32(const KVRaw<D, BF>& r, float (&v)[D]) {
+  if constexpr (BF) {
+    if constexpr (D == 1) {
+      v[0] = __builtin_bit_cast(float, r.w[0] << 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / 2; ++e) {
+        v[2 * e] = __builtin_bit_cast(float, r.w[e] << 16);
+        v[2 * e + 1] = __builtin_bit_cast(float, r.w[e] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < D; ++e) v[e] = __builtin_bit_cast(float, r.w[e]);
+  }
+}
+
+template <int HD, bool KVBF16, int G>
+__global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
+  constexpr int D = HD / 16;  // dims per lane
+  static_assert(ATTN_SPLIT == 64, "one wave holds 4 keys x 16 iterations");
+  const int item = blockIdx.x;
+  if (item >= *a.n_items_dev) return;  // grid sized for the most items a step can have
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, c = lane & 15;
+  const int b = a.items[2 * item];
+  const int s = a.items[2 * item + 1];
+  const int p = a.pos[b];
+  const int nk = p + 1;
+  const int kbeg = s * ATTN_SPLIT;  // first key of the chunk
+  const int kend = min(kbeg + ATTN_SPLIT, nk);
+
+  const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  const float* row = a.qkv + (size_t)b * a.Nqkv;
+  const float2* cs = a.rope + (size_t)b * (HD / 2);
+  const int d0 = c * D;  // first dim of this lane
+  // rotation partner of dim d is d + hd/2 (first half) or d - hd/2 (second half)
+  const bool first_half = d0 < HD / 2;
+  const int dp = first_half ? d0 + HD / 2 : d0 - HD / 2;
+
+  // Rotated queries of the group for this lane's dims (f32).
+  float q[G][D];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float* qh = row + (size_t)(g * G + j) * HD;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      const int jj = first_half ? d0 + e : d0 + e - HD / 2;
+      const float2 t = cs[jj];
+      const float x = qh[d0 + e], y = qh[dp + e];
+      q[j][e] = first_half ? x * t.x - y * t.y : x * t.x + y * t.y;
+    }
+  }
+  // The new key and value at slot p, rotated and rounded to the KV format
+  // (kept as stored words).
+  const bool has_new = nk > s * ATTN_SPLIT && nk <= s * ATTN_SPLIT + ATTN_SPLIT;
+  KVRaw<D, KVBF16> knr, vnr;
+#pragma unroll
+  for (int i = 0; i < KVRaw<D, KVBF16>::NW; ++i) knr.w[i] = vnr.w[i] = 0u;
+  if (has_new) {
+    const float* kr = row + (size_t)(a.Hq + g) * HD;
+    const float* vr = row + (size_t)(a.Hq + a.Hkv + g) * HD;
+    float kn[D], vn[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      const int jj = first_half ? d0 + e : d0 + e - HD / 2;
+      const float2 t = cs[jj];
+      const float x = kr[d0 + e], y = kr[dp + e];
+      kn[e] = first_half ? x * t.x - y * t.y : x * t.x + y * t.y;
+      vn[e] = vr[d0 + e];
+    }
+    if constexpr (KVBF16) {
+      if constexpr (D == 1) {
+        knr.w[0] = f2bf_a(kn[0]);
+        vnr.w[0] = f2bf_a(vn[0]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 2; ++e) {
+          knr.w[e] = (unsigned)f2bf_a(kn[2 * e]) | ((unsigned)f2bf_a(kn[2 * e + 1]) << 16);
+          vnr.w[e] = (unsigned)f2bf_a(vn[2 * e]) | ((unsigned)f2bf_a(vn[2 * e + 1]) << 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        knr.w[e] = __builtin_bit_cast(unsigned, kn[e]);
+        vnr.w[e] = __builtin_bit_cast(unsigned, vn[e]);
+      }
+    }
+    if (r == 0) {  // one row of lanes writes the slot
+      const long long o = base + (long long)p * HD + d0;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        if constexpr (KVBF16) {
+          const unsigned kw = D == 1 ? knr.w[0] : knr.w[e / 2] >> (16 * (e & 1));
+          const unsigned vw = D == 1 ? vnr.w[0] : vnr.w[e / 2] >> (16 * (e & 1));
+          ((uint16_t*)a.kslab)[o + e] = (uint16_t)kw;
+          ((uint16_t*)a.vslab)[o + e] = (uint16_t)vw;
+        } else {
+          ((unsigned*)a.kslab)[o + e] = knr.w[e];
+          ((unsigned*)a.vslab)[o + e] = vnr.w[e];
+        }
+      }
+    }
+  }
+
+  // Scores of the wave's 64 keys: lane (r, c) accumulates its D dims of key
+  // kbeg + 4*it + r into part[it][j]; the row then reduce-scatters so that
+  // lane (r, c) ends with the full score of key kbeg + 4*c + r.  Loads are
+  // issued in batches of KB keys before any is used (unconditional, from a
+  // key clamped into range; key p and keys past the end are replaced after
+  // the load, since slot p may be being written).
+  constexpr int KB = KVRaw<D, KVBF16>::BYTES > 16 ? 8 : 16;
+  const float inv = 1.0f / sqrtf((float)HD);
+  float part[16][G];
+#pragma unroll
+  for (int i0 = 0; i0 < 16; i0 += KB) {
+    KVRaw<D, KVBF16> kr[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int key = kbeg + 4 * (i0 + i) + r;
+      kr[i] = load_raw<D, KVBF16>(a.kslab, base + (long long)min(key, kend - 1) * HD + d0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int key = kbeg + 4 * (i0 + i) + r;
+      const unsigned take = key == p ? ~0u : 0u;
+      const unsigned keep = key < p ? ~0u : 0u;  // past the end: zero
+      raw_select<D, KVBF16>(kr[i], keep, take, knr);
+      float kv[D];
+      raw_to_f32<D, KVBF16>(kr[i], kv);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) acc += q[j][e] * kv[e];
+        part[i0 + i][j] = acc;
+      }
+    }
+  }
+  // Values of the first batch are loaded now, to be in flight during the softmax.
+  KVRaw<D, KVBF16> vr[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    const int key = kbeg + 4 * i + r;
+    vr[i] = load_raw<D, KVBF16>(a.vslab, base + (long long)min(key, kend - 1) * HD + d0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float sc[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) v[it] = part[it][j];
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+      const bool upper = (c & m) != 0;
+#pragma unroll
+      for (int i = 0; i < m; ++i) {
+        const float send = upper ? v[i] : v[i + m];
+        const float keep = upper ? v[i + m] : v[i];
+        v[i] = keep + __shfl_xor(send, m);
+      }
+    }
+    const int key = kbeg + 4 * c + r;
+    sc[j] = key < kend ? v[0] * inv : -INFINITY;
+  }
+
+  // Softmax statistics over the chunk's 64 keys.
+  float mx[G], pe[G], ls[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float m = sc[j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    mx[j] = m;
+    pe[j] = sc[j] == -INFINITY ? 0.f : expf(sc[j] - m);
+    float l = pe[j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off);
+    ls[j] = l;
+  }
+
+  // Values: lane (r, c) accumulates p * V over keys kbeg + 4*it + r for its dims.
+  float o[G][D];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[j][e] = 0.f;
+#pragma unroll
+  for (int i0 = 0; i0 < 16; i0 += KB) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int key = kbeg + 4 * (i0 + i) + r;
+        vr[i] = load_raw<D, KVBF16>(a.vslab, base + (long long)min(key, kend - 1) * HD + d0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int it = i0 + i;
+      const int key = kbeg + 4 * it + r;
+      const unsigned take = key == p ? ~0u : 0u;
+      const unsigned keep = key < p ? ~0u : 0u;
+      raw_select<D, KVBF16>(vr[i], keep, take, vnr);
+      float vv[D];
+      raw_to_f32<D, KVBF16>(vr[i], vv);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float pj = __shfl(pe[j], r * 16 + it);  // the probability of key 4*it + r
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[j][e] += pj * vv[e];
+      }
+    }
+  }
+  // Sum the four rows (fixed butterfly) and publish the chunk's (o, m, l) for
+  // the combine kernel.
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      float v = o[j][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[j][e] = v;
+    }
+  const size_t pstride = (size_t)G * (HD + 2);
+  float* dst = a.part + (((size_t)b * a.max_splits + s) * a.Hkv + g) * pstride;
+  if (r == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < D; ++e) dst[(size_t)j * (HD + 2) + d0 + e] = o[j][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      dst[(size_t)j * (HD + 2) + HD] = mx[j];
+      dst[(size_t)j * (HD + 2) + HD + 1] = ls[j];
+    }
+  }
+}
 
 template <int ACT>
 __device__ inline void put_act(void* base, size_t idx, float v) {
@@ -41,272 +340,104 @@ __device__ inline void put_act(void* base, size_t idx, float v) {
     ((_Float16*)base)[idx] = (_Float16)v;
 }
 
-// Block-wide reductions over 256 threads with a fixed combining tree.
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-template <int HD, bool KVBF16, int ACT>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  constexpr int NSUB = 256 / HD;  // key subsets in the value pass
-  const int item = blockIdx.x;
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int wid = tid >> 6;
-  const int b = a.items[2 * item];
-  const int s = a.items[2 * item + 1];
-  const int p = a.pos[b];
+// Combine a lane's chunks: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s,
+// M = max_s m_s, sums in chunk order.  One workgroup per (lane, KV head): the
+// chunk maxima and sums go through LDS (max_splits x G of each, at most
+// ATTN_MAX_STATS), the chunk outputs are read eight chunks at a time so the
+// loads overlap.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int hd) {
+  extern __shared__ float lds[];
+  float* sM = lds;
+  float* sm = lds + 8;
+  float* sl = sm + (size_t)a.max_splits * a.G;
+  const int b = blockIdx.x, g = blockIdx.y;
+  if (b >= a.B) return;
+  const int nsplit = (a.pos[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
   const int G = a.G;
-  const int nk = p + 1;
-  const int nsplit = (nk + ATTN_SPLIT - 1) / ATTN_SPLIT;
-  const int kbeg = s * ATTN_SPLIT;
-  const int kend = min(kbeg + ATTN_SPLIT, nk);
-  const int n = kend - kbeg;
-
-  __shared__ float q_s[MAXG][HD];
-  __shared__ float knew[HD], vnew[HD];
-  __shared__ float sc[MAXG][ATTN_SPLIT];
-  __shared__ float red[MAXG][4];
-  __shared__ float opart[NSUB][MAXG][HD];
-  __shared__ float stat[2][MAXG];
-  __shared__ unsigned last_flag;
-
-  const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
-  const float* row = a.qkv + (size_t)b * a.Nqkv;
-  const float2* cs = a.rope + (size_t)b * (HD / 2);
-
-  // Rotate the group's queries at p.
-  for (int e = tid; e < G * (HD / 2); e += 256) {
-    const int j = e / (HD / 2), jj = e % (HD / 2);
-    const float* qh = row + (size_t)(g * G + j) * HD;
-    const float x0 = qh[jj], x1 = qh[jj + HD / 2];
-    const float2 t = cs[jj];
-    q_s[j][jj] = x0 * t.x - x1 * t.y;
-    q_s[j][jj + HD / 2] = x1 * t.x + x0 * t.y;
-  }
-  // The split holding slot p rotates the new key, appends K and V in place.
-  if (kend == nk) {
-    const float* kr = row + (size_t)(a.Hq + g) * HD;
-    const float* vr = row + (size_t)(a.Hq + a.Hkv + g) * HD;
-    for (int jj = tid; jj < HD / 2; jj += 256) {
-      const float x0 = kr[jj], x1 = kr[jj + HD / 2];
-      const float2 t = cs[jj];
-      float k0 = x0 * t.x - x1 * t.y, k1 = x1 * t.x + x0 * t.y;
-      const long long o0 = base + (long long)p * HD + jj;
-      if constexpr (KVBF16) {
-        uint16_t h0 = f2bf_a(k0), h1 = f2bf_a(k1);
-        ((uint16_t*)a.kslab)[o0] = h0;
-        ((uint16_t*)a.kslab)[o0 + HD / 2] = h1;
-        k0 = bf2f(h0);
-        k1 = bf2f(h1);
-      } else {
-        ((float*)a.kslab)[o0] = k0;
-        ((float*)a.kslab)[o0 + HD / 2] = k1;
-      }
-      knew[jj] = k0;
-      knew[jj + HD / 2] = k1;
-    }
-    for (int d = tid; d < HD; d += 256) {
-      float v = vr[d];
-      const long long o = base + (long long)p * HD + d;
-      if constexpr (KVBF16) {
-        uint16_t h = f2bf_a(v);
-        ((uint16_t*)a.vslab)[o] = h;
-        v = bf2f(h);
-      } else {
-        ((float*)a.vslab)[o] = v;
-      }
-      vnew[d] = v;
-    }
-  }
-  __syncthreads();
-
-  // Scores: one key per thread.
-  const float inv = 1.0f / sqrtf((float)HD);
-  float dot[MAXG];
-#pragma unroll
-  for (int j = 0; j < MAXG; ++j) dot[j] = 0.f;
-  const int key = kbeg + tid;
-  const bool valid = tid < n;
-  if (valid) {
-    if (key == p) {
-      for (int d = 0; d < HD; ++d) {
-        const float kv = knew[d];
-#pragma unroll
-        for (int j = 0; j < MAXG; ++j)
-          if (j < G) dot[j] += q_s[j][d] * kv;
-      }
-    } else {
-      const long long kro = base + (long long)key * HD;
-      if constexpr (KVBF16) {
-        const u32x4* kp = (const u32x4*)((const uint16_t*)a.kslab + kro);
-#pragma unroll 4
-        for (int c = 0; c < HD / 8; ++c) {
-          const u32x4 w = kp[c];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const unsigned word = w[e >> 1];
-            const float kv = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
-#pragma unroll
-            for (int j = 0; j < MAXG; ++j)
-              if (j < G) dot[j] += q_s[j][c * 8 + e] * kv;
-          }
-        }
-      } else {
-        const u32x4* kp = (const u32x4*)((const float*)a.kslab + kro);
-#pragma unroll 4
-        for (int c = 0; c < HD / 4; ++c) {
-          // bit-cast the whole vector: a bit-cast of one vector element reads element 0
-          const f32x4 w = __builtin_bit_cast(f32x4, kp[c]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float kv = w[e];
-#pragma unroll
-            for (int j = 0; j < MAXG; ++j)
-              if (j < G) dot[j] += q_s[j][c * 4 + e] * kv;
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < MAXG; ++j) {
-    if (j >= G) break;
-    const float sj = valid ? dot[j] * inv : -INFINITY;
-    sc[j][tid] = sj;
-    const float m = wave_max(sj);
-    if ((tid & 63) == 0) red[j][wid] = m;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float m = red[tid][0];
-    for (int w = 1; w < 4; ++w) m = fmaxf(m, red[tid][w]);
-    stat[0][tid] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < MAXG; ++j) {
-    if (j >= G) break;
-    const float e = valid ? expf(sc[j][tid] - stat[0][j]) : 0.f;
-    sc[j][tid] = e;
-    const float l = wave_sum(e);
-    if ((tid & 63) == 0) red[j][wid] = l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = red[tid][0];
-    for (int w = 1; w < 4; ++w) l += red[tid][w];
-    stat[1][tid] = l;
-  }
-
-  // Values: thread (dim, key subset), then subsets summed in order.
-  {
-    const int dim = tid % HD, sub = tid / HD;
-    float o[MAXG];
-#pragma unroll
-    for (int j = 0; j < MAXG; ++j) o[j] = 0.f;
-    for (int tl = sub; tl < n; tl += NSUB) {
-      const int kk = kbeg + tl;
-      float v;
-      if (kk == p) {
-        v = vnew[dim];
-      } else {
-        const long long off = base + (long long)kk * HD + dim;
-        if constexpr (KVBF16)
-          v = bf2f(((const uint16_t*)a.vslab)[off]);
-        else
-          v = ((const float*)a.vslab)[off];
-      }
-#pragma unroll
-      for (int j = 0; j < MAXG; ++j)
-        if (j < G) o[j] += sc[j][tl] * v;
-    }
-#pragma unroll
-    for (int j = 0; j < MAXG; ++j)
-      if (j < G) opart[sub][j][dim] = o[j];
-  }
-  __syncthreads();
-
-  const int Hqd = a.Hq * HD;
-  if (nsplit == 1) {
-    for (int e = tid; e < G * HD; e += 256) {
-      const int j = e / HD, dim = e % HD;
-      float acc = opart[0][j][dim];
-      for (int u = 1; u < NSUB; ++u) acc += opart[u][j][dim];
-      put_act<ACT>(a.out, (size_t)b * Hqd + (size_t)(g * G + j) * HD + dim, acc / stat[1][j]);
-    }
-    return;
-  }
-
-  // Several splits: publish (o, m, l), the last workgroup combines in split order.
-  const size_t pstride = (size_t)G * (HD + 2);
-  float* mine = a.part + (((size_t)b * a.max_splits + s) * a.Hkv + g) * pstride;
-  for (int e = tid; e < G * HD; e += 256) {
-    const int j = e / HD, dim = e % HD;
-    float acc = opart[0][j][dim];
-    for (int u = 1; u < NSUB; ++u) acc += opart[u][j][dim];
-    mine[(size_t)j * (HD + 2) + dim] = acc;
-  }
-  if (tid < G) {
-    mine[(size_t)tid * (HD + 2) + HD] = stat[0][tid];
-    mine[(size_t)tid * (HD + 2) + HD + 1] = stat[1][tid];
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(a.cnt + (size_t)b * a.Hkv + g, 1u);
-    last_flag = (prev == (unsigned)(nsplit - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  if (tid == 0) atomicExch(a.cnt + (size_t)b * a.Hkv + g, 0u);
-  const float* P0 = a.part + ((size_t)b * a.max_splits * a.Hkv + g) * pstride;
+  const size_t pstride = (size_t)G * (hd + 2);
   const size_t sstride = (size_t)a.Hkv * pstride;
-  for (int e = tid; e < G * HD; e += 256) {
-    const int j = e / HD, dim = e % HD;
+  const float* P0 = a.part + ((size_t)b * a.max_splits * a.Hkv + g) * pstride;
+  for (int t = threadIdx.x; t < nsplit * G; t += 256) {
+    const int u = t / G, j = t % G;
+    const float* P = P0 + u * sstride + (size_t)j * (hd + 2);
+    sm[t] = P[hd];
+    sl[t] = P[hd + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int j = threadIdx.x;
     float M = -INFINITY;
-    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, P0[u * sstride + (size_t)j * (HD + 2) + HD]);
+    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, sm[u * G + j]);
+    sM[j] = M;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nsplit * G; t += 256) sm[t] = expf(sm[t] - sM[t % G]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * hd; e += 256) {
+    const int j = e / hd, dim = e % hd;
+    const float* P = P0 + (size_t)j * (hd + 2) + dim;
     float L = 0.f, O = 0.f;
-    for (int u = 0; u < nsplit; ++u) {
-      const float* P = P0 + u * sstride + (size_t)j * (HD + 2);
-      const float w = expf(P[HD] - M);
-      L += w * P[HD + 1];
-      O += w * P[dim];
+    int u = 0;
+    for (; u + 8 <= nsplit; u += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = P[(u + i) * sstride];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = sm[(u + i) * G + j];
+        L += w * sl[(u + i) * G + j];
+        O += w * x[i];
+      }
     }
-    put_act<ACT>(a.out, (size_t)b * Hqd + (size_t)(g * G + j) * HD + dim, O / L);
+    for (; u < nsplit; ++u) {
+      const float w = sm[u * G + j];
+      L += w * sl[u * G + j];
+      O += w * P[u * sstride];
+    }
+    put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * G + j) * hd + dim, O / L);
   }
 }
 
-template <int HD>
-static hipError_t launch_hd(int kv_bf16, int act, const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.n_items, a.Hkv), blk(256);
-  if (kv_bf16) {
-    hipLaunchKernelGGL((k_attn<HD, true, WT_BF16>), grid, blk, 0, st, a);
-  } else if (act == WT_Q8) {
-    hipLaunchKernelGGL((k_attn<HD, false, WT_Q8>), grid, blk, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((k_attn<HD, false, WT_F32>), grid, blk, 0, st, a);
+template <int HD, bool BF>
+static hipError_t launch_g(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn<HD, BF, 1>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<HD, BF, 2>), grid, dim3(64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn<HD, BF, 3>), grid, dim3(64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn<HD, BF, 4>), grid, dim3(64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_attn<HD, BF, 8>), grid, dim3(64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int HD>
+static hipError_t launch_hd(int kv_bf16, int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  return kv_bf16 ? launch_g<HD, true>(G, a, grid, st) : launch_g<HD, false>(G, a, grid, st);
+}
+
 hipError_t launch_attn(int hd, int kv_bf16, int act, const AttnArgs& a, hipStream_t st) {
-  if (a.n_items <= 0) return hipSuccess;
+  if (a.max_items <= 0) return hipSuccess;
+  const dim3 grid(a.max_items, a.Hkv);
+  hipError_t e;
   switch (hd) {
-    case 16: return launch_hd<16>(kv_bf16, act, a, st);
-    case 32: return launch_hd<32>(kv_bf16, act, a, st);
-    case 64: return launch_hd<64>(kv_bf16, act, a, st);
-    case 128: return launch_hd<128>(kv_bf16, act, a, st);
+    case 16: e = launch_hd<16>(kv_bf16, a.G, a, grid, st); break;
+    case 32: e = launch_hd<32>(kv_bf16, a.G, a, grid, st); break;
+    case 64: e = launch_hd<64>(kv_bf16, a.G, a, grid, st); break;
+    case 128: e = launch_hd<128>(kv_bf16, a.G, a, grid, st); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  if ((size_t)a.max_splits * a.G > ATTN_MAX_STATS) return hipErrorInvalidValue;
+  const dim3 cgrid(a.B, a.Hkv);
+  const size_t lds = (8 + 2 * (size_t)a.max_splits * a.G) * sizeof(float);
+  switch (act) {
+    case WT_F32: hipLaunchKernelGGL(k_attn_combine<WT_F32>, cgrid, dim3(256), lds, st, a, hd); break;
+    case WT_BF16: hipLaunchKernelGGL(k_attn_combine<WT_BF16>, cgrid, dim3(256), lds, st, a, hd); break;
+    default: hipLaunchKernelGGL(k_attn_combine<WT_Q8>, cgrid, dim3(256), lds, st, a, hd); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace cbd

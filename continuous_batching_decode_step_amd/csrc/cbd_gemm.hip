@@ -3,12 +3,13 @@
 // The method this serves ("MODEL-BATCHING-RESULTS — multi-user batched
 // decode, measured", section "The lever") runs each projection once over the
 // [B, d] panel of the step so each weight row is read once for all B lanes.
-// Here a wave owns GEMM_R tiles of 16 weight rows, C groups of 16 lanes and
-// one split of K: it streams its rows from HBM with 16-byte loads straight
-// into MFMA A operands (rows = MFMA M), takes the lanes' activations as the B
-// operand (lanes = MFMA N), and accumulates in f32 registers.  The same wave
-// code serves B = 1 (15 of 16 columns idle: the MFMA pipe has ample headroom
-// while HBM is the bound) and wide panels.
+// A wave owns `rows` tiles of 16 weight rows, C groups of 16 lanes and one
+// split of K: it streams its rows from HBM with 16-byte loads straight into
+// MFMA A operands (rows = MFMA M), takes the lanes' activations as the B
+// operand (lanes = MFMA N), and accumulates in f32 registers.  Loads run two
+// pipeline stages ahead of the MFMAs.  The same wave code serves B = 1 (15 of
+// 16 columns idle: the MFMA pipe has ample headroom while HBM is the bound)
+// and wide panels.
 //
 // Reduction contract (what makes lane b bit-identical to running alone, the
 // structural invariant of "Correctness — proven, not asserted"): every output
@@ -17,10 +18,16 @@
 // bounds depend on (N, K) only.  MFMA computes each output element from its
 // own row and column, so neither B nor the other lanes change a bit.
 //
-// Split partials go to the workspace; the last wave of a tile to arrive (an
-// agent-scope counter, reset by that wave) sums them in split order and runs
-// the epilogue: store, residual add, SwiGLU, or LM-head store + argmax
-// candidates.  No float atomics, no second launch.
+// A workgroup owns one output tile and runs its S splits as S waves; the
+// partials meet in LDS and wave 0 sums them in split order and runs the
+// epilogue.  Nothing crosses workgroups, so no device-scope fence is needed
+// (on MI355X those write back and invalidate an XCD's whole L2).
+//
+// Epilogues: store (QKV), residual add (O, down; also per-tile sums of x^2
+// for the next RMSNorm), SwiGLU (gate|up), and the LM head (store + per-tile
+// argmax candidates, lowest index on ties).
+#include <algorithm>
+
 #include "cbd_internal.h"
 
 namespace cbd {
@@ -50,50 +57,6 @@ struct KStep<WT_Q8> {
 };
 
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
-
-// A operand: 16 bytes of weights of `row` at element k (a lane's share of one k-step).
-template <int WT>
-__device__ inline u32x4 load_a(const GemmArgs& a, int row, int k, bool ok) {
-  if constexpr (WT == WT_F32) {
-    const float* W = (const float*)a.W;
-    size_t off = ok ? (size_t)row * a.K + k : 0;
-    u32x4 v = *(const u32x4*)(W + off);
-    return ok ? v : zero4();
-  } else if constexpr (WT == WT_BF16) {
-    const uint16_t* W = (const uint16_t*)a.W;
-    size_t off = ok ? (size_t)row * a.K + k : 0;
-    u32x4 v = *(const u32x4*)(W + off);
-    return ok ? v : zero4();
-  } else {
-    // Q8_0: 8 int8 of one block, scaled into binary16 in registers.
-    const int8_t* W = (const int8_t*)a.W;
-    size_t off = ok ? (size_t)row * a.K + k : 0;
-    size_t soff = ok ? (size_t)row * (a.K >> 5) + (k >> 5) : 0;
-    u32x2 q = *(const u32x2*)(W + off);
-    _Float16 sh = __builtin_bit_cast(_Float16, a.Ws[soff]);
-    float s = ok ? (float)sh : 0.0f;
-    f16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      unsigned wd = i < 4 ? q.x : q.y;
-      int qi = (int)(signed char)((wd >> (8 * (i & 3))) & 0xffu);
-      r[i] = (_Float16)((float)qi * s);
-    }
-    return __builtin_bit_cast(u32x4, r);
-  }
-}
-
-// B operand: 16 bytes of the activation panel of lane `col` at element k.
-template <int WT>
-__device__ inline u32x4 load_b(const GemmArgs& a, int col, int k, bool ok) {
-  size_t off = ok ? (size_t)col * a.K + k : 0;
-  u32x4 v;
-  if constexpr (WT == WT_F32)
-    v = *(const u32x4*)((const float*)a.X + off);
-  else
-    v = *(const u32x4*)((const uint16_t*)a.X + off);
-  return ok ? v : zero4();
-}
 
 template <int WT>
 __device__ inline f32x4 mma(u32x4 av, u32x4 bv, f32x4 c) {
@@ -129,48 +92,72 @@ __device__ inline void store_act(void* base, size_t idx, float v) {
     ((_Float16*)base)[idx] = (_Float16)v;
 }
 
+// Unconditional fragment loads from byte pointers (rows and columns already
+// clamped into range).
+__device__ inline u32x4 ld16(const char* p) { return *(const u32x4*)p; }
+
+// Q8_0: a lane's share of one block is 8 int8 plus the block's binary16 scale,
+// carried raw through the load pipeline as {q[0..3], q[4..7], scale, 0} and
+// scaled into binary16 MFMA operands when consumed.
+__device__ inline u32x4 ld_q8(const char* q, const uint16_t* sp) {
+  const u32x2 w = *(const u32x2*)q;
+  return u32x4{w.x, w.y, (unsigned)*sp, 0u};
+}
+
+__device__ inline u32x4 q8_to_f16(u32x4 raw) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)raw.z);
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const unsigned wd = i < 4 ? raw.x : raw.y;
+    const int qi = (int)(signed char)((wd >> (8 * (i & 3))) & 0xffu);
+    r[i] = (_Float16)((float)qi * s);
+  }
+  return __builtin_bit_cast(u32x4, r);
+}
+
 template <int WT, int EPI, int C>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  constexpr int R = GEMM_R;
+__global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
+  constexpr int R = gemm_rows(EPI);
   constexpr int KS = KStep<WT>::v;
   constexpr int PL = KStep<WT>::per_lane;
-  constexpr int U = 4;  // k-steps whose loads are issued together
+  constexpr int U = C == 1 ? 4 : 2;  // k-steps per pipeline stage
+  constexpr int EB = WT == WT_F32 ? 4 : (WT == WT_BF16 ? 2 : 1);  // weight bytes per element
+  constexpr int XB = WT == WT_F32 ? 4 : 2;                        // activation bytes per element
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int total = a.nRB * a.S * a.nCG;
-  if (wave >= total) return;
-  const int rb = wave % a.nRB;
-  const int s = (wave / a.nRB) % a.S;
-  const int cg = wave / (a.nRB * a.S);
+  const int s = threadIdx.x >> 6;  // the split this wave computes
+  const int rb = blockIdx.x % a.nRB;
+  const int cg = blockIdx.x / a.nRB;
   const int r16 = lane & 15, g4 = lane >> 4;
-
-  // Rows this lane loads (A operand row = lane % 16).
-  int arow[R];
-  bool aok[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int H = R / 2;
-      int j = rb * TILE * H + TILE * (r % H) + r16;
-      arow[r] = r < H ? j : a.N + j;
-      aok[r] = j < a.N;
-    } else {
-      int n = rb * TILE * R + TILE * r + r16;
-      arow[r] = n;
-      aok[r] = n < a.N;
-    }
-  }
-  int bcol[C];
-  bool bok[C];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    bcol[c] = cg * TILE * C + TILE * c + r16;
-    bok[c] = bcol[c] < a.B;
-  }
 
   const int kb = s * a.Ks;
   const int ke = min(kb + a.Ks, a.K);
   const int koff = PL * g4;
+
+  // Row pointers (A operand row = lane % 16).  A row past the end is clamped to
+  // the last row: it only feeds output rows that are never stored.
+  const char* ap[R];
+  const uint16_t* sp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int row;
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H = R / 2;
+      const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
+      row = r < H ? j : a.N + j;
+    } else {
+      row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
+    }
+    ap[r] = (const char*)a.W + ((size_t)row * a.K + kb + koff) * EB;
+    if constexpr (WT == WT_Q8) sp[r] = a.Ws + (size_t)row * (a.K >> 5) + (kb >> 5);
+  }
+  // Column pointers (B operand column = lane % 16), clamped the same way.
+  const char* bp[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int col = min(cg * TILE * C + TILE * c + r16, a.B - 1);
+    bp[c] = (const char*)a.X + ((size_t)col * a.K + kb + koff) * XB;
+  }
 
   f32x4 acc[R][C];
 #pragma unroll
@@ -178,36 +165,112 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int k0 = kb;
-  for (; k0 + U * KS <= ke; k0 += U * KS) {
-    u32x4 av[U][R], bv[U][C];
+  auto load_stage = [&](u32x4 (&A)[U][R], u32x4 (&Bv)[U][C], int step0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (step0 + u) * KS;  // offset from kb
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if constexpr (WT == WT_Q8)
+          A[u][r] = ld_q8(ap[r] + k, sp[r] + (k >> 5));
+        else
+          A[u][r] = ld16(ap[r] + (size_t)k * EB);
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) Bv[u][c] = ld16(bp[c] + (size_t)k * XB);
+    }
+  };
+  auto compute_stage = [&](const u32x4 (&A)[U][R], const u32x4 (&Bv)[U][C]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int r = 0; r < R; ++r) av[u][r] = load_a<WT>(a, arow[r], k0 + u * KS + koff, aok[r]);
+      for (int r = 0; r < R; ++r) {
+        u32x4 av = A[u][r];
+        if constexpr (WT == WT_Q8) av = q8_to_f16(av);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < C; ++c) bv[u][c] = load_b<WT>(a, bcol[c], k0 + u * KS + koff, bok[c]);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av[u][r], bv[u][c], acc[r][c]);
+        for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av, Bv[u][c], acc[r][c]);
+      }
+  };
+
+  // Full k-steps of this split, in stages of U, two stages in flight.
+  const int nfull = (ke - kb) / KS;
+  const int nst = nfull / U;
+  {
+    u32x4 A0[U][R], B0[U][C], A1[U][R], B1[U][C];
+    if (nst > 0) load_stage(A0, B0, 0);
+    int st = 0;
+    // steady state, no branches inside: stage st+1 (and st+2) load while st (st+1) computes
+    for (; st + 2 < nst; st += 2) {
+      load_stage(A1, B1, (st + 1) * U);
+      compute_stage(A0, B0);
+      load_stage(A0, B0, (st + 2) * U);
+      compute_stage(A1, B1);
+    }
+    if (st + 1 < nst) {
+      load_stage(A1, B1, (st + 1) * U);
+      compute_stage(A0, B0);
+      compute_stage(A1, B1);
+    } else if (st < nst) {
+      compute_stage(A0, B0);
+    }
   }
-  for (; k0 < ke; k0 += KS) {
-    const int kk = k0 + koff;
-    const bool kok = kk + PL <= a.K;  // K % PL == 0, so a lane's vector is all in or all out
+  // Leftover full steps, then the K tail (a lane's vector is all in or all out
+  // because K % PL == 0; out-of-range vectors become zero).
+  for (int st = nst * U; st * KS < ke - kb; ++st) {
+    const int k = st * KS;
+    const bool kok = kb + k + koff + PL <= a.K;
     u32x4 av[R], bv[C];
 #pragma unroll
-    for (int r = 0; r < R; ++r) av[r] = load_a<WT>(a, arow[r], kk, aok[r] && kok);
+    for (int r = 0; r < R; ++r) {
+      if constexpr (WT == WT_Q8)
+        av[r] = q8_to_f16(ld_q8(ap[r] + (kok ? k : 0), sp[r] + (kok ? (k >> 5) : 0)));
+      else
+        av[r] = ld16(ap[r] + (size_t)(kok ? k : 0) * EB);
+      if (!kok) av[r] = zero4();
+    }
 #pragma unroll
-    for (int c = 0; c < C; ++c) bv[c] = load_b<WT>(a, bcol[c], kk, bok[c] && kok);
+    for (int c = 0; c < C; ++c) {
+      bv[c] = ld16(bp[c] + (size_t)(kok ? k : 0) * XB);
+      if (!kok) bv[c] = zero4();
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av[r], bv[c], acc[r][c]);
+  }
+
+  if (a.S > 1) {
+    // Split partials through LDS, in rounds of `per_round` waves; wave 0 adds
+    // them to its own partial P_0 in ascending split order.
+    constexpr int E = R * C * 4;
+    extern __shared__ float red[];  // [per_round][E][64]
+    const int per_round = a.red_waves;
+    for (int r0 = 1; r0 < a.S; r0 += per_round) {
+      const int r1 = min(r0 + per_round, a.S);
+      if (s >= r0 && s < r1) {
+        float* dst = red + (size_t)(s - r0) * E * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[((r * C + c) * 4 + i) * 64] = acc[r][c][i];
+      }
+      __syncthreads();
+      if (s == 0) {
+        for (int s2 = r0; s2 < r1; ++s2) {
+          const float* src = red + (size_t)(s2 - r0) * E * 64 + lane;
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[r][c][i] = acc[r][c][i] + src[((r * C + c) * 4 + i) * 64];
+        }
+      }
+      __syncthreads();
+    }
+    if (s != 0) return;
   }
 
   // Output coordinates of acc[r][c][i]: row (or gate/up pair) and lane column.
@@ -219,48 +282,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       return rb * TILE * R + TILE * r + 4 * g4 + i;
     }
   };
-  auto raw_row = [&](int r, int i) -> int {
-    int n = out_row(r, i);
-    if constexpr (EPI == EPI_SWIGLU) return r < R / 2 ? n : a.N + n;
-    return n;
-  };
-
-  if (a.S > 1) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int col = cg * TILE * C + TILE * c + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (out_row(r, i) < a.N && col < a.B)
-            a.part[((size_t)s * a.B + col) * a.Nraw + raw_row(r, i)] = acc[r][c][i];
-      }
-    __threadfence();
-    const int tile = cg * a.nRB + rb;
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(a.cnt + tile, 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned)(a.S - 1)) return;
-    __threadfence();
-    if (lane == 0) atomicExch(a.cnt + tile, 0u);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int col = cg * TILE * C + TILE * c + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!(out_row(r, i) < a.N && col < a.B)) continue;
-          float v = 0.f;
-          for (int s2 = 0; s2 < a.S; ++s2) {
-            float p = (s2 == s) ? acc[r][c][i] : a.part[((size_t)s2 * a.B + col) * a.Nraw + raw_row(r, i)];
-            v = (s2 == 0) ? p : v + p;
-          }
-          acc[r][c][i] = v;
-        }
-      }
-  }
 
   // Epilogue.
 #pragma unroll
@@ -274,11 +295,28 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int j = out_row(r, i);
           if (cok && j < a.N) {
-            float g = acc[r][c][i], u = acc[r + R / 2][c][i];
-            float act = (g / (1.0f + expf(-g))) * u;
+            const float g = acc[r][c][i], u = acc[r + R / 2][c][i];
+            const float act = (g / (1.0f + expf(-g))) * u;
             store_act<WT>(a.act_out, (size_t)col * a.N + j, act);
           }
         }
+    } else if constexpr (EPI == EPI_RESID) {
+      // x += y, and this tile's sum of x^2 per lane for the next RMSNorm
+      float ss = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = out_row(r, i);
+          if (!(cok && n < a.N)) continue;
+          const size_t idx = (size_t)col * a.N + n;
+          const float xn = a.out[idx] + acc[r][c][i];
+          a.out[idx] = xn;
+          ss += xn * xn;
+        }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (g4 == 0 && cok) a.ssq_out[(size_t)rb * a.B + col] = ss;
     } else {
       float best = -INFINITY;
       int bi = 0x7fffffff;
@@ -289,12 +327,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
           const int n = out_row(r, i);
           if (!(cok && n < a.N)) continue;
           const float v = acc[r][c][i];
-          const size_t idx = (size_t)col * a.N + n;
-          if constexpr (EPI == EPI_RESID) {
-            a.out[idx] = a.out[idx] + v;
-          } else {
-            a.out[idx] = v;
-          }
+          a.out[(size_t)col * a.N + n] = v;
           if constexpr (EPI == EPI_HEAD) {
             if (v > best || (v == best && n < bi)) {
               best = v;
@@ -305,8 +338,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       if constexpr (EPI == EPI_HEAD) {
 #pragma unroll
         for (int off = 16; off < 64; off <<= 1) {
-          float ov = __shfl_xor(best, off);
-          int oi = __shfl_xor(bi, off);
+          const float ov = __shfl_xor(best, off);
+          const int oi = __shfl_xor(bi, off);
           if (ov > best || (ov == best && oi < bi)) {
             best = ov;
             bi = oi;
@@ -320,10 +353,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
 template <int WT, int EPI>
 static hipError_t launch_c(int C, const GemmArgs& a, int blocks, hipStream_t st) {
+  const dim3 blk(64 * a.S);
+  const size_t lds = a.S > 1 ? (size_t)a.red_waves * gemm_rows(EPI) * C * 4 * 64 * sizeof(float) : 0;
   switch (C) {
-    case 1: hipLaunchKernelGGL((k_gemm<WT, EPI, 1>), dim3(blocks), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<WT, EPI, 2>), dim3(blocks), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm<WT, EPI, 4>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm<WT, EPI, 1>), dim3(blocks), blk, lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<WT, EPI, 2>), dim3(blocks), blk, lds, st, a); break;
+    default: hipLaunchKernelGGL((k_gemm<WT, EPI, 4>), dim3(blocks), blk, lds, st, a); break;
   }
   return hipGetLastError();
 }
@@ -338,13 +373,18 @@ static hipError_t launch_epi(int epi, int C, const GemmArgs& a, int blocks, hipS
   }
 }
 
-hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, int n_waves, hipStream_t st) {
-  const int blocks = (n_waves + 3) / 4;
+hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st) {
+  if (a.S < 1 || a.S > GEMM_MAX_SPLIT) return hipErrorInvalidValue;
+  GemmArgs g = a;
+  // LDS per split round: at most 32 KB
+  g.red_waves =
+      (int)std::max<size_t>(1, (32768 / ((size_t)gemm_rows(epi) * C * 4 * 64 * sizeof(float))));
+  const int blocks = a.nRB * a.nCG;
   if (blocks <= 0) return hipSuccess;
   switch (wt) {
-    case WT_F32: return launch_epi<WT_F32>(epi, C, a, blocks, st);
-    case WT_BF16: return launch_epi<WT_BF16>(epi, C, a, blocks, st);
-    default: return launch_epi<WT_Q8>(epi, C, a, blocks, st);
+    case WT_F32: return launch_epi<WT_F32>(epi, C, g, blocks, st);
+    case WT_BF16: return launch_epi<WT_BF16>(epi, C, g, blocks, st);
+    default: return launch_epi<WT_Q8>(epi, C, g, blocks, st);
   }
 }
 

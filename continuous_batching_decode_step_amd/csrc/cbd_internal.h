@@ -12,10 +12,17 @@ enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
 
 // Keys per attention split.  A constant of the design: the per-lane result
 // never depends on B, on the lane's slot or on the other lanes.
-constexpr int ATTN_SPLIT = 256;
-// Rows of one MFMA tile, and 16-row tiles per wave in the projection kernels.
+constexpr int ATTN_SPLIT = 64;
+// chunk statistics per (lane, KV head) the combine step holds in LDS:
+// ceil(max_seq / ATTN_SPLIT) * (n_heads / n_kv_heads) may not exceed this
+constexpr int ATTN_MAX_STATS = 8000;
+// Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
+// epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
+// rows; the others take one tile so that d-row projections fill the chip).
 constexpr int TILE = 16;
-constexpr int GEMM_R = 2;
+__host__ __device__ constexpr int gemm_rows(int epi) { return (epi == 2 || epi == 3) ? 2 : 1; }
+// Splits of K per projection tile: one wave each, in one workgroup.
+constexpr int GEMM_MAX_SPLIT = 8;
 
 // Projection over a panel: Y[b][n] = sum_k W[n][k] * X[b][k] for b < B.
 // The reduction contract (identical in every kernel variant and batch width):
@@ -23,6 +30,10 @@ constexpr int GEMM_R = 2;
 // split's partial is a chain of MFMAs over ascending k-steps starting from
 // zero; the output is ((P_0 + P_1) + P_2) + ... in split order, then the
 // epilogue.  So lane b's outputs are the same bits whatever B is.
+//
+// RMSNorm statistics come from the producer: a projection that updates the
+// residual stream x (EPI_RESID) also writes, per row block, the partial sums
+// of x^2 of each lane, which the norm kernel adds in row-block order.
 struct GemmArgs {
   const void* W;        // data plane [Nraw, K]
   const uint16_t* Ws;   // Q8_0 scale plane [Nraw, K/32] (binary16), or null
@@ -33,13 +44,13 @@ struct GemmArgs {
   int B;
   int S;                // splits
   int Ks;               // elements per split (multiple of the k-step)
-  int nRB;              // row blocks of TILE*GEMM_R rows (SWIGLU: TILE*GEMM_R/2 pairs)
+  int nRB;              // row blocks of TILE*rows rows (SWIGLU: TILE*rows/2 pairs)
   int nCG;              // column groups
   float* out;           // STORE/HEAD: [B, N] f32; RESID: residual [B, N] updated in place
   void* act_out;        // SWIGLU: [B, N] in the activation format
-  float* part;          // split partials [S][B][Nraw]
-  unsigned* cnt;        // per (row block, column group) arrival counters, zero between launches
   float2* amax;         // HEAD: per (row block, lane) (max value, index as float bits)
+  int red_waves;        // split partials per LDS round (set by the launcher)
+  float* ssq_out;       // EPI_RESID: [nRB][B] this tile's sum of x^2 per lane
 };
 
 struct AttnArgs {
@@ -52,25 +63,25 @@ struct AttnArgs {
   int B;
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
-  const int* items;       // [n_items][2] (b, split)
-  int n_items;
-  int max_splits;         // splits per lane the partial buffer is sized for
+  const int* items;       // [n_items][2] (b, chunk)
+  const int* n_items_dev; // number of items of this step (device)
+  int max_items;          // grid size: the most items a step of B lanes can have
+  int max_splits;         // chunks per lane the partial buffer is sized for
   int Hq, Hkv, G, Nqkv;
   const float2* rope;     // [B][hd/2] (cos, sin) of each lane's position
-  float* part;            // [B][max_splits][Hkv][G][hd + 2]
-  unsigned* cnt;          // [B][Hkv] arrival counters, zero between launches
+  float* part;            // [B][max_splits][Hkv][G][hd + 2] chunk partials (o, m, l)
   void* out;              // [B, Hq*hd] in the activation format
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------------
-hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, int n_waves, hipStream_t st);
+hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
 hipError_t launch_attn(int hd, int kv_bf16, int act, const AttnArgs& a, hipStream_t st);
-// x[b] = E[token_b]; xn[b] = rmsnorm(x[b]) * g (act format); rope table of pos_b.
-hipError_t launch_embed_norm(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B,
-                             int d, int hd, float theta, float eps, const float* g, float* x, void* xn,
-                             float2* rope, hipStream_t st);
-hipError_t launch_rmsnorm(int wt, const float* x, const float* g, int B, int d, float eps, void* xn,
-                          hipStream_t st);
+// x[b] = E[token_b]; ssq[b] = sum x[b]^2; rope table of pos_b.
+hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B, int d,
+                        int hd, float theta, float* x, float* ssq, float2* rope, hipStream_t st);
+// xn[b] = (x[b] * r_b) * g in the activation format, r_b = 1 / sqrt(sum_t ssq[t][b] / d + eps).
+hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, const float* g, int B, int d, float eps,
+                       void* xn, hipStream_t st);
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st);
 

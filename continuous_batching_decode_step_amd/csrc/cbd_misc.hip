@@ -1,25 +1,9 @@
 // Per-lane row kernels of the decode step on gfx950: embedding gather with the
-// first RMSNorm and the lane's rotary table, RMSNorm of the residual stream,
-// and the final argmax over the LM head's per-tile candidates.
+// first RMSNorm's sum of squares and the lane's rotary table, and the final
+// argmax over the LM head's per-tile candidates.
 #include "cbd_internal.h"
 
 namespace cbd {
-
-__device__ inline uint16_t f2bf_m(float f) {
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-template <int ACT>
-__device__ inline void put(void* base, size_t idx, float v) {
-  if constexpr (ACT == WT_F32)
-    ((float*)base)[idx] = v;
-  else if constexpr (ACT == WT_BF16)
-    ((uint16_t*)base)[idx] = f2bf_m(v);
-  else
-    ((_Float16*)base)[idx] = (_Float16)v;
-}
 
 // Block sum of per-thread partials (256 threads): a fixed shuffle tree, then
 // the four waves in order.
@@ -34,53 +18,78 @@ __device__ inline float block_sum(float ss) {
   return t;
 }
 
-// RMSNorm: out = (x * r) * g, r = 1 / sqrt(mean(x^2) + eps), in the activation format.
-template <int ACT>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g, int d, float eps, void* xn) {
-  const int b = blockIdx.x;
-  const float* xr = x + (size_t)b * d;
-  float part = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) part += xr[i] * xr[i];
-  const float ss = block_sum(part);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += 256) put<ACT>(xn, (size_t)b * d + i, (xr[i] * r) * g[i]);
-}
-
-// x[b] = E[token_b] (exact upcast of bf16, q * scale of Q8_0), then the first
-// RMSNorm, and the rotary (cos, sin) of the lane's position for every pair:
+// x[b] = E[token_b] (exact upcast of bf16, q * scale of Q8_0), the sum of
+// x[b]^2 for the first RMSNorm (the projections that consume x normalise it),
+// and the rotary (cos, sin) of the lane's position for every pair:
 // theta_j = theta^(-2j/hd), angle = pos * theta_j, in double, rounded to f32.
 template <int WT>
-__global__ __launch_bounds__(256) void k_embed_norm(const void* E, const uint16_t* Es, const int* tokens,
-                                                    const int* pos, int d, int hd, float theta, float eps,
-                                                    const float* g, float* x, void* xn, float2* rope) {
+__global__ __launch_bounds__(256) void k_embed(const void* E, const uint16_t* Es, const int* tokens, const int* pos,
+                                               int d, int hd, float theta, float* x, float* ssq, float2* rope) {
   const int b = blockIdx.x;
   const int tok = tokens[b];
   float* xr = x + (size_t)b * d;
-  auto row = [&](int i) -> float {
+  float part = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float v;
     if constexpr (WT == WT_F32) {
-      return ((const float*)E)[(size_t)tok * d + i];
+      v = ((const float*)E)[(size_t)tok * d + i];
     } else if constexpr (WT == WT_BF16) {
-      return __builtin_bit_cast(float, (unsigned)((const uint16_t*)E)[(size_t)tok * d + i] << 16);
+      v = __builtin_bit_cast(float, (unsigned)((const uint16_t*)E)[(size_t)tok * d + i] << 16);
     } else {
       const float q = (float)((const int8_t*)E)[(size_t)tok * d + i];
       const float s = (float)__builtin_bit_cast(_Float16, Es[(size_t)tok * (d / 32) + i / 32]);
-      return q * s;
+      v = q * s;
     }
-  };
-  float part = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float v = row(i);
     xr[i] = v;
     part += v * v;
   }
   const float ss = block_sum(part);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += 256) put<WT>(xn, (size_t)b * d + i, (row(i) * r) * g[i]);
+  if (threadIdx.x == 0) ssq[b] = ss;
   const int p = pos[b];
   for (int j = threadIdx.x; j < hd / 2; j += 256) {
     const double th = pow((double)theta, -(2.0 * (double)j) / (double)hd);
     const double ang = (double)p * th;
     rope[(size_t)b * (hd / 2) + j] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+__device__ inline uint16_t f2bf_m(float f) {
+  unsigned u = __builtin_bit_cast(unsigned, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// RMSNorm of the residual stream into the activation panel the next
+// projection reads: xn = (x * r) * g with r = 1 / sqrt(mean(x^2) + eps).  The
+// sum of x^2 of lane b is the producer's per-tile partials added in a fixed
+// order (strided per thread, a shuffle tree, then the four waves in order), so
+// every workgroup of the lane gets the same r.  Workgroup (chunk, b) handles
+// 1024 elements of lane b, 4 per thread.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_norm(const float* x, const float* ssq, int ssq_n, const float* g, int B,
+                                              int d, float eps, void* xn) {
+  const int b = blockIdx.y;
+  float part = 0.f;
+  for (int t = threadIdx.x; t < ssq_n; t += 256) part += ssq[(size_t)t * B + b];
+  const float ss = block_sum(part);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= d) return;
+  const float4 xv = *(const float4*)(x + (size_t)b * d + i);
+  const float4 gv = *(const float4*)(g + i);
+  const float v0 = (xv.x * r) * gv.x, v1 = (xv.y * r) * gv.y, v2 = (xv.z * r) * gv.z, v3 = (xv.w * r) * gv.w;
+  const size_t o = (size_t)b * d + i;
+  if constexpr (ACT == WT_F32) {
+    *(float4*)((float*)xn + o) = make_float4(v0, v1, v2, v3);
+  } else if constexpr (ACT == WT_BF16) {
+    *(uint2*)((uint16_t*)xn + o) = make_uint2((unsigned)f2bf_m(v0) | ((unsigned)f2bf_m(v1) << 16),
+                                              (unsigned)f2bf_m(v2) | ((unsigned)f2bf_m(v3) << 16));
+  } else {
+    _Float16* p = (_Float16*)xn + o;
+    p[0] = (_Float16)v0;
+    p[1] = (_Float16)v1;
+    p[2] = (_Float16)v2;
+    p[3] = (_Float16)v3;
   }
 }
 
@@ -114,32 +123,30 @@ __global__ void k_fill_u32(unsigned* p, size_t n, unsigned v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-hipError_t launch_embed_norm(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B,
-                             int d, int hd, float theta, float eps, const float* g, float* x, void* xn,
-                             float2* rope, hipStream_t st) {
+hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B, int d,
+                        int hd, float theta, float* x, float* ssq, float2* rope, hipStream_t st) {
   switch (wt) {
     case WT_F32:
-      hipLaunchKernelGGL(k_embed_norm<WT_F32>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, eps, g,
-                         x, xn, rope);
+      hipLaunchKernelGGL(k_embed<WT_F32>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, x, ssq, rope);
       break;
     case WT_BF16:
-      hipLaunchKernelGGL(k_embed_norm<WT_BF16>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, eps,
-                         g, x, xn, rope);
+      hipLaunchKernelGGL(k_embed<WT_BF16>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, x, ssq,
+                         rope);
       break;
     default:
-      hipLaunchKernelGGL(k_embed_norm<WT_Q8>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, eps, g,
-                         x, xn, rope);
+      hipLaunchKernelGGL(k_embed<WT_Q8>, dim3(B), dim3(256), 0, st, E, Es, tokens, pos, d, hd, theta, x, ssq, rope);
       break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(int wt, const float* x, const float* g, int B, int d, float eps, void* xn,
-                          hipStream_t st) {
+hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, const float* g, int B, int d, float eps,
+                       void* xn, hipStream_t st) {
+  const dim3 grid((d + 1023) / 1024, B);
   switch (wt) {
-    case WT_F32: hipLaunchKernelGGL(k_rmsnorm<WT_F32>, dim3(B), dim3(256), 0, st, x, g, d, eps, xn); break;
-    case WT_BF16: hipLaunchKernelGGL(k_rmsnorm<WT_BF16>, dim3(B), dim3(256), 0, st, x, g, d, eps, xn); break;
-    default: hipLaunchKernelGGL(k_rmsnorm<WT_Q8>, dim3(B), dim3(256), 0, st, x, g, d, eps, xn); break;
+    case WT_F32: hipLaunchKernelGGL(k_norm<WT_F32>, grid, dim3(256), 0, st, x, ssq, ssq_n, g, B, d, eps, xn); break;
+    case WT_BF16: hipLaunchKernelGGL(k_norm<WT_BF16>, grid, dim3(256), 0, st, x, ssq, ssq_n, g, B, d, eps, xn); break;
+    default: hipLaunchKernelGGL(k_norm<WT_Q8>, grid, dim3(256), 0, st, x, ssq, ssq_n, g, B, d, eps, xn); break;
   }
   return hipGetLastError();
 }

@@ -12,6 +12,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <string>
@@ -42,9 +43,9 @@ int fail(int code, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(CBD_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-constexpr int TARGET_WAVES = 2048;  // split-K is chosen so a B=1 step has this many waves
+constexpr int TARGET_WAVES = 4096;  // split-K is chosen so a B=1 step has this many waves
 constexpr int MIN_KS = 256;         // but no split shorter than this many elements
-constexpr int NSLOT = 4;            // pinned staging slots for per-step metadata
+constexpr int NSLOT = 4;  // pinned staging slots for per-step metadata
 
 struct Plan {
   int N, Nraw, K, S, Ks, nRB;
@@ -57,7 +58,7 @@ Plan make_plan(int N, int Nraw, int K, int kstep, int rows_per_rb) {
   p.K = K;
   p.nRB = (N + rows_per_rb - 1) / rows_per_rb;
   int S = (TARGET_WAVES + p.nRB - 1) / p.nRB;
-  S = std::max(1, std::min(S, K / MIN_KS));
+  S = std::max(1, std::min(std::min(S, K / MIN_KS), GEMM_MAX_SPLIT));
   int Ks = (K + S - 1) / S;
   Ks = (Ks + kstep - 1) / kstep * kstep;
   p.Ks = Ks;
@@ -79,6 +80,20 @@ struct cbd_model {
   std::vector<cbd_matrix> qkv, o, gu, down;
   Plan p_qkv, p_o, p_gu, p_down, p_head;
   int variant = 0;
+  // captured step graphs, keyed by everything their kernel arguments depend on
+  struct GraphKey {
+    int B;
+    const void *ws, *arena, *logits, *argmax;
+    size_t ws_bytes;
+    int max_seq, n_lanes;
+    bool operator==(const GraphKey& o) const {
+      return B == o.B && ws == o.ws && arena == o.arena && logits == o.logits && argmax == o.argmax &&
+             ws_bytes == o.ws_bytes && max_seq == o.max_seq && n_lanes == o.n_lanes;
+    }
+  };
+  std::vector<std::pair<GraphKey, hipGraphExec_t>> graphs;
+  hipStream_t cap_stream = nullptr;
+  bool use_graphs = true;
   // pinned staging for per-step metadata
   void* slot[NSLOT] = {};
   size_t slot_bytes[NSLOT] = {};
@@ -91,10 +106,6 @@ struct cbd_model {
   std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> pending;
   double prof_ms[16] = {};
   long long prof_n[16] = {};
-  // the workspace whose counters are known to be zero
-  const void* ws_ready = nullptr;
-  size_t ws_ready_bytes = 0;
-  int ws_ready_seq = 0;
 };
 
 struct cbd_arena {
@@ -111,7 +122,7 @@ struct cbd_arena {
 namespace {
 
 struct WsLayout {
-  size_t cnt_gemm, n_cnt_gemm, cnt_attn, n_cnt_attn, meta, x, xn, qkv, o, a, part, amax, rope, apart, total;
+  size_t meta, x, xn, ssq, qkv, o, a, amax, rope, apart, total;
   int maxB, MS;
 };
 
@@ -126,24 +137,14 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
     off += align256(bytes);
     return o;
   };
-  const Plan* plans[] = {&m->p_qkv, &m->p_o, &m->p_gu, &m->p_down, &m->p_head};
-  size_t ncg = (size_t)(maxB + TILE - 1) / TILE;
-  size_t ncnt = 0, npart = 0;
-  for (const Plan* p : plans) {
-    ncnt = std::max(ncnt, (size_t)p->nRB * ncg);
-    if (p->S > 1) npart = std::max(npart, (size_t)p->S * maxB * p->Nraw);
-  }
-  L.n_cnt_gemm = ncnt;
-  L.n_cnt_attn = (size_t)maxB * c.n_kv_heads;
-  L.cnt_gemm = take(4 * L.n_cnt_gemm);
-  L.cnt_attn = take(4 * L.n_cnt_attn);
-  L.meta = take(4 * ((size_t)3 * maxB + (size_t)2 * maxB * L.MS));
+  L.meta = take(4 * ((size_t)3 * maxB + 1 + (size_t)2 * maxB * L.MS));
   L.x = take(4 * (size_t)maxB * c.d_model);
   L.xn = take((size_t)m->actb * maxB * c.d_model);
+  const int ssq_rows = std::max(std::max(m->p_o.nRB, m->p_down.nRB), 1);
+  L.ssq = take(4 * (size_t)ssq_rows * maxB);
   L.qkv = take(4 * (size_t)maxB * m->n_qkv);
   L.o = take((size_t)m->actb * maxB * m->q_dim);
   L.a = take((size_t)m->actb * maxB * c.ffn_dim);
-  L.part = take(4 * npart);
   L.amax = take(8 * (size_t)m->p_head.nRB * maxB);
   L.rope = take(8 * (size_t)maxB * (c.head_dim / 2));
   L.apart = take(4 * (size_t)maxB * L.MS * c.n_kv_heads * m->G * (c.head_dim + 2));
@@ -173,8 +174,8 @@ int check_matrix(const cbd_matrix& mt, int wt, const char* name) {
   return CBD_OK;
 }
 
-const char* const kClassNames[] = {"meta_copy", "embed_norm", "gemm_qkv", "attention", "gemm_o",
-                                   "rmsnorm",   "gemm_gu",    "gemm_down", "gemm_head", "argmax"};
+const char* const kClassNames[] = {"meta_copy", "embed", "gemm_qkv", "attention", "gemm_o",
+                                   "rmsnorm",   "gemm_gu", "gemm_down", "gemm_head", "argmax"};
 enum { P_META, P_EMBED, P_QKV, P_ATTN, P_O, P_NORM, P_GU, P_DOWN, P_HEAD, P_ARGMAX, P_N };
 
 hipEvent_t take_event(cbd_model* m) {
@@ -283,12 +284,11 @@ int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** ou
     m->gu.push_back(w->w_gu[l]);
     m->down.push_back(w->w_down[l]);
   }
-  const int rows = TILE * GEMM_R;
-  m->p_qkv = make_plan(m->n_qkv, m->n_qkv, c.d_model, m->kstep, rows);
-  m->p_o = make_plan(c.d_model, c.d_model, qd, m->kstep, rows);
-  m->p_gu = make_plan(c.ffn_dim, 2 * c.ffn_dim, c.d_model, m->kstep, rows / 2);
-  m->p_down = make_plan(c.d_model, c.d_model, c.ffn_dim, m->kstep, rows);
-  m->p_head = make_plan(c.vocab, c.vocab, c.d_model, m->kstep, rows);
+  m->p_qkv = make_plan(m->n_qkv, m->n_qkv, c.d_model, m->kstep, TILE * gemm_rows(EPI_STORE));
+  m->p_o = make_plan(c.d_model, c.d_model, qd, m->kstep, TILE * gemm_rows(EPI_RESID));
+  m->p_gu = make_plan(c.ffn_dim, 2 * c.ffn_dim, c.d_model, m->kstep, TILE * gemm_rows(EPI_SWIGLU) / 2);
+  m->p_down = make_plan(c.d_model, c.d_model, c.ffn_dim, m->kstep, TILE * gemm_rows(EPI_RESID));
+  m->p_head = make_plan(c.vocab, c.vocab, c.d_model, m->kstep, TILE * gemm_rows(EPI_HEAD));
   *out = m;
   return CBD_OK;
 }
@@ -297,6 +297,8 @@ void cbd_model_destroy(cbd_model* m) {
   if (!m) return;
   (void)drain_profile(m, true);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.second);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   for (int i = 0; i < NSLOT; ++i) {
     if (m->ev[i]) {
       (void)hipEventSynchronize(m->ev[i]);
@@ -320,6 +322,9 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   if ((uintptr_t)dev_mem & 255u) return fail(CBD_E_ARG, "arena memory must be 256-byte aligned");
   const size_t need = cbd_arena_bytes(&m->c, n_lanes, max_seq);
   if (dev_bytes < need) return fail(CBD_E_ARG, "arena needs %zu bytes, got %zu", need, dev_bytes);
+  if ((long long)(max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * m->G > ATTN_MAX_STATS)
+    return fail(CBD_E_UNSUPPORTED, "max_seq %d too long: ceil(max_seq / %d) * %d query heads per KV head exceeds %d",
+                max_seq, ATTN_SPLIT, m->G, ATTN_MAX_STATS);
   cbd_arena* a = new cbd_arena();
   a->m = m;
   a->n_lanes = n_lanes;
@@ -437,6 +442,12 @@ int cbd_profile_classes(void) { return P_N; }
 
 const char* cbd_profile_class_name(int cls) { return cls >= 0 && cls < P_N ? kClassNames[cls] : nullptr; }
 
+int cbd_set_graph_replay(cbd_model* m, int enable) {
+  if (!m) return fail(CBD_E_ARG, "null model");
+  m->use_graphs = enable != 0;
+  return CBD_OK;
+}
+
 int cbd_set_variant(cbd_model* m, int variant) {
   if (!m || variant < 0 || variant > 1) return fail(CBD_E_ARG, "variant must be 0 or 1");
   m->variant = variant;
@@ -460,12 +471,85 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.nCG = (B + TILE * C - 1) / (TILE * C);
   g.out = out;
   g.act_out = act_out;
-  g.part = (float*)(ws + L.part);
-  g.cnt = (unsigned*)(ws + L.cnt_gemm);
   g.amax = (float2*)(ws + L.amax);
-  const int n_waves = g.nRB * g.S * g.nCG;
+  g.ssq_out = (float*)(ws + L.ssq);
   ProfScope ps(m, cls, st);
-  HIP_TRY(launch_gemm(m->wt, epi, C, g, n_waves, st));
+  HIP_TRY(launch_gemm(m->wt, epi, C, g, st));
+  return CBD_OK;
+}
+
+// Every kernel of one step, in order, on `st` (plain launches or a capture).
+// Arguments depend only on (B, workspace layout, arena, outputs): the per-step
+// data (lanes, positions, tokens, attention items) is read from the workspace.
+static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLayout& L, float* logits,
+                        int32_t* argmax, hipStream_t st) {
+  const cbd_config& c = m->c;
+  const int32_t* dmeta = (const int32_t*)(ws + L.meta);
+  const int* d_lanes = dmeta;
+  const int* d_pos = dmeta + B;
+  const int* d_tok = dmeta + 2 * B;
+  const int* d_nitems = dmeta + 3 * B;
+  const int* d_items = dmeta + 3 * B + 1;
+  float* x = (float*)(ws + L.x);
+  float* ssq = (float*)(ws + L.ssq);
+  float* qkv = (float*)(ws + L.qkv);
+  void* o = ws + L.o;
+  void* act = ws + L.a;
+  float2* rope = (float2*)(ws + L.rope);
+  const int d = c.d_model;
+
+  {
+    ProfScope ps(m, P_EMBED, st);
+    HIP_TRY(launch_embed(m->wt, m->embed.data, (const uint16_t*)m->embed.scale, d_tok, d_pos, B, d, c.head_dim,
+                         c.rope_theta, x, ssq, rope, st));
+  }
+  AttnArgs at{};
+  at.qkv = qkv;
+  at.kslab = a->base;
+  at.vslab = a->base + a->region_bytes;
+  at.lane_stride = a->lane_stride;
+  at.max_seq = a->max_seq;
+  at.B = B;
+  at.lanes = d_lanes;
+  at.pos = d_pos;
+  at.items = d_items;
+  at.n_items_dev = d_nitems;
+  at.max_items = B * L.MS;
+  at.max_splits = L.MS;
+  at.Hq = c.n_heads;
+  at.Hkv = c.n_kv_heads;
+  at.G = m->G;
+  at.Nqkv = m->n_qkv;
+  at.rope = rope;
+  at.part = (float*)(ws + L.apart);
+  at.out = o;
+  int rc;
+  void* xn = ws + L.xn;
+  // RMSNorm of x into xn; ssq_n = row blocks of the last producer of x (the embedding: one)
+  auto norm = [&](const float* g, int ssq_n) -> int {
+    ProfScope ps(m, P_NORM, st);
+    HIP_TRY(launch_norm(m->wt, x, ssq, ssq_n, g, B, d, c.rms_eps, xn, st));
+    return CBD_OK;
+  };
+  if ((rc = norm(m->attn_norm[0], 1))) return rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
+    at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
+    {
+      ProfScope ps(m, P_ATTN, st);
+      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
+    }
+    if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
+    if ((rc = norm(m->ffn_norm[l], m->p_o.nRB))) return rc;
+    if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
+    if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
+    if ((rc = norm(l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm, m->p_down.nRB))) return rc;
+  }
+  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
+  if (argmax) {
+    ProfScope ps(m, P_ARGMAX, st);
+    HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+  }
   return CBD_OK;
 }
 
@@ -502,20 +586,14 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
 
-  // Counters must be zero; every kernel that uses them leaves them zero.
-  if (m->ws_ready != workspace || m->ws_ready_bytes != workspace_bytes || m->ws_ready_seq != a->max_seq) {
-    HIP_TRY(launch_fill_u32((unsigned*)(ws + L.cnt_gemm), (L.cnt_attn - L.cnt_gemm) / 4 + L.n_cnt_attn, 0u, st));
-    m->ws_ready = workspace;
-    m->ws_ready_bytes = workspace_bytes;
-    m->ws_ready_seq = a->max_seq;
-  }
-
-  // Per-step metadata: lanes, positions, tokens, attention work items (b, split).
+  // Per-step metadata: lanes, positions, tokens, item count, attention work
+  // items (b, chunk).
   std::vector<int32_t> meta;
-  meta.reserve((size_t)3 * B + 2 * (size_t)B * L.MS);
+  meta.reserve((size_t)3 * B + 1 + 2 * (size_t)B * L.MS);
   meta.insert(meta.end(), lanes, lanes + B);
   meta.insert(meta.end(), positions, positions + B);
   meta.insert(meta.end(), tokens, tokens + B);
+  meta.push_back(0);
   int n_items = 0;
   for (int b = 0; b < B; ++b) {
     const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
@@ -525,6 +603,7 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
       ++n_items;
     }
   }
+  meta[3 * B] = n_items;
   const size_t meta_bytes = meta.size() * 4;
   const int si = m->next_slot;
   m->next_slot = (si + 1) % NSLOT;
@@ -546,69 +625,37 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   }
   HIP_TRY(hipEventRecord(m->ev[si], st));
   m->ev_live[si] = true;
-  const int* d_lanes = dmeta;
-  const int* d_pos = dmeta + B;
-  const int* d_tok = dmeta + 2 * B;
-  const int* d_items = dmeta + 3 * B;
 
-  float* x = (float*)(ws + L.x);
-  void* xn = ws + L.xn;
-  float* qkv = (float*)(ws + L.qkv);
-  void* o = ws + L.o;
-  void* act = ws + L.a;
-  float2* rope = (float2*)(ws + L.rope);
-  const int d = c.d_model;
-
-  {
-    ProfScope ps(m, P_EMBED, st);
-    HIP_TRY(launch_embed_norm(m->wt, m->embed.data, (const uint16_t*)m->embed.scale, d_tok, d_pos, B, d, c.head_dim,
-                              c.rope_theta, c.rms_eps, m->attn_norm[0], x, xn, rope, st));
-  }
-  AttnArgs at{};
-  at.qkv = qkv;
-  at.kslab = a->base;
-  at.vslab = a->base + a->region_bytes;
-  at.lane_stride = a->lane_stride;
-  at.max_seq = a->max_seq;
-  at.B = B;
-  at.lanes = d_lanes;
-  at.pos = d_pos;
-  at.items = d_items;
-  at.n_items = n_items;
-  at.max_splits = L.MS;
-  at.Hq = c.n_heads;
-  at.Hkv = c.n_kv_heads;
-  at.G = m->G;
-  at.Nqkv = m->n_qkv;
-  at.rope = rope;
-  at.part = (float*)(ws + L.apart);
-  at.cnt = (unsigned*)(ws + L.cnt_attn);
-  at.out = o;
   int rc;
-  for (int l = 0; l < c.n_layers; ++l) {
-    if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
-    at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
-    {
-      ProfScope ps(m, P_ATTN, st);
-      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
+  const bool graph = m->use_graphs && !m->prof;
+  if (!graph) {
+    if ((rc = enqueue_step(m, a, B, ws, L, logits, argmax, st))) return rc;
+  } else {
+    const cbd_model::GraphKey key{B, workspace, a->base, logits, argmax, workspace_bytes, a->max_seq, a->n_lanes};
+    hipGraphExec_t exec = nullptr;
+    for (auto& g : m->graphs)
+      if (g.first == key) exec = g.second;
+    if (!exec) {
+      if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+      hipGraph_t graph_def = nullptr;
+      HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+      rc = enqueue_step(m, a, B, ws, L, logits, argmax, m->cap_stream);
+      hipError_t e = hipStreamEndCapture(m->cap_stream, &graph_def);
+      if (rc) {
+        if (graph_def) (void)hipGraphDestroy(graph_def);
+        return rc;
+      }
+      if (e != hipSuccess) return fail(CBD_E_HIP, "graph capture failed: %s", hipGetErrorString(e));
+      e = hipGraphInstantiate(&exec, graph_def, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph_def);
+      if (e != hipSuccess) return fail(CBD_E_HIP, "graph instantiate failed: %s", hipGetErrorString(e));
+      if (m->graphs.size() >= 64) {
+        (void)hipGraphExecDestroy(m->graphs.front().second);
+        m->graphs.erase(m->graphs.begin());
+      }
+      m->graphs.push_back({key, exec});
     }
-    if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
-    {
-      ProfScope ps(m, P_NORM, st);
-      HIP_TRY(launch_rmsnorm(m->wt, x, m->ffn_norm[l], B, d, c.rms_eps, xn, st));
-    }
-    if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
-    if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
-    const float* g_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
-    {
-      ProfScope ps(m, P_NORM, st);
-      HIP_TRY(launch_rmsnorm(m->wt, x, g_next, B, d, c.rms_eps, xn, st));
-    }
-  }
-  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
-  if (argmax) {
-    ProfScope ps(m, P_ARGMAX, st);
-    HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+    HIP_TRY(hipGraphLaunch(exec, st));
   }
   if (m->prof && (rc = drain_profile(m, false))) return rc;
 

@@ -73,6 +73,8 @@ def kernel_bytes(cfg, cls: str, positions: Sequence[int]) -> float:
     wb = _wbytes_per_elem(cfg.wtype)
     ab = act_bytes(cfg.wtype)
     d, F, V = cfg.d, cfg.ffn, cfg.vocab
+    # projections that consume the normalised stream read it in the activation
+    # format; the residual projections read and write the f32 residual x
     if cls == "gemm_qkv":
         return cfg.n_qkv * d * wb + B * d * ab + B * cfg.n_qkv * 4
     if cls == "gemm_o":
@@ -88,8 +90,8 @@ def kernel_bytes(cfg, cls: str, positions: Sequence[int]) -> float:
         return sum(positions) * per_pos + B * per_pos + B * (cfg.n_qkv * 4 + cfg.q_dim * ab)
     if cls == "rmsnorm":
         return B * d * 4 + B * d * ab + d * 4
-    if cls == "embed_norm":
-        return B * d * (wb + 4 + ab) + d * 4
+    if cls == "embed":
+        return B * d * (wb + 4)
     return 0.0
 
 

@@ -126,7 +126,10 @@ size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq);
 
 /* Create a lane arena over caller-owned device memory dev_mem of dev_bytes
  * (>= cbd_arena_bytes) bytes, 256-byte aligned.  All lanes start free.
- * Errors: CBD_E_ARG. */
+ * Attention combines per-64-key chunk statistics in on-chip memory, which
+ * bounds max_seq: ceil(max_seq / 64) * (n_heads / n_kv_heads) <= 8000
+ * (128000 positions at 4 query heads per KV head).
+ * Errors: CBD_E_ARG, CBD_E_UNSUPPORTED (max_seq beyond that bound). */
 int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes,
                      cbd_arena** out);
 void cbd_arena_destroy(cbd_arena* a);
@@ -203,6 +206,13 @@ int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launche
 /* Number of kernel classes, and the name of class `cls` (NULL if out of range). */
 int cbd_profile_classes(void);
 const char* cbd_profile_class_name(int cls);
+
+/* Step launch mode of this model: 1 (default) = each step's kernel sequence is
+ * captured once per (B, workspace, arena, outputs) into a HIP graph and
+ * replayed on the caller's stream; 0 = plain kernel launches.  Both run the
+ * same kernels with the same arguments, so results are bitwise identical.
+ * While profiling is enabled, steps launch plainly.  Errors: CBD_E_ARG. */
+int cbd_set_graph_replay(cbd_model* m, int enable);
 
 /* Projection kernel family for steps of this model: 0 = automatic by batch
  * width, 1 = weight-streaming split-K tiles at every width.  Every family

@@ -175,3 +175,23 @@ def test_errors_on_gpu_kv_full_evicted_and_usage():
     assert e.value.name == "CBD_E_LANE_NOT_LIVE"
     a.lane_evict(l0)
     assert a.used_bytes == 0 and a.live_lanes == 0
+
+
+def test_graph_replay_matches_plain_launches_bitwise():
+    # The same steps with graph replay (captured once, replayed every step, with host
+    # synchronisation and eager work between replays) and with plain launches.
+    from continuous_batching_decode_step_amd.driver import generate_lockstep
+    for cfg in (SMALL_GQA, SMALL_GQA.with_wtype(synth.WTYPE_BF16), synth.TINY):
+        say("case: graph replay vs plain, %s wtype %d" % (cfg.name, cfg.wtype))
+        W = synth.make_weights(cfg)
+        prompts = [synth.prompt_tokens(cfg, 60 + b, n) for b, n in enumerate([4, 2, 6])]
+        runs = []
+        for graphs in (False, True):
+            eng = engine_for(cfg, W, 3, 16)
+            eng.model.set_graph_replay(graphs)
+            gen, logs = generate_lockstep(eng, prompts, 5, want_logits=True)
+            runs.append((gen, logs))
+        assert runs[0][0] == runs[1][0]
+        for la, lb in zip(runs[0][1], runs[1][1]):
+            for x, y in zip(la, lb):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

@@ -63,12 +63,16 @@ class Engine:
         return k, v
 
 
-def generate_lockstep(eng: Engine, prompts: Sequence[Sequence[int]], n_new, want_logits: bool = False):
+def generate_lockstep(eng: Engine, prompts: Sequence[Sequence[int]], n_new, want_logits=False):
     """Greedy generation of B jobs in lockstep, one batched step over the lanes still live.
 
-    Returns (tokens per job, logits per job per step or None)."""
+    want_logits: False, True (every step of every job), or a predicate
+    keep(job, step) selecting the steps whose logits are copied back (the step
+    index counts the job's own steps from 0).  Returns (tokens per job, logits
+    per job per step or None; unselected steps hold None)."""
     B = len(prompts)
     n_new = [n_new] * B if np.isscalar(n_new) else list(n_new)
+    keep = (lambda b, i: True) if want_logits is True else (want_logits or None)
     lanes = [eng.arena.lane_alloc() for _ in range(B)]
     pos = np.zeros(B, np.int32)
     feed = [0] * B
@@ -81,18 +85,22 @@ def generate_lockstep(eng: Engine, prompts: Sequence[Sequence[int]], n_new, want
             break
         toks = [int(prompts[b][feed[b]]) if feed[b] < len(prompts[b]) else last[b] for b in live]
         p = pos[live].copy()
-        am, lg = eng.step_sync([lanes[b] for b in live], p, toks, want_logits)
+        eng.step([lanes[b] for b in live], p, toks)
+        am = eng.argmax[:len(live)].cpu().numpy()
+        rows = [i for i, b in enumerate(live) if keep is not None and keep(b, feed[b])]
+        lg = eng.logits[rows].cpu().numpy() if rows else None
+        at = {i: j for j, i in enumerate(rows)}
         pos[live] = p
         for i, b in enumerate(live):
+            if keep is not None:
+                logs[b].append(lg[at[i]] if i in at else None)
             feed[b] += 1
-            if want_logits:
-                logs[b].append(lg[i])
             if feed[b] >= len(prompts[b]):
                 last[b] = int(am[i])
                 gen[b].append(last[b])
     for l in lanes:
         eng.arena.lane_evict(l)
-    return gen, (logs if want_logits else None)
+    return gen, (logs if keep is not None else None)
 
 
 @dataclass

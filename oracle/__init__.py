@@ -14,8 +14,12 @@ token per step, the step that feeds the last prompt token yields generated
 token 1, and every generated token but the last is fed back, so a job with a
 prompt of P tokens and n new tokens takes P + n - 1 steps.
 
-Parity status of each piece is listed in the design doc; the pins are in
-``tests/test_oracle_pins.py`` and ``tests/test_oracle_invariants.py``.
+Two builds of the same source: the default accumulates every sum in double
+(sums exact up to double rounding, rounded to f32 where a value is stored);
+``accumulate="f32"`` builds it with f32 accumulators instead.  The second is a
+plain f32 evaluation of the same definition; comparing the two measures how
+far any correct f32-accumulating implementation can drift from the exact
+result at a given shape (used to size bf16 parity bars at full depth).
 """
 from __future__ import annotations
 
@@ -28,20 +32,22 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
-_lib = None
+_LIBS = {"exact": os.path.join(_HERE, "liboracle.so"), "f32": os.path.join(_HERE, "liboracle_f32acc.so")}
+_DEFS = {"exact": [], "f32": ["-DORC_ACC=float"]}
+_lib = {}
 
 ORC_F32, ORC_BF16, ORC_Q8_0 = 0, 1, 2
 
 
-def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc: -O2, no fast-math, no FMA contraction, OpenMP."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = False, accumulate: str = "exact") -> str:
+    """Compile the oracle library with gcc: -O2, no fast-math, no FMA contraction, OpenMP."""
+    out = _LIBS[accumulate]
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp"]
+                              + _DEFS[accumulate] + ["-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _Config(ctypes.Structure):
@@ -62,11 +68,9 @@ class _Weights(ctypes.Structure):
                 ("w_gu", ctypes.POINTER(_Mat)), ("w_down", ctypes.POINTER(_Mat))]
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+def lib(accumulate: str = "exact"):
+    if accumulate not in _lib:
+        L = ctypes.CDLL(build(accumulate=accumulate))
         vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
         L.orc_model_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights)]
         L.orc_model_create.restype = vp
@@ -102,8 +106,8 @@ def lib():
         for f in (L.orc_model_destroy, L.orc_lane_destroy, L.orc_lane_clear, L.orc_matvec, L.orc_rmsnorm,
                   L.orc_rope_cs, L.orc_rope, L.orc_attention):
             f.restype = None
-        _lib = L
-    return _lib
+        _lib[accumulate] = L
+    return _lib[accumulate]
 
 
 def _p(a: np.ndarray) -> int:
@@ -184,9 +188,13 @@ def num_threads() -> int:
 # ---- model -------------------------------------------------------------------
 
 class Model:
-    """Borrows the arrays of a ``synth.Weights`` (kept alive by this object)."""
+    """Borrows the arrays of a ``synth.Weights`` (kept alive by this object).
 
-    def __init__(self, W):
+    accumulate: "exact" (double accumulators, the oracle) or "f32" (the same
+    definition with f32 accumulators)."""
+
+    def __init__(self, W, accumulate: str = "exact"):
+        self.L = lib(accumulate)
         c = W.cfg
         self.cfg = c
         self.W = W
@@ -205,13 +213,13 @@ class Model:
                            ctypes.cast(self._attn, ctypes.POINTER(ctypes.c_void_p)),
                            ctypes.cast(self._ffn, ctypes.POINTER(ctypes.c_void_p)),
                            self._qkv, self._o, self._gu, self._down)
-        self.h = lib().orc_model_create(ctypes.byref(self._cfg), ctypes.byref(self._w))
+        self.h = self.L.orc_model_create(ctypes.byref(self._cfg), ctypes.byref(self._w))
         if not self.h:
             raise ValueError("oracle rejected the model config")
 
     def __del__(self):
         if getattr(self, "h", None):
-            lib().orc_model_destroy(self.h)
+            self.L.orc_model_destroy(self.h)
             self.h = None
 
     def lane(self, max_seq: int) -> "Lane":
@@ -219,7 +227,7 @@ class Model:
 
     def step(self, lane: "Lane", token: int) -> np.ndarray:
         out = np.empty(self.cfg.vocab, dtype=np.float32)
-        rc = lib().orc_step(self.h, lane.h, int(token), _p(out))
+        rc = self.L.orc_step(self.h, lane.h, int(token), _p(out))
         if rc != 0:
             raise ValueError("oracle step rejected (token out of range or lane full)")
         return out
@@ -229,7 +237,7 @@ class Model:
         toks = np.ascontiguousarray(tokens, dtype=np.int32)
         arr = (ctypes.c_void_p * B)(*[ln.h for ln in lanes])
         out = np.empty((B, self.cfg.vocab), dtype=np.float32)
-        rc = lib().orc_step_batch(self.h, arr, B, _p(toks), _p(out))
+        rc = self.L.orc_step_batch(self.h, arr, B, _p(toks), _p(out))
         if rc != 0:
             raise ValueError("oracle batch step rejected (rc=%d)" % rc)
         return out
@@ -238,28 +246,29 @@ class Model:
 class Lane:
     def __init__(self, model: Model, max_seq: int):
         self.model = model
+        self.L = model.L
         self.max_seq = max_seq
-        self.h = lib().orc_lane_create(model.h, max_seq)
+        self.h = self.L.orc_lane_create(model.h, max_seq)
         if not self.h:
             raise MemoryError("oracle lane allocation failed")
 
     def __del__(self):
         if getattr(self, "h", None):
-            lib().orc_lane_destroy(self.h)
+            self.L.orc_lane_destroy(self.h)
             self.h = None
 
     def clear(self):
-        lib().orc_lane_clear(self.h)
+        self.L.orc_lane_clear(self.h)
 
     @property
     def length(self) -> int:
-        return lib().orc_lane_length(self.h)
+        return self.L.orc_lane_length(self.h)
 
     def set_kv(self, k: np.ndarray, v: np.ndarray):
         """k, v: f32 ``[L, Hkv, length, hd]`` (post-rotary keys)."""
         k, v = _f32(k), _f32(v)
         c = self.model.cfg
-        if lib().orc_lane_set_kv(self.h, k.shape[2], c.head_dim, _p(k), _p(v)) != 0:
+        if self.L.orc_lane_set_kv(self.h, k.shape[2], c.head_dim, _p(k), _p(v)) != 0:
             raise ValueError("length exceeds the lane capacity")
 
     def get_kv(self):
@@ -268,7 +277,7 @@ class Lane:
         shape = (c.n_layers, c.n_kv_heads, n, c.head_dim)
         k = np.empty(shape, dtype=np.float32)
         v = np.empty(shape, dtype=np.float32)
-        lib().orc_lane_get_kv(self.h, c.head_dim, _p(k), _p(v))
+        self.L.orc_lane_get_kv(self.h, c.head_dim, _p(k), _p(v))
         return k, v
 
 

@@ -285,6 +285,7 @@ def make_weights(cfg: ModelConfig, seed: int = SEED_WEIGHTS, std: float = 0.02,
     from are ``make_weights(cfg, wtype=WTYPE_F32)``: the same draws).
     """
     wt = cfg.wtype if wtype is None else wtype
+    cfg = cfg.with_wtype(wt)
     ones = np.ones(cfg.d, dtype=np.float32)
     W = Weights(cfg=cfg,
                 embed=_make_matrix(cfg, seed, stream_id("embed"), (cfg.vocab, cfg.d), wt, std),

@@ -4,11 +4,23 @@ synthetic post-rotary K/V (seed 3), one decode step over the first B lanes
 for B in {1, 2, 4, 8, 16, 32, 64}.
 
 Checked: sampled lanes' logits against the CPU oracle (teacher-forced: same
-token, same cache) within 2e-2 max relative error; the same lane's logits are
-bit-identical at every B; the GPU argmax equals the argmax of the GPU logits;
-the step writes the new K/V at slot len_b (within 2e-2 of the oracle's) and
-leaves the older slots untouched.
+token, same cache); the same lane's logits are bit-identical at every B; the
+GPU argmax equals the argmax of the GPU logits; the step writes the new K/V
+at slot len_b and leaves the older slots untouched.
+
+The bar.  At this depth bf16 activations amplify rounding-order differences:
+the oracle built with f32 accumulators (the same definition, every bf16
+rounding point the same) differs from the exact-sum oracle by 1.5-2.1% in
+max relative logit error on the sampled lanes (tests/golden/bf16_7b_floor.json,
+written by tests/golden/make_bf16_7b_floor.py from the oracle alone).  Any
+correct f32-accumulating implementation lands near that floor, so each lane
+is held to max(2e-2, 1.5 x its floor), for the logits and for the appended
+K/V of all layers.  Layer 0's appended K/V depends on one projection only and
+is held to 2^-8 (a flipped bf16 rounding of single elements at most).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -20,19 +32,24 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BATCHES = [1, 2, 4, 8, 16, 32, 64]
 SAMPLE = [0, 7, 63]
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_7b_floor.json")) as _f:
+    FLOOR = json.load(_f)["lanes"]
+LAYER0_TOL = 2.0 ** -8
+
+
+def _bar(b, key):
+    return max(TOL_BF16, 1.5 * FLOOR[str(b)][key])
 
 
 @pytest.fixture(scope="module")
-def setup7b():
+def setup7b(weights_7b, device_weights_7b):
     import torch
-    import continuous_batching_decode_step_amd as cbd
     from continuous_batching_decode_step_amd.driver import Engine
     cfg = synth.MISTRAL7B
-    say("7B: generating weights")
-    W = synth.make_weights(cfg)
+    W = weights_7b
     lens = synth.kv_lengths(64)
     toks = synth.step_tokens(cfg, 64)
-    eng = Engine(cfg, cbd.upload_weights(W), 64, int(lens.max()) + 1, max_batch=64)
+    eng = Engine(cfg, device_weights_7b, 64, int(lens.max()) + 1, max_batch=64)
     lanes = [eng.arena.lane_alloc() for _ in range(64)]
     kv = {}
     say("7B: loading KV of 64 lanes")
@@ -71,13 +88,19 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         lane.set_kv(synth.bf16_to_f32(k), synth.bf16_to_f32(v))
         say("7B: oracle lane %d (len %d)" % (b, n))
         ref = M.step(lane, int(toks[b]))
+        assert FLOOR[str(b)]["kv_len"] == n and FLOOR[str(b)]["token"] == int(toks[b])
         err = rel_err(got[b], ref)
-        say("7B: lane %d max rel err %.3g" % (b, err))
-        assert err <= TOL_BF16
+        say("7B: lane %d max rel err %.4g (bar %.4g, f32-accumulation floor %.4g)" % (
+            b, err, _bar(b, "max_rel"), FLOOR[str(b)]["max_rel"]))
+        assert err <= _bar(b, "max_rel")
         # KV: old slots untouched, new slot close to the oracle's
         gk, gv = eng.kv_export(lanes[b])
         assert gk.shape[2] == n + 1
         assert np.array_equal(gk[:, :, :n], k) and np.array_equal(gv[:, :, :n], v)
         ok, ov = lane.get_kv()
-        assert rel_err(synth.bf16_to_f32(gk[:, :, n]), ok[:, :, n]) <= TOL_BF16
-        assert rel_err(synth.bf16_to_f32(gv[:, :, n]), ov[:, :, n]) <= TOL_BF16
+        gkn, gvn = synth.bf16_to_f32(gk[:, :, n]), synth.bf16_to_f32(gv[:, :, n])
+        ek, ev = rel_err(gkn, ok[:, :, n]), rel_err(gvn, ov[:, :, n])
+        ek0, ev0 = rel_err(gkn[0], ok[0, :, n]), rel_err(gvn[0], ov[0, :, n])
+        say("7B: lane %d new K/V rel err %.3g / %.3g, layer 0 %.3g / %.3g" % (b, ek, ev, ek0, ev0))
+        assert ek <= _bar(b, "k_new_max_rel") and ev <= _bar(b, "v_new_max_rel")
+        assert ek0 <= LAYER0_TOL and ev0 <= LAYER0_TOL

@@ -256,3 +256,22 @@ def test_q8_0_oracle_is_faithful_to_f32_oracle():
         a, b = Mf.step(lf, t).astype(np.float64), Mq.step(lq, t).astype(np.float64)
         cos.append(a @ b / np.linalg.norm(a) / np.linalg.norm(b))
     assert min(cos) > 0.999
+
+
+def test_f32_accumulation_build_is_the_same_definition():
+    # The accumulate="f32" build differs from the exact-sum oracle only by the
+    # rounding of its sums: on a small f32 model the logits agree to ~1e-6, and
+    # the two builds are not bit-identical (the flag took effect).
+    cfg = synth.TINY
+    W = synth.make_weights(cfg)
+    prompts = [synth.prompt_tokens(cfg, b, n) for b, n in enumerate([3, 5])]
+    exact = oracle.generate_lockstep(oracle.Model(W), prompts, 4, return_logits=True)
+    f32 = oracle.generate_lockstep(oracle.Model(W, accumulate="f32"), prompts, 4, return_logits=True)
+    assert exact[0] == f32[0]
+    worst, same = 0.0, True
+    for la, lb in zip(exact[1], f32[1]):
+        for x, y in zip(la, lb):
+            worst = max(worst, float(np.max(np.abs(x - y)) / np.max(np.abs(x))))
+            same = same and np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert worst < 1e-5
+    assert not same

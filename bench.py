@@ -32,6 +32,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Source files of each kernel class: stored counter readings apply only while these are unchanged.
+KERNEL_SOURCES = {
+    "attention": ["cbd_attn.hip", "cbd_internal.h"],
+    "attn_combine": ["cbd_attn.hip", "cbd_internal.h"],
+    "gemm_qkv": ["cbd_gemm.hip", "cbd_internal.h"], "gemm_o": ["cbd_gemm.hip", "cbd_internal.h"],
+    "gemm_gu": ["cbd_gemm.hip", "cbd_internal.h"], "gemm_down": ["cbd_gemm.hip", "cbd_internal.h"],
+    "gemm_head": ["cbd_gemm.hip", "cbd_internal.h"], "rmsnorm": ["cbd_misc.hip", "cbd_internal.h"],
+}
+
+
+def kernel_source_hash(cls: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(cls, []):
+        with open(os.path.join(ROOT, "continuous_batching_decode_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(cls: str, B: int):
+    """HBM bytes per launch of `cls` at batch B from profiles/traffic.md (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs scaled by a plain copy), or None if absent or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash(cls)
+    with open(path) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 8 and cells[0] == cls and cells[1] == str(B) and cells[2] == want:
+                try:
+                    return float(cells[7])
+                except ValueError:
+                    return None
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -41,6 +78,9 @@ def main() -> int:
     ap.add_argument("--lanes", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="end with one device-to-device copy of MIB MiB (a known-size kernel for "
+                         "scaling HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -67,13 +107,10 @@ def main() -> int:
     max_seq = int(lens.max()) + 1
     eng = Engine(cfg, dw, n_lanes, max_seq, max_batch=max(batches))
     lanes = [eng.arena.lane_alloc() for _ in range(n_lanes)]
-    keep_kv = {}
     t0 = time.time()
     for b in range(n_lanes):
         k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
         eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
-        if b < 8 and not args.no_cpu_baseline:
-            keep_kv[b] = (k, v)
     torch.cuda.synchronize()
     log("KV of %d lanes generated and loaded in %.1fs" % (n_lanes, time.time() - t0))
 
@@ -127,8 +164,9 @@ def main() -> int:
     dom = max((k for k in per if per[k]["alg_bytes"] > 0), key=lambda k: per[k]["total_ms"])
     d = per[dom]
     achieved = d["achieved_GBs"]
+    traffic = stored_traffic(dom, B)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / rf.HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+            "frac": round(achieved / rf.HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
             "alg_bytes_per_launch": d["alg_bytes"], "avg_launch_us": round(d["avg_us"], 2),
             "launches": d["launches"]}
 
@@ -137,8 +175,8 @@ def main() -> int:
         import oracle
         M = oracle.Model(W)
         done, t_cpu = 0, 0.0
-        for b in sorted(keep_kv):
-            k, v = keep_kv[b]
+        for b in range(n_lanes):
+            k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))  # regenerated, not timed
             lane = M.lane(int(lens[b]) + 1)
             lane.set_kv(synth.bf16_to_f32(k), synth.bf16_to_f32(v))
             t1 = time.perf_counter()
@@ -150,8 +188,18 @@ def main() -> int:
                 break
         cpu = {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "%d lane-steps of the same workload (lanes 0..%d at their KV lengths, one decode step "
-                         "each, serial f32 oracle on bf16 weights), %.1f s" % (done, done - 1, t_cpu)}
+                         "each, serial CPU oracle on bf16 weights: sums in double, values stored in f32), %.1f s" % (done, done - 1, t_cpu)}
         log("cpu oracle: %s" % cpu)
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes read and written" % n)
+        del src, dst
 
     out = {
         "metric": "aggregate decode tokens/s vs batch B; % HBM roofline",

@@ -417,18 +417,20 @@ static hipError_t launch_hd(int kv_bf16, int G, const AttnArgs& a, dim3 grid, hi
   return kv_bf16 ? launch_g<HD, true>(G, a, grid, st) : launch_g<HD, false>(G, a, grid, st);
 }
 
-hipError_t launch_attn(int hd, int kv_bf16, int act, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
   const dim3 grid(a.max_items, a.Hkv);
-  hipError_t e;
   switch (hd) {
-    case 16: e = launch_hd<16>(kv_bf16, a.G, a, grid, st); break;
-    case 32: e = launch_hd<32>(kv_bf16, a.G, a, grid, st); break;
-    case 64: e = launch_hd<64>(kv_bf16, a.G, a, grid, st); break;
-    case 128: e = launch_hd<128>(kv_bf16, a.G, a, grid, st); break;
+    case 16: return launch_hd<16>(kv_bf16, a.G, a, grid, st);
+    case 32: return launch_hd<32>(kv_bf16, a.G, a, grid, st);
+    case 64: return launch_hd<64>(kv_bf16, a.G, a, grid, st);
+    case 128: return launch_hd<128>(kv_bf16, a.G, a, grid, st);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
+}
+
+hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st) {
+  if (a.max_items <= 0) return hipSuccess;
   if ((size_t)a.max_splits * a.G > ATTN_MAX_STATS) return hipErrorInvalidValue;
   const dim3 cgrid(a.B, a.Hkv);
   const size_t lds = (8 + 2 * (size_t)a.max_splits * a.G) * sizeof(float);

@@ -75,7 +75,10 @@ struct AttnArgs {
 
 // ---- launchers (return hipError_t of the launch) -------------------------------
 hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
-hipError_t launch_attn(int hd, int kv_bf16, int act, const AttnArgs& a, hipStream_t st);
+// chunk partials of every (lane, KV head, 64-key chunk) item; RoPE and KV append
+hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
+// combine a lane's chunks into the attention output (activation format act)
+hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st);
 // x[b] = E[token_b]; ssq[b] = sum x[b]^2; rope table of pos_b.
 hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B, int d,
                         int hd, float theta, float* x, float* ssq, float2* rope, hipStream_t st);

@@ -174,9 +174,9 @@ int check_matrix(const cbd_matrix& mt, int wt, const char* name) {
   return CBD_OK;
 }
 
-const char* const kClassNames[] = {"meta_copy", "embed", "gemm_qkv", "attention", "gemm_o",
-                                   "rmsnorm",   "gemm_gu", "gemm_down", "gemm_head", "argmax"};
-enum { P_META, P_EMBED, P_QKV, P_ATTN, P_O, P_NORM, P_GU, P_DOWN, P_HEAD, P_ARGMAX, P_N };
+const char* const kClassNames[] = {"meta_copy", "embed",     "gemm_qkv",  "attention", "attn_combine", "gemm_o",
+                                   "rmsnorm",   "gemm_gu",   "gemm_down", "gemm_head", "argmax"};
+enum { P_META, P_EMBED, P_QKV, P_ATTN, P_COMB, P_O, P_NORM, P_GU, P_DOWN, P_HEAD, P_ARGMAX, P_N };
 
 hipEvent_t take_event(cbd_model* m) {
   if (!m->ev_pool.empty()) {
@@ -537,7 +537,11 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
     at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
     {
       ProfScope ps(m, P_ATTN, st);
-      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, m->wt, at, st));
+      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
+    }
+    {
+      ProfScope ps(m, P_COMB, st);
+      HIP_TRY(launch_attn_combine(c.head_dim, m->wt, at, st));
     }
     if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
     if ((rc = norm(m->ffn_norm[l], m->p_o.nRB))) return rc;

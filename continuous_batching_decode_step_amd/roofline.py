@@ -86,8 +86,11 @@ def kernel_bytes(cfg, cls: str, positions: Sequence[int]) -> float:
     if cls == "gemm_head":
         return V * d * wb + B * d * ab + B * V * 4
     if cls == "attention":
+        # K and V of every cached position read once, the new K/V written, q/k/v read
         per_pos = 2 * cfg.kv_dim * kv_bytes(cfg.wtype)  # K and V of one position, one layer
-        return sum(positions) * per_pos + B * per_pos + B * (cfg.n_qkv * 4 + cfg.q_dim * ab)
+        return sum(positions) * per_pos + B * per_pos + B * cfg.n_qkv * 4
+    if cls == "attn_combine":
+        return B * cfg.q_dim * ab  # the attention output
     if cls == "rmsnorm":
         return B * d * 4 + B * d * ab + d * 4
     if cls == "embed":

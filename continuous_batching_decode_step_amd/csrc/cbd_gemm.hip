@@ -116,6 +116,89 @@ __device__ inline u32x4 q8_to_f16(u32x4 raw) {
   return __builtin_bit_cast(u32x4, r);
 }
 
+// The epilogue of one wave's output tile: R row tiles x C column tiles of
+// 16 x 16 results, the wave's row block rb and column group cg.
+template <int WT, int EPI, int R, int C>
+__device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, const f32x4 (&acc)[R][C]) {
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // Output coordinates of acc[r][c][i]: row (or gate/up pair) and lane column.
+  auto out_row = [&](int r, int i) -> int {
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H = R / 2;
+      return rb * TILE * H + TILE * (r % H) + 4 * g4 + i;
+    } else {
+      return rb * TILE * R + TILE * r + 4 * g4 + i;
+    }
+  };
+
+  // Epilogue.
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int col = cg * TILE * C + TILE * c + r16;
+    const bool cok = col < a.B;
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int r = 0; r < R / 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = out_row(r, i);
+          if (cok && j < a.N) {
+            const float g = acc[r][c][i], u = acc[r + R / 2][c][i];
+            const float act = (g / (1.0f + expf(-g))) * u;
+            store_act<WT>(a.act_out, (size_t)col * a.N + j, act);
+          }
+        }
+    } else if constexpr (EPI == EPI_RESID) {
+      // x += y, and this tile's sum of x^2 per lane for the next RMSNorm
+      float ss = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = out_row(r, i);
+          if (!(cok && n < a.N)) continue;
+          const size_t idx = (size_t)col * a.N + n;
+          const float xn = a.out[idx] + acc[r][c][i];
+          a.out[idx] = xn;
+          ss += xn * xn;
+        }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (g4 == 0 && cok) a.ssq_out[(size_t)rb * a.B + col] = ss;
+    } else {
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = out_row(r, i);
+          if (!(cok && n < a.N)) continue;
+          const float v = acc[r][c][i];
+          a.out[(size_t)col * a.N + n] = v;
+          if constexpr (EPI == EPI_HEAD) {
+            if (v > best || (v == best && n < bi)) {
+              best = v;
+              bi = n;
+            }
+          }
+        }
+      if constexpr (EPI == EPI_HEAD) {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+          const float ov = __shfl_xor(best, off);
+          const int oi = __shfl_xor(bi, off);
+          if (ov > best || (ov == best && oi < bi)) {
+            best = ov;
+            bi = oi;
+          }
+        }
+        if (g4 == 0 && cok) a.amax[(size_t)rb * a.B + col] = make_float2(best, __int_as_float(bi));
+      }
+    }
+  }
+}
+
 template <int WT, int EPI, int C>
 __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
   constexpr int R = gemm_rows(EPI);
@@ -273,82 +356,270 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
     if (s != 0) return;
   }
 
-  // Output coordinates of acc[r][c][i]: row (or gate/up pair) and lane column.
-  auto out_row = [&](int r, int i) -> int {
+  epilogue<WT, EPI, R, C>(a, rb, cg, lane, acc);
+}
+
+
+// ---- wide panels: the activation panel staged in LDS ---------------------------
+//
+// At wide B the per-wave re-reads of the activation panel, not the weight
+// stream, bound the split-K kernel above.  Here a workgroup of PW waves owns
+// PW row blocks (the same R row tiles per wave as above) and one column group
+// of 16*C lanes; the waves walk K together, staging each chunk of U k-steps
+// of the [16*C, K] panel into LDS once for all of them (double-buffered, one
+// barrier per chunk), while each wave streams its own weight rows from HBM.
+//
+// Same reduction contract: a wave runs the S splits of its row block one after
+// the other, each a chain of MFMAs over ascending k-steps from zero, and keeps
+// the running total ((P_0 + P_1) + ...) in registers, so every output bit
+// equals the split-K kernel's.  In split mode (for projections with few row
+// blocks) a workgroup runs one split only and writes P_s to a partial buffer
+// [S][B][row blocks][rows per block]; k_fold then adds the partials in split
+// order and runs the epilogue.
+//
+// Workgroups are numbered so that the column groups of one (row group, split)
+// are consecutive and land on the same XCD (workgroups are dealt to the 8 XCDs
+// in turn), so that their shared weight rows are read from HBM once into that
+// XCD's L2.
+constexpr int PW = 4;  // waves per workgroup in the panel kernel
+
+template <int WT, int C>
+struct PanelShape {
+  static constexpr int KS = KStep<WT>::v;
+  static constexpr int XB = WT == WT_F32 ? 4 : 2;
+  static constexpr int U = C >= 8 ? 2 : 4;                 // k-steps per chunk
+  static constexpr int CHUNK_BYTES = U * KS * XB;          // bytes of one lane row per chunk
+  static constexpr int ROW_BYTES = CHUNK_BYTES + 16;       // padded LDS row
+  static constexpr int COLS = TILE * C;
+  static constexpr int BUF_BYTES = COLS * ROW_BYTES;
+  static constexpr int PIECES = COLS * CHUNK_BYTES / 16;   // 16-byte pieces per chunk
+  static constexpr int PER_THREAD = PIECES / (PW * 64);
+  static_assert(PIECES % (PW * 64) == 0, "chunk pieces must divide evenly over the workgroup");
+};
+
+__host__ __device__ constexpr size_t panel_lds_bytes(int wt, int C) {
+  return 2 * (size_t)(TILE * C) * ((C >= 8 ? 2 : 4) * (wt == WT_F32 ? 16 * 4 : 32 * 2) + 16);
+}
+
+template <int WT, int EPI, int C, bool SPLIT>
+__global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
+  using PS = PanelShape<WT, C>;
+  constexpr int R = gemm_rows(EPI);
+  constexpr int KS = PS::KS;
+  constexpr int PL = KStep<WT>::per_lane;
+  constexpr int U = PS::U;
+  constexpr int EB = WT == WT_F32 ? 4 : (WT == WT_BF16 ? 2 : 1);
+  constexpr int XB = PS::XB;
+  extern __shared__ __attribute__((aligned(16))) char xl[];  // [2][COLS][ROW_BYTES]
+
+  // workgroup -> (row group, split, column group), XCD-aware
+  const int nRG = (a.nRB + PW - 1) / PW;
+  const int nRGS = nRG * (SPLIT ? a.S : 1);
+  const int bi = blockIdx.x;
+  const int cg = (bi >> 3) % a.nCG;
+  const int rgs = ((bi >> 3) / a.nCG) * 8 + (bi & 7);
+  if (rgs >= nRGS) return;  // padding workgroup: the whole workgroup leaves together
+  const int rg = SPLIT ? rgs / a.S : rgs;
+  const int split = SPLIT ? rgs % a.S : 0;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int rb = rg * PW + w;  // this wave's row block (may be past the end: then it only helps stage)
+  const int koff = PL * g4;
+
+  // k-steps this workgroup walks: all of K, or one split
+  const int nks = (a.K + KS - 1) / KS;
+  const int kps = a.Ks / KS;  // k-steps per split
+  const int t0 = SPLIT ? split * kps : 0;
+  const int t1 = SPLIT ? min(t0 + kps, nks) : nks;
+  const int nst = (t1 - t0 + U - 1) / U;
+
+  const char* ap[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int row;
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int H = R / 2;
-      return rb * TILE * H + TILE * (r % H) + 4 * g4 + i;
+      const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
+      row = r < H ? j : a.N + j;
     } else {
-      return rb * TILE * R + TILE * r + 4 * g4 + i;
+      row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
+    }
+    ap[r] = (const char*)a.W + ((size_t)row * a.K + koff) * EB;
+  }
+  const uint16_t* sp[R];
+  if constexpr (WT == WT_Q8) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int row;
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int H = R / 2;
+        const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
+        row = r < H ? j : a.N + j;
+      } else {
+        row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
+      }
+      sp[r] = a.Ws + (size_t)row * (a.K >> 5);
+    }
+  }
+
+  // weight fragments of chunk st (k-steps t0 + st*U + u); k-steps past t1 load
+  // a clamped, in-range step and are never used; the last, partial k-step of
+  // K is zero where a lane's vector lies past K
+  auto load_w = [&](u32x4 (&A)[U][R], int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + st * U + u, t1 - 1);
+      const bool kok = t * KS + koff + PL <= a.K;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int k = kok ? t * KS : 0;
+        if constexpr (WT == WT_Q8)
+          A[u][r] = ld_q8(ap[r] + k, sp[r] + (k >> 5));
+        else
+          A[u][r] = ld16(ap[r] + (size_t)k * EB);
+        if (!kok) A[u][r] = zero4();
+      }
+    }
+  };
+  // the panel's chunk st: PER_THREAD 16-byte pieces per thread, zero past K
+  constexpr int PPC = PS::CHUNK_BYTES / 16;  // pieces per lane row
+  auto load_x = [&](u32x4 (&xr)[PS::PER_THREAD], int st) {
+    const int kc = (t0 + st * U) * KS;  // first element of the chunk
+#pragma unroll
+    for (int j = 0; j < PS::PER_THREAD; ++j) {
+      const int pc = j * PW * 64 + tid;
+      const int cl = pc / PPC, part = pc % PPC;
+      const int col = min(cg * PS::COLS + cl, a.B - 1);
+      const int k = kc + part * (16 / XB);
+      const bool ok = k + 16 / XB <= a.K;
+      xr[j] = ld16((const char*)a.X + ((size_t)col * a.K + (ok ? k : 0)) * XB);
+      if (!ok) xr[j] = zero4();
+    }
+  };
+  auto store_x = [&](const u32x4 (&xr)[PS::PER_THREAD], int buf) {
+    char* base = xl + (size_t)buf * PS::BUF_BYTES;
+#pragma unroll
+    for (int j = 0; j < PS::PER_THREAD; ++j) {
+      const int pc = j * PW * 64 + tid;
+      const int cl = pc / PPC, part = pc % PPC;
+      *(u32x4*)(base + (size_t)cl * PS::ROW_BYTES + part * 16) = xr[j];
     }
   };
 
-  // Epilogue.
+  f32x4 acc[R][C], tot[R][C];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int col = cg * TILE * C + TILE * c + r16;
-    const bool cok = col < a.B;
-    if constexpr (EPI == EPI_SWIGLU) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int r = 0; r < R / 2; ++r)
+    for (int c = 0; c < C; ++c) acc[r][c] = tot[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool have_tot = false;
+  // split boundary: fold the finished split's chain into the running total
+  auto fold = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = out_row(r, i);
-          if (cok && j < a.N) {
-            const float g = acc[r][c][i], u = acc[r + R / 2][c][i];
-            const float act = (g / (1.0f + expf(-g))) * u;
-            store_act<WT>(a.act_out, (size_t)col * a.N + j, act);
-          }
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (have_tot) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[r][c][i] = tot[r][c][i] + acc[r][c][i];
+        } else {
+          tot[r][c] = acc[r][c];
         }
-    } else if constexpr (EPI == EPI_RESID) {
-      // x += y, and this tile's sum of x^2 per lane for the next RMSNorm
-      float ss = 0.f;
+        acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    have_tot = true;
+  };
+  auto compute = [&](const u32x4 (&A)[U][R], int buf, int st) {
+    const char* base = xl + (size_t)buf * PS::BUF_BYTES + (size_t)r16 * PS::ROW_BYTES + g4 * 16;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + st * U + u;
+      if (t >= t1) break;
+      if (!SPLIT && t > 0 && t % kps == 0) fold();
+      u32x4 bv[C];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = out_row(r, i);
-          if (!(cok && n < a.N)) continue;
-          const size_t idx = (size_t)col * a.N + n;
-          const float xn = a.out[idx] + acc[r][c][i];
-          a.out[idx] = xn;
-          ss += xn * xn;
-        }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      if (g4 == 0 && cok) a.ssq_out[(size_t)rb * a.B + col] = ss;
-    } else {
-      float best = -INFINITY;
-      int bi = 0x7fffffff;
+      for (int c = 0; c < C; ++c) bv[c] = *(const u32x4*)(base + (size_t)c * TILE * PS::ROW_BYTES + u * KS * XB);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r) {
+        u32x4 av = A[u][r];
+        if constexpr (WT == WT_Q8) av = q8_to_f16(av);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = out_row(r, i);
-          if (!(cok && n < a.N)) continue;
-          const float v = acc[r][c][i];
-          a.out[(size_t)col * a.N + n] = v;
-          if constexpr (EPI == EPI_HEAD) {
-            if (v > best || (v == best && n < bi)) {
-              best = v;
-              bi = n;
-            }
-          }
-        }
-      if constexpr (EPI == EPI_HEAD) {
-#pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
-          const float ov = __shfl_xor(best, off);
-          const int oi = __shfl_xor(bi, off);
-          if (ov > best || (ov == best && oi < bi)) {
-            best = ov;
-            bi = oi;
-          }
-        }
-        if (g4 == 0 && cok) a.amax[(size_t)rb * a.B + col] = make_float2(best, __int_as_float(bi));
+        for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av, bv[c], acc[r][c]);
       }
     }
+  };
+
+  {
+    u32x4 A0[U][R], A1[U][R], xr[PS::PER_THREAD];
+    load_x(xr, 0);
+    load_w(A0, 0);
+    store_x(xr, 0);
+    if (nst > 1) {
+      load_x(xr, 1);
+      load_w(A1, 1);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+      compute(A0, 0, st);
+      if (st + 1 < nst) store_x(xr, 1);
+      if (st + 2 < nst) {
+        load_x(xr, st + 2);
+        load_w(A0, st + 2);
+      }
+      __syncthreads();
+      if (st + 1 >= nst) break;
+      compute(A1, 1, st + 1);
+      if (st + 2 < nst) store_x(xr, 0);
+      if (st + 3 < nst) {
+        load_x(xr, st + 3);
+        load_w(A1, st + 3);
+      }
+      __syncthreads();
+    }
   }
+  if (rb >= a.nRB) return;
+  if constexpr (SPLIT) {
+    // P_s of this wave's R row tiles for the lanes of the column group, as
+    // [split][lane][rb][R tiles][16] (row tile r of row block rb)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = cg * PS::COLS + TILE * c + r16;
+      if (col >= a.B) continue;
+      float* dst = a.part + (((size_t)split * a.B + col) * a.nRB + rb) * (R * TILE) + 4 * g4;
+#pragma unroll
+      for (int r = 0; r < R; ++r) *(f32x4*)(dst + r * TILE) = acc[r][c];
+    }
+  } else {
+    fold();
+    epilogue<WT, EPI, R, C>(a, rb, cg, lane, tot);
+  }
+}
+
+// Split mode's second half: out = ((P_0 + P_1) + ...) + P_{S-1}, then the
+// epilogue, one wave per (row block, 16 lanes).
+template <int WT, int EPI>
+__global__ __launch_bounds__(64) void k_fold(GemmArgs a) {
+  constexpr int R = gemm_rows(EPI);
+  const int rb = blockIdx.x % a.nRB;
+  const int ct = blockIdx.x / a.nRB;
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int col = min(ct * TILE + r16, a.B - 1);
+  const size_t sstride = (size_t)a.B * a.nRB * (R * TILE);
+  const float* src = a.part + ((size_t)col * a.nRB + rb) * (R * TILE) + 4 * g4;
+  f32x4 acc[R][1];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    f32x4 v = *(const f32x4*)(src + r * TILE);
+    for (int s = 1; s < a.S; ++s) {
+      const f32x4 w = *(const f32x4*)(src + s * sstride + r * TILE);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = v[i] + w[i];
+    }
+    acc[r][0] = v;
+  }
+  epilogue<WT, EPI, R, 1>(a, rb, ct, lane, acc);
 }
 
 template <int WT, int EPI>
@@ -385,6 +656,61 @@ hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st
     case WT_F32: return launch_epi<WT_F32>(epi, C, g, blocks, st);
     case WT_BF16: return launch_epi<WT_BF16>(epi, C, g, blocks, st);
     default: return launch_epi<WT_Q8>(epi, C, g, blocks, st);
+  }
+}
+
+int panel_workgroups(const GemmArgs& a, int C, int split) {
+  const int nRG = (a.nRB + PW - 1) / PW;
+  const int nRGS = nRG * (split ? a.S : 1);
+  const int nCG = (a.B + TILE * C - 1) / (TILE * C);
+  return ((nRGS + 7) / 8) * 8 * nCG;
+}
+
+template <int WT, int EPI, int C>
+static hipError_t launch_panel_c(int split, const GemmArgs& a, hipStream_t st) {
+  const size_t lds = panel_lds_bytes(WT, C);
+  const int blocks = panel_workgroups(a, C, split);
+  if (split) {
+    hipLaunchKernelGGL((k_panel<WT, EPI, C, true>), dim3(blocks), dim3(PW * 64), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nct = (a.B + TILE - 1) / TILE;
+    hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_panel<WT, EPI, C, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int WT, int EPI>
+static hipError_t launch_panel_epi(int C, int split, const GemmArgs& a, hipStream_t st) {
+  switch (C) {
+    case 2: return launch_panel_c<WT, EPI, 2>(split, a, st);
+    case 4: return launch_panel_c<WT, EPI, 4>(split, a, st);
+    case 8: return launch_panel_c<WT, EPI, 8>(split, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WT>
+static hipError_t launch_panel_wt(int epi, int C, int split, const GemmArgs& a, hipStream_t st) {
+  switch (epi) {
+    case EPI_STORE: return launch_panel_epi<WT, EPI_STORE>(C, split, a, st);
+    case EPI_RESID: return launch_panel_epi<WT, EPI_RESID>(C, split, a, st);
+    case EPI_SWIGLU: return launch_panel_epi<WT, EPI_SWIGLU>(C, split, a, st);
+    default: return launch_panel_epi<WT, EPI_HEAD>(C, split, a, st);
+  }
+}
+
+hipError_t launch_panel(int wt, int epi, int C, int split, const GemmArgs& a, hipStream_t st) {
+  if (a.S < 1) return hipErrorInvalidValue;
+  if (a.nRB <= 0 || a.B <= 0) return hipSuccess;
+  GemmArgs g = a;
+  g.nCG = (a.B + TILE * C - 1) / (TILE * C);
+  switch (wt) {
+    case WT_F32: return launch_panel_wt<WT_F32>(epi, C, split, g, st);
+    case WT_BF16: return launch_panel_wt<WT_BF16>(epi, C, split, g, st);
+    default: return launch_panel_wt<WT_Q8>(epi, C, split, g, st);
   }
 }
 

@@ -51,6 +51,7 @@ struct GemmArgs {
   float2* amax;         // HEAD: per (row block, lane) (max value, index as float bits)
   int red_waves;        // split partials per LDS round (set by the launcher)
   float* ssq_out;       // EPI_RESID: [nRB][B] this tile's sum of x^2 per lane
+  float* part;          // panel split mode: [S][B][nRB][rows per row block] split partials
 };
 
 struct AttnArgs {
@@ -75,6 +76,13 @@ struct AttnArgs {
 
 // ---- launchers (return hipError_t of the launch) -------------------------------
 hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
+// Wide-panel projection (activation panel staged in LDS, 16*C lanes per
+// workgroup, C in {2, 4, 8}); split = 1 writes split partials to a.part and
+// adds them in order in a second kernel.
+// Same output bits as launch_gemm.
+hipError_t launch_panel(int wt, int epi, int C, int split, const GemmArgs& a, hipStream_t st);
+// workgroups of one panel launch (for sizing decisions)
+int panel_workgroups(const GemmArgs& a, int C, int split);
 // chunk partials of every (lane, KV head, 64-key chunk) item; RoPE and KV append
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
 // combine a lane's chunks into the attention output (activation format act)

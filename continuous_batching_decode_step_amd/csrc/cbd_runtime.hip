@@ -85,10 +85,10 @@ struct cbd_model {
     int B;
     const void *ws, *arena, *logits, *argmax;
     size_t ws_bytes;
-    int max_seq, n_lanes;
+    int max_seq, n_lanes, variant;
     bool operator==(const GraphKey& o) const {
       return B == o.B && ws == o.ws && arena == o.arena && logits == o.logits && argmax == o.argmax &&
-             ws_bytes == o.ws_bytes && max_seq == o.max_seq && n_lanes == o.n_lanes;
+             ws_bytes == o.ws_bytes && max_seq == o.max_seq && n_lanes == o.n_lanes && variant == o.variant;
     }
   };
   std::vector<std::pair<GraphKey, hipGraphExec_t>> graphs;
@@ -122,7 +122,7 @@ struct cbd_arena {
 namespace {
 
 struct WsLayout {
-  size_t meta, x, xn, ssq, qkv, o, a, amax, rope, apart, total;
+  size_t meta, x, xn, ssq, qkv, o, a, amax, rope, apart, gpart, total;
   int maxB, MS;
 };
 
@@ -148,6 +148,13 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
   L.amax = take(8 * (size_t)m->p_head.nRB * maxB);
   L.rope = take(8 * (size_t)maxB * (c.head_dim / 2));
   L.apart = take(4 * (size_t)maxB * L.MS * c.n_kv_heads * m->G * (c.head_dim + 2));
+  // split partials of the wide-panel projections that run in split mode
+  size_t gp = 0;
+  const Plan* plans[] = {&m->p_qkv, &m->p_o, &m->p_gu, &m->p_down, &m->p_head};
+  const int rows[] = {TILE * gemm_rows(EPI_STORE), TILE * gemm_rows(EPI_RESID), TILE * gemm_rows(EPI_SWIGLU),
+                      TILE * gemm_rows(EPI_RESID), TILE * gemm_rows(EPI_HEAD)};
+  for (int i = 0; i < 5; ++i) gp = std::max(gp, (size_t)plans[i]->S * plans[i]->nRB * rows[i]);
+  L.gpart = take(4 * gp * maxB);
   L.total = off;
   return L;
 }
@@ -449,10 +456,17 @@ int cbd_set_graph_replay(cbd_model* m, int enable) {
 }
 
 int cbd_set_variant(cbd_model* m, int variant) {
-  if (!m || variant < 0 || variant > 1) return fail(CBD_E_ARG, "variant must be 0 or 1");
+  if (!m || variant < 0 || variant > 2) return fail(CBD_E_ARG, "variant must be 0, 1 or 2");
   m->variant = variant;
   return CBD_OK;
 }
+
+// Panel width (lanes per workgroup / 16) for a step of B lanes.
+static int panel_c(int B) { return B <= 32 ? 2 : (B <= 64 ? 4 : 8); }
+// Automatic choice: the wide-panel kernel from this many lanes on.
+constexpr int PANEL_MIN_B = 32;
+// A panel projection runs in split mode when full mode would give fewer waves.
+constexpr int PANEL_MIN_WAVES = 1024;
 
 static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
                     void* act_out, char* ws, const WsLayout& L, hipStream_t st) {
@@ -467,14 +481,23 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.S = p.S;
   g.Ks = p.Ks;
   g.nRB = p.nRB;
-  const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  g.nCG = (B + TILE * C - 1) / (TILE * C);
   g.out = out;
   g.act_out = act_out;
   g.amax = (float2*)(ws + L.amax);
   g.ssq_out = (float*)(ws + L.ssq);
+  g.part = (float*)(ws + L.gpart);
+  const bool panel = m->variant == 2 || (m->variant == 0 && B >= PANEL_MIN_B);
   ProfScope ps(m, cls, st);
-  HIP_TRY(launch_gemm(m->wt, epi, C, g, st));
+  if (panel) {
+    const int C = panel_c(B);
+    const int nCG = (B + TILE * C - 1) / (TILE * C);
+    const int split = p.S > 1 && (long long)p.nRB * nCG < PANEL_MIN_WAVES ? 1 : 0;
+    HIP_TRY(launch_panel(m->wt, epi, C, split, g, st));
+  } else {
+    const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+    g.nCG = (B + TILE * C - 1) / (TILE * C);
+    HIP_TRY(launch_gemm(m->wt, epi, C, g, st));
+  }
   return CBD_OK;
 }
 
@@ -635,7 +658,8 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   if (!graph) {
     if ((rc = enqueue_step(m, a, B, ws, L, logits, argmax, st))) return rc;
   } else {
-    const cbd_model::GraphKey key{B, workspace, a->base, logits, argmax, workspace_bytes, a->max_seq, a->n_lanes};
+    const cbd_model::GraphKey key{B,         workspace,   a->base,     logits,    argmax,
+                                  workspace_bytes, a->max_seq, a->n_lanes, m->variant};
     hipGraphExec_t exec = nullptr;
     for (auto& g : m->graphs)
       if (g.first == key) exec = g.second;

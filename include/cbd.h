@@ -215,7 +215,9 @@ const char* cbd_profile_class_name(int cls);
 int cbd_set_graph_replay(cbd_model* m, int enable);
 
 /* Projection kernel family for steps of this model: 0 = automatic by batch
- * width, 1 = weight-streaming split-K tiles at every width.  Every family
+ * width (split-K tiles below 32 lanes, wide panels from 32 on), 1 =
+ * weight-streaming split-K tiles at every width, 2 = wide panels (the
+ * activation panel staged in on-chip memory) at every width.  Every family
  * computes each output with the same chunked reduction, so the choice changes
  * speed only, never a bit of the result.  Errors: CBD_E_ARG. */
 int cbd_set_variant(cbd_model* m, int variant);

@@ -195,3 +195,27 @@ def test_graph_replay_matches_plain_launches_bitwise():
         for la, lb in zip(runs[0][1], runs[1][1]):
             for x, y in zip(la, lb):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_projection_families_are_bitwise_identical():
+    # Split-K tiles (1), wide panels (2) and the automatic choice (0) follow the
+    # same reduction contract, so every logit bit agrees.  B = 40 covers panel
+    # split mode and full mode, ragged columns, and (tiny) a ragged K of 172.
+    from continuous_batching_decode_step_amd.driver import generate_lockstep
+    cases = [(synth.TINY, 40), (SMALL_GQA, 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 40),
+             (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5)]
+    for cfg, B in cases:
+        say("case: projection families, %s wtype %d B=%d" % (cfg.name, cfg.wtype, B))
+        W = synth.make_weights(cfg)
+        prompts = [synth.prompt_tokens(cfg, 80 + b, 2 + b % 5) for b in range(B)]
+        runs = []
+        for variant in (1, 2, 0):
+            eng = engine_for(cfg, W, B, 12)
+            eng.model.set_variant(variant)
+            runs.append(generate_lockstep(eng, prompts, 4, want_logits=True))
+            del eng
+        for gen, logs in runs[1:]:
+            assert gen == runs[0][0]
+            for la, lb in zip(runs[0][1], logs):
+                for x, y in zip(la, lb):
+                    assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

@@ -76,8 +76,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batches", default="1,2,4,8,16,32,64", help="B sweep; the last is the headline B")
     ap.add_argument("--lanes", type=int, default=64)
+    ap.add_argument("--kv-max", type=int, default=4096,
+                    help="KV lengths are uniform in [128, KV_MAX] (seed 2); 2047 keeps 512 lanes within HBM")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
+                    help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="end with one device-to-device copy of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -102,10 +106,11 @@ def main() -> int:
     W = synth.make_weights(cfg)
     log("weights generated in %.1fs" % (time.time() - t0))
     dw = cbd.upload_weights(W)
-    lens = synth.kv_lengths(n_lanes)  # U[128, 4096]
+    lens = synth.kv_lengths(n_lanes, hi=args.kv_max)  # U[128, kv_max]
     toks = synth.step_tokens(cfg, n_lanes)
     max_seq = int(lens.max()) + 1
     eng = Engine(cfg, dw, n_lanes, max_seq, max_batch=max(batches))
+    eng.model.set_variant(args.variant)
     lanes = [eng.arena.lane_alloc() for _ in range(n_lanes)]
     t0 = time.time()
     for b in range(n_lanes):
@@ -214,8 +219,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "mistral-7b-shape bf16 decode step, ragged KV lengths U[128,4096] (seed 2), "
-                               "one token per lane", "batch": B, "lanes": n_lanes, "d": cfg.d,
+        "config": {"workload": "mistral-7b-shape bf16 decode step, ragged KV lengths U[128,%d] (seed 2), "
+                               "one token per lane" % args.kv_max, "batch": B, "lanes": n_lanes, "d": cfg.d,
                    "layers": cfg.n_layers, "heads": "%d/%d" % (cfg.n_heads, cfg.n_kv_heads),
                    "head_dim": cfg.head_dim, "ffn": cfg.ffn, "vocab": cfg.vocab,
                    "mean_kv_len": float(np.mean(lens[:B])), "parallelism": "single GPU"},

@@ -110,8 +110,8 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int b = a.items[2 * item];
-  const int s = a.items[2 * item + 1];
+  const int b = a.items[4 * item];
+  const int s = a.items[4 * item + 1];  // one chunk per item for this kernel
   const int p = a.pos[b];
   const int nk = p + 1;
   const int kbeg = s * ATTN_SPLIT;  // first key of the chunk
@@ -330,6 +330,232 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   }
 }
 
+
+// ---- bf16 KV: scores on the matrix cores ---------------------------------------
+//
+// Same work and the same per-chunk results contract as k_attn (chunk partials
+// (o, m, l) of 64 keys, combined in chunk order by k_attn_combine), with the
+// q.k products on MFMA: for each 16-key tile, S^T[key][col] over head_dim as a
+// chain of v_mfma_f32_16x16x32_bf16 with the keys (bf16, as stored) as the A
+// operand and, as the B operand, each query head's rotated f32 query split
+// into bf16 high and low parts (q = hi + lo + O(2^-16 |q|)) in columns j and
+// G + j; the score is col j + col G + j.  Products of bf16 values are exact in
+// f32, so the scores keep f32-level accuracy.  P.V stays on the vector ALUs.
+//
+// A wave takes `nc` consecutive chunks of one lane (an item); each chunk's
+// K and V are loaded one chunk ahead.  Lane mapping for the MFMA: row l16 =
+// key in the tile, lane group g4 holds head dims [g4*HD/4, (g4+1)*HD/4) over
+// the HD/32 k-steps; for P.V, lane (r, c) = (g4, l16) holds dims
+// [c*HD/16, (c+1)*HD/16) of keys 16*(it/4) + 4*r + it%4, it = 0..15, whose
+// probabilities sit in lane 16*r + j, register (it/4, it%4), of the score
+// layout.
+__device__ inline u32x4 zero4a() { return u32x4{0u, 0u, 0u, 0u}; }
+
+template <int HD, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
+  constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
+  constexpr int DQ = HD / 4;    // dims per lane group in the score layout
+  constexpr int D = HD / 16;    // dims per lane in the P.V layout
+  static_assert(ATTN_SPLIT == 64 && 2 * G <= 16, "four 16-key tiles; hi/lo columns fit in 16");
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+  const int item = blockIdx.x;
+  if (item >= *a.n_items_dev) return;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int4 it4 = *(const int4*)(a.items + 4 * item);
+  const int b = it4.x, c0 = it4.y, nc = it4.z, p = it4.w;
+  const int nk = p + 1;
+  const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  const float* row = a.qkv + (size_t)b * a.Nqkv;
+  const float2* cs = a.rope + (size_t)b * (HD / 2);
+  const uint16_t* kslab = (const uint16_t*)a.kslab;
+  const uint16_t* vslab = (const uint16_t*)a.vslab;
+
+  // Whole chunks are read: a slab holds a whole number of chunks, and the
+  // slots past p (old or never written) are masked or zeroed after the load.
+  const uint16_t* kbase = kslab + base + (long long)l16 * HD + g4 * 8;
+  const uint16_t* vbase = vslab + base + (long long)(4 * g4) * HD + l16 * D;
+  auto load_k = [&](u32x4 (&kr)[4][KK], int c) {
+    const uint16_t* src = kbase + (long long)c * ATTN_SPLIT * HD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kr[t][kk] = *(const u32x4*)(src + 16 * t * HD + kk * 32);
+  };
+  auto load_v = [&](KVRaw<D, true> (&vr)[16], int c) {
+    const uint16_t* src = vbase + (long long)c * ATTN_SPLIT * HD;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) vr[it] = load_raw<D, true>(src, (16 * (it / 4) + it % 4) * HD);
+  };
+  u32x4 kr[4][KK];
+  KVRaw<D, true> vr[16];
+  load_k(kr, c0);
+  load_v(vr, c0);
+
+  // rotated value of dim d of an f32 head vector v (rotate-half pairing)
+  auto rot = [&](const float* v, int d) -> float {
+    const bool first = d < HD / 2;
+    const float2 t = cs[first ? d : d - HD / 2];
+    const float x = v[d], y = v[first ? d + HD / 2 : d - HD / 2];
+    return first ? x * t.x - y * t.y : x * t.x + y * t.y;
+  };
+  // The wave rotates the group's queries (split into bf16 hi and lo) and, if
+  // its last chunk holds slot p, the new key and value, each lane a few dims,
+  // through LDS; lanes then read their MFMA operand rows from there.
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2 * G][HD];
+  __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
+#pragma unroll
+  for (int e = 0; e < G * HD / 64; ++e) {
+    const int idx = e * 64 + lane, j = idx / HD, d = idx % HD;
+    const float q = rot(row + (size_t)(g * G + j) * HD, d);
+    const uint16_t hi = f2bf_a(q);
+    qs[j][d] = hi;
+    qs[G + j][d] = f2bf_a(q - bf2f(hi));
+  }
+  const int clast = c0 + nc - 1;
+  const bool item_new = p >= clast * ATTN_SPLIT;  // the item's last chunk holds slot p
+  if (item_new) {
+    const float* kn = row + (size_t)(a.Hq + g) * HD;
+    const float* vn = row + (size_t)(a.Hq + a.Hkv + g) * HD;
+#pragma unroll
+    for (int e = 0; e < HD / 64; ++e) {
+      const int d = e * 64 + lane;
+      const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
+      kvn[0][d] = kw;
+      kvn[1][d] = vw;
+      ((uint16_t*)a.kslab)[base + (long long)p * HD + d] = kw;
+      ((uint16_t*)a.vslab)[base + (long long)p * HD + d] = vw;
+    }
+  }
+  __syncthreads();
+  u32x4 bq[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const u32x4 v = *(const u32x4*)&qs[l16 < 2 * G ? l16 : 0][kk * 32 + g4 * 8];
+    bq[kk] = l16 < 2 * G ? v : zero4a();
+  }
+
+  const float inv = 1.0f / sqrtf((float)HD);
+  const size_t pstride = (size_t)G * (HD + 2);
+  for (int ci = 0; ci < nc; ++ci) {
+    const int c = c0 + ci;
+    const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
+    const bool has_new = p >= kb && p < kb + ATTN_SPLIT;
+    // the new key and value replace slot p's old contents
+    KVRaw<D, true> vnr;
+#pragma unroll
+    for (int i = 0; i < KVRaw<D, true>::NW; ++i) vnr.w[i] = 0u;
+    if (has_new) {
+      vnr = *(const KVRaw<D, true>*)&kvn[1][l16 * D];
+      const int tp = (p - kb) >> 4, rp = (p - kb) & 15;
+      const unsigned take = l16 == rp ? ~0u : 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t == tp) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 knr = *(const u32x4*)&kvn[0][kk * 32 + g4 * 8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kr[t][kk][e] = (kr[t][kk][e] & ~take) | (knr[e] & take);
+          }
+        }
+    }
+
+    // scores: S^T[key][col] per 16-key tile
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t][kk]),
+                                                      __builtin_bit_cast(bf16x8, bq[kk]), acc, 0, 0, 0);
+      sc[t] = acc;
+    }
+    // next chunk's keys (unconditional, so the buffers are reused in place;
+    // the last iteration reloads its own chunk)
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kr, min(c + 1, clast));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // hi + lo, scale, mask; softmax statistics of head l16 (lanes l16 < G)
+    float pr[4][4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __shfl(sc[t][i], lane + G < 64 ? lane + G : lane);
+        const int key = kb + 16 * t + 4 * g4 + i;
+        const float v = (sc[t][i] + lo) * inv;
+        pr[t][i] = key < ke ? v : -INFINITY;
+        m = fmaxf(m, pr[t][i]);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[t][i] = pr[t][i] == -INFINITY ? 0.f : expf(pr[t][i] - m);
+        l += pr[t][i];
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    // P.V on the vector ALUs
+    float o[G][D];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[j][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
+      const unsigned take = key == p ? ~0u : 0u;
+      const unsigned keep = key < p ? ~0u : 0u;
+      raw_select<D, true>(vr[it], keep, take, vnr);
+      float vv[D];
+      raw_to_f32<D, true>(vr[it], vv);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float pj = __shfl(pr[it / 4][it % 4], 16 * g4 + j);
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[j][e] += pj * vv[e];
+      }
+      if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(vr, min(c + 1, clast));
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        float v = o[j][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        o[j][e] = v;
+      }
+    float* dst = a.part + (((size_t)b * a.max_splits + c) * a.Hkv + g) * pstride;
+    if (g4 == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < D; ++e) dst[(size_t)j * (HD + 2) + l16 * D + e] = o[j][e];
+      if (l16 < G) {
+        dst[(size_t)l16 * (HD + 2) + HD] = m;
+        dst[(size_t)l16 * (HD + 2) + HD + 1] = l;
+      }
+    }
+  }
+}
+
 template <int ACT>
 __device__ inline void put_act(void* base, size_t idx, float v) {
   if constexpr (ACT == WT_F32)
@@ -417,9 +643,28 @@ static hipError_t launch_hd(int kv_bf16, int G, const AttnArgs& a, dim3 grid, hi
   return kv_bf16 ? launch_g<HD, true>(G, a, grid, st) : launch_g<HD, false>(G, a, grid, st);
 }
 
+template <int HD>
+static hipError_t launch_mf(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn_mf<HD, 1>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_mf<HD, 2>), grid, dim3(64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_mf<HD, 3>), grid, dim3(64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_mf<HD, 4>), grid, dim3(64), 0, st, a); break;
+    case 8:
+      if constexpr (HD == 64) {
+        hipLaunchKernelGGL((k_attn_mf<HD, 8>), grid, dim3(64), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
   const dim3 grid(a.max_items, a.Hkv);
+  if (attn_mfma_supported(hd, kv_bf16 != 0, a.G)) return hd == 128 ? launch_mf<128>(a.G, a, grid, st) : launch_mf<64>(a.G, a, grid, st);
   switch (hd) {
     case 16: return launch_hd<16>(kv_bf16, a.G, a, grid, st);
     case 32: return launch_hd<32>(kv_bf16, a.G, a, grid, st);

@@ -60,11 +60,11 @@ struct AttnArgs {
   void* vslab;            // arena V region
   long long lane_stride;  // elements per lane per region: L * Hkv * max_seq * hd
   long long layer_off;    // l * Hkv * max_seq * hd
-  int max_seq;
+  int max_seq;            // positions per (lane, layer, KV head) slab (a multiple of ATTN_SPLIT)
   int B;
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
-  const int* items;       // [n_items][2] (b, chunk)
+  const int* items;       // [n_items][4] {b, first chunk, chunks, position}, 16-byte aligned
   const int* n_items_dev; // number of items of this step (device)
   int max_items;          // grid size: the most items a step of B lanes can have
   int max_splits;         // chunks per lane the partial buffer is sized for
@@ -83,6 +83,12 @@ hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st
 hipError_t launch_panel(int wt, int epi, int C, int split, const GemmArgs& a, hipStream_t st);
 // workgroups of one panel launch (for sizing decisions)
 int panel_workgroups(const GemmArgs& a, int C, int split);
+// Whether the MFMA attention kernel serves this shape (bf16 KV; head_dim 64
+// with up to 8, or 128 with up to 4 query heads per KV head, the shapes that
+// fit two waves per SIMD); otherwise items carry one chunk.
+__host__ __device__ constexpr bool attn_mfma_supported(int hd, bool kv_bf16, int G) {
+  return kv_bf16 && G >= 1 && ((hd == 64 && G <= 8) || (hd == 128 && G <= 4));
+}
 // chunk partials of every (lane, KV head, 64-key chunk) item; RoPE and KV append
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
 // combine a lane's chunks into the attention output (activation format act)

@@ -111,6 +111,7 @@ struct cbd_model {
 struct cbd_arena {
   cbd_model* m;
   int n_lanes, max_seq;
+  int slab;  // positions per (lane, layer, KV head) slab: max_seq rounded up to a whole attention chunk
   char* base;
   size_t bytes;
   long long lane_stride;  // elements per lane in each of the K and V regions
@@ -126,6 +127,22 @@ struct WsLayout {
   int maxB, MS;
 };
 
+// Attention waves a step aims for when it groups chunks (see k_attn_mf).
+constexpr long long ATTN_TARGET_WAVES = 4096;
+
+// 64-key chunks per attention wave: 1 for the one-chunk kernel; for the MFMA
+// kernel enough to bring the step's waves down towards ATTN_TARGET_WAVES.
+int attn_chunks_per_wave(const cbd_model* m, long long chunks) {
+  if (!attn_mfma_supported(m->c.head_dim, m->wt == WT_BF16, m->G)) return 1;
+  const long long waves = chunks * m->c.n_kv_heads;
+  return (int)std::max(1LL, std::min(8LL, waves / ATTN_TARGET_WAVES));
+}
+
+// Per-step metadata: lanes[B], positions[B], tokens[B], n_items, padding to a
+// multiple of 4 ints, then the attention work items {b, first chunk, chunks,
+// position}, 16-byte aligned.
+size_t meta_header(int B) { return ((size_t)3 * B + 1 + 3) & ~(size_t)3; }
+
 WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
   WsLayout L{};
   const cbd_config& c = m->c;
@@ -137,7 +154,7 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
     off += align256(bytes);
     return o;
   };
-  L.meta = take(4 * ((size_t)3 * maxB + 1 + (size_t)2 * maxB * L.MS));
+  L.meta = take(4 * (meta_header(maxB) + (size_t)4 * maxB * L.MS));
   L.x = take(4 * (size_t)maxB * c.d_model);
   L.xn = take((size_t)m->actb * maxB * c.d_model);
   const int ssq_rows = std::max(std::max(m->p_o.nRB, m->p_down.nRB), 1);
@@ -320,7 +337,8 @@ size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq) {
   if (!cfg || n_lanes <= 0 || max_seq <= 0 || cfg->n_layers <= 0 || cfg->n_kv_heads <= 0 || cfg->head_dim <= 0)
     return 0;
   const size_t kvb = cfg->wtype == CBD_BF16 ? 2 : 4;
-  return 2 * (size_t)n_lanes * cfg->n_layers * cfg->n_kv_heads * (size_t)max_seq * cfg->head_dim * kvb;
+  const size_t slab = ((size_t)max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * ATTN_SPLIT;
+  return 2 * (size_t)n_lanes * cfg->n_layers * cfg->n_kv_heads * slab * cfg->head_dim * kvb;
 }
 
 int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes, cbd_arena** out) {
@@ -336,9 +354,10 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   a->m = m;
   a->n_lanes = n_lanes;
   a->max_seq = max_seq;
+  a->slab = (max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * ATTN_SPLIT;
   a->base = (char*)dev_mem;
   a->bytes = dev_bytes;
-  a->lane_stride = (long long)m->c.n_layers * m->c.n_kv_heads * max_seq * m->c.head_dim;
+  a->lane_stride = (long long)m->c.n_layers * m->c.n_kv_heads * a->slab * m->c.head_dim;
   a->region_bytes = need / 2;
   a->live.assign(n_lanes, 0);
   a->len.assign(n_lanes, 0);
@@ -512,7 +531,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   const int* d_pos = dmeta + B;
   const int* d_tok = dmeta + 2 * B;
   const int* d_nitems = dmeta + 3 * B;
-  const int* d_items = dmeta + 3 * B + 1;
+  const int* d_items = dmeta + meta_header(B);
   float* x = (float*)(ws + L.x);
   float* ssq = (float*)(ws + L.ssq);
   float* qkv = (float*)(ws + L.qkv);
@@ -531,7 +550,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   at.kslab = a->base;
   at.vslab = a->base + a->region_bytes;
   at.lane_stride = a->lane_stride;
-  at.max_seq = a->max_seq;
+  at.max_seq = a->slab;
   at.B = B;
   at.lanes = d_lanes;
   at.pos = d_pos;
@@ -557,7 +576,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   if ((rc = norm(m->attn_norm[0], 1))) return rc;
   for (int l = 0; l < c.n_layers; ++l) {
     if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
-    at.layer_off = (long long)l * c.n_kv_heads * a->max_seq * c.head_dim;
+    at.layer_off = (long long)l * c.n_kv_heads * a->slab * c.head_dim;
     {
       ProfScope ps(m, P_ATTN, st);
       HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
@@ -614,19 +633,27 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   char* ws = (char*)workspace;
 
   // Per-step metadata: lanes, positions, tokens, item count, attention work
-  // items (b, chunk).
+  // items {b, first chunk, chunks, position}: a wave of the attention kernel
+  // takes up to `per` consecutive 64-key chunks of one lane (per-chunk
+  // results do not depend on the grouping).
   std::vector<int32_t> meta;
-  meta.reserve((size_t)3 * B + 1 + 2 * (size_t)B * L.MS);
+  const size_t hdr = meta_header(B);
+  long long chunks = 0;
+  for (int b = 0; b < B; ++b) chunks += (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  const int per = attn_chunks_per_wave(m, chunks);
+  meta.reserve(hdr + 4 * (size_t)chunks);
   meta.insert(meta.end(), lanes, lanes + B);
   meta.insert(meta.end(), positions, positions + B);
   meta.insert(meta.end(), tokens, tokens + B);
-  meta.push_back(0);
+  meta.resize(hdr, 0);
   int n_items = 0;
   for (int b = 0; b < B; ++b) {
     const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
-    for (int s = 0; s < ns; ++s) {
+    for (int s0 = 0; s0 < ns; s0 += per) {
       meta.push_back(b);
-      meta.push_back(s);
+      meta.push_back(s0);
+      meta.push_back(std::min(per, ns - s0));
+      meta.push_back(positions[b]);
       ++n_items;
     }
   }
@@ -711,7 +738,7 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
   if (len > 0) {
     const size_t kvb = a->m->kvb;
     const size_t width = (size_t)len * c.head_dim * kvb;
-    const size_t spitch = (size_t)a->max_seq * c.head_dim * kvb;
+    const size_t spitch = (size_t)a->slab * c.head_dim * kvb;
     const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
     const size_t off = (size_t)lane * a->lane_stride * kvb;
     HIP_TRY(hipMemcpy2DAsync(k_dst, width, a->base + off, spitch, width, rows, hipMemcpyDefault, st));
@@ -733,7 +760,7 @@ int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, co
   if (length > 0) {
     const size_t kvb = a->m->kvb;
     const size_t width = (size_t)length * c.head_dim * kvb;
-    const size_t dpitch = (size_t)a->max_seq * c.head_dim * kvb;
+    const size_t dpitch = (size_t)a->slab * c.head_dim * kvb;
     const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
     const size_t off = (size_t)lane * a->lane_stride * kvb;
     HIP_TRY(hipMemcpy2DAsync(a->base + off, dpitch, k_src, width, width, rows, hipMemcpyDefault, st));

@@ -120,8 +120,10 @@ int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** ou
 void cbd_model_destroy(cbd_model* m);
 
 /* Device bytes an arena of n_lanes lanes of max_seq positions needs:
- * K and V slabs [n_lanes][n_layers][n_kv_heads][max_seq][head_dim] each, in
- * the KV format of the model's wtype.  Returns 0 for invalid arguments. */
+ * K and V slabs [n_lanes][n_layers][n_kv_heads][slab][head_dim] each, in the
+ * KV format of the model's wtype, where slab = max_seq rounded up to a
+ * multiple of 64 (attention reads whole 64-position chunks).  Returns 0 for
+ * invalid arguments. */
 size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq);
 
 /* Create a lane arena over caller-owned device memory dev_mem of dev_bytes

@@ -74,10 +74,13 @@ def test_model_create_validates_shapes():
 
 
 def test_arena_bytes_per_token():
-    # K and V, every layer and KV head: 2 * L * Hkv * hd * bytes per token per lane
-    assert cbd.arena_bytes(synth.MISTRAL7B, 1, 1) == 131072
-    assert cbd.arena_bytes(synth.SMOL135M, 1, 1) == 46080
-    assert cbd.arena_bytes(synth.TINY, 3, 10) == 3 * 10 * 1024
+    # K and V, every layer and KV head: 2 * L * Hkv * hd * bytes per position per
+    # lane, for max_seq rounded up to whole 64-position chunks
+    assert cbd.arena_bytes(synth.MISTRAL7B, 1, 64) == 64 * 131072
+    assert cbd.arena_bytes(synth.MISTRAL7B, 1, 1) == 64 * 131072
+    assert cbd.arena_bytes(synth.SMOL135M, 1, 128) == 128 * 46080
+    assert cbd.arena_bytes(synth.SMOL135M, 1, 65) == 128 * 46080
+    assert cbd.arena_bytes(synth.TINY, 3, 10) == 3 * 64 * 1024
     assert cbd.arena_bytes(synth.TINY, 0, 10) == 0
 
 

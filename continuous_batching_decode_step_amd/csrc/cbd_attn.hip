@@ -567,62 +567,96 @@ __device__ inline void put_act(void* base, size_t idx, float v) {
 }
 
 // Combine a lane's chunks: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s,
-// M = max_s m_s, sums in chunk order.  One workgroup per (lane, KV head): the
-// chunk maxima and sums go through LDS (max_splits x G of each, at most
-// ATTN_MAX_STATS), the chunk outputs are read eight chunks at a time so the
-// loads overlap.
+// M = max_s m_s.  A workgroup takes 128 outputs (group head, dim) of one
+// (lane, KV head); chunks go in batches of COMB_BATCH = 64, each batch in
+// four contiguous quarters, one per group of 128 threads, each folded in
+// chunk order; then the quarters are added in order, then the batches.  The
+// order depends on the chunk count only, never on B.  Every thread issues its
+// quarter's loads together with the batch's statistics (through LDS): one
+// memory round trip per batch after the lane's position.
+constexpr int COMB_BATCH = 64;
+constexpr int COMB_Q = 4;                        // quarters per batch
+constexpr int COMB_PER = COMB_BATCH / COMB_Q;    // chunks per quarter
+constexpr int COMB_OUT = 128;                    // outputs per workgroup
+
 template <int ACT>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int hd) {
-  extern __shared__ float lds[];
-  float* sM = lds;
-  float* sm = lds + 8;
-  float* sl = sm + (size_t)a.max_splits * a.G;
+__global__ __launch_bounds__(COMB_Q * COMB_OUT) void k_attn_combine(AttnArgs a, int hd) {
+  __shared__ float sm[COMB_BATCH * 8], sl[COMB_BATCH * 8], sM[8];
+  __shared__ float qO[COMB_Q][COMB_OUT], qL[COMB_Q][COMB_OUT];
   const int b = blockIdx.x, g = blockIdx.y;
   if (b >= a.B) return;
+  const int tid = threadIdx.x;
+  const int q = tid / COMB_OUT, el = tid % COMB_OUT;
   const int nsplit = (a.pos[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
   const int G = a.G;
   const size_t pstride = (size_t)G * (hd + 2);
   const size_t sstride = (size_t)a.Hkv * pstride;
   const float* P0 = a.part + ((size_t)b * a.max_splits * a.Hkv + g) * pstride;
-  for (int t = threadIdx.x; t < nsplit * G; t += 256) {
-    const int u = t / G, j = t % G;
-    const float* P = P0 + u * sstride + (size_t)j * (hd + 2);
-    sm[t] = P[hd];
-    sl[t] = P[hd + 1];
+  const int e = blockIdx.z * COMB_OUT + el;
+  const bool live = e < G * hd;
+  const int j = live ? e / hd : 0, dim = live ? e % hd : 0;
+  const float* P = P0 + (size_t)j * (hd + 2) + dim;
+  if (nsplit > COMB_BATCH) {  // the maximum over all chunks first
+    __shared__ float red[COMB_Q * COMB_OUT];
+    float mx = -INFINITY;
+    for (int t = tid; t < nsplit * G; t += COMB_Q * COMB_OUT)
+      mx = fmaxf(mx, P0[(size_t)(t / G) * sstride + (size_t)(t % G) * (hd + 2) + hd]);
+    red[tid] = mx;
+    __syncthreads();
+    if (tid < G) {
+      float m = -INFINITY;
+      for (int t = tid; t < COMB_Q * COMB_OUT; t += G) m = fmaxf(m, red[t]);
+      sM[tid] = m;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int j = threadIdx.x;
-    float M = -INFINITY;
-    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, sm[u * G + j]);
-    sM[j] = M;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nsplit * G; t += 256) sm[t] = expf(sm[t] - sM[t % G]);
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * hd; e += 256) {
-    const int j = e / hd, dim = e % hd;
-    const float* P = P0 + (size_t)j * (hd + 2) + dim;
-    float L = 0.f, O = 0.f;
-    int u = 0;
-    for (; u + 8 <= nsplit; u += 8) {
-      float x[8];
+  float Ot = 0.f, Lt = 0.f;
+  for (int u0 = 0; u0 < nsplit; u0 += COMB_BATCH) {
+    const int nb = min(COMB_BATCH, nsplit - u0);
+    const int cq = (nb + COMB_Q - 1) / COMB_Q;
+    const int lo = q * cq, hi = min(lo + cq, nb);  // this quarter's chunks, relative to u0
+    float ov[COMB_PER];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = P[(u + i) * sstride];
+    for (int i = 0; i < COMB_PER; ++i) ov[i] = P[(size_t)(u0 + min(lo + i, nb - 1)) * sstride];
+    if (tid < nb * G) {
+      const float* Q = P0 + (size_t)(u0 + tid / G) * sstride + (size_t)(tid % G) * (hd + 2);
+      sm[tid] = Q[hd];
+      sl[tid] = Q[hd + 1];
+    }
+    __syncthreads();
+    if (nsplit <= COMB_BATCH && tid < G) {
+      float m = -INFINITY;
+      for (int u = 0; u < nb; ++u) m = fmaxf(m, sm[u * G + tid]);
+      sM[tid] = m;
+    }
+    __syncthreads();
+    if (tid < nb * G) sm[tid] = expf(sm[tid] - sM[tid % G]);
+    __syncthreads();
+    float O = 0.f, L = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float w = sm[(u + i) * G + j];
-        L += w * sl[(u + i) * G + j];
-        O += w * x[i];
+    for (int i = 0; i < COMB_PER; ++i) {
+      if (lo + i < hi) {
+        const float w = sm[(lo + i) * G + j];
+        L += w * sl[(lo + i) * G + j];
+        O += w * ov[i];
       }
     }
-    for (; u < nsplit; ++u) {
-      const float w = sm[u * G + j];
-      L += w * sl[u * G + j];
-      O += w * P[u * sstride];
+    qO[q][el] = O;
+    qL[q][el] = L;
+    __syncthreads();
+    if (q == 0) {
+      float Ob = qO[0][el], Lb = qL[0][el];
+#pragma unroll
+      for (int k = 1; k < COMB_Q; ++k) {
+        Ob = Ob + qO[k][el];
+        Lb = Lb + qL[k][el];
+      }
+      Ot = u0 == 0 ? Ob : Ot + Ob;
+      Lt = u0 == 0 ? Lb : Lt + Lb;
     }
-    put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * G + j) * hd + dim, O / L);
+    __syncthreads();
   }
+  if (q == 0 && live) put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * G + j) * hd + dim, Ot / Lt);
 }
 
 template <int HD, bool BF>
@@ -676,13 +710,13 @@ hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
-  if ((size_t)a.max_splits * a.G > ATTN_MAX_STATS) return hipErrorInvalidValue;
-  const dim3 cgrid(a.B, a.Hkv);
-  const size_t lds = (8 + 2 * (size_t)a.max_splits * a.G) * sizeof(float);
+  if (a.G > 8) return hipErrorInvalidValue;
+  const dim3 cgrid(a.B, a.Hkv, (a.G * hd + COMB_OUT - 1) / COMB_OUT);
+  const dim3 blk(COMB_Q * COMB_OUT);
   switch (act) {
-    case WT_F32: hipLaunchKernelGGL(k_attn_combine<WT_F32>, cgrid, dim3(256), lds, st, a, hd); break;
-    case WT_BF16: hipLaunchKernelGGL(k_attn_combine<WT_BF16>, cgrid, dim3(256), lds, st, a, hd); break;
-    default: hipLaunchKernelGGL(k_attn_combine<WT_Q8>, cgrid, dim3(256), lds, st, a, hd); break;
+    case WT_F32: hipLaunchKernelGGL(k_attn_combine<WT_F32>, cgrid, blk, 0, st, a, hd); break;
+    case WT_BF16: hipLaunchKernelGGL(k_attn_combine<WT_BF16>, cgrid, blk, 0, st, a, hd); break;
+    default: hipLaunchKernelGGL(k_attn_combine<WT_Q8>, cgrid, blk, 0, st, a, hd); break;
   }
   return hipGetLastError();
 }

@@ -13,9 +13,6 @@ enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
 // Keys per attention split.  A constant of the design: the per-lane result
 // never depends on B, on the lane's slot or on the other lanes.
 constexpr int ATTN_SPLIT = 64;
-// chunk statistics per (lane, KV head) the combine step holds in LDS:
-// ceil(max_seq / ATTN_SPLIT) * (n_heads / n_kv_heads) may not exceed this
-constexpr int ATTN_MAX_STATS = 8000;
 // Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
 // epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
 // rows; the others take one tile so that d-row projections fill the chip).

@@ -69,14 +69,17 @@ template <int ACT>
 __global__ __launch_bounds__(256) void k_norm(const float* x, const float* ssq, int ssq_n, const float* g, int B,
                                               int d, float eps, void* xn) {
   const int b = blockIdx.y;
+  // this thread's x and gain first, so their loads overlap the reduction
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const bool live = i < d;
+  const int ic = live ? i : 0;
+  const float4 xv = *(const float4*)(x + (size_t)b * d + ic);
+  const float4 gv = *(const float4*)(g + ic);
   float part = 0.f;
   for (int t = threadIdx.x; t < ssq_n; t += 256) part += ssq[(size_t)t * B + b];
   const float ss = block_sum(part);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= d) return;
-  const float4 xv = *(const float4*)(x + (size_t)b * d + i);
-  const float4 gv = *(const float4*)(g + i);
+  if (!live) return;
   const float v0 = (xv.x * r) * gv.x, v1 = (xv.y * r) * gv.y, v2 = (xv.z * r) * gv.z, v3 = (xv.w * r) * gv.w;
   const size_t o = (size_t)b * d + i;
   if constexpr (ACT == WT_F32) {

@@ -347,9 +347,6 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   if ((uintptr_t)dev_mem & 255u) return fail(CBD_E_ARG, "arena memory must be 256-byte aligned");
   const size_t need = cbd_arena_bytes(&m->c, n_lanes, max_seq);
   if (dev_bytes < need) return fail(CBD_E_ARG, "arena needs %zu bytes, got %zu", need, dev_bytes);
-  if ((long long)(max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * m->G > ATTN_MAX_STATS)
-    return fail(CBD_E_UNSUPPORTED, "max_seq %d too long: ceil(max_seq / %d) * %d query heads per KV head exceeds %d",
-                max_seq, ATTN_SPLIT, m->G, ATTN_MAX_STATS);
   cbd_arena* a = new cbd_arena();
   a->m = m;
   a->n_lanes = n_lanes;

@@ -128,10 +128,7 @@ size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq);
 
 /* Create a lane arena over caller-owned device memory dev_mem of dev_bytes
  * (>= cbd_arena_bytes) bytes, 256-byte aligned.  All lanes start free.
- * Attention combines per-64-key chunk statistics in on-chip memory, which
- * bounds max_seq: ceil(max_seq / 64) * (n_heads / n_kv_heads) <= 8000
- * (128000 positions at 4 query heads per KV head).
- * Errors: CBD_E_ARG, CBD_E_UNSUPPORTED (max_seq beyond that bound). */
+ * Errors: CBD_E_ARG. */
 int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes,
                      cbd_arena** out);
 void cbd_arena_destroy(cbd_arena* a);

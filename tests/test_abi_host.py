@@ -123,14 +123,12 @@ def test_arena_create_rejects_small_or_misaligned_memory():
         cbd.Arena(m, 2, 8, FAKE + 64, need)
 
 
-def test_arena_max_seq_bound_of_chunk_statistics():
-    # TINY has one query head per KV head: 8000 chunks of 64 positions fit, one more does not
+def test_arena_accepts_long_contexts():
+    # no bound on max_seq beyond memory: 512k positions of the tiny model
     m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
-    ok = 8000 * 64
-    cbd.Arena(m, 1, ok, FAKE, cbd.arena_bytes(synth.TINY, 1, ok))
-    with pytest.raises(cbd.CbdError) as e:
-        cbd.Arena(m, 1, ok + 1, FAKE, cbd.arena_bytes(synth.TINY, 1, ok + 1))
-    assert e.value.name == "CBD_E_UNSUPPORTED"
+    n = 512 * 1024
+    a = cbd.Arena(m, 1, n, FAKE, cbd.arena_bytes(synth.TINY, 1, n))
+    assert a.max_seq == n
 
 
 def step_err(m, a, lanes, pos, toks, ws=FAKE, wsb=None, logits=FAKE):

@@ -351,6 +351,22 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 // layout.
 __device__ inline u32x4 zero4a() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Buffer-descriptor loads over one (lane, layer, KV head) slab: a byte offset
+// at or past the slab's size reads zeros without touching memory (the raw
+// buffer range check), which lets a prefetch be switched off by its offset
+// alone.  Descriptor word 3 = 0x00020000 (32-bit data format) on gfx9 parts.
+constexpr unsigned SLAB_OFF = 0x80000000u;  // an offset past any slab
+
+__device__ inline __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 slab_ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ inline u32x2 slab_ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
   constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
@@ -376,19 +392,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 
   // Whole chunks are read: a slab holds a whole number of chunks, and the
   // slots past p (old or never written) are masked or zeroed after the load.
-  const uint16_t* kbase = kslab + base + (long long)l16 * HD + g4 * 8;
-  const uint16_t* vbase = vslab + base + (long long)(4 * g4) * HD + l16 * D;
+  // Chunk -1 means no chunk: every load's offset lies past the slab.
+  const unsigned slab_bytes = (unsigned)a.max_seq * HD * 2;
+  const __amdgpu_buffer_rsrc_t krs = slab_rsrc(kslab + base, slab_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(vslab + base, slab_bytes);
+  const unsigned koff0 = ((unsigned)l16 * HD + g4 * 8) * 2;
+  const unsigned voff0 = ((unsigned)(4 * g4) * HD + l16 * D) * 2;
   auto load_k = [&](u32x4 (&kr)[4][KK], int c) {
-    const uint16_t* src = kbase + (long long)c * ATTN_SPLIT * HD;
+    const unsigned o = c < 0 ? SLAB_OFF : koff0 + (unsigned)c * ATTN_SPLIT * HD * 2;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[t][kk] = *(const u32x4*)(src + 16 * t * HD + kk * 32);
+      for (int kk = 0; kk < KK; ++kk) kr[t][kk] = slab_ld16(krs, o + (16 * t * HD + kk * 32) * 2);
   };
   auto load_v = [&](KVRaw<D, true> (&vr)[16], int c) {
-    const uint16_t* src = vbase + (long long)c * ATTN_SPLIT * HD;
+    const unsigned o = c < 0 ? SLAB_OFF : voff0 + (unsigned)c * ATTN_SPLIT * HD * 2;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) vr[it] = load_raw<D, true>(src, (16 * (it / 4) + it % 4) * HD);
+    for (int it = 0; it < 16; ++it) {
+      const unsigned oi = o + (16 * (it / 4) + it % 4) * HD * 2;
+      if constexpr (D == 8) {
+        const u32x4 v = slab_ld16(vrs, oi);
+        vr[it].w[0] = v.x;
+        vr[it].w[1] = v.y;
+        vr[it].w[2] = v.z;
+        vr[it].w[3] = v.w;
+      } else {
+        const u32x2 v = slab_ld8(vrs, oi);
+        vr[it].w[0] = v.x;
+        vr[it].w[1] = v.y;
+      }
+    }
   };
   u32x4 kr[4][KK];
   KVRaw<D, true> vr[16];
@@ -475,10 +508,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
                                                       __builtin_bit_cast(bf16x8, bq[kk]), acc, 0, 0, 0);
       sc[t] = acc;
     }
-    // next chunk's keys (unconditional, so the buffers are reused in place;
-    // the last iteration reloads its own chunk)
+    // next chunk's keys (an unconditional load, so the buffers are reused in
+    // place; after the last chunk it reads nothing)
     __builtin_amdgcn_sched_barrier(0);
-    load_k(kr, min(c + 1, clast));
+    load_k(kr, c < clast ? c + 1 : -1);
     __builtin_amdgcn_sched_barrier(0);
 
     // hi + lo, scale, mask; softmax statistics of head l16 (lanes l16 < G)
@@ -530,7 +563,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_v(vr, min(c + 1, clast));
+    load_v(vr, c < clast ? c + 1 : -1);
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll

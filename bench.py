@@ -69,6 +69,119 @@ def stored_traffic(cls: str, B: int):
     return None
 
 
+GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_gu", "gemm_down", "gemm_head")
+
+
+def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
+    """Time `steps` decode steps over the first B lanes (each step rewrites the same slot of every lane),
+    then a second pass with events around every kernel class.  Returns (sweep row, per-class summary)."""
+    import torch
+
+    def step():
+        for b in range(B):
+            eng.arena.lane_truncate(lanes[b], int(lens[b]))
+        pos = lens[:B].astype(np.int32).copy()
+        eng.step(lanes[:B], pos, toks[:B])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / steps
+    pos = [int(x) for x in lens[:B]]
+    t_roof = rf.roofline_time_s(cfg, pos)
+    eng.model.profile_reset()
+    eng.model.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = eng.model.profile_read()
+    eng.model.profile_enable(False)
+    per = rf.per_class_summary(cfg, prof, pos)
+    gemm_ms = sum(per[k]["total_ms"] for k in GEMM_CLASSES if k in per) / steps
+    gemm_flops = sum(rf.kernel_flops(cfg, k, pos) * (1 if k == "gemm_head" else cfg.n_layers) for k in GEMM_CLASSES)
+    row = {"B": B, "tok_s": B / (ms * 1e-3), "ms_per_step": ms, "wall_ms_per_step": wall * 1e3 / steps,
+           "step_alg_GB": rf.step_bytes(cfg, pos) / 1e9, "roofline_tok_s": B / t_roof,
+           "roofline_frac": t_roof / (ms * 1e-3),
+           "gemm_mfma_util": gemm_flops / (gemm_ms * 1e-3) / (rf.MFMA_PEAK_TFLOPS["bf16"] * 1e12),
+           "kernels": {k: {"avg_us": round(v["avg_us"], 2), "share": round(v["total_ms"] / max(
+               1e-9, sum(x["total_ms"] for x in per.values())), 4),
+               "GBs": None if v["achieved_GBs"] is None else round(v["achieved_GBs"], 1)}
+               for k, v in per.items()}}
+    return row, per
+
+
+def wide_leg(cfg, dw, args, rf, log):
+    """B = 256 (KV U[128,4096]) and B = 512 (KV U[128,2047], so the arena fits in HBM): tokens/s and
+    the projections' bf16 MFMA utilisation (GEMM flops / summed GEMM kernel time / 2.5 PFLOP/s)."""
+    import gc
+    import torch
+    import synth
+    from continuous_batching_decode_step_amd.driver import Engine
+    out = []
+    for B, hi in ((256, 4096), (512, 2047)):
+        lens = synth.kv_lengths(B, hi=hi)
+        toks = synth.step_tokens(cfg, B)
+        eng = Engine(cfg, dw, B, int(lens.max()) + 1, max_batch=B)
+        eng.model.set_variant(args.variant)
+        lanes = [eng.arena.lane_alloc() for _ in range(B)]
+        t0 = time.time()
+        for b in range(B):
+            k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
+            eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
+        torch.cuda.synchronize()
+        log("wide B=%d: KV loaded in %.1fs" % (B, time.time() - t0))
+        row, _ = measure(eng, lanes, lens, toks, B, max(3, args.steps // 2), max(1, args.warmup), cfg, rf,
+                         torch.cuda.current_stream())
+        row["kv_lengths"] = "U[128,%d]" % hi
+        log("wide B=%3d  %8.1f tok/s  %.3f ms/step  roofline %.3f  projections at %.1f%% of bf16 MFMA peak" % (
+            B, row["tok_s"], row["ms_per_step"], row["roofline_frac"], 100 * row["gemm_mfma_util"]))
+        out.append(row)
+        del eng
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
+def q8_leg(args, rf, log):
+    """The pages' own benchmark shape: SmolLM2-135M with Q8_0 weights, lanes holding 16 positions
+    (the prompt length of that benchmark; synthetic f32 K/V, seed 3), one decode step per lane, at
+    B in {1, 64, 256, 512, 960}.  Context only (their figures come from a CPU)."""
+    import gc
+    import torch
+    import synth
+    import continuous_batching_decode_step_amd as cbd
+    from continuous_batching_decode_step_amd.driver import Engine
+    cfg = synth.SMOL135M_Q8
+    dw = cbd.upload_weights(synth.make_weights(cfg))
+    Bmax, ctx = 960, 16
+    lens = np.full(Bmax, ctx, dtype=np.int64)
+    toks = synth.step_tokens(cfg, Bmax)
+    eng = Engine(cfg, dw, Bmax, ctx + 1, max_batch=Bmax)
+    lanes = [eng.arena.lane_alloc() for _ in range(Bmax)]
+    for b in range(Bmax):
+        k, v = synth.lane_kv_f32(cfg, b, ctx)
+        eng.arena.kv_import(lanes[b], ctx, k, v, eng.stream)
+    torch.cuda.synchronize()
+    out = []
+    for B in (1, 64, 256, 512, 960):
+        row, _ = measure(eng, lanes, lens, toks, B, args.steps, args.warmup, cfg, rf, torch.cuda.current_stream())
+        log("q8-135m B=%3d  %9.1f tok/s  %.3f ms/step" % (B, row["tok_s"], row["ms_per_step"]))
+        out.append({"B": B, "tok_s": round(row["tok_s"], 1), "ms_per_step": round(row["ms_per_step"], 4),
+                    "roofline_frac": round(row["roofline_frac"], 4)})
+    del eng, dw
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +195,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
                     help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels")
+    ap.add_argument("--no-q8", action="store_true",
+                    help="skip the SmolLM2-135M Q8_0 leg (decode steps at 16-position contexts, B = 1..960)")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the wide-batch leg (B = 256 with KV U[128,4096], B = 512 with KV U[128,2047]) "
+                         "that reports the projections' bf16 MFMA utilisation")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="end with one device-to-device copy of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -119,51 +237,16 @@ def main() -> int:
     torch.cuda.synchronize()
     log("KV of %d lanes generated and loaded in %.1fs" % (n_lanes, time.time() - t0))
 
-    def step(B):
-        for b in range(B):
-            eng.arena.lane_truncate(lanes[b], int(lens[b]))
-        pos = lens[:B].astype(np.int32).copy()
-        eng.step(lanes[:B], pos, toks[:B])
-
     stream = torch.cuda.current_stream()
     sweep = []
     headline = None
     for B in batches:
-        for _ in range(args.warmup):
-            step(B)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step(B)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        ms = e0.elapsed_time(e1) / args.steps
-        pos = [int(x) for x in lens[:B]]
-        t_roof = rf.roofline_time_s(cfg, pos)
-        # per-kernel durations: a second pass with events around every launch
-        eng.model.profile_reset()
-        eng.model.profile_enable(True)
-        for _ in range(args.steps):
-            step(B)
-        torch.cuda.synchronize()
-        prof = eng.model.profile_read()
-        eng.model.profile_enable(False)
-        per = rf.per_class_summary(cfg, prof, pos)
-        row = {"B": B, "tok_s": B / (ms * 1e-3), "ms_per_step": ms, "wall_ms_per_step": wall * 1e3 / args.steps,
-               "step_alg_GB": rf.step_bytes(cfg, pos) / 1e9, "roofline_tok_s": B / t_roof,
-               "roofline_frac": t_roof / (ms * 1e-3),
-               "kernels": {k: {"avg_us": round(v["avg_us"], 2), "share": round(v["total_ms"] / max(
-                   1e-9, sum(x["total_ms"] for x in per.values())), 4),
-                   "GBs": None if v["achieved_GBs"] is None else round(v["achieved_GBs"], 1)}
-                   for k, v in per.items()}}
+        row, per = measure(eng, lanes, lens, toks, B, args.steps, args.warmup, cfg, rf, stream)
         sweep.append(row)
         log("B=%3d  %8.1f tok/s  %.3f ms/step  roofline %.3f  %s" % (
-            B, row["tok_s"], ms, row["roofline_frac"],
+            B, row["tok_s"], row["ms_per_step"], row["roofline_frac"],
             " ".join("%s=%.1fus/%sGB/s" % (k, v["avg_us"], v["GBs"]) for k, v in row["kernels"].items())))
-        headline = (B, ms, per, pos)
+        headline = (B, row["ms_per_step"], per, [int(x) for x in lens[:B]])
 
     B, ms, per, pos = headline
     dom = max((k for k in per if per[k]["alg_bytes"] > 0), key=lambda k: per[k]["total_ms"])
@@ -195,6 +278,18 @@ def main() -> int:
                "sample": "%d lane-steps of the same workload (lanes 0..%d at their KV lengths, one decode step "
                          "each, serial CPU oracle on bf16 weights: sums in double, values stored in f32), %.1f s" % (done, done - 1, t_cpu)}
         log("cpu oracle: %s" % cpu)
+
+    q8 = None
+    if not args.no_q8:
+        q8 = q8_leg(args, rf, log)
+
+    wide = None
+    if not args.no_wide:
+        del eng
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        wide = wide_leg(cfg, dw, args, rf, log)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -228,6 +323,9 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+        "context_q8_smollm135m": q8,
+        "wide": None if wide is None else [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                                           for r in wide],
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -200,10 +200,12 @@ def test_graph_replay_matches_plain_launches_bitwise():
 def test_projection_families_are_bitwise_identical():
     # Split-K tiles (1), wide panels (2) and the automatic choice (0) follow the
     # same reduction contract, so every logit bit agrees.  B = 40 covers panel
-    # split mode and full mode, ragged columns, and (tiny) a ragged K of 172.
+    # split mode and full mode, ragged columns, and (tiny) a ragged K of 172;
+    # B = 100 the 128-lane panel width.
     from continuous_batching_decode_step_amd.driver import generate_lockstep
     cases = [(synth.TINY, 40), (SMALL_GQA, 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 40),
-             (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5)]
+             (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5),
+             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100)]
     for cfg, B in cases:
         say("case: projection families, %s wtype %d B=%d" % (cfg.name, cfg.wtype, B))
         W = synth.make_weights(cfg)

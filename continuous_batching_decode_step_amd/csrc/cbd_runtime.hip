@@ -477,12 +477,28 @@ int cbd_set_variant(cbd_model* m, int variant) {
   return CBD_OK;
 }
 
-// Panel width (lanes per workgroup / 16) for a step of B lanes.
-static int panel_c(int B) { return B <= 32 ? 2 : (B <= 64 ? 4 : 8); }
 // Automatic choice: the wide-panel kernel from this many lanes on.
 constexpr int PANEL_MIN_B = 32;
-// A panel projection runs in split mode when full mode would give fewer waves.
-constexpr int PANEL_MIN_WAVES = 1024;
+
+// Panel width C (lanes per workgroup / 16) and mode for one projection at B
+// lanes. Up to 64 lanes C follows B and a projection splits when full mode
+// would give fewer than 1024 waves. Above 64 lanes, 64-lane panels (which fit
+// two workgroups per CU) run in full mode when the reduction is short and they
+// already give 2048 waves; otherwise 128-lane panels, split below 4096 waves.
+// Both the width and the mode leave every output's reduction order unchanged.
+static void panel_shape(int B, const Plan& p, int* C, int* split) {
+  auto units = [&](int c) { return (long long)p.nRB * ((B + TILE * c - 1) / (TILE * c)); };
+  if (B <= 64) {
+    *C = B <= 32 ? 2 : 4;
+    *split = p.S > 1 && units(*C) < 1024;
+  } else if (p.K <= 4096 && units(4) >= 2048) {
+    *C = 4;
+    *split = 0;
+  } else {
+    *C = 8;
+    *split = p.S > 1 && units(8) < 4096;
+  }
+}
 
 static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
                     void* act_out, char* ws, const WsLayout& L, hipStream_t st) {
@@ -505,9 +521,8 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   const bool panel = m->variant == 2 || (m->variant == 0 && B >= PANEL_MIN_B);
   ProfScope ps(m, cls, st);
   if (panel) {
-    const int C = panel_c(B);
-    const int nCG = (B + TILE * C - 1) / (TILE * C);
-    const int split = p.S > 1 && (long long)p.nRB * nCG < PANEL_MIN_WAVES ? 1 : 0;
+    int C, split;
+    panel_shape(B, p, &C, &split);
     HIP_TRY(launch_panel(m->wt, epi, C, split, g, st));
   } else {
     const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);

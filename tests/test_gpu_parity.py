@@ -21,6 +21,10 @@ pytestmark = pytest.mark.gpu
 
 SMALL_GQA = synth.ModelConfig("small-gqa", d=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=32, ffn=96,
                               vocab=300)
+# Enough head rows that 64-lane panels at 260 lanes run in full mode, and an FFN
+# long enough that the down projection splits under 128-lane panels.
+WIDE_VOCAB = synth.ModelConfig("wide-vocab", d=128, n_layers=1, n_heads=4, n_kv_heads=2, head_dim=32, ffn=512,
+                               vocab=20000, wtype=synth.WTYPE_BF16)
 
 
 def _run(cfg, W, prompts, n_new, n_lanes=None, max_seq=None):
@@ -201,11 +205,12 @@ def test_projection_families_are_bitwise_identical():
     # Split-K tiles (1), wide panels (2) and the automatic choice (0) follow the
     # same reduction contract, so every logit bit agrees.  B = 40 covers panel
     # split mode and full mode, ragged columns, and (tiny) a ragged K of 172;
-    # B = 100 the 128-lane panel width.
+    # B = 100 the 128-lane panel width; B = 260 on the wide vocabulary 64-lane
+    # panels in full mode beside 128-lane panels in split mode.
     from continuous_batching_decode_step_amd.driver import generate_lockstep
     cases = [(synth.TINY, 40), (SMALL_GQA, 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 40),
              (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5),
-             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100)]
+             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100), (WIDE_VOCAB, 260)]
     for cfg, B in cases:
         say("case: projection families, %s wtype %d B=%d" % (cfg.name, cfg.wtype, B))
         W = synth.make_weights(cfg)

@@ -401,6 +401,24 @@ __host__ __device__ constexpr size_t panel_lds_bytes(int wt, int C) {
   return 2 * (size_t)(TILE * C) * ((C >= 8 ? 2 : 4) * (wt == WT_F32 ? 16 * 4 : 32 * 2) + 16);
 }
 
+// Buffer-descriptor loads (raw buffer, 32-bit data format): per-lane byte
+// offsets stay in registers across the K walk and the k-step's offset is a
+// scalar, so a fragment load costs no vector instructions.  An offset at or past
+// the buffer's size reads zeros without touching memory.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(unsigned)std::min<size_t>(bytes, 0xffffffffu), 0x00020000);
+}
+__device__ inline u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ inline u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ inline unsigned buf_ld2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
 template <int WT, int EPI, int C, bool SPLIT>
 __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   using PS = PanelShape<WT, C>;
@@ -428,14 +446,21 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   const int rb = rg * PW + w;  // this wave's row block (may be past the end: then it only helps stage)
   const int koff = PL * g4;
 
-  // k-steps this workgroup walks: all of K, or one split
+  // k-steps this workgroup walks: all of K, or one split.  When K is not a
+  // multiple of the k-step, the last k-step of K is partial; it runs after the
+  // chunk loop with per-lane masks, so the loop itself needs none.
   const int nks = (a.K + KS - 1) / KS;
   const int kps = a.Ks / KS;  // k-steps per split
   const int t0 = SPLIT ? split * kps : 0;
   const int t1 = SPLIT ? min(t0 + kps, nks) : nks;
-  const int nst = (t1 - t0 + U - 1) / U;
+  const bool tail = t1 == nks && a.K % KS != 0;
+  const int tm = tail ? t1 - 1 : t1;  // end of the full k-steps
+  const int nst = (tm - t0 + U - 1) / U;
 
-  const char* ap[R];
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, (size_t)a.Nraw * a.K * EB);
+  const __amdgpu_buffer_rsrc_t srs = buf_rsrc(a.Ws, WT == WT_Q8 ? (size_t)a.Nraw * (a.K >> 5) * 2 : 0);
+  const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X, (size_t)a.B * a.K * XB);
+  unsigned wv[R], sv[R];  // byte offsets of this lane's weight vector at k = 0 (and its Q8 scale)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int row;
@@ -446,65 +471,49 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
     } else {
       row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
     }
-    ap[r] = (const char*)a.W + ((size_t)row * a.K + koff) * EB;
+    wv[r] = (unsigned)(((size_t)row * a.K + koff) * EB);
+    sv[r] = (unsigned)((size_t)row * (a.K >> 5) * 2);
   }
-  const uint16_t* sp[R];
-  if constexpr (WT == WT_Q8) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int row;
-      if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int H = R / 2;
-        const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
-        row = r < H ? j : a.N + j;
-      } else {
-        row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
-      }
-      sp[r] = a.Ws + (size_t)row * (a.K >> 5);
+  auto ld_w = [&](int r, int t) -> u32x4 {
+    if constexpr (WT == WT_Q8) {
+      const u32x2 q = buf_ld8(wrs, wv[r], (unsigned)t * KS);
+      return u32x4{q.x, q.y, buf_ld2(srs, sv[r], (unsigned)t * 2), 0u};
+    } else {
+      return buf_ld16(wrs, wv[r], (unsigned)t * KS * EB);
     }
-  }
+  };
 
-  // weight fragments of chunk st (k-steps t0 + st*U + u); k-steps past t1 load
-  // a clamped, in-range step and are never used; the last, partial k-step of
-  // K is zero where a lane's vector lies past K
+  // Weight fragments of chunk st: full k-steps t0 + st*U + u; steps past the
+  // last full one reload it (an L1/L2 hit) and are never used.
   auto load_w = [&](u32x4 (&A)[U][R], int st) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + st * U + u, t1 - 1);
-      const bool kok = t * KS + koff + PL <= a.K;
+      const int t = max(t0, min(t0 + st * U + u, tm - 1));
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int k = kok ? t * KS : 0;
-        if constexpr (WT == WT_Q8)
-          A[u][r] = ld_q8(ap[r] + k, sp[r] + (k >> 5));
-        else
-          A[u][r] = ld16(ap[r] + (size_t)k * EB);
-        if (!kok) A[u][r] = zero4();
-      }
+      for (int r = 0; r < R; ++r) A[u][r] = ld_w(r, t);
     }
   };
-  // the panel's chunk st: PER_THREAD 16-byte pieces per thread, zero past K
+  // The panel's chunk st: PER_THREAD 16-byte pieces per thread.  Chunks past the
+  // last reload it; pieces past K (in a last, partial chunk) are never read.
   constexpr int PPC = PS::CHUNK_BYTES / 16;  // pieces per lane row
-  auto load_x = [&](u32x4 (&xr)[PS::PER_THREAD], int st) {
-    const int kc = (t0 + st * U) * KS;  // first element of the chunk
+  unsigned xv[PS::PER_THREAD];
 #pragma unroll
-    for (int j = 0; j < PS::PER_THREAD; ++j) {
-      const int pc = j * PW * 64 + tid;
-      const int cl = pc / PPC, part = pc % PPC;
-      const int col = min(cg * PS::COLS + cl, a.B - 1);
-      const int k = kc + part * (16 / XB);
-      const bool ok = k + 16 / XB <= a.K;
-      xr[j] = ld16((const char*)a.X + ((size_t)col * a.K + (ok ? k : 0)) * XB);
-      if (!ok) xr[j] = zero4();
-    }
+  for (int j = 0; j < PS::PER_THREAD; ++j) {
+    const int pc = j * PW * 64 + tid;
+    const int col = min(cg * PS::COLS + pc / PPC, a.B - 1);
+    xv[j] = (unsigned)(((size_t)col * a.K + (pc % PPC) * (16 / XB)) * XB);
+  }
+  auto load_x = [&](u32x4 (&xr)[PS::PER_THREAD], int st) {
+    const unsigned kc = (unsigned)(t0 + min(st, max(nst - 1, 0)) * U) * KS * XB;
+#pragma unroll
+    for (int j = 0; j < PS::PER_THREAD; ++j) xr[j] = buf_ld16(xrs, xv[j] + kc, 0u);
   };
   auto store_x = [&](const u32x4 (&xr)[PS::PER_THREAD], int buf) {
     char* base = xl + (size_t)buf * PS::BUF_BYTES;
 #pragma unroll
     for (int j = 0; j < PS::PER_THREAD; ++j) {
       const int pc = j * PW * 64 + tid;
-      const int cl = pc / PPC, part = pc % PPC;
-      *(u32x4*)(base + (size_t)cl * PS::ROW_BYTES + part * 16) = xr[j];
+      *(u32x4*)(base + (size_t)(pc / PPC) * PS::ROW_BYTES + (pc % PPC) * 16) = xr[j];
     }
   };
 
@@ -514,6 +523,7 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[r][c] = tot[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool have_tot = false;
+  int tf = t0 + kps;  // full mode: the first k-step of the next split
   // split boundary: fold the finished split's chain into the running total
   auto fold = [&]() {
 #pragma unroll
@@ -530,53 +540,77 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
       }
     have_tot = true;
   };
-  auto compute = [&](const u32x4 (&A)[U][R], int buf, int st) {
+  auto step = [&](u32x4 av0[R], const u32x4 (&bv)[C], int t) {
+    if (!SPLIT && t == tf) {
+      fold();
+      tf += kps;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      u32x4 av = av0[r];
+      if constexpr (WT == WT_Q8) av = q8_to_f16(av);
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av, bv[c], acc[r][c]);
+    }
+  };
+  auto compute = [&](u32x4 (&A)[U][R], int buf, int st) {
     const char* base = xl + (size_t)buf * PS::BUF_BYTES + (size_t)r16 * PS::ROW_BYTES + g4 * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + st * U + u;
-      if (t >= t1) break;
-      if (!SPLIT && t > 0 && t % kps == 0) fold();
+      if (t >= tm) break;
       u32x4 bv[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) bv[c] = *(const u32x4*)(base + (size_t)c * TILE * PS::ROW_BYTES + u * KS * XB);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        u32x4 av = A[u][r];
-        if constexpr (WT == WT_Q8) av = q8_to_f16(av);
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc[r][c] = mma<WT>(av, bv[c], acc[r][c]);
-      }
+      step(A[u], bv, t);
     }
   };
 
   {
+    // Two chunks of weights in flight.  The loop has no exit between its two
+    // halves and the LDS stores are unconditional (a chunk past the end stores
+    // data nobody reads), which keeps the compiler's waits on the loads exact.
     u32x4 A0[U][R], A1[U][R], xr[PS::PER_THREAD];
     load_x(xr, 0);
     load_w(A0, 0);
     store_x(xr, 0);
-    if (nst > 1) {
-      load_x(xr, 1);
-      load_w(A1, 1);
-    }
+    load_x(xr, 1);
+    load_w(A1, 1);
     __syncthreads();
     for (int st = 0; st < nst; st += 2) {
       compute(A0, 0, st);
-      if (st + 1 < nst) store_x(xr, 1);
+      store_x(xr, 1);
       if (st + 2 < nst) {
         load_x(xr, st + 2);
         load_w(A0, st + 2);
       }
       __syncthreads();
-      if (st + 1 >= nst) break;
-      compute(A1, 1, st + 1);
-      if (st + 2 < nst) store_x(xr, 0);
+      compute(A1, 1, st + 1);  // nothing when st + 1 == nst
+      store_x(xr, 0);
       if (st + 3 < nst) {
         load_x(xr, st + 3);
         load_w(A1, st + 3);
       }
       __syncthreads();
     }
+  }
+  if (tail) {
+    // The partial last k-step: lane vectors past K are zero on both sides.
+    const int t = tm;
+    const bool kok = t * KS + koff + PL <= a.K;
+    u32x4 av[R], bv[C];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      av[r] = ld_w(r, kok ? t : 0);
+      if (!kok) av[r] = zero4();
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = min(cg * PS::COLS + TILE * c + r16, a.B - 1);
+      bv[c] = buf_ld16(xrs, (unsigned)(((size_t)col * a.K + (kok ? t * KS + koff : 0)) * XB), 0u);
+      if (!kok) bv[c] = zero4();
+    }
+    step(av, bv, t);
   }
   if (rb >= a.nRB) return;
   if constexpr (SPLIT) {

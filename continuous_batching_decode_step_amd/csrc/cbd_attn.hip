@@ -611,10 +611,11 @@ constexpr int COMB_BATCH = 64;
 constexpr int COMB_Q = 4;                        // quarters per batch
 constexpr int COMB_PER = COMB_BATCH / COMB_Q;    // chunks per quarter
 constexpr int COMB_OUT = 128;                    // outputs per workgroup
+constexpr int COMB_MS = 16;                      // threads per group head in the maximum
 
 template <int ACT>
 __global__ __launch_bounds__(COMB_Q * COMB_OUT) void k_attn_combine(AttnArgs a, int hd) {
-  __shared__ float sm[COMB_BATCH * 8], sl[COMB_BATCH * 8], sM[8];
+  __shared__ float sm[COMB_BATCH * 8], sl[COMB_BATCH * 8], sM[8], sR[COMB_MS * 8];
   __shared__ float qO[COMB_Q][COMB_OUT], qL[COMB_Q][COMB_OUT];
   const int b = blockIdx.x, g = blockIdx.y;
   if (b >= a.B) return;
@@ -636,9 +637,15 @@ __global__ __launch_bounds__(COMB_Q * COMB_OUT) void k_attn_combine(AttnArgs a, 
       mx = fmaxf(mx, P0[(size_t)(t / G) * sstride + (size_t)(t % G) * (hd + 2) + hd]);
     red[tid] = mx;
     __syncthreads();
+    if (tid < G * COMB_MS) {
+      float m = -INFINITY;
+      for (int t = tid; t < COMB_Q * COMB_OUT; t += G * COMB_MS) m = fmaxf(m, red[t]);
+      sR[tid] = m;
+    }
+    __syncthreads();
     if (tid < G) {
       float m = -INFINITY;
-      for (int t = tid; t < COMB_Q * COMB_OUT; t += G) m = fmaxf(m, red[t]);
+      for (int s2 = 0; s2 < COMB_MS; ++s2) m = fmaxf(m, sR[s2 * G + tid]);
       sM[tid] = m;
     }
     __syncthreads();
@@ -657,10 +664,21 @@ __global__ __launch_bounds__(COMB_Q * COMB_OUT) void k_attn_combine(AttnArgs a, 
       sl[tid] = Q[hd + 1];
     }
     __syncthreads();
-    if (nsplit <= COMB_BATCH && tid < G) {
-      float m = -INFINITY;
-      for (int u = 0; u < nb; ++u) m = fmaxf(m, sm[u * G + tid]);
-      sM[tid] = m;
+    if (nsplit <= COMB_BATCH) {
+      // the batch's maximum per group head: COMB_MS threads per head take every
+      // COMB_MS-th chunk, then one thread per head their results (a maximum is
+      // exact in any order)
+      if (tid < G * COMB_MS) {
+        float m = -INFINITY;
+        for (int u = tid / G; u < nb; u += COMB_MS) m = fmaxf(m, sm[u * G + tid % G]);
+        sR[tid] = m;
+      }
+      __syncthreads();
+      if (tid < G) {
+        float m = -INFINITY;
+        for (int s2 = 0; s2 < COMB_MS; ++s2) m = fmaxf(m, sR[s2 * G + tid]);
+        sM[tid] = m;
+      }
     }
     __syncthreads();
     if (tid < nb * G) sm[tid] = expf(sm[tid] - sM[tid % G]);

@@ -642,15 +642,23 @@ __global__ __launch_bounds__(64) void k_fold(GemmArgs a) {
   const int col = min(ct * TILE + r16, a.B - 1);
   const size_t sstride = (size_t)a.B * a.nRB * (R * TILE);
   const float* src = a.part + ((size_t)col * a.nRB + rb) * (R * TILE) + 4 * g4;
+  // All partials are loaded before the first add (one memory round trip; slots
+  // past S reload the last split and are not added), then summed in split order.
+  f32x4 pv[R][GEMM_MAX_SPLIT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < GEMM_MAX_SPLIT; ++s) pv[r][s] = *(const f32x4*)(src + min(s, a.S - 1) * sstride + r * TILE);
   f32x4 acc[R][1];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    f32x4 v = *(const f32x4*)(src + r * TILE);
-    for (int s = 1; s < a.S; ++s) {
-      const f32x4 w = *(const f32x4*)(src + s * sstride + r * TILE);
+    f32x4 v = pv[r][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = v[i] + w[i];
-    }
+    for (int s = 1; s < GEMM_MAX_SPLIT; ++s)
+      if (s < a.S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = v[i] + pv[r][s][i];
+      }
     acc[r][0] = v;
   }
   epilogue<WT, EPI, R, 1>(a, rb, ct, lane, acc);

@@ -182,6 +182,35 @@ def q8_leg(args, rf, log):
     return out
 
 
+def trace_leg(cfg, dw, rf, log):
+    """Continuous batching at the 7B shape: 8 lanes, 64 seeded jobs with Poisson
+    arrivals (mean gap 4 steps), prompts U[32, 1024] fed one token per step, U[16, 256] new tokens
+    (seed 4); greedy tokens fed back, so every step waits for its argmax.  Reports generated
+    tokens per wall-clock second and the per-step roofline times summed over the trace."""
+    import torch
+    import synth
+    from continuous_batching_decode_step_amd.driver import Engine, run_trace
+    jobs = synth.make_trace(cfg)
+    max_seq = max(len(j.prompt) + j.max_new_tokens for j in jobs)
+    eng = Engine(cfg, dw, 8, max_seq, max_batch=8)
+    warm = synth.make_trace(cfg, n_jobs=2, seed=5)  # graph capture of the small B values
+    run_trace(eng, warm, 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out, st = run_trace(eng, jobs, 8, record_positions=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_roof = sum(rf.roofline_time_s(cfg, [int(x) for x in p]) for p in st.positions)
+    res = {"jobs": len(jobs), "lanes": 8, "steps": st.steps, "idle_steps": st.idle_steps,
+           "lane_steps": st.lane_steps, "generated": st.generated, "wall_s": round(wall, 3),
+           "tok_s": round(st.generated / wall, 1), "lane_steps_per_s": round(st.lane_steps / wall, 1),
+           "mean_occupancy": round(float(np.mean(st.occupancy)), 3),
+           "roofline_frac": round(t_roof / wall, 4)}
+    log("trace C5: %s" % res)
+    del eng
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +229,8 @@ def main() -> int:
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the wide-batch leg (B = 256 with KV U[128,4096], B = 512 with KV U[128,2047]) "
                          "that reports the projections' bf16 MFMA utilisation")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the continuous-batching trace leg (8 lanes, 64 Poisson-arriving jobs, ~40 s)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="end with one device-to-device copy of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -291,6 +322,10 @@ def main() -> int:
         torch.cuda.empty_cache()
         wide = wide_leg(cfg, dw, args, rf, log)
 
+    trace = None
+    if not args.no_trace:
+        trace = trace_leg(cfg, dw, rf, log)
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -326,6 +361,7 @@ def main() -> int:
         "context_q8_smollm135m": q8,
         "wide": None if wide is None else [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                                            for r in wide],
+        "trace_c5": trace,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -110,13 +110,15 @@ class TraceStats:
     lane_steps: int = 0      # sum of live lanes over steps
     generated: int = 0       # generated tokens
     occupancy: List[int] = field(default_factory=list)
+    positions: List[np.ndarray] = field(default_factory=list)  # per step, if recorded: positions before it
 
 
-def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7):
+def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_positions: bool = False):
     """Continuous batching of `jobs` (arrival_step, prompt, max_new_tokens) over n_lanes lanes.
 
     FIFO admission at the start of each step into the lowest free lane.  Returns
-    ({job_id: generated tokens}, TraceStats)."""
+    ({job_id: generated tokens}, TraceStats); with record_positions the stats keep
+    every step's lane positions (before the step)."""
     pending = sorted(jobs, key=lambda j: (j.arrival_step, j.job_id))
     qi = 0
     lane_job: Dict[int, object] = {}
@@ -147,6 +149,8 @@ def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7):
             continue
         toks = [int(lane_job[s].prompt[feed[s]]) if feed[s] < len(lane_job[s].prompt) else last[s] for s in live]
         p = np.array([pos[s] for s in live], np.int32)
+        if record_positions:
+            st.positions.append(p.copy())
         am, _ = eng.step_sync([lane_ids[s] for s in live], p, toks)
         st.steps += 1
         st.lane_steps += len(live)

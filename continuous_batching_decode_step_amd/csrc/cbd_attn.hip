@@ -367,6 +367,34 @@ __device__ inline u32x2 slab_ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+// Cross-lane moves within a row of 16 lanes by DPP (a vector-ALU operand modifier,
+// no trip through the LDS crossbar): every lane of row r takes lane 16r + J, or
+// lane i takes lane i + N of its row (the row's last N lanes keep their own value).
+template <int J>
+__device__ inline float row_bcast(float v) {
+  static_assert(J >= 0 && J < 16, "lane within a row");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               0x150 + J, 0xF, 0xF, false));
+}
+template <int N>
+__device__ inline float row_shl(float v) {
+  static_assert(N >= 1 && N < 16, "shift within a row");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               0x100 + N, 0xF, 0xF, false));
+}
+template <int J>
+struct RowBcastAll {
+  // out[j] = row_bcast<j>(v) for j < J
+  __device__ static inline void run(float v, float* out) {
+    RowBcastAll<J - 1>::run(v, out);
+    out[J - 1] = row_bcast<J - 1>(v);
+  }
+};
+template <>
+struct RowBcastAll<0> {
+  __device__ static inline void run(float, float*) {}
+};
+
 template <int HD, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
   constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
@@ -521,7 +549,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lo = __shfl(sc[t][i], lane + G < 64 ? lane + G : lane);
+        const float lo = row_shl<G>(sc[t][i]);  // column G + j (used by the lanes of columns j < G)
         const int key = kb + 16 * t + 4 * g4 + i;
         const float v = (sc[t][i] + lo) * inv;
         pr[t][i] = key < ke ? v : -INFINITY;
@@ -554,11 +582,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       raw_select<D, true>(vr[it], keep, take, vnr);
       float vv[D];
       raw_to_f32<D, true>(vr[it], vv);
+      float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
+      RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float pj = __shfl(pr[it / 4][it % 4], 16 * g4 + j);
 #pragma unroll
-        for (int e = 0; e < D; ++e) o[j][e] += pj * vv[e];
+        for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
       }
       if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
     }

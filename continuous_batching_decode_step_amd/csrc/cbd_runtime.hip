@@ -482,7 +482,9 @@ constexpr int PANEL_MIN_B = 32;
 
 // Panel width C (lanes per workgroup / 16) and mode for one projection at B
 // lanes. Up to 64 lanes C follows B and a projection splits when full mode
-// would give fewer than 1024 waves. Above 64 lanes, 64-lane panels (which fit
+// would give fewer than 512 waves (measured at 32 and 64 lanes: gate|up and the
+// head, 896 and 1000 waves, run 10-15% faster in full mode than split; QKV, O
+// and down, 256-384 waves, need the split). Above 64 lanes, 64-lane panels (which fit
 // two workgroups per CU) run in full mode when the reduction is short and they
 // already give 2048 waves; otherwise 128-lane panels, split below 4096 waves.
 // Both the width and the mode leave every output's reduction order unchanged.
@@ -490,7 +492,7 @@ static void panel_shape(int B, const Plan& p, int* C, int* split) {
   auto units = [&](int c) { return (long long)p.nRB * ((B + TILE * c - 1) / (TILE * c)); };
   if (B <= 64) {
     *C = B <= 32 ? 2 : 4;
-    *split = p.S > 1 && units(*C) < 1024;
+    *split = p.S > 1 && units(*C) < 512;
   } else if (p.K <= 4096 && units(4) >= 2048) {
     *C = 4;
     *split = 0;

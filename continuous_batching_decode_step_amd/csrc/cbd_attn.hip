@@ -6,8 +6,12 @@
 // (layer, KV head) in the arena, so there is no padding and no mask: a lane at
 // position p reads slots [0, p] and writes slot p.
 //
-// Work item = (lane, KV head, chunk of ATTN_SPLIT = 64 keys), one workgroup of
-// one wave, so a single lane's keys spread over many CUs.  Inside the wave, 16
+// Two kernels produce per-chunk partials.  The matrix-core kernel (bf16 KV,
+// head_dim 64/128, k_attn_mf) takes one workgroup per (lane, KV head, aligned
+// group of ATTN_GROUP chunks of ATTN_SPLIT = 64 keys), one wave per chunk,
+// and merges the group's chunks in LDS into one partial.  The general kernel
+// (k_attn) takes one workgroup of one wave per (lane, KV head, chunk), so a
+// single lane's keys spread over many CUs.  Inside the general kernel's wave, 16
 // lanes share one key row: lane
 // (r, c) = (lane / 16, lane % 16) holds dims [c*D, c*D + D) of key 4*it + r
 // for it = 0..15, D = hd / 16, so every load instruction reads 4 whole rows
@@ -16,15 +20,17 @@
 // and V row is read once per group.  Scores are f32 dot products of the
 // rotated f32 query with the stored keys; a reduce-scatter across the 16
 // lanes of a row leaves lane (r, c) with the score of key 4c + r.  Softmax
-// statistics and the value sum are exact f32 per chunk; chunks meet in a
-// second, small kernel that rescales by each chunk's max and sums them in
-// chunk order.  Chunk size is a constant, so a lane's result depends on its
-// own position only, never on B or on other lanes.
+// statistics and the value sum are exact f32 per chunk; partials meet in a
+// second, small kernel that rescales by each partial's max and sums them in
+// order.  Chunk and group sizes are constants, so a lane's result depends on
+// its own position only, never on B or on other lanes.
 //
 // The workgroup whose chunk holds slot p rotates the new key at p (the same
 // position as the queries: "parallel-slots.md", "S1b decode: design traps",
 // trap 2), rounds K and V to the KV format, writes them in place, and uses
 // the rounded values for key p.
+#include <algorithm>
+
 #include "cbd_internal.h"
 
 namespace cbd {
@@ -395,23 +401,33 @@ struct RowBcastAll<0> {
   __device__ static inline void run(float, float*) {}
 };
 
+// One workgroup per (lane, KV head, aligned group of ATTN_GROUP chunks), one
+// wave per chunk.  Each wave computes its chunk's partial (o, m, l) exactly as
+// a one-chunk work item would; the partials meet in LDS and are merged in
+// chunk order, M = max(Mr, m), Or = Or e^(Mr - M) + o e^(m - M), likewise Lr,
+// into the group's partial.  The group is a function of the lane's position
+// only, so the result never depends on B.
+constexpr int MF_WAVES = ATTN_GROUP;
+
 template <int HD, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
+__global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
   constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
-  constexpr int DQ = HD / 4;    // dims per lane group in the score layout
   constexpr int D = HD / 16;    // dims per lane in the P.V layout
   static_assert(ATTN_SPLIT == 64 && 2 * G <= 16, "four 16-key tiles; hi/lo columns fit in 16");
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 
   const int item = blockIdx.x;
-  if (item >= *a.n_items_dev) return;
+  if (item >= *a.n_items_dev) return;  // the whole workgroup leaves together
   const int g = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int4 it4 = *(const int4*)(a.items + 4 * item);
   const int b = it4.x, c0 = it4.y, nc = it4.z, p = it4.w;
   const int nk = p + 1;
+  const int c = c0 + w;  // this wave's chunk
+  const bool active = w < nc;
   const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
@@ -420,41 +436,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 
   // Whole chunks are read: a slab holds a whole number of chunks, and the
   // slots past p (old or never written) are masked or zeroed after the load.
-  // Chunk -1 means no chunk: every load's offset lies past the slab.
+  // A wave without a chunk loads at an offset past the slab: zeros, no access.
   const unsigned slab_bytes = (unsigned)a.max_seq * HD * 2;
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc(kslab + base, slab_bytes);
   const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(vslab + base, slab_bytes);
-  const unsigned koff0 = ((unsigned)l16 * HD + g4 * 8) * 2;
-  const unsigned voff0 = ((unsigned)(4 * g4) * HD + l16 * D) * 2;
-  auto load_k = [&](u32x4 (&kr)[4][KK], int c) {
-    const unsigned o = c < 0 ? SLAB_OFF : koff0 + (unsigned)c * ATTN_SPLIT * HD * 2;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[t][kk] = slab_ld16(krs, o + (16 * t * HD + kk * 32) * 2);
-  };
-  auto load_v = [&](KVRaw<D, true> (&vr)[16], int c) {
-    const unsigned o = c < 0 ? SLAB_OFF : voff0 + (unsigned)c * ATTN_SPLIT * HD * 2;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const unsigned oi = o + (16 * (it / 4) + it % 4) * HD * 2;
-      if constexpr (D == 8) {
-        const u32x4 v = slab_ld16(vrs, oi);
-        vr[it].w[0] = v.x;
-        vr[it].w[1] = v.y;
-        vr[it].w[2] = v.z;
-        vr[it].w[3] = v.w;
-      } else {
-        const u32x2 v = slab_ld8(vrs, oi);
-        vr[it].w[0] = v.x;
-        vr[it].w[1] = v.y;
-      }
-    }
-  };
+  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 + (unsigned)c * ATTN_SPLIT * HD * 2 : SLAB_OFF;
+  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 + (unsigned)c * ATTN_SPLIT * HD * 2 : SLAB_OFF;
   u32x4 kr[4][KK];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = slab_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
   KVRaw<D, true> vr[16];
-  load_k(kr, c0);
-  load_v(vr, c0);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const unsigned oi = voff + (16 * (it / 4) + it % 4) * HD * 2;
+    if constexpr (D == 8) {
+      const u32x4 v = slab_ld16(vrs, oi);
+      vr[it].w[0] = v.x;
+      vr[it].w[1] = v.y;
+      vr[it].w[2] = v.z;
+      vr[it].w[3] = v.w;
+    } else {
+      const u32x2 v = slab_ld8(vrs, oi);
+      vr[it].w[0] = v.x;
+      vr[it].w[1] = v.y;
+    }
+  }
 
   // rotated value of dim d of an f32 head vector v (rotate-half pairing)
   auto rot = [&](const float* v, int d) -> float {
@@ -463,27 +471,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const float x = v[d], y = v[first ? d + HD / 2 : d - HD / 2];
     return first ? x * t.x - y * t.y : x * t.x + y * t.y;
   };
-  // The wave rotates the group's queries (split into bf16 hi and lo) and, if
-  // its last chunk holds slot p, the new key and value, each lane a few dims,
-  // through LDS; lanes then read their MFMA operand rows from there.
+  // The workgroup rotates the group's queries (split into bf16 hi and lo)
+  // and, if its last chunk holds slot p, the new key and value, through LDS;
+  // lanes then read their MFMA operand rows from there.
   __shared__ __attribute__((aligned(16))) uint16_t qs[2 * G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
-#pragma unroll
-  for (int e = 0; e < G * HD / 64; ++e) {
-    const int idx = e * 64 + lane, j = idx / HD, d = idx % HD;
+  __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
+  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+    const int j = idx / HD, d = idx % HD;
     const float q = rot(row + (size_t)(g * G + j) * HD, d);
     const uint16_t hi = f2bf_a(q);
     qs[j][d] = hi;
     qs[G + j][d] = f2bf_a(q - bf2f(hi));
   }
   const int clast = c0 + nc - 1;
-  const bool item_new = p >= clast * ATTN_SPLIT;  // the item's last chunk holds slot p
-  if (item_new) {
+  if (p >= clast * ATTN_SPLIT) {  // the group's last chunk holds slot p
     const float* kn = row + (size_t)(a.Hq + g) * HD;
     const float* vn = row + (size_t)(a.Hq + a.Hkv + g) * HD;
-#pragma unroll
-    for (int e = 0; e < HD / 64; ++e) {
-      const int d = e * 64 + lane;
+    for (int d = tid; d < HD; d += 64 * MF_WAVES) {
       const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;
       kvn[1][d] = vw;
@@ -492,17 +497,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   }
   __syncthreads();
-  u32x4 bq[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const u32x4 v = *(const u32x4*)&qs[l16 < 2 * G ? l16 : 0][kk * 32 + g4 * 8];
-    bq[kk] = l16 < 2 * G ? v : zero4a();
-  }
 
-  const float inv = 1.0f / sqrtf((float)HD);
-  const size_t pstride = (size_t)G * (HD + 2);
-  for (int ci = 0; ci < nc; ++ci) {
-    const int c = c0 + ci;
+  if (active) {
+    u32x4 bq[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 v = *(const u32x4*)&qs[l16 < 2 * G ? l16 : 0][kk * 32 + g4 * 8];
+      bq[kk] = l16 < 2 * G ? v : zero4a();
+    }
+    const float inv = 1.0f / sqrtf((float)HD);
     const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
     const bool has_new = p >= kb && p < kb + ATTN_SPLIT;
     // the new key and value replace slot p's old contents
@@ -536,11 +539,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
                                                       __builtin_bit_cast(bf16x8, bq[kk]), acc, 0, 0, 0);
       sc[t] = acc;
     }
-    // next chunk's keys (an unconditional load, so the buffers are reused in
-    // place; after the last chunk it reads nothing)
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(kr, c < clast ? c + 1 : -1);
-    __builtin_amdgcn_sched_barrier(0);
 
     // hi + lo, scale, mask; softmax statistics of head l16 (lanes l16 < G)
     float pr[4][4];
@@ -591,10 +589,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       }
       if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
     }
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(vr, c < clast ? c + 1 : -1);
-    __builtin_amdgcn_sched_barrier(0);
-
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -604,16 +598,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         v += __shfl_xor(v, 32);
         o[j][e] = v;
       }
-    float* dst = a.part + (((size_t)b * a.max_splits + c) * a.Hkv + g) * pstride;
     if (g4 == 0) {
 #pragma unroll
       for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int e = 0; e < D; ++e) dst[(size_t)j * (HD + 2) + l16 * D + e] = o[j][e];
+        for (int e = 0; e < D; ++e) os[w][j][l16 * D + e] = o[j][e];
       if (l16 < G) {
-        dst[(size_t)l16 * (HD + 2) + HD] = m;
-        dst[(size_t)l16 * (HD + 2) + HD + 1] = l;
+        ms[w][l16] = m;
+        ls[w][l16] = l;
       }
+    }
+  }
+  __syncthreads();
+
+  // the group's partial: its chunks merged in chunk order (the first chunk
+  // scales the empty state by e^(-inf) = 0)
+  const size_t pstride = (size_t)G * (HD + 2);
+  float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
+  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+    const int j = idx / HD, d = idx % HD;
+    float Mr = -INFINITY, Lr = 0.f, Or = 0.f;
+    for (int k = 0; k < nc; ++k) {
+      const float mk = ms[k][j];
+      const float M = fmaxf(Mr, mk);
+      const float sa = expf(Mr - M), sb = expf(mk - M);
+      Or = Or * sa + os[k][j][d] * sb;
+      Lr = Lr * sa + ls[k][j] * sb;
+      Mr = M;
+    }
+    dst[(size_t)j * (HD + 2) + d] = Or;
+    if (d == 0) {
+      dst[(size_t)j * (HD + 2) + HD] = Mr;
+      dst[(size_t)j * (HD + 2) + HD + 1] = Lr;
     }
   }
 }
@@ -628,115 +644,51 @@ __device__ inline void put_act(void* base, size_t idx, float v) {
     ((_Float16*)base)[idx] = (_Float16)v;
 }
 
-// Combine a lane's chunks: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s,
-// M = max_s m_s.  A workgroup takes 128 outputs (group head, dim) of one
-// (lane, KV head); chunks go in batches of COMB_BATCH = 64, each batch in
-// four contiguous quarters, one per group of 128 threads, each folded in
-// chunk order; then the quarters are added in order, then the batches.  The
-// order depends on the chunk count only, never on B.  Every thread issues its
-// quarter's loads together with the batch's statistics (through LDS): one
-// memory round trip per batch after the lane's position.
-constexpr int COMB_BATCH = 64;
-constexpr int COMB_Q = 4;                        // quarters per batch
-constexpr int COMB_PER = COMB_BATCH / COMB_Q;    // chunks per quarter
-constexpr int COMB_OUT = 128;                    // outputs per workgroup
-constexpr int COMB_MS = 16;                      // threads per group head in the maximum
+// Combine a lane's partials (one per chunk, or per group of chunks):
+// o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s, M = max_s m_s.  One
+// thread per output (group head j, dim) of one (lane, KV head); it loads its
+// partials in batches of COMB_BATCH (one memory round trip per batch) and adds
+// them in partial order, so the result depends on the lane's position only.
+constexpr int COMB_BATCH = 16;
+constexpr int COMB_THREADS = 512;
 
 template <int ACT>
-__global__ __launch_bounds__(COMB_Q * COMB_OUT) void k_attn_combine(AttnArgs a, int hd) {
-  __shared__ float sm[COMB_BATCH * 8], sl[COMB_BATCH * 8], sM[8], sR[COMB_MS * 8];
-  __shared__ float qO[COMB_Q][COMB_OUT], qL[COMB_Q][COMB_OUT];
+__global__ __launch_bounds__(COMB_THREADS) void k_attn_combine(AttnArgs a, int hd) {
   const int b = blockIdx.x, g = blockIdx.y;
-  if (b >= a.B) return;
-  const int tid = threadIdx.x;
-  const int q = tid / COMB_OUT, el = tid % COMB_OUT;
-  const int nsplit = (a.pos[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
-  const int G = a.G;
-  const size_t pstride = (size_t)G * (hd + 2);
-  const size_t sstride = (size_t)a.Hkv * pstride;
-  const float* P0 = a.part + ((size_t)b * a.max_splits * a.Hkv + g) * pstride;
-  const int e = blockIdx.z * COMB_OUT + el;
-  const bool live = e < G * hd;
-  const int j = live ? e / hd : 0, dim = live ? e % hd : 0;
-  const float* P = P0 + (size_t)j * (hd + 2) + dim;
-  if (nsplit > COMB_BATCH) {  // the maximum over all chunks first
-    __shared__ float red[COMB_Q * COMB_OUT];
-    float mx = -INFINITY;
-    for (int t = tid; t < nsplit * G; t += COMB_Q * COMB_OUT)
-      mx = fmaxf(mx, P0[(size_t)(t / G) * sstride + (size_t)(t % G) * (hd + 2) + hd]);
-    red[tid] = mx;
-    __syncthreads();
-    if (tid < G * COMB_MS) {
-      float m = -INFINITY;
-      for (int t = tid; t < COMB_Q * COMB_OUT; t += G * COMB_MS) m = fmaxf(m, red[t]);
-      sR[tid] = m;
-    }
-    __syncthreads();
-    if (tid < G) {
-      float m = -INFINITY;
-      for (int s2 = 0; s2 < COMB_MS; ++s2) m = fmaxf(m, sR[s2 * G + tid]);
-      sM[tid] = m;
-    }
-    __syncthreads();
-  }
-  float Ot = 0.f, Lt = 0.f;
-  for (int u0 = 0; u0 < nsplit; u0 += COMB_BATCH) {
-    const int nb = min(COMB_BATCH, nsplit - u0);
-    const int cq = (nb + COMB_Q - 1) / COMB_Q;
-    const int lo = q * cq, hi = min(lo + cq, nb);  // this quarter's chunks, relative to u0
-    float ov[COMB_PER];
+  const int e = blockIdx.z * blockDim.x + threadIdx.x;  // output j * hd + dim of the group
+  if (b >= a.B || e >= a.G * hd) return;
+  const int j = e / hd, dim = e % hd;
+  const int nchunk = (a.pos[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  const int ns = (nchunk + a.per - 1) / a.per;
+  const size_t sstride = (size_t)a.Hkv * a.G * (hd + 2);
+  const float* P = a.part + (((size_t)b * a.max_splits * a.Hkv + g) * a.G + j) * (hd + 2);
+  float M = -INFINITY;
+  if (ns > COMB_BATCH)  // more than one batch: the maximum over all partials first
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, P[(size_t)s * sstride + hd]);
+  float O = 0.f, L = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += COMB_BATCH) {
+    float mv[COMB_BATCH], ov[COMB_BATCH], lv[COMB_BATCH];
 #pragma unroll
-    for (int i = 0; i < COMB_PER; ++i) ov[i] = P[(size_t)(u0 + min(lo + i, nb - 1)) * sstride];
-    if (tid < nb * G) {
-      const float* Q = P0 + (size_t)(u0 + tid / G) * sstride + (size_t)(tid % G) * (hd + 2);
-      sm[tid] = Q[hd];
-      sl[tid] = Q[hd + 1];
+    for (int i = 0; i < COMB_BATCH; ++i) {
+      const float* q = P + (size_t)min(s0 + i, ns - 1) * sstride;
+      mv[i] = q[hd];
+      lv[i] = q[hd + 1];
+      ov[i] = q[dim];
     }
-    __syncthreads();
-    if (nsplit <= COMB_BATCH) {
-      // the batch's maximum per group head: COMB_MS threads per head take every
-      // COMB_MS-th chunk, then one thread per head their results (a maximum is
-      // exact in any order)
-      if (tid < G * COMB_MS) {
-        float m = -INFINITY;
-        for (int u = tid / G; u < nb; u += COMB_MS) m = fmaxf(m, sm[u * G + tid % G]);
-        sR[tid] = m;
-      }
-      __syncthreads();
-      if (tid < G) {
-        float m = -INFINITY;
-        for (int s2 = 0; s2 < COMB_MS; ++s2) m = fmaxf(m, sR[s2 * G + tid]);
-        sM[tid] = m;
-      }
-    }
-    __syncthreads();
-    if (tid < nb * G) sm[tid] = expf(sm[tid] - sM[tid % G]);
-    __syncthreads();
-    float O = 0.f, L = 0.f;
+    if (ns <= COMB_BATCH) {
 #pragma unroll
-    for (int i = 0; i < COMB_PER; ++i) {
-      if (lo + i < hi) {
-        const float w = sm[(lo + i) * G + j];
-        L += w * sl[(lo + i) * G + j];
+      for (int i = 0; i < COMB_BATCH; ++i)
+        if (i < ns) M = fmaxf(M, mv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < COMB_BATCH; ++i)
+      if (s0 + i < ns) {
+        const float w = expf(mv[i] - M);
         O += w * ov[i];
+        L += w * lv[i];
       }
-    }
-    qO[q][el] = O;
-    qL[q][el] = L;
-    __syncthreads();
-    if (q == 0) {
-      float Ob = qO[0][el], Lb = qL[0][el];
-#pragma unroll
-      for (int k = 1; k < COMB_Q; ++k) {
-        Ob = Ob + qO[k][el];
-        Lb = Lb + qL[k][el];
-      }
-      Ot = u0 == 0 ? Ob : Ot + Ob;
-      Lt = u0 == 0 ? Lb : Lt + Lb;
-    }
-    __syncthreads();
   }
-  if (q == 0 && live) put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * G + j) * hd + dim, Ot / Lt);
+  put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * a.G + j) * hd + dim, O / L);
 }
 
 template <int HD, bool BF>
@@ -760,13 +712,13 @@ static hipError_t launch_hd(int kv_bf16, int G, const AttnArgs& a, dim3 grid, hi
 template <int HD>
 static hipError_t launch_mf(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_mf<HD, 1>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_mf<HD, 2>), grid, dim3(64), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_mf<HD, 3>), grid, dim3(64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_mf<HD, 4>), grid, dim3(64), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_attn_mf<HD, 1>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_mf<HD, 2>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_mf<HD, 3>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_mf<HD, 4>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
     case 8:
       if constexpr (HD == 64) {
-        hipLaunchKernelGGL((k_attn_mf<HD, 8>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((k_attn_mf<HD, 8>), grid, dim3(64 * MF_WAVES), 0, st, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -791,8 +743,9 @@ hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
 hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
   if (a.G > 8) return hipErrorInvalidValue;
-  const dim3 cgrid(a.B, a.Hkv, (a.G * hd + COMB_OUT - 1) / COMB_OUT);
-  const dim3 blk(COMB_Q * COMB_OUT);
+  const int nthr = std::min(COMB_THREADS, (a.G * hd + 63) / 64 * 64);
+  const dim3 cgrid(a.B, a.Hkv, (a.G * hd + nthr - 1) / nthr);
+  const dim3 blk(nthr);
   switch (act) {
     case WT_F32: hipLaunchKernelGGL(k_attn_combine<WT_F32>, cgrid, blk, 0, st, a, hd); break;
     case WT_BF16: hipLaunchKernelGGL(k_attn_combine<WT_BF16>, cgrid, blk, 0, st, a, hd); break;

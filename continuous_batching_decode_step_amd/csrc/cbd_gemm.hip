@@ -118,8 +118,14 @@ __device__ inline u32x4 q8_to_f16(u32x4 raw) {
 
 // The epilogue of one wave's output tile: R row tiles x C column tiles of
 // 16 x 16 results, the wave's row block rb and column group cg.
-template <int WT, int EPI, int R, int C>
+//
+// A wave may own RM consecutive row blocks (rb is then the index of that group
+// and R = RM x the row tiles of one block).  Per-row-block side outputs (sums
+// of x^2, argmax candidates) are written per row block, exactly as a wave
+// owning one block writes them.
+template <int WT, int EPI, int R, int C, int RM = 1>
 __device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, const f32x4 (&acc)[R][C]) {
+  constexpr int R0 = R / RM;  // row tiles of one row block
   const int r16 = lane & 15, g4 = lane >> 4;
   // Output coordinates of acc[r][c][i]: row (or gate/up pair) and lane column.
   auto out_row = [&](int r, int i) -> int {
@@ -149,51 +155,59 @@ __device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, con
           }
         }
     } else if constexpr (EPI == EPI_RESID) {
-      // x += y, and this tile's sum of x^2 per lane for the next RMSNorm
-      float ss = 0.f;
+      // x += y, and each row block's sum of x^2 per lane for the next RMSNorm
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int m = 0; m < RM; ++m) {
+        float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = out_row(r, i);
-          if (!(cok && n < a.N)) continue;
-          const size_t idx = (size_t)col * a.N + n;
-          const float xn = a.out[idx] + acc[r][c][i];
-          a.out[idx] = xn;
-          ss += xn * xn;
-        }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      if (g4 == 0 && cok) a.ssq_out[(size_t)rb * a.B + col] = ss;
+        for (int r = m * R0; r < (m + 1) * R0; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = out_row(r, i);
+            if (!(cok && n < a.N)) continue;
+            const size_t idx = (size_t)col * a.N + n;
+            const float xn = a.out[idx] + acc[r][c][i];
+            a.out[idx] = xn;
+            ss += xn * xn;
+          }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const int ob = rb * RM + m;
+        if (g4 == 0 && cok && ob < a.nRB) a.ssq_out[(size_t)ob * a.B + col] = ss;
+      }
     } else {
-      float best = -INFINITY;
-      int bi = 0x7fffffff;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int m = 0; m < RM; ++m) {
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = out_row(r, i);
-          if (!(cok && n < a.N)) continue;
-          const float v = acc[r][c][i];
-          a.out[(size_t)col * a.N + n] = v;
-          if constexpr (EPI == EPI_HEAD) {
-            if (v > best || (v == best && n < bi)) {
-              best = v;
-              bi = n;
+        for (int r = m * R0; r < (m + 1) * R0; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = out_row(r, i);
+            if (!(cok && n < a.N)) continue;
+            const float v = acc[r][c][i];
+            a.out[(size_t)col * a.N + n] = v;
+            if constexpr (EPI == EPI_HEAD) {
+              if (v > best || (v == best && n < bi)) {
+                best = v;
+                bi = n;
+              }
             }
           }
-        }
-      if constexpr (EPI == EPI_HEAD) {
+        if constexpr (EPI == EPI_HEAD) {
 #pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
-          const float ov = __shfl_xor(best, off);
-          const int oi = __shfl_xor(bi, off);
-          if (ov > best || (ov == best && oi < bi)) {
-            best = ov;
-            bi = oi;
+          for (int off = 16; off < 64; off <<= 1) {
+            const float ov = __shfl_xor(best, off);
+            const int oi = __shfl_xor(bi, off);
+            if (ov > best || (ov == best && oi < bi)) {
+              best = ov;
+              bi = oi;
+            }
           }
+          const int ob = rb * RM + m;
+          if (g4 == 0 && cok && ob < a.nRB) a.amax[(size_t)ob * a.B + col] = make_float2(best, __int_as_float(bi));
         }
-        if (g4 == 0 && cok) a.amax[(size_t)rb * a.B + col] = make_float2(best, __int_as_float(bi));
       }
     }
   }
@@ -419,10 +433,11 @@ __device__ inline unsigned buf_ld2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsi
   return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
-template <int WT, int EPI, int C, bool SPLIT>
+template <int WT, int EPI, int C, int RM, bool SPLIT>
 __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   using PS = PanelShape<WT, C>;
-  constexpr int R = gemm_rows(EPI);
+  constexpr int R0 = gemm_rows(EPI);  // row tiles of one row block
+  constexpr int R = R0 * RM;          // row tiles of one wave: RM consecutive row blocks
   constexpr int KS = PS::KS;
   constexpr int PL = KStep<WT>::per_lane;
   constexpr int U = PS::U;
@@ -431,7 +446,8 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char xl[];  // [2][COLS][ROW_BYTES]
 
   // workgroup -> (row group, split, column group), XCD-aware
-  const int nRG = (a.nRB + PW - 1) / PW;
+  const int nWB = (a.nRB + RM - 1) / RM;  // groups of RM row blocks, one per wave
+  const int nRG = (nWB + PW - 1) / PW;
   const int nRGS = nRG * (SPLIT ? a.S : 1);
   const int bi = blockIdx.x;
   const int cg = (bi >> 3) % a.nCG;
@@ -443,7 +459,7 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int rb = rg * PW + w;  // this wave's row block (may be past the end: then it only helps stage)
+  const int rb = rg * PW + w;  // this wave's group of row blocks (past the end: it only helps stage)
   const int koff = PL * g4;
 
   // k-steps this workgroup walks: all of K, or one split.  When K is not a
@@ -612,21 +628,27 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
     }
     step(av, bv, t);
   }
-  if (rb >= a.nRB) return;
+  if (rb >= nWB) return;
   if constexpr (SPLIT) {
-    // P_s of this wave's R row tiles for the lanes of the column group, as
-    // [split][lane][rb][R tiles][16] (row tile r of row block rb)
+    // P_s of this wave's row tiles for the lanes of the column group, as
+    // [split][lane][row block][R0 tiles][16]; wave tile r belongs to row block
+    // rb*RM + r % RM as its gate (r < RM) or up tile (SwiGLU), else to row
+    // block rb*RM + r / R0 as its tile r % R0.
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int col = cg * PS::COLS + TILE * c + r16;
       if (col >= a.B) continue;
-      float* dst = a.part + (((size_t)split * a.B + col) * a.nRB + rb) * (R * TILE) + 4 * g4;
+      float* dst = a.part + (size_t)split * a.B * a.nRB * (R0 * TILE) + (size_t)col * a.nRB * (R0 * TILE) + 4 * g4;
 #pragma unroll
-      for (int r = 0; r < R; ++r) *(f32x4*)(dst + r * TILE) = acc[r][c];
+      for (int r = 0; r < R; ++r) {
+        const int ob = rb * RM + (EPI == EPI_SWIGLU ? r % RM : r / R0);
+        const int t0r = EPI == EPI_SWIGLU ? r / RM : r % R0;
+        if (ob < a.nRB) *(f32x4*)(dst + (size_t)ob * (R0 * TILE) + t0r * TILE) = acc[r][c];
+      }
     }
   } else {
     fold();
-    epilogue<WT, EPI, R, C>(a, rb, cg, lane, tot);
+    epilogue<WT, EPI, R, C, RM>(a, rb, cg, lane, tot);
   }
 }
 
@@ -701,58 +723,79 @@ hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st
   }
 }
 
-int panel_workgroups(const GemmArgs& a, int C, int split) {
-  const int nRG = (a.nRB + PW - 1) / PW;
+int panel_workgroups(const GemmArgs& a, int C, int rm, int split) {
+  const int nRG = ((a.nRB + rm - 1) / rm + PW - 1) / PW;
   const int nRGS = nRG * (split ? a.S : 1);
   const int nCG = (a.B + TILE * C - 1) / (TILE * C);
   return ((nRGS + 7) / 8) * 8 * nCG;
 }
 
-template <int WT, int EPI, int C>
+template <int WT, int EPI, int C, int RM>
 static hipError_t launch_panel_c(int split, const GemmArgs& a, hipStream_t st) {
   const size_t lds = panel_lds_bytes(WT, C);
-  const int blocks = panel_workgroups(a, C, split);
+  const int blocks = panel_workgroups(a, C, RM, split);
   if (split) {
-    hipLaunchKernelGGL((k_panel<WT, EPI, C, true>), dim3(blocks), dim3(PW * 64), lds, st, a);
+    hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, true>), dim3(blocks), dim3(PW * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nct = (a.B + TILE - 1) / TILE;
     hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
   } else {
-    hipLaunchKernelGGL((k_panel<WT, EPI, C, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
+    hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
   }
   return hipGetLastError();
 }
 
 template <int WT, int EPI>
-static hipError_t launch_panel_epi(int C, int split, const GemmArgs& a, hipStream_t st) {
-  switch (C) {
-    case 2: return launch_panel_c<WT, EPI, 2>(split, a, st);
-    case 4: return launch_panel_c<WT, EPI, 4>(split, a, st);
-    case 8: return launch_panel_c<WT, EPI, 8>(split, a, st);
-    default: return hipErrorInvalidValue;
+static hipError_t launch_panel_epi(int C, int rm, int split, const GemmArgs& a, hipStream_t st) {
+  // Row blocks per wave: RM x gemm_rows(EPI) row tiles of 16, at most 4.
+  constexpr int R0 = gemm_rows(EPI);
+  if (rm == 1) {
+    switch (C) {
+      case 2: return launch_panel_c<WT, EPI, 2, 1>(split, a, st);
+      case 4: return launch_panel_c<WT, EPI, 4, 1>(split, a, st);
+      case 8: return launch_panel_c<WT, EPI, 8, 1>(split, a, st);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (rm == 2) {
+    switch (C) {
+      case 4: return launch_panel_c<WT, EPI, 4, 2>(split, a, st);
+      case 8: return launch_panel_c<WT, EPI, 8, 2>(split, a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if constexpr (R0 == 1) {
+    if (rm == 4) {
+      switch (C) {
+        case 4: return launch_panel_c<WT, EPI, 4, 4>(split, a, st);
+        case 8: return launch_panel_c<WT, EPI, 8, 4>(split, a, st);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int WT>
-static hipError_t launch_panel_wt(int epi, int C, int split, const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_panel_wt(int epi, int C, int rm, int split, const GemmArgs& a, hipStream_t st) {
   switch (epi) {
-    case EPI_STORE: return launch_panel_epi<WT, EPI_STORE>(C, split, a, st);
-    case EPI_RESID: return launch_panel_epi<WT, EPI_RESID>(C, split, a, st);
-    case EPI_SWIGLU: return launch_panel_epi<WT, EPI_SWIGLU>(C, split, a, st);
-    default: return launch_panel_epi<WT, EPI_HEAD>(C, split, a, st);
+    case EPI_STORE: return launch_panel_epi<WT, EPI_STORE>(C, rm, split, a, st);
+    case EPI_RESID: return launch_panel_epi<WT, EPI_RESID>(C, rm, split, a, st);
+    case EPI_SWIGLU: return launch_panel_epi<WT, EPI_SWIGLU>(C, rm, split, a, st);
+    default: return launch_panel_epi<WT, EPI_HEAD>(C, rm, split, a, st);
   }
 }
 
-hipError_t launch_panel(int wt, int epi, int C, int split, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_panel(int wt, int epi, int C, int rm, int split, const GemmArgs& a, hipStream_t st) {
   if (a.S < 1) return hipErrorInvalidValue;
   if (a.nRB <= 0 || a.B <= 0) return hipSuccess;
   GemmArgs g = a;
   g.nCG = (a.B + TILE * C - 1) / (TILE * C);
   switch (wt) {
-    case WT_F32: return launch_panel_wt<WT_F32>(epi, C, split, g, st);
-    case WT_BF16: return launch_panel_wt<WT_BF16>(epi, C, split, g, st);
-    default: return launch_panel_wt<WT_Q8>(epi, C, split, g, st);
+    case WT_F32: return launch_panel_wt<WT_F32>(epi, C, rm, split, g, st);
+    case WT_BF16: return launch_panel_wt<WT_BF16>(epi, C, rm, split, g, st);
+    default: return launch_panel_wt<WT_Q8>(epi, C, rm, split, g, st);
   }
 }
 

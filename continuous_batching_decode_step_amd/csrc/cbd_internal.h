@@ -13,6 +13,10 @@ enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
 // Keys per attention split.  A constant of the design: the per-lane result
 // never depends on B, on the lane's slot or on the other lanes.
 constexpr int ATTN_SPLIT = 64;
+// Chunks per attention work item of the matrix-core kernel: aligned groups of
+// a lane's chunks, merged in chunk order inside the wave into one partial.  A
+// constant of the design, like ATTN_SPLIT.
+constexpr int ATTN_GROUP = 4;
 // Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
 // epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
 // rows; the others take one tile so that d-row projections fill the chip).
@@ -64,22 +68,24 @@ struct AttnArgs {
   const int* items;       // [n_items][4] {b, first chunk, chunks, position}, 16-byte aligned
   const int* n_items_dev; // number of items of this step (device)
   int max_items;          // grid size: the most items a step of B lanes can have
-  int max_splits;         // chunks per lane the partial buffer is sized for
+  int max_splits;         // partials per lane the partial buffer is sized for
+  int per;                // chunks per partial: ATTN_GROUP (matrix-core kernel) or 1
   int Hq, Hkv, G, Nqkv;
   const float2* rope;     // [B][hd/2] (cos, sin) of each lane's position
-  float* part;            // [B][max_splits][Hkv][G][hd + 2] chunk partials (o, m, l)
+  float* part;            // [B][max_splits][Hkv][G][hd + 2] partials (o, m, l) per chunk or group
   void* out;              // [B, Hq*hd] in the activation format
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------------
 hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
 // Wide-panel projection (activation panel staged in LDS, 16*C lanes per
-// workgroup, C in {2, 4, 8}); split = 1 writes split partials to a.part and
-// adds them in order in a second kernel.
+// workgroup, C in {2, 4, 8}; rm row blocks per wave, rm in {1, 2} and 4 for
+// one-tile blocks, with C >= 4 when rm > 1); split = 1 writes split partials to
+// a.part and adds them in order in a second kernel.
 // Same output bits as launch_gemm.
-hipError_t launch_panel(int wt, int epi, int C, int split, const GemmArgs& a, hipStream_t st);
+hipError_t launch_panel(int wt, int epi, int C, int rm, int split, const GemmArgs& a, hipStream_t st);
 // workgroups of one panel launch (for sizing decisions)
-int panel_workgroups(const GemmArgs& a, int C, int split);
+int panel_workgroups(const GemmArgs& a, int C, int rm, int split);
 // Whether the MFMA attention kernel serves this shape (bf16 KV; head_dim 64
 // with up to 8, or 128 with up to 4 query heads per KV head, the shapes that
 // fit two waves per SIMD); otherwise items carry one chunk.

@@ -127,15 +127,11 @@ struct WsLayout {
   int maxB, MS;
 };
 
-// Attention waves a step aims for when it groups chunks (see k_attn_mf).
-constexpr long long ATTN_TARGET_WAVES = 4096;
-
-// 64-key chunks per attention wave: 1 for the one-chunk kernel; for the MFMA
-// kernel enough to bring the step's waves down towards ATTN_TARGET_WAVES.
-int attn_chunks_per_wave(const cbd_model* m, long long chunks) {
-  if (!attn_mfma_supported(m->c.head_dim, m->wt == WT_BF16, m->G)) return 1;
-  const long long waves = chunks * m->c.n_kv_heads;
-  return (int)std::max(1LL, std::min(8LL, waves / ATTN_TARGET_WAVES));
+// 64-key chunks per attention work item (and per partial): 1 for the one-chunk
+// kernel; aligned groups of ATTN_GROUP for the matrix-core kernel, which
+// merges a group inside the wave.  Never a function of B.
+int attn_chunks_per_item(const cbd_model* m) {
+  return attn_mfma_supported(m->c.head_dim, m->wt == WT_BF16, m->G) ? ATTN_GROUP : 1;
 }
 
 // Per-step metadata: lanes[B], positions[B], tokens[B], n_items, padding to a
@@ -480,25 +476,33 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // Automatic choice: the wide-panel kernel from this many lanes on.
 constexpr int PANEL_MIN_B = 32;
 
-// Panel width C (lanes per workgroup / 16) and mode for one projection at B
-// lanes. Up to 64 lanes C follows B and a projection splits when full mode
-// would give fewer than 512 waves (measured at 32 and 64 lanes: gate|up and the
-// head, 896 and 1000 waves, run 10-15% faster in full mode than split; QKV, O
-// and down, 256-384 waves, need the split). Above 64 lanes, 64-lane panels (which fit
-// two workgroups per CU) run in full mode when the reduction is short and they
-// already give 2048 waves; otherwise 128-lane panels, split below 4096 waves.
-// Both the width and the mode leave every output's reduction order unchanged.
-static void panel_shape(int B, const Plan& p, int* C, int* split) {
+// Panel width C (lanes per workgroup / 16), row blocks per wave and mode for
+// one projection at B lanes (measured per projection at 64-512 lanes on the
+// 7B shapes). Up to 64 lanes C follows B and a projection splits when full mode
+// would give fewer than 512 waves (gate|up and the head, 896 and 1000 waves,
+// run 10-15% faster in full mode than split; QKV, O and down, 256-384 waves,
+// need the split); a split with a long reduction (down) gives each wave two
+// row blocks (10% faster at 64 lanes). Above 64 lanes, 64-lane panels (which
+// fit two workgroups per CU) run in full mode when the reduction is short and
+// they already give 1536 waves; otherwise 128-lane panels, split below 4096
+// waves, with two row blocks per wave for one-tile blocks (QKV, O, down:
+// 5-20% faster). Neither width, row blocks per wave nor mode changes any
+// output's reduction order.
+static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* split) {
   auto units = [&](int c) { return (long long)p.nRB * ((B + TILE * c - 1) / (TILE * c)); };
+  const bool one_tile = gemm_rows(epi) == 1;
+  *rm = 1;
   if (B <= 64) {
     *C = B <= 32 ? 2 : 4;
     *split = p.S > 1 && units(*C) < 512;
-  } else if (p.K <= 4096 && units(4) >= 2048) {
+    if (*split && B > 32 && one_tile && p.K > 4096) *rm = 2;
+  } else if (p.K <= 4096 && units(4) >= 1536) {
     *C = 4;
     *split = 0;
   } else {
     *C = 8;
     *split = p.S > 1 && units(8) < 4096;
+    if (*split && one_tile) *rm = 2;
   }
 }
 
@@ -523,9 +527,9 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   const bool panel = m->variant == 2 || (m->variant == 0 && B >= PANEL_MIN_B);
   ProfScope ps(m, cls, st);
   if (panel) {
-    int C, split;
-    panel_shape(B, p, &C, &split);
-    HIP_TRY(launch_panel(m->wt, epi, C, split, g, st));
+    int C, rm, split;
+    panel_shape(B, p, epi, &C, &rm, &split);
+    HIP_TRY(launch_panel(m->wt, epi, C, rm, split, g, st));
   } else {
     const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
     g.nCG = (B + TILE * C - 1) / (TILE * C);
@@ -570,7 +574,8 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   at.pos = d_pos;
   at.items = d_items;
   at.n_items_dev = d_nitems;
-  at.max_items = B * L.MS;
+  at.per = attn_chunks_per_item(m);
+  at.max_items = B * ((L.MS + at.per - 1) / at.per);
   at.max_splits = L.MS;
   at.Hq = c.n_heads;
   at.Hkv = c.n_kv_heads;
@@ -648,13 +653,13 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
 
   // Per-step metadata: lanes, positions, tokens, item count, attention work
   // items {b, first chunk, chunks, position}: a wave of the attention kernel
-  // takes up to `per` consecutive 64-key chunks of one lane (per-chunk
-  // results do not depend on the grouping).
+  // takes one aligned group of up to `per` consecutive 64-key chunks of one
+  // lane, the same groups whatever B is.
   std::vector<int32_t> meta;
   const size_t hdr = meta_header(B);
   long long chunks = 0;
   for (int b = 0; b < B; ++b) chunks += (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
-  const int per = attn_chunks_per_wave(m, chunks);
+  const int per = attn_chunks_per_item(m);
   meta.reserve(hdr + 4 * (size_t)chunks);
   meta.insert(meta.end(), lanes, lanes + B);
   meta.insert(meta.end(), positions, positions + B);

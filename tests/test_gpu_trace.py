@@ -22,8 +22,12 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 N_LANES = 8
 
 
-def test_trace_jobs_equal_serial_runs(device_weights_7b):
-    from continuous_batching_decode_step_amd.driver import Engine, generate_lockstep, run_trace
+QUARTERS = 4  # the serial runs are checked in four tests, so progress shows between them
+
+
+@pytest.fixture(scope="module")
+def trace_run(device_weights_7b):
+    from continuous_batching_decode_step_amd.driver import Engine, run_trace
     cfg = synth.MISTRAL7B
     jobs = synth.make_trace(cfg)
     max_seq = max(len(j.prompt) + j.max_new_tokens for j in jobs)
@@ -32,14 +36,27 @@ def test_trace_jobs_equal_serial_runs(device_weights_7b):
     out, st = run_trace(eng, jobs, N_LANES)
     say("trace: %d steps (%d idle), %d lane-steps, mean occupancy %.2f" % (
         st.steps, st.idle_steps, st.lane_steps, np.mean(st.occupancy)))
+    yield eng, jobs, out, st
+    del eng
+
+
+def test_trace_runs_every_job_and_frees_the_arena(trace_run):
+    eng, jobs, out, st = trace_run
     assert st.lane_steps == sum(len(j.prompt) + j.max_new_tokens - 1 for j in jobs)
     assert max(st.occupancy) == N_LANES
     assert eng.arena.used_bytes == 0 and eng.arena.live_lanes == 0
     for j in jobs:
         assert len(out[j.job_id]) == j.max_new_tokens
+
+
+@pytest.mark.parametrize("quarter", range(QUARTERS))
+def test_trace_jobs_equal_serial_runs(trace_run, quarter):
+    from continuous_batching_decode_step_amd.driver import generate_lockstep
+    eng, jobs, out, _ = trace_run
+    for j in jobs[quarter::QUARTERS]:
         gen, _ = generate_lockstep(eng, [j.prompt], j.max_new_tokens)
         same = gen[0] == out[j.job_id]
-        if j.job_id % 8 == 0 or not same:
+        if j.job_id % 8 == quarter or not same:
             say("trace: job %d (prompt %d, %d new) serial %s" % (
                 j.job_id, len(j.prompt), j.max_new_tokens, "identical" if same else "DIFFERS"))
         assert same, j.job_id

@@ -533,34 +533,43 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
     }
   };
 
+  // The running total starts at -0: (-0) + x is x bit for bit for every x
+  // (-0 included), so adding P_0 to it gives exactly P_0.
   f32x4 acc[R][C], tot[R][C];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[r][c] = tot[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool have_tot = false;
+    for (int c = 0; c < C; ++c) {
+      acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tot[r][c] = f32x4{-0.f, -0.f, -0.f, -0.f};
+    }
   int tf = t0 + kps;  // full mode: the first k-step of the next split
-  // split boundary: fold the finished split's chain into the running total
+  // split boundary: fold the finished split's chain into the running total.
+  // Split lengths are whole multiples of two chunks, so boundaries fall
+  // between chunk pairs (or before the partial last k-step of K).
   auto fold = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        if (have_tot) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tot[r][c][i] = tot[r][c][i] + acc[r][c][i];
-        } else {
-          tot[r][c] = acc[r][c];
-        }
+        for (int i = 0; i < 4; ++i) tot[r][c][i] = tot[r][c][i] + acc[r][c][i];
         acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    have_tot = true;
+  };
+  // A uniform branch taken once per split: the volatile statement keeps it a
+  // branch outside the MFMA stream.
+  auto fold_at = [&](int t) {
+    if constexpr (!SPLIT) {
+      if (t == tf) {
+        __asm__ volatile("");
+        fold();
+        tf += kps;
+      }
+    }
   };
   auto step = [&](u32x4 av0[R], const u32x4 (&bv)[C], int t) {
-    if (!SPLIT && t == tf) {
-      fold();
-      tf += kps;
-    }
+    (void)t;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       u32x4 av = av0[r];
@@ -594,6 +603,7 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
     load_w(A1, 1);
     __syncthreads();
     for (int st = 0; st < nst; st += 2) {
+      fold_at(t0 + st * U);
       compute(A0, 0, st);
       store_x(xr, 1);
       if (st + 2 < nst) {
@@ -613,6 +623,7 @@ __global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
   if (tail) {
     // The partial last k-step: lane vectors past K are zero on both sides.
     const int t = tm;
+    fold_at(t);
     const bool kok = t * KS + koff + PL <= a.K;
     u32x4 av[R], bv[C];
 #pragma unroll

@@ -45,6 +45,10 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int TARGET_WAVES = 4096;  // split-K is chosen so a B=1 step has this many waves
 constexpr int MIN_KS = 256;         // but no split shorter than this many elements
+// Split lengths are whole multiples of this many elements, so that every split
+// of a wide-panel walk covers an even number of LDS chunks (a chunk is at most
+// 128 elements) and the running total is folded between chunk pairs only.
+constexpr int KS_ALIGN = 256;
 constexpr int NSLOT = 4;  // pinned staging slots for per-step metadata
 
 struct Plan {
@@ -60,7 +64,8 @@ Plan make_plan(int N, int Nraw, int K, int kstep, int rows_per_rb) {
   int S = (TARGET_WAVES + p.nRB - 1) / p.nRB;
   S = std::max(1, std::min(std::min(S, K / MIN_KS), GEMM_MAX_SPLIT));
   int Ks = (K + S - 1) / S;
-  Ks = (Ks + kstep - 1) / kstep * kstep;
+  Ks = (Ks + KS_ALIGN - 1) / KS_ALIGN * KS_ALIGN;
+  (void)kstep;  // KS_ALIGN is a multiple of every k-step
   p.Ks = Ks;
   p.S = (K + Ks - 1) / Ks;
   return p;
@@ -480,14 +485,14 @@ constexpr int PANEL_MIN_B = 32;
 // one projection at B lanes (measured per projection at 64-512 lanes on the
 // 7B shapes). Up to 64 lanes C follows B and a projection splits when full mode
 // would give fewer than 512 waves (gate|up and the head, 896 and 1000 waves,
-// run 10-15% faster in full mode than split; QKV, O and down, 256-384 waves,
+// run 10-20% faster in full mode than split; QKV, O and down, 256-384 waves,
 // need the split); a split with a long reduction (down) gives each wave two
-// row blocks (10% faster at 64 lanes). Above 64 lanes, 64-lane panels (which
-// fit two workgroups per CU) run in full mode when the reduction is short and
-// they already give 1536 waves; otherwise 128-lane panels, split below 4096
-// waves, with two row blocks per wave for one-tile blocks (QKV, O, down:
-// 5-20% faster). Neither width, row blocks per wave nor mode changes any
-// output's reduction order.
+// row blocks (10% faster at 64 lanes). Above 64 lanes: two-tile row blocks
+// (gate|up, the head) run 128-lane panels in full mode; short one-tile
+// projections (QKV, O) run 64-lane panels in full mode once those give 1536
+// waves, else 128-lane panels split with two row blocks per wave, as does the
+// long reduction (down). Neither width, row blocks per wave nor mode changes
+// any output's reduction order.
 static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* split) {
   auto units = [&](int c) { return (long long)p.nRB * ((B + TILE * c - 1) / (TILE * c)); };
   const bool one_tile = gemm_rows(epi) == 1;
@@ -496,13 +501,16 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
     *C = B <= 32 ? 2 : 4;
     *split = p.S > 1 && units(*C) < 512;
     if (*split && B > 32 && one_tile && p.K > 4096) *rm = 2;
+  } else if (!one_tile) {
+    *C = 8;
+    *split = 0;
   } else if (p.K <= 4096 && units(4) >= 1536) {
     *C = 4;
     *split = 0;
   } else {
     *C = 8;
-    *split = p.S > 1 && units(8) < 4096;
-    if (*split && one_tile) *rm = 2;
+    *split = p.S > 1;
+    if (*split) *rm = 2;
   }
 }
 

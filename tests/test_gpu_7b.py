@@ -104,3 +104,47 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         say("7B: lane %d new K/V rel err %.3g / %.3g, layer 0 %.3g / %.3g" % (b, ek, ev, ek0, ev0))
         assert ek <= _bar(b, "k_new_max_rel") and ev <= _bar(b, "v_new_max_rel")
         assert ek0 <= LAYER0_TOL and ev0 <= LAYER0_TOL
+
+
+WIDE_BATCHES = [128, 256, 512]
+WIDE_SAMPLE = [0, 77, 127]
+
+
+def test_mistral7b_wide_batches_bit_identical_to_lane_alone(device_weights_7b):
+    """Above 64 lanes the projections run as 64- and 128-lane panels, in full
+    or split mode, with one or two row blocks per wave (a choice per
+    projection and B); one lane alone runs the split-K tiles.  All follow one
+    reduction contract, so sampled lanes' logits must be bitwise equal to the
+    lane stepped alone at B = 128, 256 and 512 (short KV, U[1, 48], so the
+    arena stays small)."""
+    import torch
+    from continuous_batching_decode_step_amd.driver import Engine
+    cfg = synth.MISTRAL7B
+    nl = max(WIDE_BATCHES)
+    lens = synth.kv_lengths(nl, lo=1, hi=48)
+    toks = synth.step_tokens(cfg, nl)
+    eng = Engine(cfg, device_weights_7b, nl, int(lens.max()) + 1, max_batch=nl)
+    lanes = [eng.arena.lane_alloc() for _ in range(nl)]
+    say("7B wide: loading KV of %d lanes" % nl)
+    for b in range(nl):
+        k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
+        eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
+    torch.cuda.synchronize()
+    alone = {}
+    for b in WIDE_SAMPLE:
+        eng.arena.lane_truncate(lanes[b], int(lens[b]))
+        p1 = np.array([lens[b]], np.int32)
+        am1, lg1 = eng.step_sync([lanes[b]], p1, [int(toks[b])], want_logits=True)
+        assert int(am1[0]) == int(np.argmax(lg1[0]))
+        alone[b] = lg1[0].copy()
+    for B in WIDE_BATCHES:
+        say("7B wide: step B=%d" % B)
+        for b in range(B):
+            eng.arena.lane_truncate(lanes[b], int(lens[b]))
+        pos = lens[:B].astype(np.int32).copy()
+        am, lg = eng.step_sync(lanes[:B], pos, toks[:B], want_logits=True)
+        assert np.array_equal(pos, lens[:B] + 1)
+        assert np.array_equal(am, np.argmax(lg, axis=1))
+        for b in WIDE_SAMPLE:
+            assert np.array_equal(lg[b].view(np.uint32), alone[b].view(np.uint32)), (b, B)
+    del eng

@@ -116,14 +116,15 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int b = a.items[4 * item];
-  const int s = a.items[4 * item + 1];  // one chunk per item for this kernel
+  const int4 it4 = *(const int4*)(a.items + 4 * item);
+  const int b = it4.x & 0xffffff;
+  const int s = it4.y;  // one chunk per item for this kernel
   const int p = a.pos[b];
   const int nk = p + 1;
   const int kbeg = s * ATTN_SPLIT;  // first key of the chunk
   const int kend = min(kbeg + ATTN_SPLIT, nk);
 
-  const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  const long long base = (long long)it4.w * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
   const int d0 = c * D;  // first dim of this lane
@@ -424,11 +425,11 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int4 it4 = *(const int4*)(a.items + 4 * item);
-  const int b = it4.x, c0 = it4.y, nc = it4.z, p = it4.w;
+  const int b = it4.x & 0xffffff, nc = it4.x >> 24, c0 = it4.y, p = it4.z;
   const int nk = p + 1;
   const int c = c0 + w;  // this wave's chunk
   const bool active = w < nc;
-  const long long base = (long long)a.lanes[b] * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  const long long base = (long long)it4.w * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
   const uint16_t* kslab = (const uint16_t*)a.kslab;

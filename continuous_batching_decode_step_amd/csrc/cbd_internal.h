@@ -65,7 +65,7 @@ struct AttnArgs {
   int B;
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
-  const int* items;       // [n_items][4] {b, first chunk, chunks, position}, 16-byte aligned
+  const int* items;       // [n_items][4] {b | chunks << 24, first chunk, position, arena lane}, 16-byte aligned
   const int* n_items_dev; // number of items of this step (device)
   int max_items;          // grid size: the most items a step of B lanes can have
   int max_splits;         // partials per lane the partial buffer is sized for

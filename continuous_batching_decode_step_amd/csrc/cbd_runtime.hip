@@ -140,8 +140,8 @@ int attn_chunks_per_item(const cbd_model* m) {
 }
 
 // Per-step metadata: lanes[B], positions[B], tokens[B], n_items, padding to a
-// multiple of 4 ints, then the attention work items {b, first chunk, chunks,
-// position}, 16-byte aligned.
+// multiple of 4 ints, then the attention work items {b | chunks << 24, first
+// chunk, position, arena lane}, 16-byte aligned (B is at most 65536).
 size_t meta_header(int B) { return ((size_t)3 * B + 1 + 3) & ~(size_t)3; }
 
 WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
@@ -478,8 +478,21 @@ int cbd_set_variant(cbd_model* m, int variant) {
   return CBD_OK;
 }
 
-// Automatic choice: the wide-panel kernel from this many lanes on.
-constexpr int PANEL_MIN_B = 32;
+// Automatic choice of the projection family: wide panels from this many
+// lanes on, per projection (measured on the 7B shapes at 1-32 lanes, each
+// projection alone): below these widths the split-K tiles are as fast or
+// faster; above them their per-wave activation re-reads cost more than a
+// mostly idle 32-lane panel (at 16 lanes the four layer projections take
+// 116 us as split-K tiles, 97 us as panels).  The long reduction (down) is
+// faster as a panel even for one lane.
+static int panel_min_b(int epi, int K) {
+  switch (epi) {
+    case EPI_STORE: return 4;               // QKV
+    case EPI_SWIGLU: return 8;              // gate|up
+    case EPI_HEAD: return 4;
+    default: return K > 4096 ? 1 : 24;      // down; O
+  }
+}
 
 // Panel width C (lanes per workgroup / 16), row blocks per wave and mode for
 // one projection at B lanes (measured per projection at 64-512 lanes on the
@@ -532,7 +545,7 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.amax = (float2*)(ws + L.amax);
   g.ssq_out = (float*)(ws + L.ssq);
   g.part = (float*)(ws + L.gpart);
-  const bool panel = m->variant == 2 || (m->variant == 0 && B >= PANEL_MIN_B);
+  const bool panel = m->variant == 2 || (m->variant == 0 && B >= panel_min_b(epi, p.K));
   ProfScope ps(m, cls, st);
   if (panel) {
     int C, rm, split;
@@ -660,9 +673,9 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   char* ws = (char*)workspace;
 
   // Per-step metadata: lanes, positions, tokens, item count, attention work
-  // items {b, first chunk, chunks, position}: a wave of the attention kernel
-  // takes one aligned group of up to `per` consecutive 64-key chunks of one
-  // lane, the same groups whatever B is.
+  // items {b | chunks << 24, first chunk, position, arena lane}: a workgroup of
+  // the attention kernel takes one aligned group of up to `per` consecutive
+  // 64-key chunks of one lane, the same groups whatever B is.
   std::vector<int32_t> meta;
   const size_t hdr = meta_header(B);
   long long chunks = 0;
@@ -677,10 +690,10 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   for (int b = 0; b < B; ++b) {
     const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
     for (int s0 = 0; s0 < ns; s0 += per) {
-      meta.push_back(b);
+      meta.push_back(b | (std::min(per, ns - s0) << 24));
       meta.push_back(s0);
-      meta.push_back(std::min(per, ns - s0));
       meta.push_back(positions[b]);
+      meta.push_back(lanes[b]);
       ++n_items;
     }
   }

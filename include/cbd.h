@@ -214,7 +214,9 @@ const char* cbd_profile_class_name(int cls);
 int cbd_set_graph_replay(cbd_model* m, int enable);
 
 /* Projection kernel family for steps of this model: 0 = automatic by batch
- * width (split-K tiles below 32 lanes, wide panels from 32 on), 1 =
+ * width and projection (wide panels from 4 lanes for QKV and the LM head, 8
+ * for gate|up, 24 for the output projection, always for a reduction longer
+ * than 4096; split-K tiles below), 1 =
  * weight-streaming split-K tiles at every width, 2 = wide panels (the
  * activation panel staged in on-chip memory) at every width.  Every family
  * computes each output with the same chunked reduction, so the choice changes

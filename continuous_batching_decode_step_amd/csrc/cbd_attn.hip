@@ -30,6 +30,7 @@
 // trap 2), rounds K and V to the KV format, writes them in place, and uses
 // the rounded values for key p.
 #include <algorithm>
+#include <type_traits>
 
 #include "cbd_internal.h"
 
@@ -556,12 +557,14 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       }
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
+    // exponentials by the hardware exp2 with the log2(e) scale (about 1 ulp;
+    // this kernel serves bf16 caches only)
     float l = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[t][i] = pr[t][i] == -INFINITY ? 0.f : expf(pr[t][i] - m);
+        pr[t][i] = pr[t][i] == -INFINITY ? 0.f : __expf(pr[t][i] - m);
         l += pr[t][i];
       }
     l += __shfl_xor(l, 16);
@@ -573,23 +576,33 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     for (int j = 0; j < G; ++j)
 #pragma unroll
       for (int e = 0; e < D; ++e) o[j][e] = 0.f;
+    // A chunk wholly below slot p needs no masking: every key is an old, valid
+    // one (a uniform branch).
+    auto pv_pass = [&](auto masked) {
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
-      const unsigned take = key == p ? ~0u : 0u;
-      const unsigned keep = key < p ? ~0u : 0u;
-      raw_select<D, true>(vr[it], keep, take, vnr);
-      float vv[D];
-      raw_to_f32<D, true>(vr[it], vv);
-      float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
-      RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
+      for (int it = 0; it < 16; ++it) {
+        if constexpr (decltype(masked)::value) {
+          const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
+          const unsigned take = key == p ? ~0u : 0u;
+          const unsigned keep = key < p ? ~0u : 0u;
+          raw_select<D, true>(vr[it], keep, take, vnr);
+        }
+        float vv[D];
+        raw_to_f32<D, true>(vr[it], vv);
+        float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
+        RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+        for (int j = 0; j < G; ++j) {
 #pragma unroll
-        for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
+          for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
+        }
+        if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
       }
-      if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
-    }
+    };
+    if (p >= kb + ATTN_SPLIT)
+      pv_pass(std::false_type{});
+    else
+      pv_pass(std::true_type{});
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -613,25 +626,32 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   __syncthreads();
 
   // the group's partial: its chunks merged in chunk order (the first chunk
-  // scales the empty state by e^(-inf) = 0)
+  // scales the empty state by e^(-inf) = 0).  The scales of chunk k, e^(Mr - M)
+  // and e^(m_k - M), depend on the head only: one thread per head takes them
+  // (and the maximum and sum) in order, then every output uses them.
   const size_t pstride = (size_t)G * (HD + 2);
   float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
-  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
-    const int j = idx / HD, d = idx % HD;
-    float Mr = -INFINITY, Lr = 0.f, Or = 0.f;
+  __shared__ float sca[MF_WAVES][G], scb[MF_WAVES][G];
+  if (tid < G) {
+    float Mr = -INFINITY, Lr = 0.f;
     for (int k = 0; k < nc; ++k) {
-      const float mk = ms[k][j];
+      const float mk = ms[k][tid];
       const float M = fmaxf(Mr, mk);
-      const float sa = expf(Mr - M), sb = expf(mk - M);
-      Or = Or * sa + os[k][j][d] * sb;
-      Lr = Lr * sa + ls[k][j] * sb;
+      const float sa = __expf(Mr - M), sb = __expf(mk - M);
+      sca[k][tid] = sa;
+      scb[k][tid] = sb;
+      Lr = Lr * sa + ls[k][tid] * sb;
       Mr = M;
     }
+    dst[(size_t)tid * (HD + 2) + HD] = Mr;
+    dst[(size_t)tid * (HD + 2) + HD + 1] = Lr;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+    const int j = idx / HD, d = idx % HD;
+    float Or = 0.f;
+    for (int k = 0; k < nc; ++k) Or = Or * sca[k][j] + os[k][j][d] * scb[k][j];
     dst[(size_t)j * (HD + 2) + d] = Or;
-    if (d == 0) {
-      dst[(size_t)j * (HD + 2) + HD] = Mr;
-      dst[(size_t)j * (HD + 2) + HD + 1] = Lr;
-    }
   }
 }
 

@@ -168,7 +168,7 @@ __device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, con
             const size_t idx = (size_t)col * a.N + n;
             const float xn = a.out[idx] + acc[r][c][i];
             a.out[idx] = xn;
-            ss += xn * xn;
+            ss = __builtin_fmaf(xn, xn, ss);  // the same operation in k_fold_norm
           }
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
@@ -697,6 +697,69 @@ __global__ __launch_bounds__(64) void k_fold(GemmArgs a) {
   epilogue<WT, EPI, R, 1>(a, rb, ct, lane, acc);
 }
 
+// Split mode's second half for a residual projection followed by RMSNorm, one
+// workgroup per lane: x += ((P_0 + P_1) + ...) + P_{S-1}, then the next
+// norm's xn = (x * r) * g.  Every value is the one the separate kernels give:
+// thread t owns row blocks t, t + 256 (16 rows each); a block's sum of squares
+// is taken as the residual epilogue takes it (rows 4j..4j+3 in order with
+// fused multiply-adds, then (s0 + s1) + (s2 + s3)), the lane's statistic as
+// the norm kernel takes it (the row blocks strided over 256 threads, then
+// block_sum), and r = 1 / sqrt(ss / N + eps).
+template <int WT>
+__global__ __launch_bounds__(256) void k_fold_norm(GemmArgs a) {
+  constexpr int MAXRB = 2;  // row blocks per thread: N up to 8192
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t sstride = (size_t)a.B * a.nRB * TILE;
+  float xv[MAXRB][TILE];
+  float part = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXRB; ++k) {
+    const int rb = t + 256 * k;
+    if (rb >= a.nRB) break;
+    const float* src = a.part + ((size_t)b * a.nRB + rb) * TILE;
+    f32x4 pv[GEMM_MAX_SPLIT][4];
+#pragma unroll
+    for (int s2 = 0; s2 < GEMM_MAX_SPLIT; ++s2)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pv[s2][q] = *(const f32x4*)(src + min(s2, a.S - 1) * sstride + 4 * q);
+    float* xr = a.out + (size_t)b * a.N + rb * TILE;
+    float sg[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v = pv[0][q];
+#pragma unroll
+      for (int s2 = 1; s2 < GEMM_MAX_SPLIT; ++s2)
+        if (s2 < a.S) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = v[i] + pv[s2][q][i];
+        }
+      const f32x4 xo = *(const f32x4*)(xr + 4 * q);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = xo[i] + v[i];
+        xv[k][4 * q + i] = x;
+        ss = __builtin_fmaf(x, x, ss);
+      }
+      *(f32x4*)(xr + 4 * q) = f32x4{xv[k][4 * q], xv[k][4 * q + 1], xv[k][4 * q + 2], xv[k][4 * q + 3]};
+      sg[q] = ss;
+    }
+    part += (sg[0] + sg[1]) + (sg[2] + sg[3]);
+  }
+  const float ss = block_sum(part);
+  const float r = 1.0f / sqrtf(ss / (float)a.N + a.norm_eps);
+#pragma unroll
+  for (int k = 0; k < MAXRB; ++k) {
+    const int rb = t + 256 * k;
+    if (rb >= a.nRB) break;
+#pragma unroll
+    for (int i = 0; i < TILE; ++i) {
+      const int n = rb * TILE + i;
+      store_act<WT>(a.norm_out, (size_t)b * a.N + n, (xv[k][i] * r) * a.norm_g[n]);
+    }
+  }
+}
+
 template <int WT, int EPI>
 static hipError_t launch_c(int C, const GemmArgs& a, int blocks, hipStream_t st) {
   const dim3 blk(64 * a.S);
@@ -749,8 +812,13 @@ static hipError_t launch_panel_c(int split, const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, true>), dim3(blocks), dim3(PW * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nct = (a.B + TILE - 1) / TILE;
-    hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
+    if (EPI == EPI_RESID && a.norm_out) {
+      if (!fold_norm_supported(a.N)) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_fold_norm<WT>), dim3(a.B), dim3(256), 0, st, a);
+    } else {
+      const int nct = (a.B + TILE - 1) / TILE;
+      hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
+    }
   } else {
     hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
   }

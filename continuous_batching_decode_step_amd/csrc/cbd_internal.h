@@ -53,6 +53,12 @@ struct GemmArgs {
   int red_waves;        // split partials per LDS round (set by the launcher)
   float* ssq_out;       // EPI_RESID: [nRB][B] this tile's sum of x^2 per lane
   float* part;          // panel split mode: [S][B][nRB][rows per row block] split partials
+  // EPI_RESID in panel split mode only: if norm_out is set, the fold also runs
+  // the next RMSNorm, xn = (x * r) * g into norm_out (activation format), and
+  // writes no sums of squares.
+  const float* norm_g;
+  float norm_eps;
+  void* norm_out;
 };
 
 struct AttnArgs {
@@ -76,6 +82,20 @@ struct AttnArgs {
   void* out;              // [B, Hq*hd] in the activation format
 };
 
+// Block sum of per-thread partials (256 threads): a fixed shuffle tree, then
+// the four waves in order.  The one reduction every RMSNorm statistic goes
+// through, whichever kernel computes it.
+__device__ inline float block_sum(float ss) {
+  __shared__ float red[4];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float t = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return t;
+}
+
 // ---- launchers (return hipError_t of the launch) -------------------------------
 hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
 // Wide-panel projection (activation panel staged in LDS, 16*C lanes per
@@ -84,6 +104,9 @@ hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st
 // a.part and adds them in order in a second kernel.
 // Same output bits as launch_gemm.
 hipError_t launch_panel(int wt, int epi, int C, int rm, int split, const GemmArgs& a, hipStream_t st);
+// Whether a split-mode EPI_RESID panel can fold and normalise in one kernel
+// (a.norm_out set): N up to 8192, a multiple of 16.
+__host__ __device__ constexpr bool fold_norm_supported(int N) { return N % 16 == 0 && N <= 8192; }
 // workgroups of one panel launch (for sizing decisions)
 int panel_workgroups(const GemmArgs& a, int C, int rm, int split);
 // Whether the MFMA attention kernel serves this shape (bf16 KV; head_dim 64

@@ -5,19 +5,6 @@
 
 namespace cbd {
 
-// Block sum of per-thread partials (256 threads): a fixed shuffle tree, then
-// the four waves in order.
-__device__ inline float block_sum(float ss) {
-  __shared__ float red[4];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float t = ((red[0] + red[1]) + red[2]) + red[3];
-  __syncthreads();
-  return t;
-}
-
 // x[b] = E[token_b] (exact upcast of bf16, q * scale of Q8_0), the sum of
 // x[b]^2 for the first RMSNorm (the projections that consume x normalise it),
 // and the rotary (cos, sin) of the lane's position for every pair:

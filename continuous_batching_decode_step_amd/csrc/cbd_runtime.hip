@@ -527,8 +527,12 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
   }
 }
 
+// norm_g: for a residual projection, the gain of the RMSNorm that follows; if
+// the projection runs as a split-mode panel its fold also normalises x into
+// xn, and *normed says so (the caller then launches no norm).
 static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
-                    void* act_out, char* ws, const WsLayout& L, hipStream_t st) {
+                    void* act_out, char* ws, const WsLayout& L, hipStream_t st, const float* norm_g = nullptr,
+                    bool* normed = nullptr) {
   GemmArgs g{};
   g.W = W.data;
   g.Ws = (const uint16_t*)W.scale;
@@ -550,6 +554,12 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   if (panel) {
     int C, rm, split;
     panel_shape(B, p, epi, &C, &rm, &split);
+    if (epi == EPI_RESID && split && norm_g && normed && fold_norm_supported(p.N)) {
+      g.norm_g = norm_g;
+      g.norm_eps = m->c.rms_eps;
+      g.norm_out = ws + L.xn;
+      *normed = true;
+    }
     HIP_TRY(launch_panel(m->wt, epi, C, rm, split, g, st));
   } else {
     const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
@@ -625,11 +635,16 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
       ProfScope ps(m, P_COMB, st);
       HIP_TRY(launch_attn_combine(c.head_dim, m->wt, at, st));
     }
-    if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st))) return rc;
-    if ((rc = norm(m->ffn_norm[l], m->p_o.nRB))) return rc;
+    bool normed = false;
+    if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st, m->ffn_norm[l], &normed)))
+      return rc;
+    if (!normed && (rc = norm(m->ffn_norm[l], m->p_o.nRB))) return rc;
     if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
-    if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st))) return rc;
-    if ((rc = norm(l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm, m->p_down.nRB))) return rc;
+    const float* gnext = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
+    normed = false;
+    if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st, gnext, &normed)))
+      return rc;
+    if (!normed && (rc = norm(gnext, m->p_down.nRB))) return rc;
   }
   if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
   if (argmax) {

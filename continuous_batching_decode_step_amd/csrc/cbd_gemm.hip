@@ -433,8 +433,11 @@ __device__ inline unsigned buf_ld2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsi
   return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
+// At most 256 registers per lane (two waves per SIMD): the 128-lane full-mode
+// panels otherwise take 294 with their accumulators in AGPRs, one wave per
+// SIMD, and wait on memory with nothing to switch to.
 template <int WT, int EPI, int C, int RM, bool SPLIT>
-__global__ __launch_bounds__(PW * 64) void k_panel(GemmArgs a) {
+__global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_panel(GemmArgs a) {
   using PS = PanelShape<WT, C>;
   constexpr int R0 = gemm_rows(EPI);  // row tiles of one row block
   constexpr int R = R0 * RM;          // row tiles of one wave: RM consecutive row blocks
@@ -820,15 +823,19 @@ static hipError_t launch_panel_c(int split, const GemmArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
     }
   } else {
-    hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
+    // full mode with one row block per wave only (two would not fit in 256
+    // registers with the running total)
+    if constexpr (RM == 1)
+      hipLaunchKernelGGL((k_panel<WT, EPI, C, RM, false>), dim3(blocks), dim3(PW * 64), lds, st, a);
+    else
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int WT, int EPI>
 static hipError_t launch_panel_epi(int C, int rm, int split, const GemmArgs& a, hipStream_t st) {
-  // Row blocks per wave: RM x gemm_rows(EPI) row tiles of 16, at most 4.
-  constexpr int R0 = gemm_rows(EPI);
+  // Row blocks per wave: 1, or 2 in split mode.
   if (rm == 1) {
     switch (C) {
       case 2: return launch_panel_c<WT, EPI, 2, 1>(split, a, st);
@@ -842,15 +849,6 @@ static hipError_t launch_panel_epi(int C, int rm, int split, const GemmArgs& a, 
       case 4: return launch_panel_c<WT, EPI, 4, 2>(split, a, st);
       case 8: return launch_panel_c<WT, EPI, 8, 2>(split, a, st);
       default: return hipErrorInvalidValue;
-    }
-  }
-  if constexpr (R0 == 1) {
-    if (rm == 4) {
-      switch (C) {
-        case 4: return launch_panel_c<WT, EPI, 4, 4>(split, a, st);
-        case 8: return launch_panel_c<WT, EPI, 8, 4>(split, a, st);
-        default: return hipErrorInvalidValue;
-      }
     }
   }
   return hipErrorInvalidValue;

@@ -99,9 +99,9 @@ __device__ inline float block_sum(float ss) {
 // ---- launchers (return hipError_t of the launch) -------------------------------
 hipError_t launch_gemm(int wt, int epi, int C, const GemmArgs& a, hipStream_t st);
 // Wide-panel projection (activation panel staged in LDS, 16*C lanes per
-// workgroup, C in {2, 4, 8}; rm row blocks per wave, rm in {1, 2} and 4 for
-// one-tile blocks, with C >= 4 when rm > 1); split = 1 writes split partials to
-// a.part and adds them in order in a second kernel.
+// workgroup, C in {2, 4, 8}; rm row blocks per wave, 1, or 2 in split mode
+// with C >= 4); split = 1 writes split partials to a.part and adds them in
+// order in a second kernel.
 // Same output bits as launch_gemm.
 hipError_t launch_panel(int wt, int epi, int C, int rm, int split, const GemmArgs& a, hipStream_t st);
 // Whether a split-mode EPI_RESID panel can fold and normalise in one kernel

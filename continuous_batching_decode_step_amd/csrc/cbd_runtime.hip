@@ -502,7 +502,7 @@ static int panel_min_b(int epi, int K) {
 // need the split); a split with a long reduction (down) gives each wave two
 // row blocks (10% faster at 64 lanes). Above 64 lanes: two-tile row blocks
 // (gate|up, the head) run 128-lane panels in full mode; short one-tile
-// projections (QKV, O) run 64-lane panels in full mode once those give 1536
+// projections (QKV, O) run 64-lane panels in full mode once those give 1024
 // waves, else 128-lane panels split with two row blocks per wave, as does the
 // long reduction (down). Neither width, row blocks per wave nor mode changes
 // any output's reduction order.
@@ -517,7 +517,7 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
   } else if (!one_tile) {
     *C = 8;
     *split = 0;
-  } else if (p.K <= 4096 && units(4) >= 1536) {
+  } else if (p.K <= 4096 && units(4) >= 1024) {
     *C = 4;
     *split = 0;
   } else {

@@ -479,17 +479,47 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __attribute__((aligned(16))) uint16_t qs[2 * G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
   __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
+  const int clast = c0 + nc - 1;
+  const bool holds_p = p >= clast * ATTN_SPLIT;  // the group's last chunk holds slot p
+  // When the QKV projection ran in split mode without its fold, the workgroup
+  // adds the split partials of the values it needs itself, in split order, as
+  // the fold would: P_s of lane b at [(s * B + b) * Nqkv + n].  The sums (the
+  // group's queries, and the new key and value if it holds slot p) go to LDS.
+  __shared__ float qsum[(G + 2) * HD];
+  const float* qv = row;   // the group's head vectors: q of head g*G + j at qv + j*HD ...
+  const float* kn = row + (size_t)(a.Hq + g) * HD;
+  const float* vn = row + (size_t)(a.Hq + a.Hkv + g) * HD;
+  if (a.qkv_S > 0) {
+    const int nsum = (holds_p ? G + 2 : G) * HD;
+    const size_t sstride = (size_t)a.B * a.Nqkv;
+    const float* P = a.qkv_part + (size_t)b * a.Nqkv;
+    for (int idx = tid; idx < nsum; idx += 64 * MF_WAVES) {
+      const int hv = idx / HD, d = idx % HD;
+      const int n = (hv < G ? (g * G + hv) : hv == G ? a.Hq + g : a.Hq + a.Hkv + g) * HD + d;
+      float pv[GEMM_MAX_SPLIT];
+#pragma unroll
+      for (int s2 = 0; s2 < GEMM_MAX_SPLIT; ++s2) pv[s2] = P[min(s2, a.qkv_S - 1) * sstride + n];
+      float v = pv[0];
+#pragma unroll
+      for (int s2 = 1; s2 < GEMM_MAX_SPLIT; ++s2)
+        if (s2 < a.qkv_S) v = v + pv[s2];
+      qsum[idx] = v;
+    }
+    __syncthreads();
+    qv = qsum;
+    kn = qsum + G * HD;
+    vn = qsum + (G + 1) * HD;
+  } else {
+    qv = row + (size_t)g * G * HD;
+  }
   for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
     const int j = idx / HD, d = idx % HD;
-    const float q = rot(row + (size_t)(g * G + j) * HD, d);
+    const float q = rot(qv + (size_t)j * HD, d);
     const uint16_t hi = f2bf_a(q);
     qs[j][d] = hi;
     qs[G + j][d] = f2bf_a(q - bf2f(hi));
   }
-  const int clast = c0 + nc - 1;
-  if (p >= clast * ATTN_SPLIT) {  // the group's last chunk holds slot p
-    const float* kn = row + (size_t)(a.Hq + g) * HD;
-    const float* vn = row + (size_t)(a.Hq + a.Hkv + g) * HD;
+  if (holds_p) {
     for (int d = tid; d < HD; d += 64 * MF_WAVES) {
       const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;

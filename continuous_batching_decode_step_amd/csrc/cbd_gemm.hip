@@ -818,6 +818,8 @@ static hipError_t launch_panel_c(int split, const GemmArgs& a, hipStream_t st) {
     if (EPI == EPI_RESID && a.norm_out) {
       if (!fold_norm_supported(a.N)) return hipErrorInvalidValue;
       hipLaunchKernelGGL((k_fold_norm<WT>), dim3(a.B), dim3(256), 0, st, a);
+    } else if (EPI == EPI_STORE && a.fold_elsewhere) {
+      // the consumer (attention) adds the partials
     } else {
       const int nct = (a.B + TILE - 1) / TILE;
       hipLaunchKernelGGL((k_fold<WT, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);

@@ -53,6 +53,7 @@ struct GemmArgs {
   int red_waves;        // split partials per LDS round (set by the launcher)
   float* ssq_out;       // EPI_RESID: [nRB][B] this tile's sum of x^2 per lane
   float* part;          // panel split mode: [S][B][nRB][rows per row block] split partials
+  int fold_elsewhere;   // EPI_STORE split mode: leave the partials unfolded (the consumer adds them)
   // EPI_RESID in panel split mode only: if norm_out is set, the fold also runs
   // the next RMSNorm, xn = (x * r) * g into norm_out (activation format), and
   // writes no sums of squares.
@@ -78,6 +79,11 @@ struct AttnArgs {
   int per;                // chunks per partial: ATTN_GROUP (matrix-core kernel) or 1
   int Hq, Hkv, G, Nqkv;
   const float2* rope;     // [B][hd/2] (cos, sin) of each lane's position
+  // Matrix-core kernel only: if qkv_S > 0 the QKV projection left its split
+  // partials [qkv_S][B][Nqkv] unfolded in qkv_part, and attention adds them
+  // (in split order) instead of reading qkv.
+  const float* qkv_part;
+  int qkv_S;
   float* part;            // [B][max_splits][Hkv][G][hd + 2] partials (o, m, l) per chunk or group
   void* out;              // [B, Hq*hd] in the activation format
 };

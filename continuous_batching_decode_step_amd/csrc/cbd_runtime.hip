@@ -529,10 +529,12 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
 
 // norm_g: for a residual projection, the gain of the RMSNorm that follows; if
 // the projection runs as a split-mode panel its fold also normalises x into
-// xn, and *normed says so (the caller then launches no norm).
+// xn, and *normed says so (the caller then launches no norm).  unfolded: for
+// QKV, the consumer can add split partials itself; if the projection runs as
+// a split-mode panel its fold is skipped and *unfolded says so.
 static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
                     void* act_out, char* ws, const WsLayout& L, hipStream_t st, const float* norm_g = nullptr,
-                    bool* normed = nullptr) {
+                    bool* normed = nullptr, bool* unfolded = nullptr) {
   GemmArgs g{};
   g.W = W.data;
   g.Ws = (const uint16_t*)W.scale;
@@ -559,6 +561,10 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
       g.norm_eps = m->c.rms_eps;
       g.norm_out = ws + L.xn;
       *normed = true;
+    }
+    if (epi == EPI_STORE && split && unfolded) {
+      g.fold_elsewhere = 1;
+      *unfolded = true;
     }
     HIP_TRY(launch_panel(m->wt, epi, C, rm, split, g, st));
   } else {
@@ -625,7 +631,13 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   };
   if ((rc = norm(m->attn_norm[0], 1))) return rc;
   for (int l = 0; l < c.n_layers; ++l) {
-    if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st))) return rc;
+    // the matrix-core attention kernel adds the QKV split partials itself
+    bool unfolded = false;
+    if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st, nullptr, nullptr,
+                       attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G) ? &unfolded : nullptr)))
+      return rc;
+    at.qkv_part = unfolded ? (const float*)(ws + L.gpart) : nullptr;
+    at.qkv_S = unfolded ? m->p_qkv.S : 0;
     at.layer_off = (long long)l * c.n_kv_heads * a->slab * c.head_dim;
     {
       ProfScope ps(m, P_ATTN, st);

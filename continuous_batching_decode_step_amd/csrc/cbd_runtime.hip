@@ -631,10 +631,14 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   };
   if ((rc = norm(m->attn_norm[0], 1))) return rc;
   for (int l = 0; l < c.n_layers; ++l) {
-    // the matrix-core attention kernel adds the QKV split partials itself
+    // Up to 8 lanes the matrix-core attention kernel adds the QKV split partials
+    // itself (no fold launch); wider, each lane's partials would be re-read by
+    // all its attention workgroups from beyond L2 (at 64 lanes +36 MB per
+    // launch, more than the fold kernel costs).
     bool unfolded = false;
+    const bool attn_folds = B <= 8 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
     if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st, nullptr, nullptr,
-                       attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G) ? &unfolded : nullptr)))
+                       attn_folds ? &unfolded : nullptr)))
       return rc;
     at.qkv_part = unfolded ? (const float*)(ws + L.gpart) : nullptr;
     at.qkv_S = unfolded ? m->p_qkv.S : 0;

@@ -30,7 +30,8 @@ SYMBOLS = [
     "cbd_lane_length", "cbd_arena_used_bytes", "cbd_arena_live_lanes", "cbd_workspace_bytes",
     "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
     "cbd_lane_truncate", "cbd_profile_enable", "cbd_profile_reset", "cbd_profile_read", "cbd_profile_classes",
-    "cbd_profile_class_name", "cbd_set_graph_replay",
+    "cbd_profile_class_name", "cbd_set_graph_replay", "cbd_arena_block_bytes", "cbd_arena_n_blocks",
+    "cbd_arena_free_blocks",
 ]
 
 
@@ -79,6 +80,10 @@ def lib():
         L.cbd_model_destroy.restype = None
         L.cbd_arena_bytes.argtypes = [ctypes.POINTER(Config), i32, i32]
         L.cbd_arena_bytes.restype = sz
+        L.cbd_arena_block_bytes.argtypes = [ctypes.POINTER(Config)]
+        L.cbd_arena_block_bytes.restype = sz
+        L.cbd_arena_n_blocks.argtypes = [vp]
+        L.cbd_arena_free_blocks.argtypes = [vp]
         L.cbd_arena_create.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(vp)]
         L.cbd_arena_destroy.argtypes = [vp]
         L.cbd_arena_destroy.restype = None
@@ -282,8 +287,15 @@ class Model:
 
 
 def arena_bytes(cfg, n_lanes: int, max_seq: int) -> int:
+    """Bytes for every one of n_lanes lanes to hold max_seq positions at once."""
     c = config_of(cfg)
     return lib().cbd_arena_bytes(ctypes.byref(c), n_lanes, max_seq)
+
+
+def arena_block_bytes(cfg) -> int:
+    """Bytes of one KV block (64 positions of one lane, every layer and KV head, K and V)."""
+    c = config_of(cfg)
+    return lib().cbd_arena_block_bytes(ctypes.byref(c))
 
 
 class Arena:
@@ -334,6 +346,14 @@ class Arena:
     @property
     def live_lanes(self) -> int:
         return lib().cbd_arena_live_lanes(self.h)
+
+    @property
+    def n_blocks(self) -> int:
+        return lib().cbd_arena_n_blocks(self.h)
+
+    @property
+    def free_blocks(self) -> int:
+        return lib().cbd_arena_free_blocks(self.h)
 
     def kv_export(self, lane: int, k_dst, v_dst, stream=None):
         _check(lib().cbd_lane_kv_export(self.h, lane, _ptr(k_dst), _ptr(v_dst), _stream(stream)))

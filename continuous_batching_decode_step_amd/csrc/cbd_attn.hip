@@ -117,7 +117,8 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int4 it4 = *(const int4*)(a.items + 4 * item);
+  const int4 it4 = *(const int4*)(a.items + ITEM_INTS * item);
+  const int blk = a.items[ITEM_INTS * item + 4];  // the chunk's block
   const int b = it4.x & 0xffffff;
   const int s = it4.y;  // one chunk per item for this kernel
   const int p = a.pos[b];
@@ -125,7 +126,9 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   const int kbeg = s * ATTN_SPLIT;  // first key of the chunk
   const int kend = min(kbeg + ATTN_SPLIT, nk);
 
-  const long long base = (long long)it4.w * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  // key t of the chunk sits at base + t * HD (base is the chunk's block, minus kbeg keys)
+  const long long base = (long long)blk * a.block_elems + a.layer_off + (long long)g * ATTN_SPLIT * HD -
+                         (long long)kbeg * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
   const int d0 = c * D;  // first dim of this lane
@@ -425,25 +428,33 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int4 it4 = *(const int4*)(a.items + 4 * item);
+  const int4 it4 = *(const int4*)(a.items + ITEM_INTS * item);
+  const int4 bl4 = *(const int4*)(a.items + ITEM_INTS * item + 4);  // blocks of the group's chunks
   const int b = it4.x & 0xffffff, nc = it4.x >> 24, c0 = it4.y, p = it4.z;
   const int nk = p + 1;
   const int c = c0 + w;  // this wave's chunk
   const bool active = w < nc;
-  const long long base = (long long)it4.w * a.lane_stride + a.layer_off + (long long)g * a.max_seq * HD;
+  // (layer, head) offset inside a block; base: this wave's chunk (inactive
+  // waves: the last chunk's, never read); lbase: the group's last chunk,
+  // which holds slot p when the group is the lane's last
+  const long long hoff = a.layer_off + (long long)g * ATTN_SPLIT * HD;
+  const int myblk = w == 0 ? bl4.x : w == 1 ? bl4.y : w == 2 ? bl4.z : bl4.w;
+  const int lastblk = nc == 1 ? bl4.x : nc == 2 ? bl4.y : nc == 3 ? bl4.z : bl4.w;
+  const long long base = (long long)(active ? myblk : lastblk) * a.block_elems + hoff;
+  const long long lbase = (long long)lastblk * a.block_elems + hoff - (long long)(c0 + nc - 1) * ATTN_SPLIT * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
   const uint16_t* kslab = (const uint16_t*)a.kslab;
   const uint16_t* vslab = (const uint16_t*)a.vslab;
 
-  // Whole chunks are read: a slab holds a whole number of chunks, and the
-  // slots past p (old or never written) are masked or zeroed after the load.
-  // A wave without a chunk loads at an offset past the slab: zeros, no access.
-  const unsigned slab_bytes = (unsigned)a.max_seq * HD * 2;
-  const __amdgpu_buffer_rsrc_t krs = slab_rsrc(kslab + base, slab_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(vslab + base, slab_bytes);
-  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 + (unsigned)c * ATTN_SPLIT * HD * 2 : SLAB_OFF;
-  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 + (unsigned)c * ATTN_SPLIT * HD * 2 : SLAB_OFF;
+  // Whole chunks are read (a block holds whole chunks), and the slots past p
+  // (old or never written) are masked or zeroed after the load.  A wave
+  // without a chunk loads at an offset past its chunk's buffer: zeros, no access.
+  const unsigned chunk_bytes = (unsigned)ATTN_SPLIT * HD * 2;
+  const __amdgpu_buffer_rsrc_t krs = slab_rsrc(kslab + base, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(vslab + base, chunk_bytes);
+  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 : SLAB_OFF;
+  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : SLAB_OFF;
   u32x4 kr[4][KK];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
   __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
   const int clast = c0 + nc - 1;
-  const bool holds_p = p >= clast * ATTN_SPLIT;  // the group's last chunk holds slot p
+  const bool holds_p = p / ATTN_SPLIT == clast;  // the group's last chunk holds slot p (the lane's last group)
   // When the QKV projection ran in split mode without its fold, the workgroup
   // adds the split partials of the values it needs itself, in split order, as
   // the fold would: P_s of lane b at [(s * B + b) * Nqkv + n].  The sums (the
@@ -524,8 +535,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;
       kvn[1][d] = vw;
-      ((uint16_t*)a.kslab)[base + (long long)p * HD + d] = kw;
-      ((uint16_t*)a.vslab)[base + (long long)p * HD + d] = vw;
+      ((uint16_t*)a.kslab)[lbase + (long long)p * HD + d] = kw;
+      ((uint16_t*)a.vslab)[lbase + (long long)p * HD + d] = vw;
     }
   }
   __syncthreads();

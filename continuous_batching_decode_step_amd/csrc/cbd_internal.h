@@ -17,6 +17,9 @@ constexpr int ATTN_SPLIT = 64;
 // a lane's chunks, merged in chunk order inside the wave into one partial.  A
 // constant of the design, like ATTN_SPLIT.
 constexpr int ATTN_GROUP = 4;
+// ints per attention work item: lane index | chunk count << 24, first chunk,
+// position, padding, then the arena block of each of up to ATTN_GROUP chunks.
+constexpr int ITEM_INTS = 8;
 // Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
 // epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
 // rows; the others take one tile so that d-row projections fill the chip).
@@ -64,15 +67,18 @@ struct GemmArgs {
 
 struct AttnArgs {
   const float* qkv;       // [B, Nqkv] f32, before rotation
-  void* kslab;            // arena K region
-  void* vslab;            // arena V region
-  long long lane_stride;  // elements per lane per region: L * Hkv * max_seq * hd
-  long long layer_off;    // l * Hkv * max_seq * hd
-  int max_seq;            // positions per (lane, layer, KV head) slab (a multiple of ATTN_SPLIT)
+  void* kslab;            // arena K block pool
+  void* vslab;            // arena V block pool
+  // A block holds ATTN_SPLIT positions of one lane for every layer and KV
+  // head; the pools are layer-major, [L][n_blocks][Hkv][ATTN_SPLIT][hd]:
+  // chunk c of a lane is the block the work item names for it, and (layer l,
+  // head g) of block j sits at j * block_elems + layer_off + g * ATTN_SPLIT * hd.
+  long long block_elems;  // Hkv * ATTN_SPLIT * hd
+  long long layer_off;    // l * n_blocks * block_elems
   int B;
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
-  const int* items;       // [n_items][4] {b | chunks << 24, first chunk, position, arena lane}, 16-byte aligned
+  const int* items;       // [n_items][ITEM_INTS] {b | chunks << 24, first chunk, position, 0, block of each chunk (up to 4)}, 16-byte aligned
   const int* n_items_dev; // number of items of this step (device)
   int max_items;          // grid size: the most items a step of B lanes can have
   int max_splits;         // partials per lane the partial buffer is sized for

@@ -113,16 +113,27 @@ struct cbd_model {
   long long prof_n[16] = {};
 };
 
+// A pool of KV blocks over caller-owned memory: a block holds ATTN_SPLIT
+// positions (one attention chunk) of one lane for every layer and KV head.
+// The pool is layer-major, K [L][n_blocks][Hkv][ATTN_SPLIT][hd] then V alike:
+// one layer's blocks are contiguous, which loads 13% faster in attention than
+// a pool of whole blocks [n_blocks][L][...] (5.95 vs 5.26 TB/s for the same
+// chunks, whatever the blocks' placement).  A lane
+// holds the blocks of its chunks in order (any blocks of the pool); a step
+// takes a free block when a lane's new slot opens a chunk, and clear, evict
+// and truncate return blocks to the pool.
 struct cbd_arena {
   cbd_model* m;
   int n_lanes, max_seq;
-  int slab;  // positions per (lane, layer, KV head) slab: max_seq rounded up to a whole attention chunk
   char* base;
   size_t bytes;
-  long long lane_stride;  // elements per lane in each of the K and V regions
-  size_t region_bytes;
+  int n_blocks;
+  long long block_elems;  // elements of one block of one layer: Hkv * ATTN_SPLIT * hd
+  size_t region_bytes;    // bytes of the K pool (the V pool follows)
   std::vector<uint8_t> live;
   std::vector<int> len;
+  std::vector<std::vector<int>> blocks;  // per lane, the block of each chunk
+  std::vector<int> free_blocks;          // a stack; the lowest block on top
 };
 
 namespace {
@@ -155,7 +166,7 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
     off += align256(bytes);
     return o;
   };
-  L.meta = take(4 * (meta_header(maxB) + (size_t)4 * maxB * L.MS));
+  L.meta = take(4 * (meta_header(maxB) + (size_t)ITEM_INTS * maxB * L.MS));
   L.x = take(4 * (size_t)maxB * c.d_model);
   L.xn = take((size_t)m->actb * maxB * c.d_model);
   const int ssq_rows = std::max(std::max(m->p_o.nRB, m->p_down.nRB), 1);
@@ -334,6 +345,12 @@ void cbd_model_destroy(cbd_model* m) {
   delete m;
 }
 
+size_t cbd_arena_block_bytes(const cbd_config* cfg) {
+  if (!cfg || cfg->n_layers <= 0 || cfg->n_kv_heads <= 0 || cfg->head_dim <= 0) return 0;
+  const size_t kvb = cfg->wtype == CBD_BF16 ? 2 : 4;
+  return 2 * (size_t)cfg->n_layers * cfg->n_kv_heads * ATTN_SPLIT * cfg->head_dim * kvb;
+}
+
 size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq) {
   if (!cfg || n_lanes <= 0 || max_seq <= 0 || cfg->n_layers <= 0 || cfg->n_kv_heads <= 0 || cfg->head_dim <= 0)
     return 0;
@@ -346,19 +363,24 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   if (!m || !out || !dev_mem) return fail(CBD_E_ARG, "null argument");
   if (n_lanes <= 0 || max_seq <= 0) return fail(CBD_E_ARG, "n_lanes and max_seq must be positive");
   if ((uintptr_t)dev_mem & 255u) return fail(CBD_E_ARG, "arena memory must be 256-byte aligned");
-  const size_t need = cbd_arena_bytes(&m->c, n_lanes, max_seq);
-  if (dev_bytes < need) return fail(CBD_E_ARG, "arena needs %zu bytes, got %zu", need, dev_bytes);
+  const size_t bb = cbd_arena_block_bytes(&m->c);
+  if (dev_bytes < bb) return fail(CBD_E_ARG, "arena needs at least one block of %zu bytes, got %zu", bb, dev_bytes);
+  const size_t nb = dev_bytes / bb;
+  if (nb > (size_t)INT32_MAX) return fail(CBD_E_ARG, "arena of %zu blocks is too large", nb);
   cbd_arena* a = new cbd_arena();
   a->m = m;
   a->n_lanes = n_lanes;
   a->max_seq = max_seq;
-  a->slab = (max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * ATTN_SPLIT;
   a->base = (char*)dev_mem;
   a->bytes = dev_bytes;
-  a->lane_stride = (long long)m->c.n_layers * m->c.n_kv_heads * a->slab * m->c.head_dim;
-  a->region_bytes = need / 2;
+  a->n_blocks = (int)nb;
+  a->block_elems = (long long)m->c.n_kv_heads * ATTN_SPLIT * m->c.head_dim;
+  a->region_bytes = nb * (bb / 2);
   a->live.assign(n_lanes, 0);
   a->len.assign(n_lanes, 0);
+  a->blocks.assign(n_lanes, std::vector<int>());
+  a->free_blocks.resize(nb);
+  for (size_t i = 0; i < nb; ++i) a->free_blocks[i] = (int)(nb - 1 - i);
   *out = a;
   return CBD_OK;
 }
@@ -384,20 +406,34 @@ static int check_lane(const cbd_arena* a, int lane) {
   return CBD_OK;
 }
 
+// Keep the blocks of a lane's first `length` positions, return the rest.
+static void lane_keep(cbd_arena* a, int lane, int length) {
+  std::vector<int>& bl = a->blocks[lane];
+  const size_t keep = ((size_t)length + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  while (bl.size() > keep) {
+    a->free_blocks.push_back(bl.back());
+    bl.pop_back();
+  }
+  a->len[lane] = length;
+}
+
 int cbd_lane_clear(cbd_arena* a, int lane) {
   int rc = check_lane(a, lane);
   if (rc) return rc;
-  a->len[lane] = 0;
+  lane_keep(a, lane, 0);
   return CBD_OK;
 }
 
 int cbd_lane_evict(cbd_arena* a, int lane) {
   int rc = check_lane(a, lane);
   if (rc) return rc;
+  lane_keep(a, lane, 0);
   a->live[lane] = 0;
-  a->len[lane] = 0;
   return CBD_OK;
 }
+
+int cbd_arena_free_blocks(const cbd_arena* a) { return a ? (int)a->free_blocks.size() : -1; }
+int cbd_arena_n_blocks(const cbd_arena* a) { return a ? a->n_blocks : -1; }
 
 int cbd_lane_length(const cbd_arena* a, int lane) {
   int rc = check_lane(a, lane);
@@ -432,7 +468,7 @@ int cbd_lane_truncate(cbd_arena* a, int lane, int length) {
   if (rc) return rc;
   if (length < 0 || length > a->len[lane])
     return fail(CBD_E_ARG, "length %d outside [0, %d] for lane %d", length, a->len[lane], lane);
-  a->len[lane] = length;
+  lane_keep(a, lane, length);
   return CBD_OK;
 }
 
@@ -604,8 +640,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
   at.qkv = qkv;
   at.kslab = a->base;
   at.vslab = a->base + a->region_bytes;
-  at.lane_stride = a->lane_stride;
-  at.max_seq = a->slab;
+  at.block_elems = a->block_elems;
   at.B = B;
   at.lanes = d_lanes;
   at.pos = d_pos;
@@ -642,7 +677,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
       return rc;
     at.qkv_part = unfolded ? (const float*)(ws + L.gpart) : nullptr;
     at.qkv_S = unfolded ? m->p_qkv.S : 0;
-    at.layer_off = (long long)l * c.n_kv_heads * a->slab * c.head_dim;
+    at.layer_off = (long long)l * a->n_blocks * a->block_elems;
     {
       ProfScope ps(m, P_ATTN, st);
       HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
@@ -693,6 +728,13 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
     if (tokens[b] < 0 || tokens[b] >= c.vocab)
       return fail(CBD_E_TOKEN, "tokens[%d] = %d outside [0, %d)", b, tokens[b], c.vocab);
   }
+  // slot positions[b] opens a new chunk for lanes whose blocks end there
+  int new_blocks = 0;
+  for (int b = 0; b < B; ++b)
+    if ((size_t)positions[b] / ATTN_SPLIT >= a->blocks[lanes[b]].size()) ++new_blocks;
+  if (new_blocks > (int)a->free_blocks.size())
+    return fail(CBD_E_KV_FULL, "the step needs %d new KV blocks, %zu of %d are free", new_blocks,
+                a->free_blocks.size(), a->n_blocks);
   if (!workspace) return fail(CBD_E_WORKSPACE, "null workspace");
   if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
   const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
@@ -703,16 +745,24 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
 
+  // The step's new blocks (validated above: the pool has them).
+  for (int b = 0; b < B; ++b) {
+    std::vector<int>& bl = a->blocks[lanes[b]];
+    if ((size_t)positions[b] / ATTN_SPLIT >= bl.size()) {
+      bl.push_back(a->free_blocks.back());
+      a->free_blocks.pop_back();
+    }
+  }
   // Per-step metadata: lanes, positions, tokens, item count, attention work
-  // items {b | chunks << 24, first chunk, position, arena lane}: a workgroup of
-  // the attention kernel takes one aligned group of up to `per` consecutive
-  // 64-key chunks of one lane, the same groups whatever B is.
+  // items {b | chunks << 24, first chunk, position, 0, block of each chunk}: a
+  // workgroup of the attention kernel takes one aligned group of up to `per`
+  // consecutive 64-key chunks of one lane, the same groups whatever B is.
   std::vector<int32_t> meta;
   const size_t hdr = meta_header(B);
   long long chunks = 0;
   for (int b = 0; b < B; ++b) chunks += (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
   const int per = attn_chunks_per_item(m);
-  meta.reserve(hdr + 4 * (size_t)chunks);
+  meta.reserve(hdr + ITEM_INTS * (size_t)chunks);
   meta.insert(meta.end(), lanes, lanes + B);
   meta.insert(meta.end(), positions, positions + B);
   meta.insert(meta.end(), tokens, tokens + B);
@@ -720,11 +770,14 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   int n_items = 0;
   for (int b = 0; b < B; ++b) {
     const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
+    const std::vector<int>& bl = a->blocks[lanes[b]];
     for (int s0 = 0; s0 < ns; s0 += per) {
-      meta.push_back(b | (std::min(per, ns - s0) << 24));
+      const int n = std::min(per, ns - s0);
+      meta.push_back(b | (n << 24));
       meta.push_back(s0);
       meta.push_back(positions[b]);
-      meta.push_back(lanes[b]);
+      meta.push_back(0);
+      for (int k = 0; k < ATTN_GROUP; ++k) meta.push_back(k < n ? bl[s0 + k] : bl[s0 + n - 1]);
       ++n_items;
     }
   }
@@ -799,22 +852,40 @@ int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int
   return cbd_decode_step_batch(m, a, 1, &ln, position, &tok, logits, argmax, workspace, workspace_bytes, stream);
 }
 
+// Copy one block's K or V between the pool and rows [L][Hkv][len][hd] of a
+// lane (host or device), positions [64 j, 64 j + n) of each row: per layer,
+// the Hkv rows of the block are consecutive in the pool.
+static int copy_block(cbd_arena* a, int blk, int j, int n, int len, char* rows, bool to_pool, bool v, hipStream_t st) {
+  const cbd_config& c = a->m->c;
+  const size_t kvb = a->m->kvb;
+  const size_t width = (size_t)n * c.head_dim * kvb;
+  const size_t bpitch = (size_t)ATTN_SPLIT * c.head_dim * kvb;   // row stride inside a block
+  const size_t rpitch = (size_t)len * c.head_dim * kvb;          // row stride of the lane rows
+  const size_t lstride = (size_t)a->n_blocks * a->block_elems * kvb;  // one layer of the pool
+  char* pool = a->base + (v ? a->region_bytes : 0) + (size_t)blk * a->block_elems * kvb;
+  char* r0 = rows + (size_t)j * ATTN_SPLIT * c.head_dim * kvb;
+  for (int l = 0; l < c.n_layers; ++l) {
+    char* pl = pool + l * lstride;
+    char* rl = r0 + (size_t)l * c.n_kv_heads * rpitch;
+    if (to_pool)
+      HIP_TRY(hipMemcpy2DAsync(pl, bpitch, rl, rpitch, width, c.n_kv_heads, hipMemcpyDefault, st));
+    else
+      HIP_TRY(hipMemcpy2DAsync(rl, rpitch, pl, bpitch, width, c.n_kv_heads, hipMemcpyDefault, st));
+  }
+  return CBD_OK;
+}
+
 int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream) {
   int rc = check_lane(a, lane);
   if (rc) return rc;
   if (!k_dst || !v_dst) return fail(CBD_E_ARG, "null destination");
-  const cbd_config& c = a->m->c;
   const int len = a->len[lane];
   hipStream_t st = (hipStream_t)stream;
-  if (len > 0) {
-    const size_t kvb = a->m->kvb;
-    const size_t width = (size_t)len * c.head_dim * kvb;
-    const size_t spitch = (size_t)a->slab * c.head_dim * kvb;
-    const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
-    const size_t off = (size_t)lane * a->lane_stride * kvb;
-    HIP_TRY(hipMemcpy2DAsync(k_dst, width, a->base + off, spitch, width, rows, hipMemcpyDefault, st));
-    HIP_TRY(hipMemcpy2DAsync(v_dst, width, a->base + a->region_bytes + off, spitch, width, rows, hipMemcpyDefault,
-                             st));
+  for (int j = 0; j * ATTN_SPLIT < len; ++j) {
+    const int n = std::min(ATTN_SPLIT, len - j * ATTN_SPLIT);
+    const int blk = a->blocks[lane][j];
+    if ((rc = copy_block(a, blk, j, n, len, (char*)k_dst, false, false, st))) return rc;
+    if ((rc = copy_block(a, blk, j, n, len, (char*)v_dst, false, true, st))) return rc;
   }
   HIP_TRY(hipStreamSynchronize(st));
   return CBD_OK;
@@ -826,17 +897,22 @@ int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, co
   if (length < 0) return fail(CBD_E_ARG, "negative length");
   if (length > a->max_seq) return fail(CBD_E_KV_FULL, "length %d exceeds max_seq %d", length, a->max_seq);
   if (length > 0 && (!k_src || !v_src)) return fail(CBD_E_ARG, "null source");
-  const cbd_config& c = a->m->c;
+  const int need = (length + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  const int have = (int)a->blocks[lane].size();
+  if (need - have > (int)a->free_blocks.size())
+    return fail(CBD_E_KV_FULL, "importing %d positions needs %d more KV blocks, %zu are free", length, need - have,
+                a->free_blocks.size());
+  lane_keep(a, lane, std::min(a->len[lane], length));
+  while ((int)a->blocks[lane].size() < need) {
+    a->blocks[lane].push_back(a->free_blocks.back());
+    a->free_blocks.pop_back();
+  }
   hipStream_t st = (hipStream_t)stream;
-  if (length > 0) {
-    const size_t kvb = a->m->kvb;
-    const size_t width = (size_t)length * c.head_dim * kvb;
-    const size_t dpitch = (size_t)a->slab * c.head_dim * kvb;
-    const size_t rows = (size_t)c.n_layers * c.n_kv_heads;
-    const size_t off = (size_t)lane * a->lane_stride * kvb;
-    HIP_TRY(hipMemcpy2DAsync(a->base + off, dpitch, k_src, width, width, rows, hipMemcpyDefault, st));
-    HIP_TRY(hipMemcpy2DAsync(a->base + a->region_bytes + off, dpitch, v_src, width, width, rows, hipMemcpyDefault,
-                             st));
+  for (int j = 0; j < need; ++j) {
+    const int n = std::min(ATTN_SPLIT, length - j * ATTN_SPLIT);
+    const int blk = a->blocks[lane][j];
+    if ((rc = copy_block(a, blk, j, n, length, (char*)k_src, true, false, st))) return rc;
+    if ((rc = copy_block(a, blk, j, n, length, (char*)v_src, true, true, st))) return rc;
   }
   HIP_TRY(hipStreamSynchronize(st));
   a->len[lane] = length;

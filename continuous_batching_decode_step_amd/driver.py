@@ -17,21 +17,24 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import Arena, Model, arena_bytes
+from . import Arena, Model, arena_block_bytes, arena_bytes
 
 
 class Engine:
     """Model + arena + workspace + output buffers on one device and stream."""
 
     def __init__(self, cfg, dev_weights, n_lanes: int, max_seq: int, max_batch: Optional[int] = None,
-                 device: str = "cuda", stream=None):
+                 device: str = "cuda", stream=None, kv_blocks: Optional[int] = None):
+        """kv_blocks: size of the KV block pool (64 positions of one lane per
+        block); by default every lane can reach max_seq at once."""
         import torch
         self.torch = torch
         self.cfg = cfg
         self.device = device
         self.max_batch = max_batch or n_lanes
         self.model = Model(cfg, dev_weights)
-        nbytes = arena_bytes(cfg, n_lanes, max_seq)
+        nbytes = (arena_bytes(cfg, n_lanes, max_seq) if kv_blocks is None
+                  else int(kv_blocks) * arena_block_bytes(cfg))
         self.arena_mem = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.arena = Arena(self.model, n_lanes, max_seq, self.arena_mem)
         self.ws_bytes = self.model.workspace_bytes(self.max_batch, max_seq)

@@ -119,16 +119,26 @@ const char* cbd_last_error(void);
 int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** out);
 void cbd_model_destroy(cbd_model* m);
 
-/* Device bytes an arena of n_lanes lanes of max_seq positions needs:
- * K and V slabs [n_lanes][n_layers][n_kv_heads][slab][head_dim] each, in the
- * KV format of the model's wtype, where slab = max_seq rounded up to a
- * multiple of 64 (attention reads whole 64-position chunks).  Returns 0 for
- * invalid arguments. */
+/* The arena is a pool of KV blocks (paged KV): a block holds 64 positions (one
+ * attention chunk) of one lane for every layer and KV head.  The pool is
+ * layer-major: K [n_layers][n_blocks][n_kv_heads][64][head_dim], then V
+ * alike, in the KV format of the model's wtype, so that block j of every
+ * layer belongs to the same lane and one layer's blocks are contiguous.  A lane holds the blocks of its chunks, any
+ * blocks of the pool in any order; a step takes a free block when a lane's new
+ * slot opens a chunk (CBD_E_KV_FULL, changing nothing, if none is free), and
+ * clear, evict and truncate return blocks to the pool.  Bytes of one block
+ * (K and V), or 0 for an invalid config. */
+size_t cbd_arena_block_bytes(const cbd_config* cfg);
+
+/* Device bytes for every one of n_lanes lanes to reach max_seq positions at
+ * once: n_lanes * ceil(max_seq / 64) blocks.  A smaller pool serves lanes of
+ * mixed lengths (the blocks are shared).  Returns 0 for invalid arguments. */
 size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq);
 
-/* Create a lane arena over caller-owned device memory dev_mem of dev_bytes
- * (>= cbd_arena_bytes) bytes, 256-byte aligned.  All lanes start free.
- * Errors: CBD_E_ARG. */
+/* Create a lane arena of n_lanes lanes (each at most max_seq positions) over
+ * caller-owned device memory dev_mem of dev_bytes bytes, 256-byte aligned:
+ * floor(dev_bytes / cbd_arena_block_bytes) blocks, at least one.  All lanes
+ * start free and all blocks unused.  Errors: CBD_E_ARG. */
 int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes,
                      cbd_arena** out);
 void cbd_arena_destroy(cbd_arena* a);
@@ -147,6 +157,9 @@ int cbd_lane_length(const cbd_arena* a, int lane);
 size_t cbd_arena_used_bytes(const cbd_arena* a);
 /* Number of live lanes. */
 int cbd_arena_live_lanes(const cbd_arena* a);
+/* Blocks of the pool, and of them the free ones (or -1 for a null arena). */
+int cbd_arena_n_blocks(const cbd_arena* a);
+int cbd_arena_free_blocks(const cbd_arena* a);
 
 /* Device bytes of the workspace a step of up to max_batch lanes of an arena
  * of max_seq positions needs (activations, split partials, counters,
@@ -181,14 +194,16 @@ int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int
 int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream);
 
 /* Load a live lane's KV from k_src, v_src laid out as in export, with
- * `length` positions (<= max_seq), and set its length.  Keys are taken as
- * already rotated.  Synchronous with respect to `stream`.
- * Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL, CBD_E_HIP. */
+ * `length` positions (<= max_seq), and set its length (taking or returning
+ * blocks).  Keys are taken as already rotated.  Synchronous with respect to
+ * `stream`.  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL (too few free
+ * blocks or length > max_seq; nothing changes), CBD_E_HIP. */
 int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, const void* v_src, void* stream);
 
 /* Keep only the first `length` positions of a live lane (0 <= length <= its
  * current length); later slots become free and are rewritten by the next
- * steps.  Host bookkeeping only, no GPU work.  Lets a caller roll a lane back
+ * steps, and blocks past the kept positions return to the pool.  Host
+ * bookkeeping only, no GPU work.  Lets a caller roll a lane back
  * (e.g. replay the same step).  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE. */
 int cbd_lane_truncate(cbd_arena* a, int lane, int length);
 

@@ -114,13 +114,34 @@ def test_lane_alloc_clear_evict_and_usage_returns_to_zero():
     assert e.value.name == "CBD_E_ARG"
 
 
+def test_arena_is_a_block_pool():
+    # a block: 64 positions of one lane, every layer and KV head, K and V
+    assert cbd.arena_block_bytes(synth.TINY) == 2 * 2 * 4 * 64 * 16 * 4
+    assert cbd.arena_block_bytes(synth.MISTRAL7B) == 64 * 131072
+    m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
+    need = cbd.arena_bytes(synth.TINY, 2, 8)  # two lanes of one chunk each
+    a = cbd.Arena(m, 2, 8, FAKE, need)
+    assert a.n_blocks == 2 and a.free_blocks == 2
+    # less memory is a smaller pool, shared by the lanes
+    a1 = cbd.Arena(m, 2, 8, FAKE, need - 1)
+    assert a1.n_blocks == 1 and a1.free_blocks == 1
+
+
 def test_arena_create_rejects_small_or_misaligned_memory():
     m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
-    need = cbd.arena_bytes(synth.TINY, 2, 8)
+    bb = cbd.arena_block_bytes(synth.TINY)
     with pytest.raises(cbd.CbdError):
-        cbd.Arena(m, 2, 8, FAKE, need - 1)
+        cbd.Arena(m, 2, 8, FAKE, bb - 1)
     with pytest.raises(cbd.CbdError):
-        cbd.Arena(m, 2, 8, FAKE + 64, need)
+        cbd.Arena(m, 2, 8, FAKE + 64, 2 * bb)
+
+
+def test_step_needing_more_blocks_than_the_pool_changes_nothing():
+    m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
+    a = cbd.Arena(m, 2, 8, FAKE, cbd.arena_block_bytes(synth.TINY))  # one block for two lanes
+    l0, l1 = a.lane_alloc(), a.lane_alloc()
+    assert step_err(m, a, [l0, l1], [0, 0], [1, 2]) == "CBD_E_KV_FULL"
+    assert a.free_blocks == 1
 
 
 def test_arena_accepts_long_contexts():

@@ -1,0 +1,99 @@
+"""Paged KV: the arena is a pool of 64-position blocks, and a lane's chunks
+live in whatever blocks the pool hands out.  Lanes whose blocks are scattered
+over the pool (imports and evictions interleaved, steps that open new chunks
+and so take blocks mid-run) must give bit-identical logits and KV to the same
+lanes in a fresh arena, where every lane's blocks are consecutive: attention
+reads a chunk from its block and nothing else about the layout matters.  Both
+attention kernels are covered (bf16 head_dim 128, the matrix-core kernel; the
+135M shape in f32, the general kernel).  A step that needs more blocks than
+are free fails with CBD_E_KV_FULL and changes nothing; evicting every lane
+returns every block.
+"""
+import numpy as np
+import pytest
+
+import continuous_batching_decode_step_amd as cbd
+import synth
+from gpu_helpers import engine_for, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    synth.ModelConfig("paged-hd128-bf16", d=2048, n_layers=2, n_heads=16, n_kv_heads=4, head_dim=128, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+    synth.SMOL135M,
+]
+# lengths at import: lanes 1 and 3 open a chunk while stepping, lane 4 ends on a
+# chunk boundary, lane 5 spans three groups of chunks (only the last holds the
+# new slot; the others must leave the pool alone)
+LENS = [130, 61, 200, 64, 58, 600]
+STEPS = 6
+
+
+def _kv(cfg, b, n):
+    if cfg.wtype == synth.WTYPE_BF16:
+        return synth.lane_kv_bf16(cfg, b, n)
+    return synth.lane_kv_f32(cfg, b, n)
+
+
+def _run(eng, cfg, lanes, toks, steps):
+    pos = np.array([eng.arena.lane_length(l) for l in lanes], np.int32)
+    out = []
+    for s in range(steps):
+        _, lg = eng.step_sync(lanes, pos, [int(t[s]) for t in toks], want_logits=True)
+        out.append(lg.copy())
+    return out
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=[c.name for c in SHAPES])
+def test_scattered_blocks_match_consecutive_blocks(cfg):
+    say("case: %s, lanes of lengths %s, %d steps" % (cfg.name, LENS, STEPS))
+    W = synth.make_weights(cfg)
+    n = len(LENS)
+    max_seq = max(LENS) + STEPS
+    toks = [synth.uniform_int(1, 700 + b, STEPS, 0, cfg.vocab - 1) for b in range(n)]
+    kv = [_kv(cfg, b, LENS[b]) for b in range(n)]
+
+    # reference: a fresh arena, each lane's blocks consecutive
+    ref = engine_for(cfg, W, n, max_seq)
+    rl = [ref.arena.lane_alloc() for _ in range(n)]
+    for b in range(n):
+        ref.arena.kv_import(rl[b], LENS[b], kv[b][0], kv[b][1], ref.stream)
+    want = _run(ref, cfg, rl, toks, STEPS)
+    want_kv = [ref.kv_export(l) for l in rl]
+
+    # paged: a pool with exactly the blocks the run needs, handed out scattered
+    need = sum((LENS[b] + STEPS + 63) // 64 for b in range(n))
+    from continuous_batching_decode_step_amd.driver import Engine
+    eng = Engine(cfg, cbd.upload_weights(W), n + 1, max_seq, kv_blocks=need)
+    assert eng.arena.n_blocks == need
+    lanes = [eng.arena.lane_alloc() for _ in range(n + 1)]
+    spare = lanes.pop()   # a lane that takes blocks first, then gives them back
+    eng.arena.kv_import(spare, 128, *_kv(cfg, 99, 128), eng.stream)
+    for b in (4, 2, 0):
+        eng.arena.kv_import(lanes[b], LENS[b], kv[b][0], kv[b][1], eng.stream)
+    eng.arena.lane_evict(spare)
+    for b in (3, 1, 5):
+        eng.arena.kv_import(lanes[b], LENS[b], kv[b][0], kv[b][1], eng.stream)
+    got = _run(eng, cfg, lanes, toks, STEPS)
+    assert eng.arena.free_blocks == 0
+    for s in range(STEPS):
+        for b in range(n):
+            assert np.array_equal(got[s][b].view(np.uint32), want[s][b].view(np.uint32)), (s, b)
+    for b in range(n):
+        gk, gv = eng.kv_export(lanes[b])
+        assert np.array_equal(gk, want_kv[b][0]) and np.array_equal(gv, want_kv[b][1]), b
+        # the imported slots are untouched by the steps, in both arenas
+        m = LENS[b]
+        assert np.array_equal(gk[:, :, :m], kv[b][0]) and np.array_equal(gv[:, :, :m], kv[b][1]), b
+
+    # an exhausted pool: a step that opens a chunk fails and changes nothing
+    assert eng.arena.lane_length(lanes[4]) == 64
+    pos = np.array([64], np.int32)
+    with pytest.raises(cbd.CbdError) as e:
+        eng.step(lanes[4:5], pos, [1])
+    assert e.value.name == "CBD_E_KV_FULL" and int(pos[0]) == 64 == eng.arena.lane_length(lanes[4])
+    assert eng.arena.free_blocks == 0
+    for l in lanes:
+        eng.arena.lane_evict(l)
+    assert eng.arena.free_blocks == eng.arena.n_blocks and eng.arena.used_bytes == 0

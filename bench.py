@@ -119,34 +119,41 @@ def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
 
 
 def wide_leg(cfg, dw, args, rf, log):
-    """B = 256 (KV U[128,4096]) and B = 512 (KV U[128,2047], so the arena fits in HBM): tokens/s and
-    the projections' bf16 MFMA utilisation (GEMM flops / summed GEMM kernel time / 2.5 PFLOP/s)."""
+    """B = 256 and B = 512 with KV U[128,4096] (the headline distribution): tokens/s and the
+    projections' bf16 MFMA utilisation (GEMM flops / summed GEMM kernel time / 2.5 PFLOP/s).
+    The 512 lanes share one paged KV pool sized to the blocks they hold (~146 GB; an arena
+    with every lane at the longest length would need 275 GB)."""
     import gc
     import torch
     import synth
     from continuous_batching_decode_step_amd.driver import Engine
     out = []
-    for B, hi in ((256, 4096), (512, 2047)):
-        lens = synth.kv_lengths(B, hi=hi)
-        toks = synth.step_tokens(cfg, B)
-        eng = Engine(cfg, dw, B, int(lens.max()) + 1, max_batch=B)
-        eng.model.set_variant(args.variant)
-        lanes = [eng.arena.lane_alloc() for _ in range(B)]
-        t0 = time.time()
-        for b in range(B):
-            k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
-            eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
-        torch.cuda.synchronize()
-        log("wide B=%d: KV loaded in %.1fs" % (B, time.time() - t0))
+    n, hi = 512, 4096
+    lens = synth.kv_lengths(n, hi=hi)
+    toks = synth.step_tokens(cfg, n)
+    blocks = int(((lens + 1 + 63) // 64).sum())  # each lane's blocks, slot len_b included
+    eng = Engine(cfg, dw, n, int(lens.max()) + 1, max_batch=n, kv_blocks=blocks)
+    eng.model.set_variant(args.variant)
+    lanes = [eng.arena.lane_alloc() for _ in range(n)]
+    t0 = time.time()
+    for b in range(n):
+        k, v = synth.lane_kv_bf16(cfg, b, int(lens[b]))
+        eng.arena.kv_import(lanes[b], int(lens[b]), k, v, eng.stream)
+        if (b + 1) % 128 == 0 and b + 1 < n:
+            log("wide: KV of %d lanes loaded (%.1fs)" % (b + 1, time.time() - t0))
+    torch.cuda.synchronize()
+    log("wide: KV of %d lanes (%d blocks, %.1f GB) loaded in %.1fs" % (
+        n, blocks, eng.arena_mem.numel() / 1e9, time.time() - t0))
+    for B in (256, 512):
         row, _ = measure(eng, lanes, lens, toks, B, max(3, args.steps // 2), max(1, args.warmup), cfg, rf,
                          torch.cuda.current_stream())
         row["kv_lengths"] = "U[128,%d]" % hi
         log("wide B=%3d  %8.1f tok/s  %.3f ms/step  roofline %.3f  projections at %.1f%% of bf16 MFMA peak" % (
             B, row["tok_s"], row["ms_per_step"], row["roofline_frac"], 100 * row["gemm_mfma_util"]))
         out.append(row)
-        del eng
-        gc.collect()
-        torch.cuda.empty_cache()
+    del eng
+    gc.collect()
+    torch.cuda.empty_cache()
     return out
 
 
@@ -219,7 +226,7 @@ def main() -> int:
     ap.add_argument("--batches", default="1,2,4,8,16,32,64", help="B sweep; the last is the headline B")
     ap.add_argument("--lanes", type=int, default=64)
     ap.add_argument("--kv-max", type=int, default=4096,
-                    help="KV lengths are uniform in [128, KV_MAX] (seed 2); 2047 keeps 512 lanes within HBM")
+                    help="KV lengths are uniform in [128, KV_MAX] (seed 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
@@ -227,7 +234,7 @@ def main() -> int:
     ap.add_argument("--no-q8", action="store_true",
                     help="skip the SmolLM2-135M Q8_0 leg (decode steps at 16-position contexts, B = 1..960)")
     ap.add_argument("--no-wide", action="store_true",
-                    help="skip the wide-batch leg (B = 256 with KV U[128,4096], B = 512 with KV U[128,2047]) "
+                    help="skip the wide-batch leg (B = 256 and 512 with KV U[128,4096], one paged pool) "
                          "that reports the projections' bf16 MFMA utilisation")
     ap.add_argument("--no-trace", action="store_true",
                     help="skip the continuous-batching trace leg (8 lanes, 64 Poisson-arriving jobs, ~40 s)")

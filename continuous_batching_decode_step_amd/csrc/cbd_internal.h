@@ -139,5 +139,10 @@ hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, cons
                        void* xn, hipStream_t st);
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st);
+// Copy one lane's K or V rows [L * Hkv][len][hd] (device, contiguous) into its
+// blocks of a layer-major pool (to_pool), or back; blocks: the lane's block ids
+// on the device, one per 64 positions.
+hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows, int Hkv, int row_bytes,
+                          long long lstride, long long bbytes, bool to_pool, hipStream_t st);
 
 }  // namespace cbd

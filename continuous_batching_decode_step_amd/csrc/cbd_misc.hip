@@ -113,6 +113,40 @@ __global__ void k_fill_u32(unsigned* p, size_t n, unsigned v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Move one lane's K or V between rows [n_rows = L * Hkv][len][hd] (contiguous,
+// `rows`) and its blocks in a layer-major pool, 16 bytes per thread: position t
+// of row (l, g) sits at l * lstride + blocks[t / 64] * bbytes + (g * 64 + t % 64)
+// * row_bytes.  row_bytes (hd * element size) is a multiple of 16.
+__global__ __launch_bounds__(256) void k_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows,
+                                                 int Hkv, int row_bytes, long long lstride, long long bbytes,
+                                                 int to_pool) {
+  const int W = row_bytes / 16;
+  const size_t n = (size_t)n_rows * len * W;
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += (size_t)gridDim.x * blockDim.x) {
+    const int w = (int)(u % W);
+    const size_t tr = u / W;
+    const int t = (int)(tr % len), r = (int)(tr / len);
+    const int l = r / Hkv, g = r % Hkv;
+    char* pp = pool + l * lstride + blocks[t >> 6] * bbytes + ((long long)g * 64 + (t & 63)) * row_bytes + w * 16;
+    uint4* rp = (uint4*)(rows + u * 16);
+    if (to_pool)
+      *(uint4*)pp = *rp;
+    else
+      *rp = *(const uint4*)pp;
+  }
+}
+
+hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows, int Hkv, int row_bytes,
+                          long long lstride, long long bbytes, bool to_pool, hipStream_t st) {
+  const size_t n = (size_t)n_rows * len * (row_bytes / 16);
+  if (n == 0) return hipSuccess;
+  size_t wgs = (n + 255) / 256;
+  if (wgs > 8192) wgs = 8192;
+  hipLaunchKernelGGL(k_kv_rows, dim3((unsigned)wgs), dim3(256), 0, st, pool, rows, blocks, len, n_rows, Hkv,
+                     row_bytes, lstride, bbytes, (int)to_pool);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B, int d,
                         int hd, float theta, float* x, float* ssq, float2* rope, hipStream_t st) {
   switch (wt) {

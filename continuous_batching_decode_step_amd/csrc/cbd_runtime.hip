@@ -134,6 +134,10 @@ struct cbd_arena {
   std::vector<int> len;
   std::vector<std::vector<int>> blocks;  // per lane, the block of each chunk
   std::vector<int> free_blocks;          // a stack; the lowest block on top
+  // device staging for kv import/export: one lane's K or V rows, then its block
+  // ids; allocated on first use, grown as needed, freed with the arena
+  char* stage = nullptr;
+  size_t stage_bytes = 0;
 };
 
 namespace {
@@ -385,7 +389,10 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   return CBD_OK;
 }
 
-void cbd_arena_destroy(cbd_arena* a) { delete a; }
+void cbd_arena_destroy(cbd_arena* a) {
+  if (a && a->stage) (void)hipFree(a->stage);
+  delete a;
+}
 
 int cbd_lane_alloc(cbd_arena* a, int* lane) {
   if (!a || !lane) return fail(CBD_E_ARG, "null argument");
@@ -852,26 +859,40 @@ int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int
   return cbd_decode_step_batch(m, a, 1, &ln, position, &tok, logits, argmax, workspace, workspace_bytes, stream);
 }
 
-// Copy one block's K or V between the pool and rows [L][Hkv][len][hd] of a
-// lane (host or device), positions [64 j, 64 j + n) of each row: per layer,
-// the Hkv rows of the block are consecutive in the pool.
-static int copy_block(cbd_arena* a, int blk, int j, int n, int len, char* rows, bool to_pool, bool v, hipStream_t st) {
+// Copy a lane's K or V between rows [L][Hkv][len][hd] (host or device) and its
+// blocks: one contiguous copy through the arena's device staging buffer, and
+// one kernel that moves the rows to or from the blocks.
+static int copy_lane(cbd_arena* a, int lane, int len, char* rows, bool to_pool, bool v, hipStream_t st) {
   const cbd_config& c = a->m->c;
   const size_t kvb = a->m->kvb;
-  const size_t width = (size_t)n * c.head_dim * kvb;
-  const size_t bpitch = (size_t)ATTN_SPLIT * c.head_dim * kvb;   // row stride inside a block
-  const size_t rpitch = (size_t)len * c.head_dim * kvb;          // row stride of the lane rows
-  const size_t lstride = (size_t)a->n_blocks * a->block_elems * kvb;  // one layer of the pool
-  char* pool = a->base + (v ? a->region_bytes : 0) + (size_t)blk * a->block_elems * kvb;
-  char* r0 = rows + (size_t)j * ATTN_SPLIT * c.head_dim * kvb;
-  for (int l = 0; l < c.n_layers; ++l) {
-    char* pl = pool + l * lstride;
-    char* rl = r0 + (size_t)l * c.n_kv_heads * rpitch;
-    if (to_pool)
-      HIP_TRY(hipMemcpy2DAsync(pl, bpitch, rl, rpitch, width, c.n_kv_heads, hipMemcpyDefault, st));
-    else
-      HIP_TRY(hipMemcpy2DAsync(rl, rpitch, pl, bpitch, width, c.n_kv_heads, hipMemcpyDefault, st));
+  const int n_rows = c.n_layers * c.n_kv_heads;
+  const int row_bytes = c.head_dim * (int)kvb;
+  const size_t bytes = (size_t)n_rows * len * row_bytes;
+  const size_t boff = (bytes + 255) & ~(size_t)255;
+  const std::vector<int>& bl = a->blocks[lane];
+  const size_t need = boff + bl.size() * sizeof(int);
+  if (a->stage_bytes < need) {
+    HIP_TRY(hipStreamSynchronize(st));
+    if (a->stage) HIP_TRY(hipFree(a->stage));
+    a->stage = nullptr;
+    a->stage_bytes = 0;
+    HIP_TRY(hipMalloc(&a->stage, need));
+    a->stage_bytes = need;
   }
+  const long long bbytes = a->block_elems * (long long)kvb;
+  const long long lstride = (long long)a->n_blocks * bbytes;
+  char* pool = a->base + (v ? a->region_bytes : 0);
+  int* dblk = (int*)(a->stage + boff);
+  HIP_TRY(hipMemcpyAsync(dblk, bl.data(), bl.size() * sizeof(int), hipMemcpyHostToDevice, st));
+  if (to_pool) {
+    HIP_TRY(hipMemcpyAsync(a->stage, rows, bytes, hipMemcpyDefault, st));
+    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true, st));
+  } else {
+    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false, st));
+    HIP_TRY(hipMemcpyAsync(rows, a->stage, bytes, hipMemcpyDefault, st));
+  }
+  // the staging buffer (and the block list) are reused by the next copy
+  HIP_TRY(hipStreamSynchronize(st));
   return CBD_OK;
 }
 
@@ -881,11 +902,9 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
   if (!k_dst || !v_dst) return fail(CBD_E_ARG, "null destination");
   const int len = a->len[lane];
   hipStream_t st = (hipStream_t)stream;
-  for (int j = 0; j * ATTN_SPLIT < len; ++j) {
-    const int n = std::min(ATTN_SPLIT, len - j * ATTN_SPLIT);
-    const int blk = a->blocks[lane][j];
-    if ((rc = copy_block(a, blk, j, n, len, (char*)k_dst, false, false, st))) return rc;
-    if ((rc = copy_block(a, blk, j, n, len, (char*)v_dst, false, true, st))) return rc;
+  if (len > 0) {
+    if ((rc = copy_lane(a, lane, len, (char*)k_dst, false, false, st))) return rc;
+    if ((rc = copy_lane(a, lane, len, (char*)v_dst, false, true, st))) return rc;
   }
   HIP_TRY(hipStreamSynchronize(st));
   return CBD_OK;
@@ -908,11 +927,9 @@ int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, co
     a->free_blocks.pop_back();
   }
   hipStream_t st = (hipStream_t)stream;
-  for (int j = 0; j < need; ++j) {
-    const int n = std::min(ATTN_SPLIT, length - j * ATTN_SPLIT);
-    const int blk = a->blocks[lane][j];
-    if ((rc = copy_block(a, blk, j, n, length, (char*)k_src, true, false, st))) return rc;
-    if ((rc = copy_block(a, blk, j, n, length, (char*)v_src, true, true, st))) return rc;
+  if (length > 0) {
+    if ((rc = copy_lane(a, lane, length, (char*)k_src, true, false, st))) return rc;
+    if ((rc = copy_lane(a, lane, length, (char*)v_src, true, true, st))) return rc;
   }
   HIP_TRY(hipStreamSynchronize(st));
   a->len[lane] = length;

@@ -189,8 +189,11 @@ int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int
 
 /* Copy a live lane's KV out: k_dst, v_dst (host or device, hipMemcpy default
  * kind) receive [n_layers][n_kv_heads][length][head_dim] in the KV format.
- * Synchronous with respect to `stream`.  Errors: CBD_E_ARG, CBD_E_LANE_NOT_LIVE,
- * CBD_E_HIP. */
+ * Synchronous with respect to `stream`.  Import and export move the rows
+ * through a device staging buffer of one lane's K (or V) that the arena
+ * allocates on first use, grows as needed and frees in cbd_arena_destroy (not a
+ * step-path call: the step allocates nothing).  Errors: CBD_E_ARG,
+ * CBD_E_LANE_NOT_LIVE, CBD_E_HIP. */
 int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream);
 
 /* Load a live lane's KV from k_src, v_src laid out as in export, with

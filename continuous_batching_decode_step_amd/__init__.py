@@ -31,7 +31,7 @@ SYMBOLS = [
     "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
     "cbd_lane_truncate", "cbd_profile_enable", "cbd_profile_reset", "cbd_profile_read", "cbd_profile_classes",
     "cbd_profile_class_name", "cbd_set_graph_replay", "cbd_arena_block_bytes", "cbd_arena_n_blocks",
-    "cbd_arena_free_blocks",
+    "cbd_arena_free_blocks", "cbd_prefill_batch",
 ]
 
 
@@ -97,6 +97,7 @@ def lib():
         L.cbd_workspace_bytes.argtypes = [vp, i32, i32]
         L.cbd_workspace_bytes.restype = sz
         L.cbd_decode_step_batch.argtypes = [vp, vp, i32, pi32, pi32, pi32, vp, vp, vp, sz, vp]
+        L.cbd_prefill_batch.argtypes = [vp, vp, i32, pi32, pi32, pi32, pi32, vp, vp, vp, sz, vp]
         L.cbd_decode_step.argtypes = [vp, vp, i32, pi32, ctypes.c_int32, vp, vp, vp, sz, vp]
         L.cbd_lane_kv_export.argtypes = [vp, i32, vp, vp, vp]
         L.cbd_lane_kv_import.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -275,6 +276,22 @@ class Model:
             0 if workspace is None else workspace.numel() * workspace.element_size())
         _check(lib().cbd_decode_step_batch(self.h, arena.h, B, _pi32(ln), _pi32(positions), _pi32(tk),
                                            _ptr(logits), _ptr(argmax), _ptr(workspace), wsb, _stream(stream)))
+
+    def prefill_batch(self, arena: "Arena", lanes: Sequence[int], positions: np.ndarray, counts, tokens,
+                      logits, argmax=None, workspace=None, workspace_bytes: Optional[int] = None,
+                      stream=None) -> None:
+        """counts[i] tokens for lane i, tokens concatenated lane by lane; logits [len(lanes), vocab] of each
+        lane's last token.  positions: np.int32 array, advanced in place by counts on success."""
+        ln = _i32(lanes)
+        assert isinstance(positions, np.ndarray) and positions.dtype == np.int32 and positions.flags["C_CONTIGUOUS"]
+        ct = _i32(counts)
+        tk = _i32(tokens)
+        n = len(ln)
+        assert len(positions) == n and len(ct) == n and len(tk) == int(ct.astype(np.int64).sum())
+        wsb = workspace_bytes if workspace_bytes is not None else (
+            0 if workspace is None else workspace.numel() * workspace.element_size())
+        _check(lib().cbd_prefill_batch(self.h, arena.h, n, _pi32(ln), _pi32(positions), _pi32(ct), _pi32(tk),
+                                       _ptr(logits), _ptr(argmax), _ptr(workspace), wsb, _stream(stream)))
 
     def decode_step(self, arena: "Arena", lane: int, position: np.ndarray, token: int, logits, argmax=None,
                     workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:

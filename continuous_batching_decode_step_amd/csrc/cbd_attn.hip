@@ -151,7 +151,13 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   }
   // The new key and value at slot p, rotated and rounded to the KV format
   // (kept as stored words).
-  const bool has_new = nk > s * ATTN_SPLIT && nk <= s * ATTN_SPLIT + ATTN_SPLIT;
+  // Fused mode: the item whose chunk holds slot p rotates and writes the new
+  // key and value and uses them for that slot.  Append-only mode stops after
+  // the write; attend-only mode reads slot p from the cache like any key.
+  const bool fused = a.mode == ATTN_FUSED;
+  const bool has_new = a.mode != ATTN_ATTEND && nk > s * ATTN_SPLIT && nk <= s * ATTN_SPLIT + ATTN_SPLIT;
+  if (a.mode == ATTN_APPEND && !has_new) return;
+  const int pk = fused ? p : nk;  // keys below pk are read from the cache
   KVRaw<D, KVBF16> knr, vnr;
 #pragma unroll
   for (int i = 0; i < KVRaw<D, KVBF16>::NW; ++i) knr.w[i] = vnr.w[i] = 0u;
@@ -201,6 +207,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       }
     }
   }
+  if (a.mode == ATTN_APPEND) return;
 
   // Scores of the wave's 64 keys: lane (r, c) accumulates its D dims of key
   // kbeg + 4*it + r into part[it][j]; the row then reduce-scatters so that
@@ -223,8 +230,8 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const int key = kbeg + 4 * (i0 + i) + r;
-      const unsigned take = key == p ? ~0u : 0u;
-      const unsigned keep = key < p ? ~0u : 0u;  // past the end: zero
+      const unsigned take = fused && key == p ? ~0u : 0u;
+      const unsigned keep = key < pk ? ~0u : 0u;  // past the end: zero
       raw_select<D, KVBF16>(kr[i], keep, take, knr);
       float kv[D];
       raw_to_f32<D, KVBF16>(kr[i], kv);
@@ -300,8 +307,8 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
     for (int i = 0; i < KB; ++i) {
       const int it = i0 + i;
       const int key = kbeg + 4 * it + r;
-      const unsigned take = key == p ? ~0u : 0u;
-      const unsigned keep = key < p ? ~0u : 0u;
+      const unsigned take = fused && key == p ? ~0u : 0u;
+      const unsigned keep = key < pk ? ~0u : 0u;
       raw_select<D, KVBF16>(vr[i], keep, take, vnr);
       float vv[D];
       raw_to_f32<D, KVBF16>(vr[i], vv);
@@ -433,7 +440,15 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int b = it4.x & 0xffffff, nc = it4.x >> 24, c0 = it4.y, p = it4.z;
   const int nk = p + 1;
   const int c = c0 + w;  // this wave's chunk
-  const bool active = w < nc;
+  // Fused mode: the lane's last group (its last chunk holds slot p) rotates
+  // and writes the new key and value and uses them for that slot.  Append-only
+  // mode: only that group runs, and stops after the write.  Attend-only mode:
+  // slot p is read from the cache like any key.
+  const bool fused = a.mode == ATTN_FUSED;
+  const bool holds_p = a.mode != ATTN_ATTEND && p / ATTN_SPLIT == c0 + nc - 1;
+  if (a.mode == ATTN_APPEND && !holds_p) return;
+  const int pk = fused ? p : nk;  // keys below pk are read from the cache
+  const bool active = w < nc && a.mode != ATTN_APPEND;  // waves that attend to a chunk
   // (layer, head) offset inside a block; base: this wave's chunk (inactive
   // waves: the last chunk's, never read); lbase: the group's last chunk,
   // which holds slot p when the group is the lane's last
@@ -490,8 +505,6 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __attribute__((aligned(16))) uint16_t qs[2 * G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
   __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
-  const int clast = c0 + nc - 1;
-  const bool holds_p = p / ATTN_SPLIT == clast;  // the group's last chunk holds slot p (the lane's last group)
   // When the QKV projection ran in split mode without its fold, the workgroup
   // adds the split partials of the values it needs itself, in split order, as
   // the fold would: P_s of lane b at [(s * B + b) * Nqkv + n].  The sums (the
@@ -523,7 +536,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   } else {
     qv = row + (size_t)g * G * HD;
   }
-  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+  for (int idx = tid; a.mode != ATTN_APPEND && idx < G * HD; idx += 64 * MF_WAVES) {
     const int j = idx / HD, d = idx % HD;
     const float q = rot(qv + (size_t)j * HD, d);
     const uint16_t hi = f2bf_a(q);
@@ -539,6 +552,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       ((uint16_t*)a.vslab)[lbase + (long long)p * HD + d] = vw;
     }
   }
+  if (a.mode == ATTN_APPEND) return;
   __syncthreads();
 
   if (active) {
@@ -550,7 +564,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     }
     const float inv = 1.0f / sqrtf((float)HD);
     const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
-    const bool has_new = p >= kb && p < kb + ATTN_SPLIT;
+    const bool has_new = fused && p >= kb && p < kb + ATTN_SPLIT;
     // the new key and value replace slot p's old contents
     KVRaw<D, true> vnr;
 #pragma unroll
@@ -624,8 +638,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       for (int it = 0; it < 16; ++it) {
         if constexpr (decltype(masked)::value) {
           const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
-          const unsigned take = key == p ? ~0u : 0u;
-          const unsigned keep = key < p ? ~0u : 0u;
+          const unsigned take = has_new && key == p ? ~0u : 0u;
+          const unsigned keep = key < pk ? ~0u : 0u;
           raw_select<D, true>(vr[it], keep, take, vnr);
         }
         float vv[D];

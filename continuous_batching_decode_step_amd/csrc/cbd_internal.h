@@ -20,6 +20,11 @@ constexpr int ATTN_GROUP = 4;
 // ints per attention work item: lane index | chunk count << 24, first chunk,
 // position, padding, then the arena block of each of up to ATTN_GROUP chunks.
 constexpr int ITEM_INTS = 8;
+// Attention modes: fused (a decode step: each lane's new K/V is written and
+// used by the same launch), append only, attend only (several rows of a lane
+// in one call: all rows' K/V are written first, then every key is read from
+// the cache, so rows never read a slot another workgroup is writing).
+constexpr int ATTN_FUSED = 0, ATTN_APPEND = 1, ATTN_ATTEND = 2;
 // Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
 // epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
 // rows; the others take one tile so that d-row projections fill the chip).
@@ -76,6 +81,7 @@ struct AttnArgs {
   long long block_elems;  // Hkv * ATTN_SPLIT * hd
   long long layer_off;    // l * n_blocks * block_elems
   int B;
+  int mode;               // ATTN_FUSED, ATTN_APPEND or ATTN_ATTEND
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
   const int* items;       // [n_items][ITEM_INTS] {b | chunks << 24, first chunk, position, 0, block of each chunk (up to 4)}, 16-byte aligned

@@ -618,11 +618,15 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   return CBD_OK;
 }
 
-// Every kernel of one step, in order, on `st` (plain launches or a capture).
-// Arguments depend only on (B, workspace layout, arena, outputs): the per-step
-// data (lanes, positions, tokens, attention items) is read from the workspace.
-static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLayout& L, float* logits,
-                        int32_t* argmax, hipStream_t st) {
+// Every kernel of one step, in order, on `st` (plain launches or a capture),
+// over B rows (a lane at a position with a token each); the first n_out rows
+// produce logits and argmax.  multi: some lane has several rows, so attention
+// appends every row's K/V first and then reads all keys from the cache.
+// Arguments depend only on (B, n_out, multi, workspace layout, arena,
+// outputs): the per-step data (lanes, positions, tokens, attention items) is
+// read from the workspace.
+static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, char* ws, const WsLayout& L,
+                        float* logits, int32_t* argmax, hipStream_t st) {
   const cbd_config& c = m->c;
   const int32_t* dmeta = (const int32_t*)(ws + L.meta);
   const int* d_lanes = dmeta;
@@ -678,7 +682,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
     // all its attention workgroups from beyond L2 (at 64 lanes +36 MB per
     // launch, more than the fold kernel costs).
     bool unfolded = false;
-    const bool attn_folds = B <= 8 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
+    const bool attn_folds = !multi && B <= 8 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
     if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st, nullptr, nullptr,
                        attn_folds ? &unfolded : nullptr)))
       return rc;
@@ -687,6 +691,13 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
     at.layer_off = (long long)l * a->n_blocks * a->block_elems;
     {
       ProfScope ps(m, P_ATTN, st);
+      if (multi) {
+        at.mode = ATTN_APPEND;
+        HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
+        at.mode = ATTN_ATTEND;
+      } else {
+        at.mode = ATTN_FUSED;
+      }
       HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
     }
     {
@@ -704,62 +715,20 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, char* ws, const WsLay
       return rc;
     if (!normed && (rc = norm(gnext, m->p_down.nRB))) return rc;
   }
-  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, B, logits, nullptr, ws, L, st))) return rc;
+  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, n_out, logits, nullptr, ws, L, st))) return rc;
   if (argmax) {
     ProfScope ps(m, P_ARGMAX, st);
-    HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, B, argmax, st));
+    HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, n_out, argmax, st));
   }
   return CBD_OK;
 }
 
-int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
-                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (!m || !a || !lanes || !positions || !tokens || !logits) return fail(CBD_E_ARG, "null argument");
-  if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
-  if (B < 1) return fail(CBD_E_ARG, "B = %d < 1", B);
-  const cbd_config& c = m->c;
-  // lanes: range, liveness, distinctness; positions; tokens
-  std::vector<uint8_t> seen(a->n_lanes, 0);
-  for (int b = 0; b < B; ++b) {
-    const int ln = lanes[b];
-    if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", b, ln, a->n_lanes);
-    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
-    seen[ln] = 1;
-    if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
-    if (positions[b] != a->len[ln])
-      return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", b, positions[b], ln,
-                  a->len[ln]);
-    if (positions[b] >= a->max_seq)
-      return fail(CBD_E_KV_FULL, "lane %d is full (%d of %d slots)", ln, positions[b], a->max_seq);
-    if (tokens[b] < 0 || tokens[b] >= c.vocab)
-      return fail(CBD_E_TOKEN, "tokens[%d] = %d outside [0, %d)", b, tokens[b], c.vocab);
-  }
-  // slot positions[b] opens a new chunk for lanes whose blocks end there
-  int new_blocks = 0;
-  for (int b = 0; b < B; ++b)
-    if ((size_t)positions[b] / ATTN_SPLIT >= a->blocks[lanes[b]].size()) ++new_blocks;
-  if (new_blocks > (int)a->free_blocks.size())
-    return fail(CBD_E_KV_FULL, "the step needs %d new KV blocks, %zu of %d are free", new_blocks,
-                a->free_blocks.size(), a->n_blocks);
-  if (!workspace) return fail(CBD_E_WORKSPACE, "null workspace");
-  if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
-  const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
-  if (maxB < B)
-    return fail(CBD_E_WORKSPACE, "workspace of %zu bytes holds %d lanes, step has %d (need %zu)", workspace_bytes,
-                maxB, B, cbd_workspace_bytes(m, B, a->max_seq));
-  const WsLayout L = layout(m, maxB, a->max_seq);
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-
-  // The step's new blocks (validated above: the pool has them).
-  for (int b = 0; b < B; ++b) {
-    std::vector<int>& bl = a->blocks[lanes[b]];
-    if ((size_t)positions[b] / ATTN_SPLIT >= bl.size()) {
-      bl.push_back(a->free_blocks.back());
-      a->free_blocks.pop_back();
-    }
-  }
+// Copy B rows' metadata (lane, position, token) and their attention work
+// items to the workspace and run the step over them; the first n_out rows
+// produce logits and argmax.  Blocks for every row's slot are already taken.
+static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, const int32_t* lanes,
+                       const int32_t* positions, const int32_t* tokens, char* ws, size_t workspace_bytes,
+                       const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st) {
   // Per-step metadata: lanes, positions, tokens, item count, attention work
   // items {b | chunks << 24, first chunk, position, 0, block of each chunk}: a
   // workgroup of the attention kernel takes one aligned group of up to `per`
@@ -812,11 +781,11 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   m->ev_live[si] = true;
 
   int rc;
-  const bool graph = m->use_graphs && !m->prof;
+  const bool graph = m->use_graphs && !m->prof && !multi;
   if (!graph) {
-    if ((rc = enqueue_step(m, a, B, ws, L, logits, argmax, st))) return rc;
+    if ((rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, st))) return rc;
   } else {
-    const cbd_model::GraphKey key{B,         workspace,   a->base,     logits,    argmax,
+    const cbd_model::GraphKey key{B,         ws,          a->base,     logits,    argmax,
                                   workspace_bytes, a->max_seq, a->n_lanes, m->variant};
     hipGraphExec_t exec = nullptr;
     for (auto& g : m->graphs)
@@ -825,7 +794,7 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
       if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
       hipGraph_t graph_def = nullptr;
       HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-      rc = enqueue_step(m, a, B, ws, L, logits, argmax, m->cap_stream);
+      rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, m->cap_stream);
       hipError_t e = hipStreamEndCapture(m->cap_stream, &graph_def);
       if (rc) {
         if (graph_def) (void)hipGraphDestroy(graph_def);
@@ -844,10 +813,143 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
     HIP_TRY(hipGraphLaunch(exec, st));
   }
   if (m->prof && (rc = drain_profile(m, false))) return rc;
+  return CBD_OK;
+}
+
+int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!m || !a || !lanes || !positions || !tokens || !logits) return fail(CBD_E_ARG, "null argument");
+  if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
+  if (B < 1) return fail(CBD_E_ARG, "B = %d < 1", B);
+  const cbd_config& c = m->c;
+  // lanes: range, liveness, distinctness; positions; tokens
+  std::vector<uint8_t> seen(a->n_lanes, 0);
+  for (int b = 0; b < B; ++b) {
+    const int ln = lanes[b];
+    if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", b, ln, a->n_lanes);
+    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
+    seen[ln] = 1;
+    if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
+    if (positions[b] != a->len[ln])
+      return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", b, positions[b], ln,
+                  a->len[ln]);
+    if (positions[b] >= a->max_seq)
+      return fail(CBD_E_KV_FULL, "lane %d is full (%d of %d slots)", ln, positions[b], a->max_seq);
+    if (tokens[b] < 0 || tokens[b] >= c.vocab)
+      return fail(CBD_E_TOKEN, "tokens[%d] = %d outside [0, %d)", b, tokens[b], c.vocab);
+  }
+  // slot positions[b] opens a new chunk for lanes whose blocks end there
+  int new_blocks = 0;
+  for (int b = 0; b < B; ++b)
+    if ((size_t)positions[b] / ATTN_SPLIT >= a->blocks[lanes[b]].size()) ++new_blocks;
+  if (new_blocks > (int)a->free_blocks.size())
+    return fail(CBD_E_KV_FULL, "the step needs %d new KV blocks, %zu of %d are free", new_blocks,
+                a->free_blocks.size(), a->n_blocks);
+  if (!workspace) return fail(CBD_E_WORKSPACE, "null workspace");
+  if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
+  if (maxB < B)
+    return fail(CBD_E_WORKSPACE, "workspace of %zu bytes holds %d lanes, step has %d (need %zu)", workspace_bytes,
+                maxB, B, cbd_workspace_bytes(m, B, a->max_seq));
+  const WsLayout L = layout(m, maxB, a->max_seq);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  // The step's new blocks (validated above: the pool has them).
+  for (int b = 0; b < B; ++b) {
+    std::vector<int>& bl = a->blocks[lanes[b]];
+    if ((size_t)positions[b] / ATTN_SPLIT >= bl.size()) {
+      bl.push_back(a->free_blocks.back());
+      a->free_blocks.pop_back();
+    }
+  }
+  int rc = submit_rows(m, a, B, B, false, lanes, positions, tokens, ws, workspace_bytes, L, logits, argmax, st);
+  if (rc) return rc;
 
   for (int b = 0; b < B; ++b) {
     positions[b] += 1;
     a->len[lanes[b]] += 1;
+  }
+  return CBD_OK;
+}
+
+int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lanes, int32_t* positions,
+                      const int32_t* counts, const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!m || !a || !lanes || !positions || !counts || !tokens || !logits) return fail(CBD_E_ARG, "null argument");
+  if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
+  if (n_seq < 1) return fail(CBD_E_ARG, "n_seq = %d < 1", n_seq);
+  const cbd_config& c = m->c;
+  std::vector<uint8_t> seen(a->n_lanes, 0);
+  long long R = 0;
+  int new_blocks = 0;
+  bool multi = false;
+  for (int i = 0; i < n_seq; ++i) {
+    const int ln = lanes[i];
+    if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", i, ln, a->n_lanes);
+    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
+    seen[ln] = 1;
+    if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
+    if (positions[i] != a->len[ln])
+      return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", i, positions[i], ln,
+                  a->len[ln]);
+    if (counts[i] < 1) return fail(CBD_E_ARG, "counts[%d] = %d < 1", i, counts[i]);
+    if ((long long)positions[i] + counts[i] > a->max_seq)
+      return fail(CBD_E_KV_FULL, "lane %d: %d + %d positions exceed max_seq %d", ln, positions[i], counts[i],
+                  a->max_seq);
+    const long long need = ((long long)positions[i] + counts[i] + ATTN_SPLIT - 1) / ATTN_SPLIT;
+    if (need > (long long)a->blocks[ln].size()) new_blocks += (int)(need - (long long)a->blocks[ln].size());
+    multi = multi || counts[i] > 1;
+    R += counts[i];
+  }
+  for (long long r = 0; r < R; ++r)
+    if (tokens[r] < 0 || tokens[r] >= c.vocab)
+      return fail(CBD_E_TOKEN, "tokens[%lld] = %d outside [0, %d)", r, tokens[r], c.vocab);
+  if (new_blocks > (int)a->free_blocks.size())
+    return fail(CBD_E_KV_FULL, "the call needs %d new KV blocks, %zu of %d are free", new_blocks,
+                a->free_blocks.size(), a->n_blocks);
+  if (!workspace) return fail(CBD_E_WORKSPACE, "null workspace");
+  if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
+  if (maxB < R)
+    return fail(CBD_E_WORKSPACE, "workspace of %zu bytes holds %d rows, the call has %lld", workspace_bytes, maxB, R);
+  const WsLayout L = layout(m, maxB, a->max_seq);
+
+  // Blocks for every new slot (validated above: the pool has them).
+  for (int i = 0; i < n_seq; ++i) {
+    std::vector<int>& bl = a->blocks[lanes[i]];
+    const size_t need = ((size_t)positions[i] + counts[i] + ATTN_SPLIT - 1) / ATTN_SPLIT;
+    while (bl.size() < need) {
+      bl.push_back(a->free_blocks.back());
+      a->free_blocks.pop_back();
+    }
+  }
+  // Rows: each lane's last token first (rows 0..n_seq-1 give the logits), then
+  // the lane's earlier tokens in order.
+  std::vector<int32_t> rl, rp, rt;
+  rl.reserve(R);
+  rp.reserve(R);
+  rt.reserve(R);
+  std::vector<long long> off(n_seq + 1, 0);
+  for (int i = 0; i < n_seq; ++i) off[i + 1] = off[i] + counts[i];
+  for (int i = 0; i < n_seq; ++i) {
+    rl.push_back(lanes[i]);
+    rp.push_back(positions[i] + counts[i] - 1);
+    rt.push_back(tokens[off[i + 1] - 1]);
+  }
+  for (int i = 0; i < n_seq; ++i)
+    for (int t = 0; t + 1 < counts[i]; ++t) {
+      rl.push_back(lanes[i]);
+      rp.push_back(positions[i] + t);
+      rt.push_back(tokens[off[i] + t]);
+    }
+  int rc = submit_rows(m, a, (int)R, n_seq, multi, rl.data(), rp.data(), rt.data(), (char*)workspace,
+                       workspace_bytes, L, logits, argmax, (hipStream_t)stream);
+  if (rc) return rc;
+  for (int i = 0; i < n_seq; ++i) {
+    positions[i] += counts[i];
+    a->len[lanes[i]] += counts[i];
   }
   return CBD_OK;
 }

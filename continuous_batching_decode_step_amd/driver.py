@@ -55,6 +55,18 @@ class Engine:
         lg = self.logits[:B].cpu().numpy() if want_logits else None
         return am, lg
 
+    def prefill_sync(self, lanes, positions, prompts, want_logits: bool = False):
+        """Feed each lane its whole chunk of tokens in one batched prefill call; returns the argmax (and
+        logits) of each lane's last token.  positions (np.int32) advance in place by the chunk lengths."""
+        counts = [len(p) for p in prompts]
+        toks = [int(t) for p in prompts for t in p]
+        self.model.prefill_batch(self.arena, lanes, positions, counts, toks, self.logits, self.argmax, self.ws,
+                                 self.ws_bytes, self.stream)
+        n = len(lanes)
+        am = self.argmax[:n].cpu().numpy()
+        lg = self.logits[:n].cpu().numpy() if want_logits else None
+        return am, lg
+
     def kv_export(self, lane: int):
         c = self.cfg
         n = self.arena.lane_length(lane)

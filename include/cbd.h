@@ -187,6 +187,30 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
 int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int32_t token, float* logits,
                     int32_t* argmax, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Batched chunked prefill: several tokens for each of n_seq lanes in one
+ * call.  The prompt of "Fat-station continuous batching" (section "The
+ * capture") is prefilled in chunks into the lane's cache at consecutive
+ * positions; "parallel-slots.md" (section "Reuse: batched PREFILL already
+ * exists") batches prefill over rows under a causal mask that keeps each
+ * row's result independent of the others.  Here lane i takes counts[i] >= 1
+ * tokens, tokens[off_i .. off_i + counts[i]) with off_i = counts[0] + ... +
+ * counts[i-1], at positions positions[i] .. positions[i] + counts[i] - 1:
+ * each token is embedded, its K/V written at its slot, and it attends over
+ * slots [0, its position] of its own lane (the tokens before it in the same
+ * call included).  The result equals feeding the lane's tokens one decode step
+ * at a time, bit for bit (logits and KV).  Host inputs: lanes[n_seq] (distinct
+ * live lanes), positions[n_seq] (in/out: each lane's KV length on entry,
+ * advanced by counts[i] on success), counts[n_seq], tokens[sum counts].
+ * Device outputs: logits [n_seq, vocab] f32 of each lane's last token
+ * (required) and argmax [n_seq] int32 (optional, NULL to skip).  The workspace
+ * must hold sum(counts) rows: workspace_bytes >= cbd_workspace_bytes(m,
+ * sum(counts), arena max_seq).  Errors: as cbd_decode_step_batch, plus
+ * CBD_E_ARG for a count below 1 and CBD_E_KV_FULL for positions[i] +
+ * counts[i] > max_seq or too few free blocks; a failed call changes nothing. */
+int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lanes, int32_t* positions,
+                      const int32_t* counts, const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Copy a live lane's KV out: k_dst, v_dst (host or device, hipMemcpy default
  * kind) receive [n_layers][n_kv_heads][length][head_dim] in the KV format.
  * Synchronous with respect to `stream`.  Import and export move the rows

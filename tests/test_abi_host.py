@@ -200,3 +200,43 @@ def test_workspace_grows_with_batch_and_context():
     with pytest.raises(cbd.CbdError):
         m.set_variant(5)
     m.set_variant(1)
+
+
+def prefill_err(m, a, lanes, pos, counts, toks, ws=FAKE, wsb=None, logits=FAKE):
+    pos = np.array(pos, np.int32)
+    before = pos.copy()
+    lens = {l: a.lane_length(l) for l in range(a.n_lanes) if _live(a, l)}
+    free = a.free_blocks
+    wsb = m.workspace_bytes(max(1, int(sum(counts))), a.max_seq) if wsb is None else wsb
+    with pytest.raises(cbd.CbdError) as e:
+        m.prefill_batch(a, lanes, pos, counts, toks, logits, None, ws, wsb, stream=0)
+    # a failed call changes nothing
+    assert np.array_equal(pos, before) and a.free_blocks == free
+    assert lens == {l: a.lane_length(l) for l in range(a.n_lanes) if _live(a, l)}
+    return e.value.name
+
+
+def test_prefill_validation_errors_change_nothing():
+    m, a = make_model_arena()  # 4 lanes of at most 8 positions
+    l0, l1, l2 = a.lane_alloc(), a.lane_alloc(), a.lane_alloc()
+    a.lane_evict(l2)
+    assert prefill_err(m, a, [l0, l0], [0, 0], [1, 2], [1, 2, 3]) == "CBD_E_DUP_LANE"
+    assert prefill_err(m, a, [l0, l2], [0, 0], [1, 2], [1, 2, 3]) == "CBD_E_LANE_NOT_LIVE"
+    assert prefill_err(m, a, [l0, 9], [0, 0], [1, 2], [1, 2, 3]) == "CBD_E_ARG"
+    assert prefill_err(m, a, [l0, l1], [0, 1], [1, 2], [1, 2, 3]) == "CBD_E_POS_MISMATCH"
+    assert prefill_err(m, a, [l0, l1], [0, 0], [1, 0], [1]) == "CBD_E_ARG"
+    assert prefill_err(m, a, [l0, l1], [0, 0], [1, 9], [1] * 10) == "CBD_E_KV_FULL"  # 9 > max_seq 8
+    assert prefill_err(m, a, [l0, l1], [0, 0], [2, 2], [1, 2, 3, 256]) == "CBD_E_TOKEN"
+    assert prefill_err(m, a, [], [], [], []) == "CBD_E_ARG"
+    small = m.workspace_bytes(3, a.max_seq)  # 3 rows; the call has 4
+    assert prefill_err(m, a, [l0, l1], [0, 0], [2, 2], [1, 2, 3, 4], wsb=small) == "CBD_E_WORKSPACE"
+    assert prefill_err(m, a, [l0, l1], [0, 0], [2, 2], [1, 2, 3, 4], ws=0) == "CBD_E_WORKSPACE"
+
+
+def test_prefill_needing_more_blocks_than_the_pool_changes_nothing():
+    m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
+    a = cbd.Arena(m, 2, 200, FAKE, 2 * cbd.arena_block_bytes(synth.TINY))  # two blocks for two lanes
+    l0, l1 = a.lane_alloc(), a.lane_alloc()
+    # 65 tokens span two blocks, and the other lane needs one more
+    assert prefill_err(m, a, [l0, l1], [0, 0], [65, 1], [1] * 66) == "CBD_E_KV_FULL"
+    assert a.free_blocks == 2

@@ -1,0 +1,100 @@
+"""Batched chunked prefill: several tokens per lane in one call.
+
+Each lane's prompt arrives in two chunks (two prefill calls); some lanes
+start from an imported cache, and chunks cross 64-position block boundaries.
+Feeding the same tokens one decode step at a time (lockstep over the lanes
+still feeding) must give bit-identical logits at the end of each chunk and a
+bit-identical cache afterwards: a row's result depends only on its own lane
+and position.  The last logits also match the oracle fed token by token.
+Both attention kernels are covered (bf16 head_dim 128, the matrix-core
+kernel; the tiny shape in f32, the general kernel).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import TOL_BF16, TOL_F32, engine_for, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    synth.TINY,
+    synth.ModelConfig("prefill-hd128-bf16", d=2048, n_layers=2, n_heads=16, n_kv_heads=4, head_dim=128, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+]
+START = [0, 0, 30, 64, 100]    # cache length before the prompt (imported)
+TOTAL = [1, 70, 34, 130, 7]    # prompt tokens per lane
+
+
+def _kv(cfg, b, n):
+    return synth.lane_kv_bf16(cfg, b, n) if cfg.wtype == synth.WTYPE_BF16 else synth.lane_kv_f32(cfg, b, n)
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=[c.name for c in SHAPES])
+def test_chunked_prefill_equals_decode_steps(cfg):
+    n = len(TOTAL)
+    say("case: %s, starts %s, prompts %s" % (cfg.name, START, TOTAL))
+    W = synth.make_weights(cfg)
+    max_seq = max(s + t for s, t in zip(START, TOTAL))
+    prompts = [synth.uniform_int(1, 900 + b, TOTAL[b], 0, cfg.vocab - 1) for b in range(n)]
+    split = [(t + 1) // 2 for t in TOTAL]   # first chunk; the rest (if any) is the second
+    kv0 = {b: _kv(cfg, b, START[b]) for b in range(n) if START[b] > 0}
+
+    # prefill, two calls
+    pe = engine_for(cfg, W, n, max_seq, max_batch=sum(TOTAL))
+    pl = [pe.arena.lane_alloc() for _ in range(n)]
+    for b, (k, v) in kv0.items():
+        pe.arena.kv_import(pl[b], START[b], k, v, pe.stream)
+    pos = np.array(START, np.int32)
+    am1, lg1 = pe.prefill_sync(pl, pos, [prompts[b][:split[b]] for b in range(n)], want_logits=True)
+    assert np.array_equal(pos, np.array(START) + np.array(split))
+    second = [b for b in range(n) if split[b] < TOTAL[b]]
+    pos2 = pos[second].copy()
+    am2, lg2 = pe.prefill_sync([pl[b] for b in second], pos2, [prompts[b][split[b]:] for b in second],
+                               want_logits=True)
+    assert np.array_equal(pos2, np.array(START)[second] + np.array(TOTAL)[second])
+    assert np.array_equal(am1, np.argmax(lg1, axis=1)) and np.array_equal(am2, np.argmax(lg2, axis=1))
+
+    # the same tokens, one decode step at a time
+    de = engine_for(cfg, W, n, max_seq, max_batch=n)
+    dl = [de.arena.lane_alloc() for _ in range(n)]
+    for b, (k, v) in kv0.items():
+        de.arena.kv_import(dl[b], START[b], k, v, de.stream)
+    at_split, at_end = {}, {}
+    for k in range(max(TOTAL)):
+        live = [b for b in range(n) if k < TOTAL[b]]
+        p = np.array([START[b] + k for b in live], np.int32)
+        _, lg = de.step_sync([dl[b] for b in live], p, [int(prompts[b][k]) for b in live], want_logits=True)
+        for i, b in enumerate(live):
+            if k == split[b] - 1:
+                at_split[b] = lg[i].copy()
+            if k == TOTAL[b] - 1:
+                at_end[b] = lg[i].copy()
+    for b in range(n):
+        assert np.array_equal(lg1[b].view(np.uint32), at_split[b].view(np.uint32)), ("first chunk", b)
+    for i, b in enumerate(second):
+        assert np.array_equal(lg2[i].view(np.uint32), at_end[b].view(np.uint32)), ("second chunk", b)
+    for b in range(n):
+        assert pe.arena.lane_length(pl[b]) == START[b] + TOTAL[b]
+        gk, gv = pe.kv_export(pl[b])
+        rk, rv = de.kv_export(dl[b])
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv), b
+        if b in kv0:
+            assert np.array_equal(gk[:, :, :START[b]], kv0[b][0]) and np.array_equal(gv[:, :, :START[b]], kv0[b][1])
+
+    # the oracle, fed token by token, on two lanes
+    M = oracle.Model(W)
+    tol = TOL_BF16 if cfg.wtype == synth.WTYPE_BF16 else TOL_F32
+    for b in (2, 3):
+        lane = M.lane(max_seq)
+        if b in kv0:
+            k, v = kv0[b]
+            if cfg.wtype == synth.WTYPE_BF16:
+                k, v = synth.bf16_to_f32(k), synth.bf16_to_f32(v)
+            lane.set_kv(k, v)
+        for t in prompts[b]:
+            ref = M.step(lane, int(t))
+        err = rel_err(at_end[b], ref)
+        say("  lane %d (start %d, %d tokens): last logits max rel %.3g" % (b, START[b], TOTAL[b], err))
+        assert err <= tol

@@ -157,6 +157,61 @@ def wide_leg(cfg, dw, args, rf, log):
     return out
 
 
+def prefill_leg(cfg, dw, args, rf, log, n=8, count=512):
+    """Batched chunked prefill at the 7B shape: n lanes each take a count-token prompt (seeded tokens) from
+    an empty cache in one cbd_prefill_batch call of n * count rows.  Reports prompt tokens/s and the
+    projections' bf16 MFMA utilisation (GEMM flops / summed GEMM kernel time / 2.5 PFLOP/s)."""
+    import gc
+    import torch
+    import synth
+    from continuous_batching_decode_step_amd.driver import Engine
+    R = n * count
+    prompts = [synth.uniform_int(1, 1000 + b, count, 0, cfg.vocab - 1) for b in range(n)]
+    toks = np.concatenate(prompts).astype(np.int32)
+    eng = Engine(cfg, dw, n, count, max_batch=R)
+    eng.model.set_variant(args.variant)
+    lanes = [eng.arena.lane_alloc() for _ in range(n)]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        for l in lanes:
+            eng.arena.lane_clear(l)
+        pos = np.zeros(n, np.int32)
+        eng.model.prefill_batch(eng.arena, lanes, pos, [count] * n, toks, eng.logits, eng.argmax, eng.ws,
+                                eng.ws_bytes, eng.stream)
+
+    call()
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    eng.model.profile_reset()
+    eng.model.profile_enable(True)
+    call()
+    torch.cuda.synchronize()
+    prof = eng.model.profile_read()
+    eng.model.profile_enable(False)
+    rows = [t for _ in range(n) for t in range(count)]      # every row's position
+    per = rf.per_class_summary(cfg, prof, rows)
+    gemm_ms = sum(per[k]["total_ms"] for k in GEMM_CLASSES if k in per and k != "gemm_head")
+    gemm_flops = sum(rf.kernel_flops(cfg, k, rows) * cfg.n_layers for k in GEMM_CLASSES if k != "gemm_head")
+    out = {"lanes": n, "prompt_tokens": count, "rows": R, "ms_per_call": round(ms, 3),
+           "prompt_tok_s": round(R / (ms * 1e-3), 1),
+           "gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (rf.MFMA_PEAK_TFLOPS["bf16"] * 1e12), 4),
+           "kernels_ms": {k: round(v["total_ms"], 3) for k, v in per.items()}}
+    log("prefill %d lanes x %d tokens: %.1f ms per call, %.0f prompt tok/s, layer projections at %.1f%% of "
+        "bf16 MFMA peak" % (n, count, ms, out["prompt_tok_s"], 100 * out["gemm_mfma_util"]))
+    del eng
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
 def q8_leg(args, rf, log):
     """The pages' own benchmark shape: SmolLM2-135M with Q8_0 weights, lanes holding 16 positions
     (the prompt length of that benchmark; synthetic f32 K/V, seed 3), one decode step per lane, at
@@ -236,6 +291,8 @@ def main() -> int:
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the wide-batch leg (B = 256 and 512 with KV U[128,4096], one paged pool) "
                          "that reports the projections' bf16 MFMA utilisation")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the batched prefill leg (8 lanes x 512-token prompts in one call)")
     ap.add_argument("--no-trace", action="store_true",
                     help="skip the continuous-batching trace leg (8 lanes, 64 Poisson-arriving jobs, ~40 s)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -329,6 +386,10 @@ def main() -> int:
         torch.cuda.empty_cache()
         wide = wide_leg(cfg, dw, args, rf, log)
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_leg(cfg, dw, args, rf, log)
+
     trace = None
     if not args.no_trace:
         trace = trace_leg(cfg, dw, rf, log)
@@ -368,6 +429,7 @@ def main() -> int:
         "context_q8_smollm135m": q8,
         "wide": None if wide is None else [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                                            for r in wide],
+        "prefill": prefill,
         "trace_c5": trace,
     }
     print(json.dumps(out), flush=True)

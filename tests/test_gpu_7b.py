@@ -148,3 +148,42 @@ def test_mistral7b_wide_batches_bit_identical_to_lane_alone(device_weights_7b):
         for b in WIDE_SAMPLE:
             assert np.array_equal(lg[b].view(np.uint32), alone[b].view(np.uint32)), (b, B)
     del eng
+
+
+PREFILL_COUNTS = [512, 1, 700, 64, 65, 1000, 300, 1454]   # 4096 rows in one call
+PREFILL_CHECK = [0, 1, 3, 4, 7]
+
+
+def test_mistral7b_prefill_4096_rows_bit_identical_to_decode(device_weights_7b):
+    """One batched prefill call of 4096 rows (eight lanes, ragged prompts from
+    empty caches) at the 7B shape: the projections run as 128-lane panels over
+    the rows.  Sampled lanes' last-token logits and caches must be bitwise
+    equal to the same lane fed its prompt one decode step at a time."""
+    import torch
+    from continuous_batching_decode_step_amd.driver import Engine
+    cfg = synth.MISTRAL7B
+    n = len(PREFILL_COUNTS)
+    R = sum(PREFILL_COUNTS)
+    max_seq = max(PREFILL_COUNTS)
+    prompts = [synth.uniform_int(1, 1000 + b, PREFILL_COUNTS[b], 0, cfg.vocab - 1) for b in range(n)]
+    eng = Engine(cfg, device_weights_7b, n, max_seq, max_batch=R)
+    lanes = [eng.arena.lane_alloc() for _ in range(n)]
+    say("7B prefill: %d rows in one call" % R)
+    pos = np.zeros(n, np.int32)
+    am, lg = eng.prefill_sync(lanes, pos, prompts, want_logits=True)
+    assert np.array_equal(pos, PREFILL_COUNTS) and np.array_equal(am, np.argmax(lg, axis=1))
+    kv = {b: eng.kv_export(lanes[b]) for b in PREFILL_CHECK}
+    ref = Engine(cfg, device_weights_7b, 1, max_seq, max_batch=1)
+    for b in PREFILL_CHECK:
+        say("7B prefill: lane %d (%d tokens) fed one step at a time" % (b, PREFILL_COUNTS[b]))
+        l0 = ref.arena.lane_alloc()
+        p = np.zeros(1, np.int32)
+        for t in prompts[b][:-1]:
+            ref.step([l0], p, [int(t)])
+        _, lg1 = ref.step_sync([l0], p, [int(prompts[b][-1])], want_logits=True)
+        assert np.array_equal(lg1[0].view(np.uint32), lg[b].view(np.uint32)), b
+        rk, rv = ref.kv_export(l0)
+        assert np.array_equal(rk, kv[b][0]) and np.array_equal(rv, kv[b][1]), b
+        ref.arena.lane_evict(l0)
+    del eng, ref
+    torch.cuda.empty_cache()

@@ -31,7 +31,9 @@ SYMBOLS = [
     "cbd_decode_step_batch", "cbd_decode_step", "cbd_lane_kv_export", "cbd_lane_kv_import", "cbd_set_variant",
     "cbd_lane_truncate", "cbd_profile_enable", "cbd_profile_reset", "cbd_profile_read", "cbd_profile_classes",
     "cbd_profile_class_name", "cbd_set_graph_replay", "cbd_arena_block_bytes", "cbd_arena_n_blocks",
-    "cbd_arena_free_blocks", "cbd_prefill_batch",
+    "cbd_arena_free_blocks", "cbd_prefill_batch", "cbd_sched_create", "cbd_sched_create_device",
+    "cbd_sched_destroy", "cbd_sched_submit", "cbd_sched_tick", "cbd_sched_run", "cbd_sched_get_telemetry",
+    "cbd_sched_job_tokens",
 ]
 
 
@@ -58,6 +60,42 @@ class _Weights(ctypes.Structure):
                 ("attn_norm", ctypes.POINTER(ctypes.c_void_p)), ("ffn_norm", ctypes.POINTER(ctypes.c_void_p)),
                 ("w_qkv", ctypes.POINTER(_Matrix)), ("w_o", ctypes.POINTER(_Matrix)),
                 ("w_gu", ctypes.POINTER(_Matrix)), ("w_down", ctypes.POINTER(_Matrix))]
+
+
+# scheduler (host policy over the step)
+SCHED_DECISIONS = {0: "QUEUED", 1: "REJECTED_KV_BUDGET", 2: "REJECTED_SCRATCH_BUDGET", 3: "REJECTED_DUPLICATE",
+                   4: "REJECTED_QUEUE_FULL"}
+_P32 = ctypes.POINTER(ctypes.c_int32)
+PREFILL_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int, _P32, _P32, _P32, _P32, _P32)
+DECODE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int, _P32, _P32, _P32, _P32)
+ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, _P32)
+EVICT_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32)
+
+
+class SchedBudget(ctypes.Structure):
+    _fields_ = [("weight_bytes", ctypes.c_size_t), ("kv_budget_bytes", ctypes.c_size_t),
+                ("kv_bytes_per_token", ctypes.c_size_t), ("scratch_per_session", ctypes.c_size_t),
+                ("scratch_budget_bytes", ctypes.c_size_t), ("max_active", ctypes.c_int),
+                ("max_queue", ctypes.c_int), ("max_batch", ctypes.c_int),
+                ("max_prefill_tokens_per_tick", ctypes.c_int)]
+
+
+class SchedEngine(ctypes.Structure):
+    _fields_ = [("ctx", ctypes.c_void_p), ("prefill", PREFILL_FN), ("decode", DECODE_FN),
+                ("lane_alloc", ALLOC_FN), ("lane_evict", EVICT_FN)]
+
+
+class SchedTelemetry(ctypes.Structure):
+    _fields_ = [("ticks", ctypes.c_longlong), ("decode_ticks", ctypes.c_longlong), ("active", ctypes.c_int),
+                ("queued", ctypes.c_int), ("finished", ctypes.c_int), ("effective_active_cap", ctypes.c_int),
+                ("occupancy_last", ctypes.c_int), ("occupancy_max", ctypes.c_int),
+                ("occupancy_avg", ctypes.c_double), ("kv_bytes", ctypes.c_size_t),
+                ("kv_peak_bytes", ctypes.c_size_t), ("kv_budget_bytes", ctypes.c_size_t),
+                ("scratch_bytes", ctypes.c_size_t), ("scratch_budget_bytes", ctypes.c_size_t),
+                ("weight_bytes", ctypes.c_size_t), ("prefill_tokens", ctypes.c_longlong),
+                ("decode_tokens", ctypes.c_longlong), ("rejected", ctypes.c_longlong),
+                ("rejected_kv", ctypes.c_longlong), ("rejected_scratch", ctypes.c_longlong),
+                ("rejected_duplicate", ctypes.c_longlong), ("rejected_queue_full", ctypes.c_longlong)]
 
 
 _lib = None
@@ -110,6 +148,17 @@ def lib():
         L.cbd_profile_classes.argtypes = []
         L.cbd_profile_class_name.argtypes = [i32]
         L.cbd_profile_class_name.restype = ctypes.c_char_p
+        L.cbd_sched_create.argtypes = [ctypes.POINTER(SchedBudget), ctypes.POINTER(SchedEngine), ctypes.POINTER(vp)]
+        L.cbd_sched_create_device.argtypes = [ctypes.POINTER(SchedBudget), vp, vp, vp, sz, vp, vp, vp,
+                                              ctypes.POINTER(vp)]
+        L.cbd_sched_destroy.argtypes = [vp]
+        L.cbd_sched_destroy.restype = None
+        L.cbd_sched_submit.argtypes = [vp, ctypes.c_longlong, pi32, i32, i32, ctypes.POINTER(ctypes.c_int)]
+        L.cbd_sched_tick.argtypes = [vp, ctypes.POINTER(ctypes.c_int)]
+        L.cbd_sched_run.argtypes = [vp, ctypes.c_longlong]
+        L.cbd_sched_get_telemetry.argtypes = [vp, ctypes.POINTER(SchedTelemetry)]
+        L.cbd_sched_job_tokens.argtypes = [vp, ctypes.c_longlong, pi32, i32, ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]
         _lib = L
     return _lib
 
@@ -377,3 +426,66 @@ class Arena:
 
     def kv_import(self, lane: int, length: int, k_src, v_src, stream=None):
         _check(lib().cbd_lane_kv_import(self.h, lane, length, _ptr(k_src), _ptr(v_src), _stream(stream)))
+
+
+class Scheduler:
+    """cbd_sched: the continuous-batching host policy (admission budgets, decode first then bounded
+    prefill, release on completion, telemetry).  engine: a dict of Python callables
+    {prefill(n, lanes, positions, counts, tokens, next) -> int, decode(B, lanes, positions, tokens, next) -> int,
+    lane_alloc(lane_out) -> int, lane_evict(lane) -> int} taking ctypes int32 pointers, or None with
+    device=(model, arena, workspace, logits, argmax, stream) for the decode path of this library."""
+
+    def __init__(self, budget: dict, engine: Optional[dict] = None, device=None):
+        b = SchedBudget(**budget)
+        h = ctypes.c_void_p()
+        if engine is not None:
+            self._cb = SchedEngine(None, PREFILL_FN(lambda c, *a: engine["prefill"](*a)),
+                                   DECODE_FN(lambda c, *a: engine["decode"](*a)),
+                                   ALLOC_FN(lambda c, *a: engine["lane_alloc"](*a)),
+                                   EVICT_FN(lambda c, *a: engine["lane_evict"](*a)))
+            _check(lib().cbd_sched_create(ctypes.byref(b), ctypes.byref(self._cb), ctypes.byref(h)))
+        else:
+            model, arena, ws, logits, argmax, stream = device
+            self._keep = device
+            wsb = ws.numel() * ws.element_size()
+            _check(lib().cbd_sched_create_device(ctypes.byref(b), model.h, arena.h, _ptr(ws), wsb, _ptr(logits),
+                                                 _ptr(argmax), _stream(stream), ctypes.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().cbd_sched_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, job_id: int, prompt, max_new: int) -> str:
+        p = _i32(prompt)
+        d = ctypes.c_int()
+        _check(lib().cbd_sched_submit(self.h, int(job_id), _pi32(p), len(p), int(max_new), ctypes.byref(d)))
+        return SCHED_DECISIONS[d.value]
+
+    def tick(self) -> bool:
+        w = ctypes.c_int()
+        _check(lib().cbd_sched_tick(self.h, ctypes.byref(w)))
+        return bool(w.value)
+
+    def run(self, max_ticks: int = 1 << 40):
+        _check(lib().cbd_sched_run(self.h, int(max_ticks)))
+
+    def telemetry(self) -> dict:
+        t = SchedTelemetry()
+        _check(lib().cbd_sched_get_telemetry(self.h, ctypes.byref(t)))
+        return {k: getattr(t, k) for k, _ in SchedTelemetry._fields_}
+
+    def job_tokens(self, job_id: int):
+        n, done = ctypes.c_int(), ctypes.c_int()
+        _check(lib().cbd_sched_job_tokens(self.h, int(job_id), None, 0, ctypes.byref(n), ctypes.byref(done)))
+        out = np.zeros(max(1, n.value), np.int32)
+        _check(lib().cbd_sched_job_tokens(self.h, int(job_id), _pi32(out), n.value, ctypes.byref(n),
+                                          ctypes.byref(done)))
+        return out[:n.value].tolist(), bool(done.value)

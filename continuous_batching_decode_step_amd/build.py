@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcbd.so")
-SOURCES = ["cbd_runtime.hip", "cbd_gemm.hip", "cbd_attn.hip", "cbd_misc.hip"]
+SOURCES = ["cbd_runtime.hip", "cbd_gemm.hip", "cbd_attn.hip", "cbd_misc.hip", "cbd_sched.hip"]
 
 
 def hipcc() -> str:

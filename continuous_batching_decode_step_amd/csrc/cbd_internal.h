@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct cbd_arena;  // include/cbd.h
+
 namespace cbd {
 
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_Q8 = 2 };
@@ -145,6 +147,10 @@ hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, cons
                        void* xn, hipStream_t st);
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st);
+// Record a formatted message as the calling thread's last error; returns code.
+int report_error(int code, const char* fmt, ...);
+// KV bytes of one position of one lane in an arena (K and V, every layer and head).
+size_t arena_kv_bytes_per_token(const cbd_arena* a);
 // Copy one lane's K or V rows [L * Hkv][len][hd] (device, contiguous) into its
 // blocks of a layer-major pool (to_pool), or back; blocks: the lane's block ids
 // on the device, one per 64 positions.

@@ -1039,3 +1039,21 @@ int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, co
 }
 
 }  // extern "C"
+
+namespace cbd {
+
+int report_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  return fail(code, "%s", buf);
+}
+
+size_t arena_kv_bytes_per_token(const cbd_arena* a) {
+  const cbd_config& c = a->m->c;
+  return 2 * (size_t)c.n_layers * c.n_kv_heads * c.head_dim * a->m->kvb;
+}
+
+}  // namespace cbd

@@ -265,6 +265,114 @@ int cbd_set_graph_replay(cbd_model* m, int enable);
  * speed only, never a bit of the result.  Errors: CBD_E_ARG. */
 int cbd_set_variant(cbd_model* m, int variant);
 
+/* ---- Continuous-batching scheduler (host policy over the step) ----
+ *
+ * The node-local scheduler of "DGR-012" (section "Summary"): sessions are
+ * admitted against weight, KV, scratch and queue budgets, with an explicit
+ * reason when refused; every tick runs decode first (each decoding session
+ * contributes its next token to one batched step) and then bounded prefill of
+ * waiting sessions; finished sessions release their KV, so the total returns
+ * to zero.  Tick rules:
+ *   1. every decoding session (up to max_batch, least recently decoded
+ *      first) decodes one token; its KV grows by one position;
+ *   2. a session that has produced max_new tokens is released at the end of
+ *      the tick (its lane evicted, its slot free from the next tick);
+ *   3. if slots were free at the start of the tick, waiting sessions are
+ *      prefilled in arrival order into at most that many slots, while their
+ *      prompts fit max_prefill_tokens_per_tick (the first always does) and
+ *      the KV reserved by active sessions plus theirs (prompt + max_new
+ *      positions each) fits the KV budget; a prefill yields the session's
+ *      first token;
+ *   4. telemetry: KV bytes (positions held x kv_bytes_per_token) are taken
+ *      after the releases; occupancy is sessions per decode step, averaged
+ *      over ticks that decode.
+ * The engine is either the decode path of a model and arena
+ * (cbd_sched_create_device) or caller-supplied functions (cbd_sched_create).
+ * Not thread-safe: one caller drives a scheduler. */
+typedef struct cbd_sched cbd_sched;
+
+#define CBD_SCHED_QUEUED 0             /* admitted: waits for a slot */
+#define CBD_SCHED_REJECT_KV 1          /* prompt + max_new positions exceed the KV budget on their own */
+#define CBD_SCHED_REJECT_SCRATCH 2     /* one session's scratch exceeds the scratch envelope */
+#define CBD_SCHED_REJECT_DUPLICATE 3   /* the job id is already known */
+#define CBD_SCHED_REJECT_QUEUE_FULL 4  /* max_queue sessions are waiting (backpressure) */
+
+typedef struct cbd_sched_budget {
+  size_t weight_bytes;             /* resident weights (reported only) */
+  size_t kv_budget_bytes;          /* KV all sessions may hold at once */
+  size_t kv_bytes_per_token;       /* KV of one position of one session (> 0) */
+  size_t scratch_per_session;      /* activation bytes of one active session */
+  size_t scratch_budget_bytes;     /* activation envelope */
+  int max_active;                  /* active sessions (slots, lanes) */
+  int max_queue;                   /* waiting sessions */
+  int max_batch;                   /* sessions per decode step */
+  int max_prefill_tokens_per_tick; /* prompt tokens prefilled per tick (one session always may) */
+} cbd_sched_budget;
+
+/* Caller-supplied engine.  prefill: n sessions' prompts (tokens concatenated,
+ * counts[i] each) into the given lanes at positions[i] (advanced in place);
+ * next[i] = the session's next token.  decode: one token per lane, the same
+ * contract as cbd_decode_step_batch, next[b] = the next token.  lane_alloc /
+ * lane_evict: reserve and release a lane.  Each returns 0 or a negative
+ * error, which the scheduler returns unchanged. */
+typedef struct cbd_sched_engine {
+  void* ctx;
+  int (*prefill)(void* ctx, int n, const int32_t* lanes, int32_t* positions, const int32_t* counts,
+                 const int32_t* tokens, int32_t* next);
+  int (*decode)(void* ctx, int B, const int32_t* lanes, int32_t* positions, const int32_t* tokens,
+                int32_t* next);
+  int (*lane_alloc)(void* ctx, int32_t* lane);
+  int (*lane_evict)(void* ctx, int32_t lane);
+} cbd_sched_engine;
+
+typedef struct cbd_sched_telemetry {
+  long long ticks, decode_ticks;
+  int active, queued, finished, effective_active_cap;
+  int occupancy_last, occupancy_max;
+  double occupancy_avg;
+  size_t kv_bytes, kv_peak_bytes, kv_budget_bytes;
+  size_t scratch_bytes, scratch_budget_bytes, weight_bytes;
+  long long prefill_tokens, decode_tokens;
+  long long rejected, rejected_kv, rejected_scratch, rejected_duplicate, rejected_queue_full;
+} cbd_sched_telemetry;
+
+/* A scheduler over caller-supplied engine functions (copied).  The
+ * effective active cap is min(max_active, scratch_budget_bytes /
+ * scratch_per_session).  Errors: CBD_E_ARG (null, kv_bytes_per_token 0,
+ * max_active, max_queue, max_batch or max_prefill_tokens_per_tick below 1). */
+int cbd_sched_create(const cbd_sched_budget* budget, const cbd_sched_engine* engine, cbd_sched** out);
+
+/* A scheduler whose engine is the decode path: cbd_prefill_batch and
+ * cbd_decode_step_batch on (m, a) with the caller's device workspace (sized for
+ * the most rows a tick runs: the larger of max_batch and the prefill tokens
+ * of one tick), logits [rows, vocab] and argmax [rows] buffers and stream;
+ * greedy tokens are copied to the host after each call.  budget's
+ * kv_bytes_per_token is replaced by the arena's (K and V of every layer).
+ * Errors: as cbd_sched_create. */
+int cbd_sched_create_device(const cbd_sched_budget* budget, cbd_model* m, cbd_arena* a, void* workspace,
+                            size_t workspace_bytes, float* logits, int32_t* argmax, void* stream, cbd_sched** out);
+void cbd_sched_destroy(cbd_sched* s);
+
+/* Submit a job: prompt[n_prompt] (n_prompt >= 1, copied), max_new >= 1 tokens
+ * to generate.  *decision = CBD_SCHED_QUEUED or a CBD_SCHED_REJECT_* reason
+ * (a refusal is not an error).  Errors: CBD_E_ARG. */
+int cbd_sched_submit(cbd_sched* s, long long job_id, const int32_t* prompt, int n_prompt, int max_new,
+                     int* decision);
+
+/* One tick (rules above).  *worked = 0 when there was nothing to do.
+ * Errors: the engine's, unchanged. */
+int cbd_sched_tick(cbd_sched* s, int* worked);
+
+/* Ticks until no session is active or waiting; CBD_E_ARG if that takes more
+ * than max_ticks (a guard against misconfiguration). */
+int cbd_sched_run(cbd_sched* s, long long max_ticks);
+
+int cbd_sched_get_telemetry(const cbd_sched* s, cbd_sched_telemetry* t);
+
+/* Tokens generated so far for a job (up to cap into out), their count in *n,
+ * and *done = 1 once the job has finished.  Errors: CBD_E_ARG (unknown job). */
+int cbd_sched_job_tokens(const cbd_sched* s, long long job_id, int32_t* out, int cap, int* n, int* done);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1012,6 +1012,37 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
   return CBD_OK;
 }
 
+int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream) {
+  int rc = check_lane(a, src);
+  if (rc) return rc;
+  if ((rc = check_lane(a, dst))) return rc;
+  if (src == dst) return fail(CBD_E_ARG, "source and destination are the same lane %d", src);
+  if (n < 0 || n > a->len[src]) return fail(CBD_E_ARG, "n = %d outside [0, %d] for lane %d", n, a->len[src], src);
+  const size_t need = ((size_t)n + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  if (need > a->free_blocks.size() + a->blocks[dst].size())
+    return fail(CBD_E_KV_FULL, "cloning %d positions needs %zu KV blocks, %zu are free", n, need,
+                a->free_blocks.size() + a->blocks[dst].size());
+  lane_keep(a, dst, 0);
+  std::vector<int>& bl = a->blocks[dst];
+  while (bl.size() < need) {
+    bl.push_back(a->free_blocks.back());
+    a->free_blocks.pop_back();
+  }
+  // whole blocks, every layer: one strided copy per block for K and for V
+  const size_t kvb = a->m->kvb;
+  const size_t bbytes = (size_t)a->block_elems * kvb;
+  const size_t lstride = (size_t)a->n_blocks * bbytes;
+  hipStream_t st = (hipStream_t)stream;
+  for (size_t j = 0; j < need; ++j)
+    for (int v = 0; v < 2; ++v) {
+      char* pool = a->base + (v ? a->region_bytes : 0);
+      HIP_TRY(hipMemcpy2DAsync(pool + bl[j] * bbytes, lstride, pool + a->blocks[src][j] * bbytes, lstride, bbytes,
+                               a->m->c.n_layers, hipMemcpyDeviceToDevice, st));
+    }
+  a->len[dst] = n;
+  return CBD_OK;
+}
+
 int cbd_lane_kv_import(cbd_arena* a, int lane, int length, const void* k_src, const void* v_src, void* stream) {
   int rc = check_lane(a, lane);
   if (rc) return rc;

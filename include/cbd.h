@@ -220,6 +220,19 @@ int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lane
  * CBD_E_LANE_NOT_LIVE, CBD_E_HIP. */
 int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* stream);
 
+/* Prefix reuse: live lane dst takes the first n positions (0 <= n <= the
+ * length of live lane src) of src's cache, its own content dropped, and its
+ * length becomes n; src is unchanged.  Each user of "MODEL-BATCHING-RESULTS —
+ * multi-user batched decode, measured" (section "Why in-kernel batching, not
+ * vLLM") keeps a cache of its own that can be cloned for prefix reuse while
+ * decode steps are batched.  Keys are stored rotated at their own positions,
+ * so a prefix at the same positions is a plain copy: dst takes ceil(n / 64)
+ * blocks of the pool and the copies are enqueued on `stream` (later steps on
+ * that stream see them).  Errors: CBD_E_ARG (same lane, n out of range),
+ * CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL (too few free blocks; nothing changes),
+ * CBD_E_HIP. */
+int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream);
+
 /* Load a live lane's KV from k_src, v_src laid out as in export, with
  * `length` positions (<= max_seq), and set its length (taking or returning
  * blocks).  Keys are taken as already rotated.  Synchronous with respect to

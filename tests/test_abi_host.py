@@ -240,3 +240,16 @@ def test_prefill_needing_more_blocks_than_the_pool_changes_nothing():
     # 65 tokens span two blocks, and the other lane needs one more
     assert prefill_err(m, a, [l0, l1], [0, 0], [65, 1], [1] * 66) == "CBD_E_KV_FULL"
     assert a.free_blocks == 2
+
+
+def test_lane_clone_validation():
+    m, a = make_model_arena()
+    l0, l1, l2 = a.lane_alloc(), a.lane_alloc(), a.lane_alloc()
+    a.lane_evict(l2)
+    for args, name in (((l0, l0, 0), "CBD_E_ARG"), ((l0, l1, 1), "CBD_E_ARG"), ((l0, l2, 0), "CBD_E_LANE_NOT_LIVE"),
+                       ((l2, l0, 0), "CBD_E_LANE_NOT_LIVE"), ((l0, 9, 0), "CBD_E_ARG")):
+        with pytest.raises(cbd.CbdError) as e:
+            a.lane_clone(*args, stream=0)
+        assert e.value.name == name, args
+    a.lane_clone(l0, l1, 0, stream=0)  # an empty prefix: no copy
+    assert a.lane_length(l1) == 0 and a.free_blocks == a.n_blocks

@@ -97,3 +97,43 @@ def test_scattered_blocks_match_consecutive_blocks(cfg):
     for l in lanes:
         eng.arena.lane_evict(l)
     assert eng.arena.free_blocks == eng.arena.n_blocks and eng.arena.used_bytes == 0
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=[c.name for c in SHAPES])
+def test_clone_prefix_continues_bitwise(cfg):
+    """Prefix reuse: a lane cloned from another (whole, or a prefix that ends
+    inside a block) continues exactly as the original would, and as a lane
+    that imported the same prefix: same logits bits, same cache."""
+    say("case: %s, clone prefixes" % cfg.name)
+    W = synth.make_weights(cfg)
+    L0, steps = 150, 3
+    eng = engine_for(cfg, W, 4, L0 + steps + 4)
+    a, b, c, d = [eng.arena.lane_alloc() for _ in range(4)]
+    k, v = _kv(cfg, 3, L0)
+    eng.arena.kv_import(a, L0, k, v, eng.stream)
+    toks = synth.uniform_int(1, 1500, steps + 4, 0, cfg.vocab - 1)
+    pos = np.array([L0], np.int32)
+    for s in range(steps):
+        eng.step_sync([a], pos, [int(toks[s])])
+    n = L0 + steps
+    eng.arena.lane_clone(a, b, n, eng.stream)      # the whole lane
+    eng.arena.lane_clone(a, c, 100, eng.stream)    # a prefix ending inside a block
+    ka, va = eng.kv_export(a)
+    kb, vb = eng.kv_export(b)
+    assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    kc, vc = eng.kv_export(c)
+    assert np.array_equal(kc, ka[:, :, :100]) and np.array_equal(vc, va[:, :, :100])
+    # a and b continue in one step: same bits
+    p2 = np.array([n, n], np.int32)
+    _, lg = eng.step_sync([a, b], p2, [int(toks[steps])] * 2, want_logits=True)
+    assert np.array_equal(lg[0].view(np.uint32), lg[1].view(np.uint32))
+    # c continues as a lane that imported the same 100 positions
+    eng.arena.kv_import(d, 100, np.ascontiguousarray(ka[:, :, :100]), np.ascontiguousarray(va[:, :, :100]),
+                        eng.stream)
+    p3 = np.array([100, 100], np.int32)
+    _, lg = eng.step_sync([c, d], p3, [int(toks[steps + 1])] * 2, want_logits=True)
+    assert np.array_equal(lg[0].view(np.uint32), lg[1].view(np.uint32))
+    # eviction returns every block, the clones' included
+    for l in (a, b, c, d):
+        eng.arena.lane_evict(l)
+    assert eng.arena.free_blocks == eng.arena.n_blocks

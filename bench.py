@@ -270,6 +270,36 @@ def trace_leg(cfg, dw, rf, log):
            "roofline_frac": round(t_roof / wall, 4)}
     log("trace C5: %s" % res)
     del eng
+    return res, out
+
+
+def sched_trace_leg(cfg, dw, rf, log, c5_out=None, prefill_cap=1024):
+    """The C5 jobs through the continuous-batching scheduler (cbd_sched over the decode path): the same
+    8 lanes and arrivals (in ticks), but whole prompts prefilled in batched calls (up to prefill_cap
+    prompt tokens per tick) instead of one token per step.  Reports generated tokens per wall-clock
+    second, ticks, occupancy, and whether every job's tokens equal those of the one-token-per-step
+    trace."""
+    import torch
+    import synth
+    from continuous_batching_decode_step_amd.driver import Engine, run_sched_trace
+    jobs = synth.make_trace(cfg)
+    max_seq = max(len(j.prompt) + j.max_new_tokens for j in jobs)
+    rows = max(8, prefill_cap, max(len(j.prompt) for j in jobs))
+    eng = Engine(cfg, dw, 8, max_seq, max_batch=rows)
+    run_sched_trace(eng, synth.make_trace(cfg, n_jobs=2, seed=5), 8, prefill_cap)  # graph capture warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out, tel, idle = run_sched_trace(eng, jobs, 8, prefill_cap)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gen = sum(len(v) for v in out.values())
+    res = {"jobs": len(jobs), "lanes": 8, "prefill_tokens_per_tick": prefill_cap, "ticks": tel["ticks"],
+           "idle_ticks": idle, "decode_ticks": tel["decode_ticks"], "generated": gen,
+           "prompt_tokens": tel["prefill_tokens"], "wall_s": round(wall, 3), "tok_s": round(gen / wall, 1),
+           "mean_decode_occupancy": round(tel["occupancy_avg"], 3),
+           "tokens_equal_c5": None if c5_out is None else all(out[k] == c5_out[k] for k in c5_out)}
+    log("scheduler trace: %s" % res)
+    del eng
     return res
 
 
@@ -294,7 +324,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the batched prefill leg (8 lanes x 512-token prompts in one call)")
     ap.add_argument("--no-trace", action="store_true",
-                    help="skip the continuous-batching trace leg (8 lanes, 64 Poisson-arriving jobs, ~40 s)")
+                    help="skip the continuous-batching trace legs (8 lanes, 64 Poisson-arriving jobs: one token per "
+                         "step, then through the scheduler with batched prefill; ~60 s)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="end with one device-to-device copy of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -390,9 +421,10 @@ def main() -> int:
     if not args.no_prefill:
         prefill = prefill_leg(cfg, dw, args, rf, log)
 
-    trace = None
+    trace = sched = None
     if not args.no_trace:
-        trace = trace_leg(cfg, dw, rf, log)
+        trace, c5_out = trace_leg(cfg, dw, rf, log)
+        sched = sched_trace_leg(cfg, dw, rf, log, c5_out)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -431,6 +463,7 @@ def main() -> int:
                                            for r in wide],
         "prefill": prefill,
         "trace_c5": trace,
+        "sched_trace": sched,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -186,3 +186,33 @@ def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_
     for s, lid in lane_ids.items():
         eng.arena.lane_evict(lid)
     return out, st
+
+
+def run_sched_trace(eng: Engine, jobs, n_lanes: int, prefill_tokens_per_tick: int, max_ticks: int = 10 ** 7):
+    """The same jobs through the continuous-batching scheduler over the decode path (cbd_sched): each
+    job is submitted once the tick count reaches its arrival step; ticks decode first, then prefill
+    whole prompts (up to prefill_tokens_per_tick prompt tokens per tick, one prompt always) into the
+    lanes that were free at the start of the tick.  The engine's workspace must hold the larger of
+    n_lanes and prefill_tokens_per_tick rows (and the longest prompt).  Returns ({job_id: generated
+    tokens}, scheduler telemetry, idle ticks)."""
+    from . import Scheduler
+    b = dict(weight_bytes=0, kv_budget_bytes=1 << 62, kv_bytes_per_token=1, scratch_per_session=0,
+             scratch_budget_bytes=0, max_active=n_lanes, max_queue=max(1, len(jobs)), max_batch=n_lanes,
+             max_prefill_tokens_per_tick=prefill_tokens_per_tick)
+    s = Scheduler(b, device=(eng.model, eng.arena, eng.ws, eng.logits, eng.argmax, eng.stream))
+    pending = sorted(jobs, key=lambda j: (j.arrival_step, j.job_id))
+    qi, tick, idle = 0, 0, 0
+    while tick < max_ticks:
+        while qi < len(pending) and pending[qi].arrival_step <= tick:
+            job = pending[qi]
+            assert s.submit(job.job_id, job.prompt, job.max_new_tokens) == "QUEUED"
+            qi += 1
+        if not s.tick():
+            if qi >= len(pending):
+                break
+            idle += 1
+        tick += 1
+    out = {j.job_id: s.job_tokens(j.job_id)[0] for j in jobs}
+    tel = s.telemetry()
+    s.close()
+    return out, tel, idle

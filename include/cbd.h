@@ -162,7 +162,7 @@ int cbd_arena_n_blocks(const cbd_arena* a);
 int cbd_arena_free_blocks(const cbd_arena* a);
 
 /* Device bytes of the workspace a step of up to max_batch lanes of an arena
- * of max_seq positions needs (activations, split partials, counters,
+ * of max_seq positions needs (activations, split partials, attention partials,
  * per-step metadata).  Returns 0 for invalid arguments. */
 size_t cbd_workspace_bytes(const cbd_model* m, int max_batch, int max_seq);
 
@@ -175,8 +175,8 @@ size_t cbd_workspace_bytes(const cbd_model* m, int max_batch, int max_seq);
  * positions[b] of every layer, attends over slots [0, positions[b]] of its own
  * lane only, and its logits land in row b.  workspace: device memory of
  * workspace_bytes >= cbd_workspace_bytes(m, B, arena max_seq), used by one
- * model at a time; the library keeps counters in it that it clears on first
- * use of each workspace address.
+ * model at a time; nothing in it persists between steps (each step writes
+ * what it reads).
  * Errors: CBD_E_ARG, CBD_E_DUP_LANE, CBD_E_LANE_NOT_LIVE, CBD_E_POS_MISMATCH,
  * CBD_E_KV_FULL, CBD_E_TOKEN, CBD_E_WORKSPACE, CBD_E_HIP. */
 int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,

@@ -60,3 +60,23 @@ def test_trace_jobs_equal_serial_runs(trace_run, quarter):
             say("trace: job %d (prompt %d, %d new) serial %s" % (
                 j.job_id, len(j.prompt), j.max_new_tokens, "identical" if same else "DIFFERS"))
         assert same, j.job_id
+
+
+def test_scheduler_with_prefill_gives_the_trace_tokens(trace_run, device_weights_7b):
+    """The same jobs through the continuous-batching scheduler (cbd_sched over the decode path), whose
+    ticks prefill whole prompts in batched calls: every job's tokens equal the one-token-per-step
+    trace's, and the arena ends empty."""
+    from continuous_batching_decode_step_amd.driver import Engine, run_sched_trace
+    _, jobs, out, st = trace_run
+    cfg = synth.MISTRAL7B
+    max_seq = max(len(j.prompt) + j.max_new_tokens for j in jobs)
+    rows = max(len(j.prompt) for j in jobs)
+    eng = Engine(cfg, device_weights_7b, N_LANES, max_seq, max_batch=max(rows, 1024))
+    got, tel, idle = run_sched_trace(eng, jobs, N_LANES, 1024)
+    say("scheduler trace: %d ticks (%d idle, %d decoding), mean decode occupancy %.2f, against %d steps" % (
+        tel["ticks"], idle, tel["decode_ticks"], tel["occupancy_avg"], st.steps))
+    for j in jobs:
+        assert got[j.job_id] == out[j.job_id], j.job_id
+    assert tel["finished"] == len(jobs) and tel["kv_bytes"] == 0
+    assert eng.arena.used_bytes == 0 and eng.arena.live_lanes == 0
+    del eng

@@ -134,6 +134,7 @@ def wide_leg(cfg, dw, args, rf, log):
     blocks = int(((lens + 1 + 63) // 64).sum())  # each lane's blocks, slot len_b included
     eng = Engine(cfg, dw, n, int(lens.max()) + 1, max_batch=n, kv_blocks=blocks)
     eng.model.set_variant(args.variant)
+    eng.model.set_graph_replay(args.graph)
     lanes = [eng.arena.lane_alloc() for _ in range(n)]
     t0 = time.time()
     for b in range(n):
@@ -170,6 +171,7 @@ def prefill_leg(cfg, dw, args, rf, log, n=8, count=512):
     toks = np.concatenate(prompts).astype(np.int32)
     eng = Engine(cfg, dw, n, count, max_batch=R)
     eng.model.set_variant(args.variant)
+    eng.model.set_graph_replay(args.graph)
     lanes = [eng.arena.lane_alloc() for _ in range(n)]
     stream = torch.cuda.current_stream()
 
@@ -227,6 +229,7 @@ def q8_leg(args, rf, log):
     lens = np.full(Bmax, ctx, dtype=np.int64)
     toks = synth.step_tokens(cfg, Bmax)
     eng = Engine(cfg, dw, Bmax, ctx + 1, max_batch=Bmax)
+    eng.model.set_graph_replay(args.graph)
     lanes = [eng.arena.lane_alloc() for _ in range(Bmax)]
     for b in range(Bmax):
         k, v = synth.lane_kv_f32(cfg, b, ctx)
@@ -316,6 +319,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
                     help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each decode step as a captured HIP graph (cbd_set_graph_replay) instead of "
+                         "plain launches")
     ap.add_argument("--no-q8", action="store_true",
                     help="skip the SmolLM2-135M Q8_0 leg (decode steps at 16-position contexts, B = 1..960)")
     ap.add_argument("--no-wide", action="store_true",
@@ -355,6 +361,7 @@ def main() -> int:
     max_seq = int(lens.max()) + 1
     eng = Engine(cfg, dw, n_lanes, max_seq, max_batch=max(batches))
     eng.model.set_variant(args.variant)
+    eng.model.set_graph_replay(args.graph)
     lanes = [eng.arena.lane_alloc() for _ in range(n_lanes)]
     t0 = time.time()
     for b in range(n_lanes):

@@ -98,7 +98,7 @@ struct cbd_model {
   };
   std::vector<std::pair<GraphKey, hipGraphExec_t>> graphs;
   hipStream_t cap_stream = nullptr;
-  bool use_graphs = true;
+  bool use_graphs = false;
   // pinned staging for per-step metadata
   void* slot[NSLOT] = {};
   size_t slot_bytes[NSLOT] = {};

@@ -261,11 +261,13 @@ int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launche
 int cbd_profile_classes(void);
 const char* cbd_profile_class_name(int cls);
 
-/* Step launch mode of this model: 1 (default) = each step's kernel sequence is
- * captured once per (B, workspace, arena, outputs) into a HIP graph and
- * replayed on the caller's stream; 0 = plain kernel launches.  Both run the
+/* Step launch mode of this model: 0 (default) = plain kernel launches; 1 =
+ * each decode step's kernel sequence is captured once per (B, workspace,
+ * arena, outputs) into a HIP graph and replayed on the caller's stream (for
+ * callers whose host thread cannot keep up with plain launches).  Both run the
  * same kernels with the same arguments, so results are bitwise identical.
- * While profiling is enabled, steps launch plainly.  Errors: CBD_E_ARG. */
+ * While profiling is enabled, and for prefill, steps launch plainly.
+ * Errors: CBD_E_ARG. */
 int cbd_set_graph_replay(cbd_model* m, int enable);
 
 /* Projection kernel family for steps of this model: 0 = automatic by batch

@@ -214,6 +214,36 @@ def prefill_leg(cfg, dw, args, rf, log, n=8, count=512):
     return out
 
 
+def clone_leg(cfg, dw, log, n=4096, reps=5):
+    """Prefix reuse at the 7B shape: cbd_lane_clone of an n-position lane (whole 64-position blocks of
+    every layer, K and V, one copy kernel).  Reports the time per clone and the HBM rate of the copy
+    (every byte read once and written once) against 8 TB/s."""
+    import gc
+    import torch
+    import synth
+    import continuous_batching_decode_step_amd as cbd
+    from continuous_batching_decode_step_amd.driver import Engine
+    eng = Engine(cfg, dw, 2, n, max_batch=1)
+    a, b = eng.arena.lane_alloc(), eng.arena.lane_alloc()
+    k, v = synth.lane_kv_bf16(cfg, 0, n)
+    eng.arena.kv_import(a, n, k, v, eng.stream)
+    eng.arena.lane_clone(a, b, n, eng.stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        eng.arena.lane_clone(a, b, n, eng.stream)  # synchronous
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    moved = 2 * ((n + 63) // 64) * cbd.arena_block_bytes(cfg)  # read + write
+    out = {"positions": n, "bytes_moved": moved, "ms_per_clone": round(ms, 3),
+           "GBs": round(moved / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 8e12, 4)}
+    log("clone of a %d-position lane: %.3f ms, %.0f GB/s (%.1f%% of 8 TB/s; wall clock, host sync included)" % (
+        n, ms, out["GBs"], 100 * out["frac_of_hbm_peak"]))
+    del eng
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
 def q8_leg(args, rf, log):
     """The pages' own benchmark shape: SmolLM2-135M with Q8_0 weights, lanes holding 16 positions
     (the prompt length of that benchmark; synthetic f32 K/V, seed 3), one decode step per lane, at
@@ -328,7 +358,8 @@ def main() -> int:
                     help="skip the wide-batch leg (B = 256 and 512 with KV U[128,4096], one paged pool) "
                          "that reports the projections' bf16 MFMA utilisation")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the batched prefill leg (8 lanes x 512-token prompts in one call)")
+                    help="skip the batched prefill leg (8 lanes x 512-token prompts in one call) and the prefix "
+                         "clone leg (a 4096-position lane)")
     ap.add_argument("--no-trace", action="store_true",
                     help="skip the continuous-batching trace legs (8 lanes, 64 Poisson-arriving jobs: one token per "
                          "step, then through the scheduler with batched prefill; ~60 s)")
@@ -424,9 +455,10 @@ def main() -> int:
         torch.cuda.empty_cache()
         wide = wide_leg(cfg, dw, args, rf, log)
 
-    prefill = None
+    prefill = clone = None
     if not args.no_prefill:
         prefill = prefill_leg(cfg, dw, args, rf, log)
+        clone = clone_leg(cfg, dw, log)
 
     trace = sched = None
     if not args.no_trace:
@@ -469,6 +501,7 @@ def main() -> int:
         "wide": None if wide is None else [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                                            for r in wide],
         "prefill": prefill,
+        "clone": clone,
         "trace_c5": trace,
         "sched_trace": sched,
     }

@@ -423,7 +423,7 @@ class Arena:
         return lib().cbd_arena_free_blocks(self.h)
 
     def lane_clone(self, src: int, dst: int, n: int, stream=None):
-        """dst := the first n positions of src (prefix reuse), enqueued on stream."""
+        """dst := the first n positions of src (prefix reuse); synchronous with respect to stream."""
         _check(lib().cbd_lane_clone(self.h, src, dst, n, _stream(stream)))
 
     def kv_export(self, lane: int, k_dst, v_dst, stream=None):

@@ -147,6 +147,10 @@ hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, cons
                        void* xn, hipStream_t st);
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st);
+// Copy blocks src[j] -> dst[j] (j < n) of a layer-major pool in every layer,
+// K (at base) and V (at base + half); the block lists are on the device.
+hipError_t launch_kv_blocks(char* base, long long half, const int* src, const int* dst, int n, int L,
+                            long long lstride, long long bbytes, hipStream_t st);
 // Record a formatted message as the calling thread's last error; returns code.
 int report_error(int code, const char* fmt, ...);
 // KV bytes of one position of one lane in an arena (K and V, every layer and head).

@@ -147,6 +147,35 @@ hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int len, in
   return hipGetLastError();
 }
 
+// Copy whole blocks of a layer-major pool, K and V: block src[j] to block
+// dst[j] in every layer, 16 bytes per thread.  Unit u covers (pool half v,
+// layer l, pair j, 16-byte word w) with w fastest.
+__global__ __launch_bounds__(256) void k_kv_blocks(char* base, long long half, const int* src, const int* dst,
+                                                   int n, int L, long long lstride, long long bbytes) {
+  const long long W = bbytes / 16;
+  const long long total = 2LL * L * n * W;
+  for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+       u += (long long)gridDim.x * blockDim.x) {
+    const long long w = u % W;
+    const long long r = u / W;
+    const int j = (int)(r % n);
+    const int l = (int)((r / n) % L);
+    const int v = (int)(r / ((long long)n * L));
+    char* p = base + v * half + l * lstride;
+    *(uint4*)(p + dst[j] * bbytes + w * 16) = *(const uint4*)(p + src[j] * bbytes + w * 16);
+  }
+}
+
+hipError_t launch_kv_blocks(char* base, long long half, const int* src, const int* dst, int n, int L,
+                            long long lstride, long long bbytes, hipStream_t st) {
+  const long long total = 2LL * L * n * (bbytes / 16);
+  if (total == 0) return hipSuccess;
+  long long wgs = (total + 255) / 256;
+  if (wgs > 16384) wgs = 16384;
+  hipLaunchKernelGGL(k_kv_blocks, dim3((unsigned)wgs), dim3(256), 0, st, base, half, src, dst, n, L, lstride, bbytes);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* tokens, const int* pos, int B, int d,
                         int hd, float theta, float* x, float* ssq, float2* rope, hipStream_t st) {
   switch (wt) {

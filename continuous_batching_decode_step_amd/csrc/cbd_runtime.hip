@@ -1028,17 +1028,29 @@ int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream) {
     bl.push_back(a->free_blocks.back());
     a->free_blocks.pop_back();
   }
-  // whole blocks, every layer: one strided copy per block for K and for V
-  const size_t kvb = a->m->kvb;
-  const size_t bbytes = (size_t)a->block_elems * kvb;
-  const size_t lstride = (size_t)a->n_blocks * bbytes;
+  // whole blocks, every layer, K and V: one kernel over the block pairs, whose
+  // lists go to the device through the arena's staging buffer
   hipStream_t st = (hipStream_t)stream;
-  for (size_t j = 0; j < need; ++j)
-    for (int v = 0; v < 2; ++v) {
-      char* pool = a->base + (v ? a->region_bytes : 0);
-      HIP_TRY(hipMemcpy2DAsync(pool + bl[j] * bbytes, lstride, pool + a->blocks[src][j] * bbytes, lstride, bbytes,
-                               a->m->c.n_layers, hipMemcpyDeviceToDevice, st));
+  if (need > 0) {
+    const size_t lb = need * sizeof(int);
+    if (a->stage_bytes < 2 * lb) {
+      HIP_TRY(hipStreamSynchronize(st));
+      if (a->stage) HIP_TRY(hipFree(a->stage));
+      a->stage = nullptr;
+      a->stage_bytes = 0;
+      HIP_TRY(hipMalloc(&a->stage, 2 * lb));
+      a->stage_bytes = 2 * lb;
     }
+    std::vector<int> pairs(a->blocks[src].begin(), a->blocks[src].begin() + need);
+    pairs.insert(pairs.end(), bl.begin(), bl.end());
+    int* d = (int*)a->stage;
+    HIP_TRY(hipMemcpyAsync(d, pairs.data(), 2 * lb, hipMemcpyHostToDevice, st));
+    const long long bbytes = a->block_elems * (long long)a->m->kvb;
+    HIP_TRY(launch_kv_blocks(a->base, (long long)a->region_bytes, d, d + need, (int)need, a->m->c.n_layers,
+                             (long long)a->n_blocks * bbytes, bbytes, st));
+    // the staging buffer and the host list are reused by the next call
+    HIP_TRY(hipStreamSynchronize(st));
+  }
   a->len[dst] = n;
   return CBD_OK;
 }

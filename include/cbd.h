@@ -227,8 +227,9 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
  * vLLM") keeps a cache of its own that can be cloned for prefix reuse while
  * decode steps are batched.  Keys are stored rotated at their own positions,
  * so a prefix at the same positions is a plain copy: dst takes ceil(n / 64)
- * blocks of the pool and the copies are enqueued on `stream` (later steps on
- * that stream see them).  Errors: CBD_E_ARG (same lane, n out of range),
+ * blocks of the pool, copied by one kernel on `stream`; synchronous with
+ * respect to `stream` (the block lists go through the arena's staging buffer,
+ * as for import and export).  Errors: CBD_E_ARG (same lane, n out of range),
  * CBD_E_LANE_NOT_LIVE, CBD_E_KV_FULL (too few free blocks; nothing changes),
  * CBD_E_HIP. */
 int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream);

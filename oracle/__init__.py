@@ -85,6 +85,8 @@ def lib(accumulate: str = "exact"):
         L.orc_lane_set_kv.restype = i32
         L.orc_lane_get_kv.argtypes = [vp, i32, vp, vp]
         L.orc_lane_get_kv.restype = i32
+        L.orc_lane_evict_span.argtypes = [vp, vp, i32, i32]
+        L.orc_lane_evict_span.restype = i32
         L.orc_step.argtypes = [vp, vp, i32, vp]
         L.orc_step.restype = i32
         L.orc_step_batch.argtypes = [vp, vp, i32, vp, vp]
@@ -259,6 +261,11 @@ class Lane:
 
     def clear(self):
         self.L.orc_lane_clear(self.h)
+
+    def evict_span(self, begin: int, end: int):
+        """Drop positions [begin, end); later entries move down, keys rotated to their new positions."""
+        if self.L.orc_lane_evict_span(self.model.h, self.h, int(begin), int(end)) != 0:
+            raise ValueError("span outside the lane")
 
     @property
     def length(self) -> int:

@@ -343,6 +343,36 @@ static void round_act(const orc_model* m, float* x, int n) {
   for (int i = 0; i < n; ++i) x[i] = orc_round_bf16(x[i]);
 }
 
+/* Evict the span [begin, end) of a lane: the per-user Evict ("quarantine a
+ * poisoned span") of "MODEL-BATCHING-RESULTS — multi-user batched decode,
+ * measured" (section "Why in-kernel batching, not vLLM").  The page keeps
+ * each user's raw keys beside the rotated ones for it; this cache stores keys
+ * rotated at their own positions only, so the reading taken is: entries at
+ * t >= end move to t - d (d = end - begin), their stored keys rotated by the
+ * rotary angle of -d positions (orc_rope at position -d: the composition of
+ * rotations by p and by -d is the rotation by p - d) and rounded to the KV
+ * format; values move unchanged; the length drops by d.  Returns -1 for a
+ * span outside [0, length]. */
+int orc_lane_evict_span(const orc_model* m, orc_lane* ln, int begin, int end) {
+  const orc_config* c = &m->c;
+  if (begin < 0 || end < begin || end > ln->length) return -1;
+  int d = end - begin, hd = c->head_dim, kvd = ln->kvd;
+  if (d == 0) return 0;
+  for (int l = 0; l < ln->L; ++l) {
+    float* Kl = ln->K + (int64_t)l * ln->max_seq * kvd;
+    float* Vl = ln->V + (int64_t)l * ln->max_seq * kvd;
+    for (int t = end; t < ln->length; ++t) {
+      float* kd = Kl + (int64_t)(t - d) * kvd;
+      memcpy(kd, Kl + (int64_t)t * kvd, sizeof(float) * kvd);
+      memcpy(Vl + (int64_t)(t - d) * kvd, Vl + (int64_t)t * kvd, sizeof(float) * kvd);
+      for (int g = 0; g < c->n_kv_heads; ++g) orc_rope(kd + (int64_t)g * hd, hd, -d, c->rope_theta);
+      round_act(m, kd, kvd);
+    }
+  }
+  ln->length -= d;
+  return 0;
+}
+
 static void embed_row(const orc_model* m, int token, float* x) {
   for (int i = 0; i < m->c.d; ++i) x[i] = wval(&m->embed, m->c.wtype, m->c.d, token, i);
 }

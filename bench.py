@@ -238,6 +238,21 @@ def clone_leg(cfg, dw, log, n=4096, reps=5):
            "GBs": round(moved / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 8e12, 4)}
     log("clone of a %d-position lane: %.3f ms, %.0f GB/s (%.1f%% of 8 TB/s; wall clock, host sync included)" % (
         n, ms, out["GBs"], 100 * out["frac_of_hbm_peak"]))
+    # span eviction: drop [1024, 2048) of the clone; the 2048 positions after it move down (keys rotated)
+    b0, e0 = 1024, 2048
+    ev = []
+    for _ in range(reps):
+        eng.arena.lane_clone(a, b, n, eng.stream)
+        t0 = time.perf_counter()
+        eng.arena.lane_evict_span(b, b0, e0, eng.stream)  # synchronous
+        ev.append((time.perf_counter() - t0) * 1e3)
+    ems = float(np.median(ev))
+    per_pos = cbd.arena_block_bytes(cfg) // 64
+    moved_e = 2 * (n - e0) * per_pos  # the moved entries read once and written once
+    out["evict_span"] = {"positions": n, "span": [b0, e0], "moved_positions": n - e0, "bytes_moved": moved_e,
+                         "ms": round(ems, 3), "GBs": round(moved_e / (ems * 1e-3) / 1e9, 1)}
+    log("span eviction [%d, %d) of a %d-position lane: %.3f ms, %.0f GB/s of moved entries (through staging)" % (
+        b0, e0, n, ems, out["evict_span"]["GBs"]))
     del eng
     gc.collect()
     torch.cuda.empty_cache()

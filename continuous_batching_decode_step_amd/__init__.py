@@ -33,7 +33,7 @@ SYMBOLS = [
     "cbd_profile_class_name", "cbd_set_graph_replay", "cbd_arena_block_bytes", "cbd_arena_n_blocks",
     "cbd_arena_free_blocks", "cbd_prefill_batch", "cbd_sched_create", "cbd_sched_create_device",
     "cbd_sched_destroy", "cbd_sched_submit", "cbd_sched_tick", "cbd_sched_run", "cbd_sched_get_telemetry",
-    "cbd_sched_job_tokens", "cbd_lane_clone",
+    "cbd_sched_job_tokens", "cbd_lane_clone", "cbd_lane_evict_span",
 ]
 
 
@@ -149,6 +149,7 @@ def lib():
         L.cbd_profile_class_name.argtypes = [i32]
         L.cbd_profile_class_name.restype = ctypes.c_char_p
         L.cbd_lane_clone.argtypes = [vp, i32, i32, i32, vp]
+        L.cbd_lane_evict_span.argtypes = [vp, i32, i32, i32, vp]
         L.cbd_sched_create.argtypes = [ctypes.POINTER(SchedBudget), ctypes.POINTER(SchedEngine), ctypes.POINTER(vp)]
         L.cbd_sched_create_device.argtypes = [ctypes.POINTER(SchedBudget), vp, vp, vp, sz, vp, vp, vp,
                                               ctypes.POINTER(vp)]
@@ -421,6 +422,10 @@ class Arena:
     @property
     def free_blocks(self) -> int:
         return lib().cbd_arena_free_blocks(self.h)
+
+    def lane_evict_span(self, lane: int, begin: int, end: int, stream=None):
+        """Drop positions [begin, end) of a lane; later entries move down, keys rotated to their new positions."""
+        _check(lib().cbd_lane_evict_span(self.h, lane, begin, end, _stream(stream)))
 
     def lane_clone(self, src: int, dst: int, n: int, stream=None):
         """dst := the first n positions of src (prefix reuse); synchronous with respect to stream."""

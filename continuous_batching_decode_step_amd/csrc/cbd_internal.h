@@ -158,7 +158,11 @@ size_t arena_kv_bytes_per_token(const cbd_arena* a);
 // Copy one lane's K or V rows [L * Hkv][len][hd] (device, contiguous) into its
 // blocks of a layer-major pool (to_pool), or back; blocks: the lane's block ids
 // on the device, one per 64 positions.
-hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows, int Hkv, int row_bytes,
-                          long long lstride, long long bbytes, bool to_pool, hipStream_t st);
+hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
+                          int row_bytes, long long lstride, long long bbytes, bool to_pool, hipStream_t st);
+// Rotate n_vec key vectors of hd elements (bf16 or f32, device) in place by the
+// per-pair (cos, sin) table cs[hd/2] (rotate-half pairs; products and sums
+// rounded to f32 one by one), rounding to the KV format.
+hipError_t launch_kv_rot(char* rows, long long n_vec, int hd, const float2* cs, bool bf16, hipStream_t st);
 
 }  // namespace cbd

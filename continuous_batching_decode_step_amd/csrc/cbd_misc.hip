@@ -113,19 +113,20 @@ __global__ void k_fill_u32(unsigned* p, size_t n, unsigned v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// Move one lane's K or V between rows [n_rows = L * Hkv][len][hd] (contiguous,
-// `rows`) and its blocks in a layer-major pool, 16 bytes per thread: position t
-// of row (l, g) sits at l * lstride + blocks[t / 64] * bbytes + (g * 64 + t % 64)
-// * row_bytes.  row_bytes (hd * element size) is a multiple of 16.
-__global__ __launch_bounds__(256) void k_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows,
-                                                 int Hkv, int row_bytes, long long lstride, long long bbytes,
-                                                 int to_pool) {
+// Move positions [p0, p0 + len) of one lane's K or V between rows
+// [n_rows = L * Hkv][len][hd] (contiguous, `rows`) and its blocks in a
+// layer-major pool, 16 bytes per thread: position p of row (l, g) sits at
+// l * lstride + blocks[p / 64] * bbytes + (g * 64 + p % 64) * row_bytes.
+// row_bytes (hd * element size) is a multiple of 16.
+__global__ __launch_bounds__(256) void k_kv_rows(char* pool, char* rows, const int* blocks, int p0, int len,
+                                                 int n_rows, int Hkv, int row_bytes, long long lstride,
+                                                 long long bbytes, int to_pool) {
   const int W = row_bytes / 16;
   const size_t n = (size_t)n_rows * len * W;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += (size_t)gridDim.x * blockDim.x) {
     const int w = (int)(u % W);
     const size_t tr = u / W;
-    const int t = (int)(tr % len), r = (int)(tr / len);
+    const int t = p0 + (int)(tr % len), r = (int)(tr / len);
     const int l = r / Hkv, g = r % Hkv;
     char* pp = pool + l * lstride + blocks[t >> 6] * bbytes + ((long long)g * 64 + (t & 63)) * row_bytes + w * 16;
     uint4* rp = (uint4*)(rows + u * 16);
@@ -136,14 +137,65 @@ __global__ __launch_bounds__(256) void k_kv_rows(char* pool, char* rows, const i
   }
 }
 
-hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int len, int n_rows, int Hkv, int row_bytes,
-                          long long lstride, long long bbytes, bool to_pool, hipStream_t st) {
+hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
+                          int row_bytes, long long lstride, long long bbytes, bool to_pool, hipStream_t st) {
   const size_t n = (size_t)n_rows * len * (row_bytes / 16);
   if (n == 0) return hipSuccess;
   size_t wgs = (n + 255) / 256;
   if (wgs > 8192) wgs = 8192;
-  hipLaunchKernelGGL(k_kv_rows, dim3((unsigned)wgs), dim3(256), 0, st, pool, rows, blocks, len, n_rows, Hkv,
+  hipLaunchKernelGGL(k_kv_rows, dim3((unsigned)wgs), dim3(256), 0, st, pool, rows, blocks, p0, len, n_rows, Hkv,
                      row_bytes, lstride, bbytes, (int)to_pool);
+  return hipGetLastError();
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Rotate n_vec stored key vectors of hd elements in place by one rotary angle
+// per pair (cs[j] = (cos, sin) for the pair (j, j + hd/2)): (a, b) ->
+// (a c - b s, b c + a s), every product and sum rounded to f32 on its own (no
+// fused multiply-add), then rounded to the KV format (bf16 round-to-nearest-
+// even, or kept in f32).
+__global__ __launch_bounds__(256) void k_kv_rot(char* rows, long long n_vec, int hd, const float2* cs, int bf16) {
+#pragma clang fp contract(off)  // the products must round before the sum (the compiler fuses them otherwise)
+  const int h = hd / 2;
+  const long long n = n_vec * h;
+  for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += (long long)gridDim.x * blockDim.x) {
+    const long long r = u / h;
+    const int j = (int)(u % h);
+    const float2 t = cs[j];
+    float a, b;
+    if (bf16) {
+      const uint16_t* x = (const uint16_t*)rows + r * hd;
+      a = __uint_as_float((unsigned)x[j] << 16);
+      b = __uint_as_float((unsigned)x[j + h] << 16);
+    } else {
+      const float* x = (const float*)rows + r * hd;
+      a = x[j];
+      b = x[j + h];
+    }
+    const float ac = a * t.x, bs = b * t.y, bc = b * t.x, as = a * t.y;
+    const float y0 = ac - bs, y1 = bc + as;
+    if (bf16) {
+      uint16_t* x = (uint16_t*)rows + r * hd;
+      x[j] = f32_to_bf16_rne(y0);
+      x[j + h] = f32_to_bf16_rne(y1);
+    } else {
+      float* x = (float*)rows + r * hd;
+      x[j] = y0;
+      x[j + h] = y1;
+    }
+  }
+}
+
+hipError_t launch_kv_rot(char* rows, long long n_vec, int hd, const float2* cs, bool bf16, hipStream_t st) {
+  const long long n = n_vec * (hd / 2);
+  if (n == 0) return hipSuccess;
+  long long wgs = (n + 255) / 256;
+  if (wgs > 8192) wgs = 8192;
+  hipLaunchKernelGGL(k_kv_rot, dim3((unsigned)wgs), dim3(256), 0, st, rows, n_vec, hd, cs, (int)bf16);
   return hipGetLastError();
 }
 

@@ -988,9 +988,9 @@ static int copy_lane(cbd_arena* a, int lane, int len, char* rows, bool to_pool, 
   HIP_TRY(hipMemcpyAsync(dblk, bl.data(), bl.size() * sizeof(int), hipMemcpyHostToDevice, st));
   if (to_pool) {
     HIP_TRY(hipMemcpyAsync(a->stage, rows, bytes, hipMemcpyDefault, st));
-    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true, st));
+    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, 0, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true, st));
   } else {
-    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false, st));
+    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, 0, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false, st));
     HIP_TRY(hipMemcpyAsync(rows, a->stage, bytes, hipMemcpyDefault, st));
   }
   // the staging buffer (and the block list) are reused by the next copy
@@ -1052,6 +1052,60 @@ int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream) {
     HIP_TRY(hipStreamSynchronize(st));
   }
   a->len[dst] = n;
+  return CBD_OK;
+}
+
+int cbd_lane_evict_span(cbd_arena* a, int lane, int begin, int end, void* stream) {
+  int rc = check_lane(a, lane);
+  if (rc) return rc;
+  const int len = a->len[lane];
+  if (begin < 0 || end < begin || end > len)
+    return fail(CBD_E_ARG, "span [%d, %d) outside [0, %d] for lane %d", begin, end, len, lane);
+  const int d = end - begin, n = len - end;  // span length; entries that move
+  hipStream_t st = (hipStream_t)stream;
+  if (d > 0 && n > 0) {
+    const cbd_config& c = a->m->c;
+    const size_t kvb = a->m->kvb;
+    const int n_rows = c.n_layers * c.n_kv_heads, row_bytes = c.head_dim * (int)kvb, h = c.head_dim / 2;
+    const std::vector<int>& bl = a->blocks[lane];
+    // rotary angle of -d positions per pair: theta_j = theta^(-2j/hd) in double, cos and sin rounded to f32
+    std::vector<float> cs(2 * h);
+    for (int j = 0; j < h; ++j) {
+      const double th = pow((double)c.rope_theta, -(2.0 * (double)j) / (double)c.head_dim);
+      const double ang = (double)(-d) * th;
+      cs[2 * j] = (float)cos(ang);
+      cs[2 * j + 1] = (float)sin(ang);
+    }
+    // staging: the moved rows, the lane's block ids, the angle table
+    const size_t bytes = (size_t)n_rows * n * row_bytes;
+    const size_t boff = (bytes + 255) & ~(size_t)255;
+    const size_t coff = (boff + bl.size() * sizeof(int) + 255) & ~(size_t)255;
+    const size_t need = coff + cs.size() * sizeof(float);
+    if (a->stage_bytes < need) {
+      HIP_TRY(hipStreamSynchronize(st));
+      if (a->stage) HIP_TRY(hipFree(a->stage));
+      a->stage = nullptr;
+      a->stage_bytes = 0;
+      HIP_TRY(hipMalloc(&a->stage, need));
+      a->stage_bytes = need;
+    }
+    int* dblk = (int*)(a->stage + boff);
+    const float2* dcs = (const float2*)(a->stage + coff);
+    HIP_TRY(hipMemcpyAsync(dblk, bl.data(), bl.size() * sizeof(int), hipMemcpyHostToDevice, st));
+    HIP_TRY(hipMemcpyAsync(a->stage + coff, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, st));
+    const long long bbytes = a->block_elems * (long long)kvb;
+    const long long lstride = (long long)a->n_blocks * bbytes;
+    for (int v = 0; v < 2; ++v) {
+      char* pool = a->base + (v ? a->region_bytes : 0);
+      HIP_TRY(launch_kv_rows(pool, a->stage, dblk, end, n, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false,
+                             st));
+      if (!v) HIP_TRY(launch_kv_rot(a->stage, (long long)n_rows * n, c.head_dim, dcs, kvb == 2, st));
+      HIP_TRY(launch_kv_rows(pool, a->stage, dblk, begin, n, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true,
+                             st));
+    }
+    HIP_TRY(hipStreamSynchronize(st));
+  }
+  lane_keep(a, lane, len - d);
   return CBD_OK;
 }
 

@@ -234,6 +234,21 @@ int cbd_lane_kv_export(cbd_arena* a, int lane, void* k_dst, void* v_dst, void* s
  * CBD_E_HIP. */
 int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream);
 
+/* Span eviction: drop positions [begin, end) of live lane `lane` (0 <= begin
+ * <= end <= its length).  The per-user Evict of "MODEL-BATCHING-RESULTS —
+ * multi-user batched decode, measured" (section "Why in-kernel batching, not
+ * vLLM") quarantines a poisoned span of a user's cache while decode steps
+ * stay batched.  Entries after the span move down by d = end - begin, so the
+ * lane's positions stay contiguous and its length drops by d; keys are stored
+ * rotated at their positions, so each moved key is rotated by the rotary angle
+ * of -d positions (theta^(-2j/hd) in double, cos and sin rounded to f32, each
+ * product and sum rounded to f32, then to the KV format); values move
+ * unchanged; blocks past the new length return to the pool.  Synchronous with
+ * respect to `stream` (it moves the entries through the arena's staging
+ * buffer).  Errors: CBD_E_ARG (span out of range), CBD_E_LANE_NOT_LIVE,
+ * CBD_E_HIP. */
+int cbd_lane_evict_span(cbd_arena* a, int lane, int begin, int end, void* stream);
+
 /* Load a live lane's KV from k_src, v_src laid out as in export, with
  * `length` positions (<= max_seq), and set its length (taking or returning
  * blocks).  Keys are taken as already rotated.  Synchronous with respect to

@@ -253,3 +253,15 @@ def test_lane_clone_validation():
         assert e.value.name == name, args
     a.lane_clone(l0, l1, 0, stream=0)  # an empty prefix: no copy
     assert a.lane_length(l1) == 0 and a.free_blocks == a.n_blocks
+
+
+def test_lane_evict_span_validation():
+    m, a = make_model_arena()
+    l0, l1 = a.lane_alloc(), a.lane_alloc()
+    a.lane_evict(l1)
+    a.lane_evict_span(l0, 0, 0, stream=0)  # empty span of an empty lane: nothing to do
+    for args, name in (((l0, 0, 1), "CBD_E_ARG"), ((l0, 1, 0), "CBD_E_ARG"), ((l0, -1, 0), "CBD_E_ARG"),
+                       ((l1, 0, 0), "CBD_E_LANE_NOT_LIVE")):
+        with pytest.raises(cbd.CbdError) as e:
+            a.lane_evict_span(*args, stream=0)
+        assert e.value.name == name, args

@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 
 import continuous_batching_decode_step_amd as cbd
+import oracle
 import synth
-from gpu_helpers import engine_for, say
+from gpu_helpers import TOL_BF16, TOL_F32, engine_for, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +138,44 @@ def test_clone_prefix_continues_bitwise(cfg):
     for l in (a, b, c, d):
         eng.arena.lane_evict(l)
     assert eng.arena.free_blocks == eng.arena.n_blocks
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=[c.name for c in SHAPES])
+def test_evict_span_matches_the_oracle(cfg):
+    """Span eviction: the cache after dropping [37, 101) of a 200-position lane
+    equals the oracle's (moved keys rotated by -64 positions with the same f32
+    arithmetic, values moved), bit for bit; blocks past the new length return
+    to the pool; and the next decode step matches the oracle's step on its
+    evicted lane.  A second eviction of the tail is a truncation."""
+    say("case: %s, span eviction" % cfg.name)
+    W = synth.make_weights(cfg)
+    n0, b, e = 200, 37, 101
+    eng = engine_for(cfg, W, 1, n0 + 2)
+    lane = eng.arena.lane_alloc()
+    k, v = _kv(cfg, 5, n0)
+    eng.arena.kv_import(lane, n0, k, v, eng.stream)
+    free0 = eng.arena.free_blocks
+    eng.arena.lane_evict_span(lane, b, e, eng.stream)
+    n1 = n0 - (e - b)
+    assert eng.arena.lane_length(lane) == n1
+    assert eng.arena.free_blocks == free0 + (n0 + 63) // 64 - (n1 + 63) // 64
+    M = oracle.Model(W)
+    ol = M.lane(n0 + 2)
+    f32 = (lambda a: synth.bf16_to_f32(a)) if cfg.wtype == synth.WTYPE_BF16 else (lambda a: a)
+    ol.set_kv(f32(k), f32(v))
+    ol.evict_span(b, e)
+    ok, ov = ol.get_kv()
+    gk, gv = eng.kv_export(lane)
+    assert np.array_equal(f32(gv), ov)
+    assert np.array_equal(f32(gk), ok), float(np.max(np.abs(f32(gk) - ok)))
+    tok = int(synth.uniform_int(1, 1700, 1, 0, cfg.vocab - 1)[0])
+    p = np.array([n1], np.int32)
+    _, lg = eng.step_sync([lane], p, [tok], want_logits=True)
+    ref = M.step(ol, tok)
+    err = rel_err(lg[0], ref)
+    say("  after eviction: logits max rel %.3g" % err)
+    assert err <= (TOL_BF16 if cfg.wtype == synth.WTYPE_BF16 else TOL_F32)
+    # the tail: a truncation
+    eng.arena.lane_evict_span(lane, 50, n1 + 1, eng.stream)
+    gk2, _ = eng.kv_export(lane)
+    assert eng.arena.lane_length(lane) == 50 and np.array_equal(gk2, gk[:, :, :50])

@@ -2,9 +2,11 @@
 //
 // "MODEL-BATCHING-RESULTS — multi-user batched decode, measured" (section
 // "The lever") keeps attention per user: lane b's queries read only lane b's
-// own cache, over its own length.  Each lane owns a contiguous slab per
-// (layer, KV head) in the arena, so there is no padding and no mask: a lane at
-// position p reads slots [0, p] and writes slot p.
+// own cache, over its own length.  A lane's cache is a list of blocks of a
+// shared pool, one per 64-position chunk; within a block one (layer, KV head)
+// chunk is a contiguous run, and a work item names the blocks of its chunks.
+// There is no padding across lanes: a lane at position p reads slots [0, p]
+// (the tail of its last chunk is masked) and writes slot p.
 //
 // Two kernels produce per-chunk partials.  The matrix-core kernel (bf16 KV,
 // head_dim 64/128, k_attn_mf) takes one workgroup per (lane, KV head, aligned
@@ -198,11 +200,11 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
         if constexpr (KVBF16) {
           const unsigned kw = D == 1 ? knr.w[0] : knr.w[e / 2] >> (16 * (e & 1));
           const unsigned vw = D == 1 ? vnr.w[0] : vnr.w[e / 2] >> (16 * (e & 1));
-          ((uint16_t*)a.kslab)[o + e] = (uint16_t)kw;
-          ((uint16_t*)a.vslab)[o + e] = (uint16_t)vw;
+          ((uint16_t*)a.kpool)[o + e] = (uint16_t)kw;
+          ((uint16_t*)a.vpool)[o + e] = (uint16_t)vw;
         } else {
-          ((unsigned*)a.kslab)[o + e] = knr.w[e];
-          ((unsigned*)a.vslab)[o + e] = vnr.w[e];
+          ((unsigned*)a.kpool)[o + e] = knr.w[e];
+          ((unsigned*)a.vpool)[o + e] = vnr.w[e];
         }
       }
     }
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const int key = kbeg + 4 * (i0 + i) + r;
-      kr[i] = load_raw<D, KVBF16>(a.kslab, base + (long long)min(key, kend - 1) * HD + d0);
+      kr[i] = load_raw<D, KVBF16>(a.kpool, base + (long long)min(key, kend - 1) * HD + d0);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < KB; ++i) {
     const int key = kbeg + 4 * i + r;
-    vr[i] = load_raw<D, KVBF16>(a.vslab, base + (long long)min(key, kend - 1) * HD + d0);
+    vr[i] = load_raw<D, KVBF16>(a.vpool, base + (long long)min(key, kend - 1) * HD + d0);
   }
   __builtin_amdgcn_sched_barrier(0);
   float sc[G];
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
         const int key = kbeg + 4 * (i0 + i) + r;
-        vr[i] = load_raw<D, KVBF16>(a.vslab, base + (long long)min(key, kend - 1) * HD + d0);
+        vr[i] = load_raw<D, KVBF16>(a.vpool, base + (long long)min(key, kend - 1) * HD + d0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -369,19 +371,20 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 // layout.
 __device__ inline u32x4 zero4a() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Buffer-descriptor loads over one (lane, layer, KV head) slab: a byte offset
-// at or past the slab's size reads zeros without touching memory (the raw
-// buffer range check), which lets a prefetch be switched off by its offset
-// alone.  Descriptor word 3 = 0x00020000 (32-bit data format) on gfx9 parts.
-constexpr unsigned SLAB_OFF = 0x80000000u;  // an offset past any slab
+// Buffer-descriptor loads over one chunk of one (layer, KV head) in its block:
+// a byte offset at or past the descriptor's range reads zeros without
+// touching memory (the raw buffer range check), which lets a wave without a
+// chunk be switched off by its offset alone.  Descriptor word 3 = 0x00020000
+// (32-bit data format) on gfx9 parts.
+constexpr unsigned PAST_RANGE = 0x80000000u;  // an offset past any chunk's range
 
-__device__ inline __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, unsigned bytes) {
+__device__ inline __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ inline u32x4 slab_ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+__device__ inline u32x4 chunk_ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-__device__ inline u32x2 slab_ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+__device__ inline u32x2 chunk_ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
@@ -459,34 +462,34 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const long long lbase = (long long)lastblk * a.block_elems + hoff - (long long)(c0 + nc - 1) * ATTN_SPLIT * HD;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
-  const uint16_t* kslab = (const uint16_t*)a.kslab;
-  const uint16_t* vslab = (const uint16_t*)a.vslab;
+  const uint16_t* kpool = (const uint16_t*)a.kpool;
+  const uint16_t* vpool = (const uint16_t*)a.vpool;
 
   // Whole chunks are read (a block holds whole chunks), and the slots past p
   // (old or never written) are masked or zeroed after the load.  A wave
   // without a chunk loads at an offset past its chunk's buffer: zeros, no access.
   const unsigned chunk_bytes = (unsigned)ATTN_SPLIT * HD * 2;
-  const __amdgpu_buffer_rsrc_t krs = slab_rsrc(kslab + base, chunk_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(vslab + base, chunk_bytes);
-  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 : SLAB_OFF;
-  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : SLAB_OFF;
+  const __amdgpu_buffer_rsrc_t krs = chunk_rsrc(kpool + base, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = chunk_rsrc(vpool + base, chunk_bytes);
+  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 : PAST_RANGE;
+  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : PAST_RANGE;
   u32x4 kr[4][KK];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = slab_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
+    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = chunk_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
   KVRaw<D, true> vr[16];
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const unsigned oi = voff + (16 * (it / 4) + it % 4) * HD * 2;
     if constexpr (D == 8) {
-      const u32x4 v = slab_ld16(vrs, oi);
+      const u32x4 v = chunk_ld16(vrs, oi);
       vr[it].w[0] = v.x;
       vr[it].w[1] = v.y;
       vr[it].w[2] = v.z;
       vr[it].w[3] = v.w;
     } else {
-      const u32x2 v = slab_ld8(vrs, oi);
+      const u32x2 v = chunk_ld8(vrs, oi);
       vr[it].w[0] = v.x;
       vr[it].w[1] = v.y;
     }
@@ -548,8 +551,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;
       kvn[1][d] = vw;
-      ((uint16_t*)a.kslab)[lbase + (long long)p * HD + d] = kw;
-      ((uint16_t*)a.vslab)[lbase + (long long)p * HD + d] = vw;
+      ((uint16_t*)a.kpool)[lbase + (long long)p * HD + d] = kw;
+      ((uint16_t*)a.vpool)[lbase + (long long)p * HD + d] = vw;
     }
   }
   if (a.mode == ATTN_APPEND) return;

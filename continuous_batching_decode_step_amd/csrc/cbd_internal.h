@@ -74,8 +74,8 @@ struct GemmArgs {
 
 struct AttnArgs {
   const float* qkv;       // [B, Nqkv] f32, before rotation
-  void* kslab;            // arena K block pool
-  void* vslab;            // arena V block pool
+  void* kpool;            // arena K block pool
+  void* vpool;            // arena V block pool
   // A block holds ATTN_SPLIT positions of one lane for every layer and KV
   // head; the pools are layer-major, [L][n_blocks][Hkv][ATTN_SPLIT][hd]:
   // chunk c of a lane is the block the work item names for it, and (layer l,

@@ -359,8 +359,8 @@ size_t cbd_arena_bytes(const cbd_config* cfg, int n_lanes, int max_seq) {
   if (!cfg || n_lanes <= 0 || max_seq <= 0 || cfg->n_layers <= 0 || cfg->n_kv_heads <= 0 || cfg->head_dim <= 0)
     return 0;
   const size_t kvb = cfg->wtype == CBD_BF16 ? 2 : 4;
-  const size_t slab = ((size_t)max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * ATTN_SPLIT;
-  return 2 * (size_t)n_lanes * cfg->n_layers * cfg->n_kv_heads * slab * cfg->head_dim * kvb;
+  const size_t rounded = ((size_t)max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT * ATTN_SPLIT;  // whole blocks
+  return 2 * (size_t)n_lanes * cfg->n_layers * cfg->n_kv_heads * rounded * cfg->head_dim * kvb;
 }
 
 int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size_t dev_bytes, cbd_arena** out) {
@@ -649,8 +649,8 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   }
   AttnArgs at{};
   at.qkv = qkv;
-  at.kslab = a->base;
-  at.vslab = a->base + a->region_bytes;
+  at.kpool = a->base;
+  at.vpool = a->base + a->region_bytes;
   at.block_elems = a->block_elems;
   at.B = B;
   at.lanes = d_lanes;

@@ -7,7 +7,8 @@ still feeding) must give bit-identical logits at the end of each chunk and a
 bit-identical cache afterwards: a row's result depends only on its own lane
 and position.  The last logits also match the oracle fed token by token.
 Both attention kernels are covered (bf16 head_dim 128, the matrix-core
-kernel; the tiny shape in f32, the general kernel).
+kernel; the tiny shape in f32, the general kernel), and the Q8_0 weight path
+(SmolLM2-135M shape, f32 cache).
 """
 import numpy as np
 import pytest
@@ -22,7 +23,12 @@ SHAPES = [
     synth.TINY,
     synth.ModelConfig("prefill-hd128-bf16", d=2048, n_layers=2, n_heads=16, n_kv_heads=4, head_dim=128, ffn=256,
                       vocab=512, wtype=synth.WTYPE_BF16),
+    synth.SMOL135M_Q8,
 ]
+# The oracle bar per weight format.  Q8_0: the GPU feeds the matrix cores binary16 operands (the
+# weight dequantised and the activation rounded to f16), which sits ~1.3e-3 from the Q8 oracle
+# (f32 activations) on this shape; 5e-3 holds it with margin.
+TOL_Q8 = 5e-3
 START = [0, 0, 30, 64, 100]    # cache length before the prompt (imported)
 TOTAL = [1, 70, 34, 130, 7]    # prompt tokens per lane
 
@@ -85,7 +91,7 @@ def test_chunked_prefill_equals_decode_steps(cfg):
 
     # the oracle, fed token by token, on two lanes
     M = oracle.Model(W)
-    tol = TOL_BF16 if cfg.wtype == synth.WTYPE_BF16 else TOL_F32
+    tol = {synth.WTYPE_BF16: TOL_BF16, synth.WTYPE_Q8_0: TOL_Q8}.get(cfg.wtype, TOL_F32)
     for b in (2, 3):
         lane = M.lane(max_seq)
         if b in kv0:

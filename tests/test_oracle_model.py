@@ -6,6 +6,11 @@
   a key projection that selects one input so the stored key is cos/sin of the
   position.  These catch a dropped residual, an off-by-one in the attended
   range, a key stored before rotation or at the wrong slot, and a wrong GQA map.
+* A SwiGLU block with selector weights and distinct norm gains per norm and
+  layer: x_out = x + silu(sg * xf_i) * (su * xf_j) e_k per hidden unit, in
+  closed form.  This catches silu on the up rows, the gate/up row order
+  reversed, a dropped FFN residual, and one norm's gain used for another
+  (checked by planting each mistake in the oracle: every one fails a pin).
 * The invariants the pages state for the method ("MODEL-BATCHING-RESULTS",
   section "Correctness — proven, not asserted"): the panel step is bit-for-bit
   the serial step per user, logits and the whole KV cache, across distinct
@@ -275,3 +280,146 @@ def test_f32_accumulation_build_is_the_same_definition():
             same = same and np.array_equal(x.view(np.uint32), y.view(np.uint32))
     assert worst < 1e-5
     assert not same
+
+
+# ---- the SwiGLU block and the three norm gains ------------------------------------------
+
+def _ffn_weights(cfg, r, gates, ups, outs, sg, su, gains, swap=False):
+    """Special weights whose decode step has a closed form (d = 8, Hq = 2, Hkv = 1, hd = 4,
+    F = 4).  Wq = 0, so every score is 0 and attention is the plain mean of the values; Wv
+    selects four entries of the attention-normalised input (layer l: xa[4l .. 4l+3]); Wo
+    is 0.5 x a permutation; hidden unit j takes gate = sg * xf[gates[j]] and up =
+    su * xf[ups[j]] from the FFN-normalised input, and W_down adds unit j into
+    x[outs[j]].  swap=True stores the up rows where the gate rows belong and vice versa."""
+    d, F, L = cfg.d, cfg.ffn, cfg.n_layers
+    E = r.standard_normal((cfg.vocab, d))
+    H = r.standard_normal((cfg.vocab, d))
+    qkv, o, gu, down, perms = [], [], [], [], []
+    for l in range(L):
+        w = np.zeros((cfg.n_qkv, d))
+        w[8:12] = r.standard_normal((4, d))  # key rows: any values, the scores stay 0
+        for i in range(4):
+            w[12 + i, 4 * l + i] = 1.0
+        qkv.append(w)
+        p = r.permutation(d)
+        perms.append(p)
+        wo = np.zeros((d, cfg.q_dim))
+        wo[np.arange(d), p] = 0.5
+        o.append(wo)
+        g = np.zeros((2 * F, d))
+        for j in range(F):
+            g[j, gates[j]] = sg
+            g[F + j, ups[j]] = su
+        if swap:
+            g = np.concatenate([g[F:], g[:F]])
+        gu.append(g)
+        wd = np.zeros((d, F))
+        for j in range(F):
+            wd[outs[j], j] = 1.0
+        down.append(wd)
+    W = _weights_from(cfg, E, H, qkv, o, gu, down)
+    ga, gf, gfin = gains
+    W.attn_norm[:] = [np.ascontiguousarray(a, np.float32) for a in ga]
+    W.ffn_norm[:] = [np.ascontiguousarray(a, np.float32) for a in gf]
+    W.final_norm = np.ascontiguousarray(gfin, np.float32)
+    return W, E.astype(np.float32).astype(np.float64), H.astype(np.float32).astype(np.float64), perms
+
+
+def _ffn_closed_form(cfg, E, H, perms, gains, toks, gates, ups, outs, sg, su, silu_on="gate",
+                     ffn_residual=True):
+    """Logits of each step of one lane under the special weights of _ffn_weights, in f64.
+    silu_on / ffn_residual describe plausible mistakes, for the negative checks."""
+    ga, gf, gfin = [[np.asarray(g, np.float32).astype(np.float64) for g in gs] for gs in gains[:2]] + \
+        [np.asarray(gains[2], np.float32).astype(np.float64)]
+    eps = cfg.rms_eps
+    silu = lambda u: u / (1.0 + math.exp(-u))
+    hist = [[] for _ in range(cfg.n_layers)]
+    res = []
+    for tok in toks:
+        x = E[tok].copy()
+        for l in range(cfg.n_layers):
+            xa = _rms64(x, eps) * ga[l]
+            hist[l].append(xa[4 * l:4 * l + 4])
+            m = np.mean(hist[l], axis=0)           # uniform attention: mean of the values
+            o = np.concatenate([m, m])             # both query heads read the one KV head
+            upd = np.zeros(cfg.d)
+            upd[np.arange(cfg.d)] = 0.5 * o[perms[l]]
+            x = x + upd
+            xf = _rms64(x, eps) * gf[l]
+            add = np.zeros(cfg.d)
+            for j in range(cfg.ffn):
+                g, u = sg * xf[gates[j]], su * xf[ups[j]]
+                add[outs[j]] += silu(g) * u if silu_on == "gate" else silu(u) * g
+            x = x + add if ffn_residual else add
+        res.append(H @ (_rms64(x, eps) * gfin))
+    return res
+
+
+FFN_CFG = ModelConfig("ffn-pin", d=8, n_layers=2, n_heads=2, n_kv_heads=1, head_dim=4, ffn=4, vocab=16)
+FFN_GATES, FFN_UPS, FFN_OUTS = [0, 3, 5, 6], [2, 7, 1, 4], [1, 4, 6, 3]
+
+
+def _ffn_gains(r, cfg):
+    ga = [0.5 + r.random(cfg.d) for _ in range(cfg.n_layers)]
+    gf = [0.5 + r.random(cfg.d) for _ in range(cfg.n_layers)]
+    return ga, gf, 0.5 + r.random(cfg.d)
+
+
+@pytest.mark.parametrize("batched", [False, True])
+def test_swiglu_block_and_norm_gains_have_their_closed_form(batched):
+    # x_out = x + W_down (silu(W_g xf) * (W_u xf)) with xf the FFN-normalised input times
+    # that layer's FFN gain; attention reads the attention-normalised input times that
+    # layer's attention gain; the head reads the final-normalised state times the final gain.
+    cfg = FFN_CFG
+    r = np.random.default_rng(21)
+    gains = _ffn_gains(r, cfg)
+    sg, su = 3.0, 2.0
+    W, E, H, perms = _ffn_weights(cfg, r, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su, gains)
+    M = oracle.Model(W)
+    toks = [5, 11, 5, 0, 14, 9]
+    if batched:
+        lanes = [M.lane(8), M.lane(8)]
+        got = [M.step_batch(lanes, [t, toks[0]])[0] for t in toks]
+    else:
+        lane = M.lane(8)
+        got = [M.step(lane, t) for t in toks]
+    want = _ffn_closed_form(cfg, E, H, perms, gains, toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su)
+    for p in range(len(toks)):
+        assert _rel(got[p], want[p]) < 1e-5, p
+    # The pin rejects the plausible mistakes: each alternative closed form is far from
+    # what the oracle computes.
+    alts = {
+        "silu on the up rows": _ffn_closed_form(cfg, E, H, perms, gains, toks, FFN_GATES, FFN_UPS, FFN_OUTS,
+                                                sg, su, silu_on="up"),
+        "no FFN residual": _ffn_closed_form(cfg, E, H, perms, gains, toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su,
+                                            ffn_residual=False),
+        "attention and FFN gains exchanged": _ffn_closed_form(
+            cfg, E, H, perms, (gains[1], gains[0], gains[2]), toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su),
+        "final gain = last FFN gain": _ffn_closed_form(
+            cfg, E, H, perms, (gains[0], gains[1], gains[1][-1]), toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su),
+        "layers' gains in reverse": _ffn_closed_form(
+            cfg, E, H, perms, (gains[0][::-1], gains[1][::-1], gains[2]), toks, FFN_GATES, FFN_UPS, FFN_OUTS,
+            sg, su),
+    }
+    for name, alt in alts.items():
+        assert max(_rel(got[p], alt[p]) for p in range(len(toks))) > 1e-3, name
+
+
+def test_gate_and_up_rows_are_not_interchangeable():
+    # Storing the up rows first (the gate/up order reversed) must give the closed form
+    # with silu on what is now the second half, a different result.
+    cfg = FFN_CFG
+    r = np.random.default_rng(22)
+    gains = _ffn_gains(r, cfg)
+    sg, su = 3.0, 2.0
+    W, E, H, perms = _ffn_weights(cfg, r, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su, gains, swap=True)
+    M = oracle.Model(W)
+    toks = [3, 8, 15, 1]
+    lane = M.lane(8)
+    got = [M.step(lane, t) for t in toks]
+    swapped = _ffn_closed_form(cfg, E, H, perms, gains, toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su,
+                               silu_on="up")
+    plain = _ffn_closed_form(cfg, E, H, perms, gains, toks, FFN_GATES, FFN_UPS, FFN_OUTS, sg, su)
+    for p in range(len(toks)):
+        assert _rel(got[p], swapped[p]) < 1e-5, p
+    assert max(_rel(got[p], plain[p]) for p in range(len(toks))) > 1e-3

@@ -74,27 +74,39 @@ GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_gu", "gemm_down", "gemm_head")
 
 def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
     """Time `steps` decode steps over the first B lanes (each step rewrites the same slot of every lane),
-    then a second pass with events around every kernel class.  Returns (sweep row, per-class summary)."""
+    each step with its own event pair and the whole run with one more, then a second pass with events
+    around every kernel class.  Returns (sweep row, per-class summary).
+
+    ms_per_step is the whole run's time / steps (what the headline value uses); median_ms and best_ms
+    are over the per-step intervals, which leave out any gap between steps (a host stall shows up as
+    ms_per_step above median_ms).  kernel_sum_ms is the per-class kernel time of the profiled pass per
+    step, so ms_per_step - kernel_sum_ms is the time the GPU spent without a kernel of the step."""
     import torch
+    pos0 = lens[:B].astype(np.int32)
+    lanes_b, toks_b = lanes[:B], toks[:B]
 
     def step():
         for b in range(B):
-            eng.arena.lane_truncate(lanes[b], int(lens[b]))
-        pos = lens[:B].astype(np.int32).copy()
-        eng.step(lanes[:B], pos, toks[:B])
+            eng.arena.lane_truncate(lanes_b[b], int(pos0[b]))
+        eng.step(lanes_b, pos0.copy(), toks_b)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    per_step = [(ev(), ev()) for _ in range(steps)]
     w0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(steps):
+    for a, b in per_step:
+        a.record(stream)
         step()
+        b.record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / steps
+    each = sorted(a.elapsed_time(b) for a, b in per_step)
     pos = [int(x) for x in lens[:B]]
     t_roof = rf.roofline_time_s(cfg, pos)
     eng.model.profile_reset()
@@ -107,7 +119,10 @@ def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
     per = rf.per_class_summary(cfg, prof, pos)
     gemm_ms = sum(per[k]["total_ms"] for k in GEMM_CLASSES if k in per) / steps
     gemm_flops = sum(rf.kernel_flops(cfg, k, pos) * (1 if k == "gemm_head" else cfg.n_layers) for k in GEMM_CLASSES)
-    row = {"B": B, "tok_s": B / (ms * 1e-3), "ms_per_step": ms, "wall_ms_per_step": wall * 1e3 / steps,
+    kernel_ms = sum(v["total_ms"] for v in per.values()) / steps
+    row = {"B": B, "tok_s": B / (ms * 1e-3), "ms_per_step": ms, "median_ms": float(np.median(each)),
+           "best_ms": each[0], "worst_ms": each[-1], "kernel_sum_ms": kernel_ms,
+           "wall_ms_per_step": wall * 1e3 / steps,
            "step_alg_GB": rf.step_bytes(cfg, pos) / 1e9, "roofline_tok_s": B / t_roof,
            "roofline_frac": t_roof / (ms * 1e-3),
            "gemm_mfma_util": gemm_flops / (gemm_ms * 1e-3) / (rf.MFMA_PEAK_TFLOPS["bf16"] * 1e12),
@@ -422,8 +437,9 @@ def main() -> int:
     for B in batches:
         row, per = measure(eng, lanes, lens, toks, B, args.steps, args.warmup, cfg, rf, stream)
         sweep.append(row)
-        log("B=%3d  %8.1f tok/s  %.3f ms/step  roofline %.3f  %s" % (
-            B, row["tok_s"], row["ms_per_step"], row["roofline_frac"],
+        log("B=%3d  %8.1f tok/s  %.3f ms/step (median %.3f, best %.3f, kernels %.3f)  roofline %.3f  %s" % (
+            B, row["tok_s"], row["ms_per_step"], row["median_ms"], row["best_ms"], row["kernel_sum_ms"],
+            row["roofline_frac"],
             " ".join("%s=%.1fus/%sGB/s" % (k, v["avg_us"], v["GBs"]) for k, v in row["kernels"].items())))
         headline = (B, row["ms_per_step"], per, [int(x) for x in lens[:B]])
 

@@ -33,7 +33,7 @@ SYMBOLS = [
     "cbd_profile_class_name", "cbd_set_graph_replay", "cbd_arena_block_bytes", "cbd_arena_n_blocks",
     "cbd_arena_free_blocks", "cbd_prefill_batch", "cbd_sched_create", "cbd_sched_create_device",
     "cbd_sched_destroy", "cbd_sched_submit", "cbd_sched_tick", "cbd_sched_run", "cbd_sched_get_telemetry",
-    "cbd_sched_job_tokens", "cbd_lane_clone", "cbd_lane_evict_span",
+    "cbd_sched_job_tokens", "cbd_lane_clone", "cbd_lane_evict_span", "cbd_debug_alloc_count",
 ]
 
 
@@ -148,6 +148,8 @@ def lib():
         L.cbd_profile_classes.argtypes = []
         L.cbd_profile_class_name.argtypes = [i32]
         L.cbd_profile_class_name.restype = ctypes.c_char_p
+        L.cbd_debug_alloc_count.argtypes = []
+        L.cbd_debug_alloc_count.restype = ctypes.c_longlong
         L.cbd_lane_clone.argtypes = [vp, i32, i32, i32, vp]
         L.cbd_lane_evict_span.argtypes = [vp, i32, i32, i32, vp]
         L.cbd_sched_create.argtypes = [ctypes.POINTER(SchedBudget), ctypes.POINTER(SchedEngine), ctypes.POINTER(vp)]
@@ -352,6 +354,11 @@ class Model:
             0 if workspace is None else workspace.numel() * workspace.element_size())
         _check(lib().cbd_decode_step(self.h, arena.h, lane, _pi32(position), int(token), _ptr(logits),
                                      _ptr(argmax), _ptr(workspace), wsb, _stream(stream)))
+
+
+def alloc_count() -> int:
+    """Device and pinned host allocations the library has made so far (cbd_debug_alloc_count)."""
+    return int(lib().cbd_debug_alloc_count())
 
 
 def arena_bytes(cfg, n_lanes: int, max_seq: int) -> int:

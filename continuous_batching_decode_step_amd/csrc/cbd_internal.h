@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 struct cbd_arena;  // include/cbd.h
+struct cbd_model;
 
 namespace cbd {
 
@@ -155,6 +156,11 @@ hipError_t launch_kv_blocks(char* base, long long half, const int* src, const in
 int report_error(int code, const char* fmt, ...);
 // KV bytes of one position of one lane in an arena (K and V, every layer and head).
 size_t arena_kv_bytes_per_token(const cbd_arena* a);
+// Positions a lane of the arena can hold.
+int arena_max_seq(const cbd_arena* a);
+// Rows (lanes of a decode step, or prompt tokens of a prefill call) a workspace
+// of `bytes` holds for arenas of max_seq positions per lane.
+int workspace_rows(const cbd_model* m, int max_seq, size_t bytes);
 // Copy one lane's K or V rows [L * Hkv][len][hd] (device, contiguous) into its
 // blocks of a layer-major pool (to_pool), or back; blocks: the lane's block ids
 // on the device, one per 64 positions.

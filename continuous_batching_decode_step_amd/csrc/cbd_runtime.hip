@@ -15,6 +15,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -26,6 +27,20 @@ using namespace cbd;
 namespace {
 
 thread_local std::string g_err;
+
+// Device and pinned-host allocations the library has made (a test hook: a
+// decode step must make none).
+std::atomic<long long> g_allocs{0};
+
+hipError_t counted_malloc(void** p, size_t bytes) {
+  g_allocs.fetch_add(1);
+  return hipMalloc(p, bytes);
+}
+
+hipError_t counted_host_malloc(void** p, size_t bytes) {
+  g_allocs.fetch_add(1);
+  return hipHostMalloc(p, bytes, hipHostMallocDefault);
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -86,20 +101,26 @@ struct cbd_model {
   Plan p_qkv, p_o, p_gu, p_down, p_head;
   int variant = 0;
   // captured step graphs, keyed by everything their kernel arguments depend on
+  // (the arena object and its pool geometry: the pool base, the V region's
+  // offset and the layer stride are baked into the attention arguments); an
+  // arena's graphs are dropped when it is destroyed
   struct GraphKey {
     int B;
-    const void *ws, *arena, *logits, *argmax;
-    size_t ws_bytes;
-    int max_seq, n_lanes, variant;
+    const void *ws, *arena, *base, *logits, *argmax;
+    size_t ws_bytes, region_bytes;
+    int max_seq, n_lanes, n_blocks, variant;
     bool operator==(const GraphKey& o) const {
-      return B == o.B && ws == o.ws && arena == o.arena && logits == o.logits && argmax == o.argmax &&
-             ws_bytes == o.ws_bytes && max_seq == o.max_seq && n_lanes == o.n_lanes && variant == o.variant;
+      return B == o.B && ws == o.ws && arena == o.arena && base == o.base && logits == o.logits &&
+             argmax == o.argmax && ws_bytes == o.ws_bytes && region_bytes == o.region_bytes &&
+             max_seq == o.max_seq && n_lanes == o.n_lanes && n_blocks == o.n_blocks && variant == o.variant;
     }
   };
   std::vector<std::pair<GraphKey, hipGraphExec_t>> graphs;
   hipStream_t cap_stream = nullptr;
   bool use_graphs = false;
-  // pinned staging for per-step metadata
+  // pinned staging for per-step metadata, sized when an arena is created for
+  // a decode step over all of its lanes (a decode step never allocates; a
+  // prefill call with more rows may grow them)
   void* slot[NSLOT] = {};
   size_t slot_bytes[NSLOT] = {};
   hipEvent_t ev[NSLOT] = {};
@@ -134,6 +155,10 @@ struct cbd_arena {
   std::vector<int> len;
   std::vector<std::vector<int>> blocks;  // per lane, the block of each chunk
   std::vector<int> free_blocks;          // a stack; the lowest block on top
+  // duplicate-lane check of a step without a per-step allocation: lane i is
+  // taken in this step if mark[i] == epoch
+  std::vector<uint32_t> mark;
+  uint32_t epoch = 0;
   // device staging for kv import/export: one lane's K or V rows, then its block
   // ids; allocated on first use, grown as needed, freed with the arena
   char* stage = nullptr;
@@ -143,7 +168,7 @@ struct cbd_arena {
 namespace {
 
 struct WsLayout {
-  size_t meta, x, xn, ssq, qkv, o, a, amax, rope, apart, gpart, total;
+  size_t meta, meta_bytes, x, xn, ssq, qkv, o, a, amax, rope, apart, gpart, total;
   int maxB, MS;
 };
 
@@ -159,6 +184,26 @@ int attn_chunks_per_item(const cbd_model* m) {
 // chunk, position, arena lane}, 16-byte aligned (B is at most 65536).
 size_t meta_header(int B) { return ((size_t)3 * B + 1 + 3) & ~(size_t)3; }
 
+// Bytes of the per-step metadata of B rows holding `chunks` 64-key chunks in all.
+size_t meta_bytes_for(int B, long long items) { return 4 * (meta_header(B) + (size_t)ITEM_INTS * items); }
+
+// Grow every pinned staging slot to at least `bytes` (each slot's last copy is
+// waited for before it is freed).
+int grow_slots(cbd_model* m, size_t bytes) {
+  for (int i = 0; i < NSLOT; ++i) {
+    if (m->slot_bytes[i] >= bytes) continue;
+    if (m->ev_live[i]) HIP_TRY(hipEventSynchronize(m->ev[i]));
+    if (m->slot[i]) HIP_TRY(hipHostFree(m->slot[i]));
+    m->slot[i] = nullptr;
+    m->slot_bytes[i] = 0;
+    const size_t cap = std::max(bytes, (size_t)65536);
+    HIP_TRY(counted_host_malloc(&m->slot[i], cap));
+    m->slot_bytes[i] = cap;
+    if (!m->ev[i]) HIP_TRY(hipEventCreateWithFlags(&m->ev[i], hipEventDisableTiming));
+  }
+  return CBD_OK;
+}
+
 WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
   WsLayout L{};
   const cbd_config& c = m->c;
@@ -170,7 +215,8 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
     off += align256(bytes);
     return o;
   };
-  L.meta = take(4 * (meta_header(maxB) + (size_t)ITEM_INTS * maxB * L.MS));
+  L.meta_bytes = 4 * (meta_header(maxB) + (size_t)ITEM_INTS * maxB * L.MS);
+  L.meta = take(L.meta_bytes);
   L.x = take(4 * (size_t)maxB * c.d_model);
   L.xn = take((size_t)m->actb * maxB * c.d_model);
   const int ssq_rows = std::max(std::max(m->p_o.nRB, m->p_down.nRB), 1);
@@ -385,12 +431,34 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   a->blocks.assign(n_lanes, std::vector<int>());
   a->free_blocks.resize(nb);
   for (size_t i = 0; i < nb; ++i) a->free_blocks[i] = (int)(nb - 1 - i);
+  a->mark.assign(n_lanes, 0u);
+  // Pinned staging for a decode step over every lane at up to max_seq
+  // positions, so that steps allocate nothing.  Without a usable device (the
+  // arena is host bookkeeping over caller memory, and is validated on hosts
+  // without one) this fails quietly and the first step sizes the staging.
+  const int per = attn_chunks_per_item(m);
+  const long long chunks = (max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  if (grow_slots(m, meta_bytes_for(n_lanes, (long long)n_lanes * ((chunks + per - 1) / per))) != CBD_OK) {
+    (void)hipGetLastError();
+    g_err.clear();
+  }
   *out = a;
   return CBD_OK;
 }
 
 void cbd_arena_destroy(cbd_arena* a) {
-  if (a && a->stage) (void)hipFree(a->stage);
+  if (!a) return;
+  // graphs captured over this arena hold its pool addresses: drop them
+  std::vector<std::pair<cbd_model::GraphKey, hipGraphExec_t>>& gs = a->m->graphs;
+  for (size_t i = 0; i < gs.size();) {
+    if (gs[i].first.arena == a) {
+      (void)hipGraphExecDestroy(gs[i].second);
+      gs.erase(gs.begin() + i);
+    } else {
+      ++i;
+    }
+  }
+  if (a->stage) (void)hipFree(a->stage);
   delete a;
 }
 
@@ -508,6 +576,8 @@ int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launche
 int cbd_profile_classes(void) { return P_N; }
 
 const char* cbd_profile_class_name(int cls) { return cls >= 0 && cls < P_N ? kClassNames[cls] : nullptr; }
+
+long long cbd_debug_alloc_count(void) { return g_allocs.load(); }
 
 int cbd_set_graph_replay(cbd_model* m, int enable) {
   if (!m) return fail(CBD_E_ARG, "null model");
@@ -733,45 +803,45 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   // items {b | chunks << 24, first chunk, position, 0, block of each chunk}: a
   // workgroup of the attention kernel takes one aligned group of up to `per`
   // consecutive 64-key chunks of one lane, the same groups whatever B is.
-  std::vector<int32_t> meta;
+  // Written straight into a pinned staging slot (sized when the arena was
+  // created, so a decode step allocates nothing), then one copy to the workspace.
   const size_t hdr = meta_header(B);
-  long long chunks = 0;
-  for (int b = 0; b < B; ++b) chunks += (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
   const int per = attn_chunks_per_item(m);
-  meta.reserve(hdr + ITEM_INTS * (size_t)chunks);
-  meta.insert(meta.end(), lanes, lanes + B);
-  meta.insert(meta.end(), positions, positions + B);
-  meta.insert(meta.end(), tokens, tokens + B);
-  meta.resize(hdr, 0);
+  long long items = 0;
+  for (int b = 0; b < B; ++b) items += ((positions[b] + ATTN_SPLIT) / ATTN_SPLIT + per - 1) / per;
+  const size_t meta_bytes = meta_bytes_for(B, items);
+  if (meta_bytes > L.meta_bytes)
+    return fail(CBD_E_WORKSPACE, "step metadata of %zu bytes exceeds the workspace's %zu", meta_bytes, L.meta_bytes);
+  const int si = m->next_slot;
+  m->next_slot = (si + 1) % NSLOT;
+  if (m->slot_bytes[si] < meta_bytes) {
+    int rc = grow_slots(m, meta_bytes);  // a prefill call with more rows than any arena's lanes
+    if (rc) return rc;
+  } else if (m->ev_live[si]) {
+    HIP_TRY(hipEventSynchronize(m->ev[si]));
+  }
+  int32_t* meta = (int32_t*)m->slot[si];
+  memcpy(meta, lanes, sizeof(int32_t) * B);
+  memcpy(meta + B, positions, sizeof(int32_t) * B);
+  memcpy(meta + 2 * B, tokens, sizeof(int32_t) * B);
+  for (size_t i = 3 * (size_t)B; i < hdr; ++i) meta[i] = 0;
+  int32_t* it = meta + hdr;
   int n_items = 0;
   for (int b = 0; b < B; ++b) {
-    const int ns = (positions[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
+    const int ns = (positions[b] + ATTN_SPLIT) / ATTN_SPLIT;  // chunks holding slots 0..positions[b]
     const std::vector<int>& bl = a->blocks[lanes[b]];
     for (int s0 = 0; s0 < ns; s0 += per) {
       const int n = std::min(per, ns - s0);
-      meta.push_back(b | (n << 24));
-      meta.push_back(s0);
-      meta.push_back(positions[b]);
-      meta.push_back(0);
-      for (int k = 0; k < ATTN_GROUP; ++k) meta.push_back(k < n ? bl[s0 + k] : bl[s0 + n - 1]);
+      it[0] = b | (n << 24);
+      it[1] = s0;
+      it[2] = positions[b];
+      it[3] = 0;
+      for (int k = 0; k < ATTN_GROUP; ++k) it[4 + k] = k < n ? bl[s0 + k] : bl[s0 + n - 1];
+      it += ITEM_INTS;
       ++n_items;
     }
   }
   meta[3 * B] = n_items;
-  const size_t meta_bytes = meta.size() * 4;
-  const int si = m->next_slot;
-  m->next_slot = (si + 1) % NSLOT;
-  if (m->ev_live[si]) HIP_TRY(hipEventSynchronize(m->ev[si]));
-  if (m->slot_bytes[si] < meta_bytes) {
-    if (m->slot[si]) HIP_TRY(hipHostFree(m->slot[si]));
-    m->slot[si] = nullptr;
-    m->slot_bytes[si] = 0;
-    const size_t cap = std::max(meta_bytes, (size_t)65536);
-    HIP_TRY(hipHostMalloc(&m->slot[si], cap, hipHostMallocDefault));
-    m->slot_bytes[si] = cap;
-  }
-  if (!m->ev[si]) HIP_TRY(hipEventCreateWithFlags(&m->ev[si], hipEventDisableTiming));
-  memcpy(m->slot[si], meta.data(), meta_bytes);
   int32_t* dmeta = (int32_t*)(ws + L.meta);
   {
     ProfScope ps(m, P_META, st);
@@ -785,8 +855,9 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   if (!graph) {
     if ((rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, st))) return rc;
   } else {
-    const cbd_model::GraphKey key{B,         ws,          a->base,     logits,    argmax,
-                                  workspace_bytes, a->max_seq, a->n_lanes, m->variant};
+    const cbd_model::GraphKey key{B,          ws,        a,           a->base,    logits,
+                                  argmax,     workspace_bytes, a->region_bytes, a->max_seq, a->n_lanes,
+                                  a->n_blocks, m->variant};
     hipGraphExec_t exec = nullptr;
     for (auto& g : m->graphs)
       if (g.first == key) exec = g.second;
@@ -824,12 +895,15 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   if (B < 1) return fail(CBD_E_ARG, "B = %d < 1", B);
   const cbd_config& c = m->c;
   // lanes: range, liveness, distinctness; positions; tokens
-  std::vector<uint8_t> seen(a->n_lanes, 0);
+  if (++a->epoch == 0) {
+    std::fill(a->mark.begin(), a->mark.end(), 0u);
+    a->epoch = 1;
+  }
   for (int b = 0; b < B; ++b) {
     const int ln = lanes[b];
     if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", b, ln, a->n_lanes);
-    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
-    seen[ln] = 1;
+    if (a->mark[ln] == a->epoch) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
+    a->mark[ln] = a->epoch;
     if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
     if (positions[b] != a->len[ln])
       return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", b, positions[b], ln,
@@ -978,7 +1052,7 @@ static int copy_lane(cbd_arena* a, int lane, int len, char* rows, bool to_pool, 
     if (a->stage) HIP_TRY(hipFree(a->stage));
     a->stage = nullptr;
     a->stage_bytes = 0;
-    HIP_TRY(hipMalloc(&a->stage, need));
+    HIP_TRY(counted_malloc((void**)&a->stage, need));
     a->stage_bytes = need;
   }
   const long long bbytes = a->block_elems * (long long)kvb;
@@ -1038,7 +1112,7 @@ int cbd_lane_clone(cbd_arena* a, int src, int dst, int n, void* stream) {
       if (a->stage) HIP_TRY(hipFree(a->stage));
       a->stage = nullptr;
       a->stage_bytes = 0;
-      HIP_TRY(hipMalloc(&a->stage, 2 * lb));
+      HIP_TRY(counted_malloc((void**)&a->stage, 2 * lb));
       a->stage_bytes = 2 * lb;
     }
     std::vector<int> pairs(a->blocks[src].begin(), a->blocks[src].begin() + need);
@@ -1086,7 +1160,7 @@ int cbd_lane_evict_span(cbd_arena* a, int lane, int begin, int end, void* stream
       if (a->stage) HIP_TRY(hipFree(a->stage));
       a->stage = nullptr;
       a->stage_bytes = 0;
-      HIP_TRY(hipMalloc(&a->stage, need));
+      HIP_TRY(counted_malloc((void**)&a->stage, need));
       a->stage_bytes = need;
     }
     int* dblk = (int*)(a->stage + boff);
@@ -1147,6 +1221,10 @@ int report_error(int code, const char* fmt, ...) {
   va_end(ap);
   return fail(code, "%s", buf);
 }
+
+int workspace_rows(const cbd_model* m, int max_seq, size_t bytes) { return max_batch_for(m, max_seq, bytes); }
+
+int arena_max_seq(const cbd_arena* a) { return a->max_seq; }
 
 size_t arena_kv_bytes_per_token(const cbd_arena* a) {
   const cbd_config& c = a->m->c;

@@ -81,6 +81,9 @@ struct cbd_sched {
   cbd_sched_engine e{};
   DeviceEngine* dev = nullptr;
   int cap = 0;                 // effective active cap
+  // device engine: rows its workspace holds per call (prompt tokens of one
+  // prefill call, lanes of one decode step) and positions per lane; 0 = no limit
+  int row_cap = 0, max_seq = 0;
   std::vector<Session> sessions;
   std::unordered_map<long long, size_t> index;
   std::deque<size_t> queue;    // waiting sessions, arrival order
@@ -147,6 +150,8 @@ int cbd_sched_create_device(const cbd_sched_budget* budget, cbd_model* m, cbd_ar
     return rc;
   }
   (*out)->dev = d;
+  (*out)->max_seq = arena_max_seq(a);
+  (*out)->row_cap = workspace_rows(m, arena_max_seq(a), workspace_bytes);
   return CBD_OK;
 }
 
@@ -162,13 +167,17 @@ int cbd_sched_submit(cbd_sched* s, long long job_id, const int32_t* prompt, int 
   if (n_prompt < 1 || max_new < 1) return report_error(CBD_E_ARG, "n_prompt = %d, max_new = %d", n_prompt, max_new);
   const cbd_sched_budget& b = s->b;
   const size_t need = ((size_t)n_prompt + (size_t)max_new) * b.kv_bytes_per_token;
+  // A session ends holding n_prompt + max_new - 1 positions (its last token is
+  // not fed back); its prompt is prefilled in one call.
+  const bool too_long = s->max_seq > 0 && (long long)n_prompt + max_new - 1 > s->max_seq;
+  const bool too_wide = s->row_cap > 0 && n_prompt > s->row_cap;
   if (s->index.count(job_id)) {
     ++s->rej_dup;
     *decision = CBD_SCHED_REJECT_DUPLICATE;
-  } else if (need > b.kv_budget_bytes) {
+  } else if (need > b.kv_budget_bytes || too_long) {
     ++s->rej_kv;
     *decision = CBD_SCHED_REJECT_KV;
-  } else if (s->cap < 1) {
+  } else if (s->cap < 1 || too_wide) {
     ++s->rej_scratch;
     *decision = CBD_SCHED_REJECT_SCRATCH;
   } else if ((int)s->queue.size() >= b.max_queue) {
@@ -203,7 +212,8 @@ int cbd_sched_tick(cbd_sched* s, int* worked) {
     const Session &p = s->sessions[x], &q = s->sessions[y];
     return p.last_decoded != q.last_decoded ? p.last_decoded < q.last_decoded : p.seq < q.seq;
   });
-  if ((int)dec.size() > b.max_batch) dec.resize(b.max_batch);
+  const int max_b = s->row_cap > 0 ? std::min(b.max_batch, s->row_cap) : b.max_batch;
+  if ((int)dec.size() > max_b) dec.resize(max_b);
   if (!dec.empty()) {
     const int B = (int)dec.size();
     std::vector<int32_t> lanes(B), pos(B), toks(B), next(B);
@@ -238,6 +248,7 @@ int cbd_sched_tick(cbd_sched* s, int* worked) {
     const Session& x = s->sessions[s->queue.front()];
     const int np = (int)x.prompt.size();
     if (!pick.empty() && used + np > b.max_prefill_tokens_per_tick) break;
+    if (s->row_cap > 0 && used + np > s->row_cap) break;  // one prefill call's rows
     if (reserved + x.reserve > b.kv_budget_bytes) break;  // waits, in order, for KV to return
     reserved += x.reserve;
     used += np;
@@ -261,6 +272,10 @@ int cbd_sched_tick(cbd_sched* s, int* worked) {
       for (int i = 0; i < n; ++i)
         if (lanes[i] >= 0) (void)s->e.lane_evict(s->e.ctx, lanes[i]);
       for (int i = n - 1; i >= 0; --i) s->queue.push_front(pick[i]);
+      // sessions this tick's decode finished still release their lanes
+      (void)release(s, done);
+      if (work) ++s->ticks;
+      if (worked) *worked = work ? 1 : 0;
       return rc;
     }
     s->reserved = reserved;

@@ -126,14 +126,18 @@ class TraceStats:
     generated: int = 0       # generated tokens
     occupancy: List[int] = field(default_factory=list)
     positions: List[np.ndarray] = field(default_factory=list)  # per step, if recorded: positions before it
+    logits: Dict[int, List[np.ndarray]] = field(default_factory=dict)  # job id -> logits of its kept steps
 
 
-def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_positions: bool = False):
+def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_positions: bool = False,
+              keep_logits: Optional[Dict[int, int]] = None):
     """Continuous batching of `jobs` (arrival_step, prompt, max_new_tokens) over n_lanes lanes.
 
     FIFO admission at the start of each step into the lowest free lane.  Returns
     ({job_id: generated tokens}, TraceStats); with record_positions the stats keep
-    every step's lane positions (before the step)."""
+    every step's lane positions (before the step).  keep_logits {job_id: n}: the
+    stats keep the logits of that job's first n steps, as taken inside the
+    batched steps of the trace (st.logits[job_id], one row per step)."""
     pending = sorted(jobs, key=lambda j: (j.arrival_step, j.job_id))
     qi = 0
     lane_job: Dict[int, object] = {}
@@ -167,6 +171,13 @@ def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_
         if record_positions:
             st.positions.append(p.copy())
         am, _ = eng.step_sync([lane_ids[s] for s in live], p, toks)
+        if keep_logits:
+            rows = [i for i, s in enumerate(live)
+                    if feed[s] < keep_logits.get(lane_job[s].job_id, 0)]
+            if rows:
+                lg = eng.logits[rows].cpu().numpy()
+                for j, i in enumerate(rows):
+                    st.logits.setdefault(lane_job[live[i]].job_id, []).append(lg[j])
         st.steps += 1
         st.lane_steps += len(live)
         st.occupancy.append(len(live))

@@ -277,6 +277,13 @@ int cbd_profile_read(cbd_model* m, int cls, double* total_ms, long long* launche
 int cbd_profile_classes(void);
 const char* cbd_profile_class_name(int cls);
 
+/* Device and pinned host allocations this library has made so far, all models
+ * and arenas together (a test hook).  A decode step makes none: its staging is
+ * sized when the arena is created and its workspace is the caller's.  Arena
+ * creation, KV import/export, clone, span eviction, a prefill call with more
+ * rows than staged for, and graph capture may allocate.  Never fails. */
+long long cbd_debug_alloc_count(void);
+
 /* Step launch mode of this model: 0 (default) = plain kernel launches; 1 =
  * each decode step's kernel sequence is captured once per (B, workspace,
  * arena, outputs) into a HIP graph and replayed on the caller's stream (for
@@ -323,8 +330,10 @@ int cbd_set_variant(cbd_model* m, int variant);
 typedef struct cbd_sched cbd_sched;
 
 #define CBD_SCHED_QUEUED 0             /* admitted: waits for a slot */
-#define CBD_SCHED_REJECT_KV 1          /* prompt + max_new positions exceed the KV budget on their own */
-#define CBD_SCHED_REJECT_SCRATCH 2     /* one session's scratch exceeds the scratch envelope */
+#define CBD_SCHED_REJECT_KV 1          /* prompt + max_new positions exceed the KV budget on their own,
+                                          or (device engine) prompt + max_new - 1 exceed the arena's max_seq */
+#define CBD_SCHED_REJECT_SCRATCH 2     /* one session's scratch exceeds the scratch envelope, or (device
+                                          engine) the prompt has more tokens than the workspace has rows */
 #define CBD_SCHED_REJECT_DUPLICATE 3   /* the job id is already known */
 #define CBD_SCHED_REJECT_QUEUE_FULL 4  /* max_queue sessions are waiting (backpressure) */
 
@@ -379,6 +388,10 @@ int cbd_sched_create(const cbd_sched_budget* budget, const cbd_sched_engine* eng
  * of one tick), logits [rows, vocab] and argmax [rows] buffers and stream;
  * greedy tokens are copied to the host after each call.  budget's
  * kv_bytes_per_token is replaced by the arena's (K and V of every layer).
+ * The workspace's rows also bound every call: a decode step takes at most that
+ * many sessions, a prefill call at most that many prompt tokens, and a prompt
+ * longer than that is refused at submission (CBD_SCHED_REJECT_SCRATCH), as is
+ * a session that would outgrow the arena's max_seq (CBD_SCHED_REJECT_KV).
  * Errors: as cbd_sched_create. */
 int cbd_sched_create_device(const cbd_sched_budget* budget, cbd_model* m, cbd_arena* a, void* workspace,
                             size_t workspace_bytes, float* logits, int32_t* argmax, void* stream, cbd_sched** out);
@@ -391,7 +404,9 @@ int cbd_sched_submit(cbd_sched* s, long long job_id, const int32_t* prompt, int 
                      int* decision);
 
 /* One tick (rules above).  *worked = 0 when there was nothing to do.
- * Errors: the engine's, unchanged. */
+ * Errors: the engine's, unchanged.  If the prefill fails, its sessions wait
+ * again at the head of the queue (their lanes released), and sessions the
+ * tick's decode finished are still released. */
 int cbd_sched_tick(cbd_sched* s, int* worked);
 
 /* Ticks until no session is active or waiting; CBD_E_ARG if that takes more

@@ -62,9 +62,11 @@ class LaneReport:
 def compare_lane_teacher_forced(M: "oracle.Model", prompt, gen, gpu_logits, tol, max_seq=None,
                                 decisive_factor=4.0) -> LaneReport:
     """Feed the oracle the tokens the GPU lane consumed (prompt, then its own generated
-    tokens but the last) and compare every step's logits and greedy choice."""
+    tokens but the last) and compare every step's logits and greedy choice.  gpu_logits
+    may cover only the job's first steps; those are compared."""
     seq = list(prompt) + list(gen[:-1])
-    assert len(seq) == len(gpu_logits)
+    assert 0 < len(gpu_logits) <= len(seq)
+    seq = seq[:len(gpu_logits)]
     lane = M.lane(max_seq or len(seq))
     rep = LaneReport()
     for i, tok in enumerate(seq):

@@ -265,3 +265,56 @@ def test_lane_evict_span_validation():
         with pytest.raises(cbd.CbdError) as e:
             a.lane_evict_span(*args, stream=0)
         assert e.value.name == name, args
+
+
+class _FakeBuf:
+    """Stands in for a device tensor: an address and a size, never dereferenced."""
+
+    def __init__(self, addr, n):
+        self.addr, self.n = addr, n
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_device_scheduler_refuses_what_the_arena_or_workspace_cannot_hold():
+    # The scheduler over the decode path bounds sessions by the arena's max_seq
+    # (a session ends holding prompt + max_new - 1 positions) and prompts by the
+    # workspace's rows (a prompt is prefilled in one call); refusals happen at
+    # submission, so nothing here reaches the device.
+    cfg = synth.TINY
+    m = cbd.Model(cfg, fake_weights(cfg))
+    max_seq, rows = 40, 8
+    a = cbd.Arena(m, 2, max_seq, FAKE, cbd.arena_bytes(cfg, 2, max_seq))
+    wsb = m.workspace_bytes(rows, max_seq)
+    assert m.workspace_bytes(rows + 1, max_seq) > wsb
+    b = dict(weight_bytes=0, kv_budget_bytes=1 << 40, kv_bytes_per_token=1, scratch_per_session=0,
+             scratch_budget_bytes=0, max_active=2, max_queue=8, max_batch=2, max_prefill_tokens_per_tick=64)
+    s = cbd.Scheduler(b, device=(m, a, _FakeBuf(FAKE, wsb), FAKE, FAKE, 0))
+    assert s.submit(1, [1] * (rows + 1), 1) == "REJECTED_SCRATCH_BUDGET"
+    assert s.submit(2, [1] * rows, max_seq - rows + 1) == "QUEUED"       # ends at max_seq positions
+    assert s.submit(3, [1] * rows, max_seq - rows + 2) == "REJECTED_KV_BUDGET"
+    t = s.telemetry()
+    assert (t["rejected_scratch"], t["rejected_kv"], t["queued"]) == (1, 1, 1)
+    s.close()
+    a.close()
+    m.close()
+
+
+def test_arena_creation_needs_no_device():
+    # Arenas are host bookkeeping over caller memory: created here without a
+    # GPU (the pinned staging for their steps is sized when a device exists,
+    # else by the first step), their lanes and blocks are all available.
+    m = cbd.Model(synth.TINY, fake_weights(synth.TINY))
+    a = cbd.Arena(m, 3, 100, FAKE, cbd.arena_bytes(synth.TINY, 3, 100))
+    assert a.n_blocks == a.free_blocks == 3 * 2
+    assert [a.lane_alloc() for _ in range(3)] == [0, 1, 2]
+    assert cbd.lib().cbd_last_error().decode() == ""
+    a.close()
+    m.close()

@@ -8,15 +8,16 @@ token, same cache); the same lane's logits are bit-identical at every B; the
 GPU argmax equals the argmax of the GPU logits; the step writes the new K/V
 at slot len_b and leaves the older slots untouched.
 
-The bar.  At this depth bf16 activations amplify rounding-order differences:
-the oracle built with f32 accumulators (the same definition, every bf16
-rounding point the same) differs from the exact-sum oracle by 1.5-2.1% in
-max relative logit error on the sampled lanes (tests/golden/bf16_7b_floor.json,
-written by tests/golden/make_bf16_7b_floor.py from the oracle alone).  Any
-correct f32-accumulating implementation lands near that floor, so each lane
-is held to max(2e-2, 1.5 x its floor), for the logits and for the appended
-K/V of all layers.  Layer 0's appended K/V depends on one projection only and
-is held to 2^-8 (a flipped bf16 rounding of single elements at most).
+The bar: 2e-2 max relative error (||g - o||_inf / ||o||_inf) for the logits
+and for the K/V the step appends in every layer; layer 0's appended K/V
+depends on one projection only and is held to 2^-8 (a flipped bf16 rounding
+of single elements at most).  Eight lanes are checked against the oracle: the
+shortest (162 positions) and the longest (3997) of the 64, and six others
+spread over the range.  For reference the log also prints, where it is
+recorded, how far the same definition evaluated with f32 accumulators lands
+from the exact-sum oracle on that lane (tests/golden/bf16_7b_floor.json,
+written by tests/golden/make_bf16_7b_floor.py from the oracle alone): 1.5-2.1%
+at this depth, the noise floor any f32-accumulating evaluation sits near.
 """
 import json
 import os
@@ -31,14 +32,16 @@ from gpu_helpers import TOL_BF16, rel_err, say
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BATCHES = [1, 2, 4, 8, 16, 32, 64]
-SAMPLE = [0, 7, 63]
+# lanes 24 and 2 hold the shortest and the longest KV of the 64
+SAMPLE = [0, 2, 4, 7, 14, 24, 40, 63]
 with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_7b_floor.json")) as _f:
     FLOOR = json.load(_f)["lanes"]
 LAYER0_TOL = 2.0 ** -8
 
 
-def _bar(b, key):
-    return max(TOL_BF16, 1.5 * FLOOR[str(b)][key])
+def _floor_note(b):
+    f = FLOOR.get(str(b))
+    return "" if f is None else " (f32-accumulation floor %.4g)" % f["max_rel"]
 
 
 @pytest.fixture(scope="module")
@@ -88,11 +91,11 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         lane.set_kv(synth.bf16_to_f32(k), synth.bf16_to_f32(v))
         say("7B: oracle lane %d (len %d)" % (b, n))
         ref = M.step(lane, int(toks[b]))
-        assert FLOOR[str(b)]["kv_len"] == n and FLOOR[str(b)]["token"] == int(toks[b])
+        if str(b) in FLOOR:
+            assert FLOOR[str(b)]["kv_len"] == n and FLOOR[str(b)]["token"] == int(toks[b])
         err = rel_err(got[b], ref)
-        say("7B: lane %d max rel err %.4g (bar %.4g, f32-accumulation floor %.4g)" % (
-            b, err, _bar(b, "max_rel"), FLOOR[str(b)]["max_rel"]))
-        assert err <= _bar(b, "max_rel")
+        say("7B: lane %d (len %d) max rel err %.4g, bar %.4g%s" % (b, n, err, TOL_BF16, _floor_note(b)))
+        assert err <= TOL_BF16
         # KV: old slots untouched, new slot close to the oracle's
         gk, gv = eng.kv_export(lanes[b])
         assert gk.shape[2] == n + 1
@@ -102,7 +105,7 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         ek, ev = rel_err(gkn, ok[:, :, n]), rel_err(gvn, ov[:, :, n])
         ek0, ev0 = rel_err(gkn[0], ok[0, :, n]), rel_err(gvn[0], ov[0, :, n])
         say("7B: lane %d new K/V rel err %.3g / %.3g, layer 0 %.3g / %.3g" % (b, ek, ev, ek0, ev0))
-        assert ek <= _bar(b, "k_new_max_rel") and ev <= _bar(b, "v_new_max_rel")
+        assert ek <= TOL_BF16 and ev <= TOL_BF16
         assert ek0 <= LAYER0_TOL and ev0 <= LAYER0_TOL
 
 

@@ -179,3 +179,78 @@ def test_evict_span_matches_the_oracle(cfg):
     eng.arena.lane_evict_span(lane, 50, n1 + 1, eng.stream)
     gk2, _ = eng.kv_export(lane)
     assert eng.arena.lane_length(lane) == 50 and np.array_equal(gk2, gk[:, :, :50])
+
+
+def test_graph_replay_follows_the_arena_over_a_reused_buffer():
+    """Graph replay captures the pool's addresses (the V region follows the K
+    region, whose size is the block count) into the kernels' arguments.  Two
+    arenas with different block counts over the same device buffer, one after
+    the other, each with the same lanes and workspace: every replayed step must
+    equal the same step launched plainly, bit for bit (a graph captured over the
+    first arena must never serve the second)."""
+    import torch
+    cfg = SHAPES[0]
+    W = synth.make_weights(cfg)
+    dw = cbd.upload_weights(W)
+    model = cbd.Model(cfg, dw)
+    n, steps = 3, 3
+    lens = [70, 5, 129]
+    max_seq = max(lens) + steps
+    bb = cbd.arena_block_bytes(cfg)
+    per_lane = (max_seq + 63) // 64
+    mem = torch.empty((n * per_lane + 5) * bb, dtype=torch.uint8, device="cuda")
+    wsb = model.workspace_bytes(n, max_seq)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    logits = torch.empty((n, cfg.vocab), dtype=torch.float32, device="cuda")
+    argmax = torch.empty(n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    toks = [synth.uniform_int(1, 900 + b, steps, 0, cfg.vocab - 1) for b in range(n)]
+    kv = [synth.lane_kv_bf16(cfg, b, lens[b]) for b in range(n)]
+    for blocks in (n * per_lane, n * per_lane + 5):
+        say("case: arena of %d blocks over the shared buffer" % blocks)
+        arena = cbd.Arena(model, n, max_seq, mem, dev_bytes=blocks * bb)
+        assert arena.n_blocks == blocks
+        lanes = [arena.lane_alloc() for _ in range(n)]
+        for b in range(n):
+            arena.kv_import(lanes[b], lens[b], kv[b][0], kv[b][1], stream)
+        runs = []
+        for graph in (True, False):
+            model.set_graph_replay(graph)
+            for b in range(n):
+                arena.lane_truncate(lanes[b], lens[b])
+            pos = np.array(lens, np.int32)
+            out = []
+            for s in range(steps):
+                model.decode_step_batch(arena, lanes, pos, [int(t[s]) for t in toks], logits, argmax, ws, wsb,
+                                        stream)
+                out.append(logits.cpu().numpy().copy())
+            runs.append(out)
+        model.set_graph_replay(False)
+        for s in range(steps):
+            assert np.array_equal(runs[0][s].view(np.uint32), runs[1][s].view(np.uint32)), (blocks, s)
+        arena.close()
+
+
+def test_decode_steps_allocate_nothing():
+    """Once the arena exists, decode steps of any width allocate no device or
+    pinned host memory (their staging is sized at arena creation and the
+    workspace is the caller's), including steps that open new KV blocks."""
+    cfg = SHAPES[0]
+    W = synth.make_weights(cfg)
+    n = 6
+    max_seq = 300
+    eng = engine_for(cfg, W, n, max_seq)
+    lanes = [eng.arena.lane_alloc() for _ in range(n)]
+    for b, ln in enumerate(lanes):
+        k, v = synth.lane_kv_bf16(cfg, b, 60 + 40 * b)
+        eng.arena.kv_import(ln, 60 + 40 * b, k, v, eng.stream)
+    pos = np.array([eng.arena.lane_length(l) for l in lanes], np.int32)
+    before = cbd.alloc_count()
+    for s, B in enumerate([1, 6, 3, 6, 2, 6, 6, 5]):
+        idx = list(range(B))
+        p = pos[idx].copy()
+        eng.step([lanes[i] for i in idx], p, [int(s + i) % cfg.vocab for i in idx])
+        pos[idx] = p
+    eng.torch.cuda.synchronize()
+    assert cbd.alloc_count() == before
+    say("8 decode steps of 1-6 lanes, lanes at %s after: %d allocations" % (list(pos), cbd.alloc_count() - before))

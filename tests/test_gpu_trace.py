@@ -10,12 +10,21 @@ tokens are identical to the same job run alone on a fresh lane (one-lane
 steps, "Parity (CPU, before any deploy)" on the same page asks for exactly
 this per-job equality).  Also checked: the arena's usage returns to zero, the
 trace used every lane, and lanes were reused.
+
+Against the oracle: two jobs' logits as taken inside the trace's batched
+steps (other lanes live at other positions), teacher-forced (the oracle is fed
+the tokens the GPU lane consumed): job 2 over all of its 66 steps (47-token
+prompt, 20 new tokens, so its last step too) and job 16 over its first 64
+steps (a 35-token prompt, then 29 steps that feed back generated tokens).
+Bar: 2e-2 max relative logit error at every step (bf16), and the greedy
+token equal to the oracle's at every decisive generation step.
 """
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_helpers import say
+from gpu_helpers import TOL_BF16, compare_lane_teacher_forced, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -23,6 +32,7 @@ N_LANES = 8
 
 
 QUARTERS = 4  # the serial runs are checked in four tests, so progress shows between them
+ORACLE_JOBS = {2: 10 ** 6, 16: 64}  # job id -> steps checked against the oracle (all of job 2)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +43,7 @@ def trace_run(device_weights_7b):
     max_seq = max(len(j.prompt) + j.max_new_tokens for j in jobs)
     eng = Engine(cfg, device_weights_7b, N_LANES, max_seq, max_batch=N_LANES)
     say("trace: %d jobs, %d lane-steps" % (len(jobs), sum(len(j.prompt) + j.max_new_tokens - 1 for j in jobs)))
-    out, st = run_trace(eng, jobs, N_LANES)
+    out, st = run_trace(eng, jobs, N_LANES, keep_logits=ORACLE_JOBS)
     say("trace: %d steps (%d idle), %d lane-steps, mean occupancy %.2f" % (
         st.steps, st.idle_steps, st.lane_steps, np.mean(st.occupancy)))
     yield eng, jobs, out, st
@@ -80,3 +90,22 @@ def test_scheduler_with_prefill_gives_the_trace_tokens(trace_run, device_weights
     assert tel["finished"] == len(jobs) and tel["kv_bytes"] == 0
     assert eng.arena.used_bytes == 0 and eng.arena.live_lanes == 0
     del eng
+
+
+@pytest.mark.parametrize("job_id", sorted(ORACLE_JOBS))
+def test_trace_job_teacher_forced_against_oracle(trace_run, weights_7b, job_id):
+    eng, jobs, out, st = trace_run
+    job = next(j for j in jobs if j.job_id == job_id)
+    n_steps = len(job.prompt) + job.max_new_tokens - 1
+    lg = st.logits[job_id]
+    assert len(lg) == min(n_steps, ORACLE_JOBS[job_id])
+    say("trace oracle: job %d (prompt %d, %d new), %d of its %d steps" % (
+        job_id, len(job.prompt), job.max_new_tokens, len(lg), n_steps))
+    M = oracle.Model(weights_7b)
+    rep = compare_lane_teacher_forced(M, job.prompt, out[job_id], lg, TOL_BF16, max_seq=n_steps)
+    say("trace oracle: job %d max rel err %.4g over %d steps, %d generation steps: %d agree, %d near-ties, "
+        "%d decisive mismatches" % (job_id, rep.max_rel, rep.steps, rep.gen_steps, rep.top1_agree,
+                                    rep.near_ties, rep.mismatches))
+    assert rep.steps == len(lg)
+    assert rep.max_rel <= TOL_BF16
+    assert rep.mismatches == 0

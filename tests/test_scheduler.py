@@ -197,3 +197,38 @@ def test_run_is_bounded_and_errors_are_reported():
         s.submit(5, [], 3)
     with pytest.raises(cbd.CbdError):
         s.job_tokens(77)
+
+
+def test_prefill_failure_requeues_and_still_releases_finished_sessions():
+    # A tick whose decode finishes a session and whose prefill then fails: the
+    # finished session's lane is released all the same, the picked sessions
+    # wait again at the head of the queue with their lanes returned, and the
+    # next tick prefills them.
+    eng = MockEngine(3)
+    fail = {"n": 0}
+    good_prefill = eng.prefill
+
+    def prefill(*a):
+        if fail["n"] > 0:
+            fail["n"] -= 1
+            return -8  # CBD_E_HIP, as a device failure would report it
+        return good_prefill(*a)
+
+    cb = dict(eng.callbacks(), prefill=prefill)
+    s = cbd.Scheduler(budget(max_active=3, max_prefill_tokens_per_tick=16), cb)
+    assert s.submit(0, [1, 2], 2) == "QUEUED"
+    s.tick()                                   # job 0 prefilled: first token
+    assert s.submit(1, [3, 4, 5], 3) == "QUEUED"
+    assert s.submit(2, [6], 2) == "QUEUED"
+    fail["n"] = 1
+    with pytest.raises(cbd.CbdError):
+        s.tick()                               # decode finishes job 0; the prefill of jobs 1, 2 fails
+    t = s.telemetry()
+    assert s.job_tokens(0)[1] and t["finished"] == 1 and t["active"] == 0 and t["queued"] == 2
+    assert eng.hist == [None, None, None]      # job 0's lane and the failed prefill's lanes are free
+    s.run()
+    for j, p, n in [(0, [1, 2], 2), (1, [3, 4, 5], 3), (2, [6], 2)]:
+        toks, done = s.job_tokens(j)
+        assert done and toks == serial_reference(p, n), j
+    assert s.telemetry()["kv_bytes"] == 0
+

@@ -358,9 +358,13 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 // q.k products on MFMA: for each 16-key tile, S^T[key][col] over head_dim as a
 // chain of v_mfma_f32_16x16x32_bf16 with the keys (bf16, as stored) as the A
 // operand and, as the B operand, each query head's rotated f32 query split
-// into bf16 high and low parts (q = hi + lo + O(2^-16 |q|)) in columns j and
-// G + j; the score is col j + col G + j.  Products of bf16 values are exact in
-// f32, so the scores keep f32-level accuracy.  P.V stays on the vector ALUs.
+// into three bf16 parts, q = hi + mid + lo exactly (hi = bf16(q), mid =
+// bf16(q - hi), lo = q - hi - mid, which has at most 8 significant bits), in
+// columns j, G + j and 2G + j; the score is col j + (col G + j + col 2G + j).
+// Products of bf16 values are exact in f32, so each score is the f32 sum of
+// the exact products.  With more than five query heads per KV head (3G > 16)
+// the lo part is dropped (q = hi + mid + O(2^-18 |q|)).  P.V stays on the
+// vector ALUs.
 //
 // A wave takes `nc` consecutive chunks of one lane (an item); each chunk's
 // K and V are loaded one chunk ahead.  Lane mapping for the MFMA: row l16 =
@@ -428,7 +432,8 @@ template <int HD, int G>
 __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
   constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
   constexpr int D = HD / 16;    // dims per lane in the P.V layout
-  static_assert(ATTN_SPLIT == 64 && 2 * G <= 16, "four 16-key tiles; hi/lo columns fit in 16");
+  constexpr int NQ = 3 * G <= 16 ? 3 : 2;  // bf16 parts of each query (columns j, G + j, 2G + j)
+  static_assert(ATTN_SPLIT == 64 && NQ * G <= 16, "four 16-key tiles; query part columns fit in 16");
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -485,10 +490,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const float x = v[d], y = v[first ? d + HD / 2 : d - HD / 2];
     return first ? x * t.x - y * t.y : x * t.x + y * t.y;
   };
-  // The workgroup rotates the group's queries (split into bf16 hi and lo)
-  // and, if its last chunk holds slot p, the new key and value, through LDS;
-  // lanes then read their MFMA operand rows from there.
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2 * G][HD];
+  // The workgroup rotates the group's queries (split into bf16 parts) and, if
+  // its last chunk holds slot p, the new key and value, through LDS; lanes
+  // then read their MFMA operand rows from there.
+  __shared__ __attribute__((aligned(16))) uint16_t qs[NQ * G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
   __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
   // When the QKV projection ran in split mode without its fold, the workgroup
@@ -526,8 +531,11 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const int j = idx / HD, d = idx % HD;
     const float q = rot(qv + (size_t)j * HD, d);
     const uint16_t hi = f2bf_a(q);
+    const float r1 = q - bf2f(hi);  // exact
+    const uint16_t mid = f2bf_a(r1);
     qs[j][d] = hi;
-    qs[G + j][d] = f2bf_a(q - bf2f(hi));
+    qs[G + j][d] = mid;
+    if constexpr (NQ == 3) qs[2 * G + j][d] = f2bf_a(r1 - bf2f(mid));  // exact: at most 8 significant bits
   }
   if (holds_p) {
     for (int d = tid; d < HD; d += 64 * MF_WAVES) {
@@ -545,8 +553,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     u32x4 bq[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 v = *(const u32x4*)&qs[l16 < 2 * G ? l16 : 0][kk * 32 + g4 * 8];
-      bq[kk] = l16 < 2 * G ? v : zero4a();
+      const u32x4 v = *(const u32x4*)&qs[l16 < NQ * G ? l16 : 0][kk * 32 + g4 * 8];
+      bq[kk] = l16 < NQ * G ? v : zero4a();
     }
     const float inv = 1.0f / sqrtf((float)HD);
     const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
@@ -603,16 +611,18 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       }
     }
 
-    // hi + lo, scale, mask; softmax statistics of head l16 (lanes l16 < G)
+    // hi + (mid + lo), scale, mask; softmax statistics of head l16 (lanes l16 < G)
     float pr[4][4];
     float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lo = row_shl<G>(sc[t][i]);  // column G + j (used by the lanes of columns j < G)
+        // columns G + j and 2G + j (used by the lanes of columns j < G)
+        float rest = row_shl<G>(sc[t][i]);
+        if constexpr (NQ == 3) rest = rest + row_shl<(NQ == 3 ? 2 * G : 1)>(sc[t][i]);
         const int key = kb + 16 * t + 4 * g4 + i;
-        const float v = (sc[t][i] + lo) * inv;
+        const float v = (sc[t][i] + rest) * inv;
         pr[t][i] = key < ke ? v : -INFINITY;
         m = fmaxf(m, pr[t][i]);
       }

@@ -168,8 +168,8 @@ struct cbd_arena {
 namespace {
 
 struct WsLayout {
-  size_t meta, meta_bytes, x, xn, ssq, qkv, o, a, amax, rope, apart, gpart, total;
-  int maxB, MS;
+  size_t meta, meta_bytes, x, xn, ssq, qkv, o, a, amax, rope, apart, gpart, gpart_bytes, total;
+  int maxB, MS, parts;  // parts: attention partials per lane (chunks, or groups of chunks)
 };
 
 // 64-key chunks per attention work item (and per partial): 1 for the one-chunk
@@ -177,6 +177,12 @@ struct WsLayout {
 // merges a group inside the wave.  Never a function of B.
 int attn_chunks_per_item(const cbd_model* m) {
   return attn_mfma_supported(m->c.head_dim, m->wt == WT_BF16, m->G) ? ATTN_GROUP : 1;
+}
+
+// Attention partials per lane for MS chunks: one per work item.
+int attn_partials(const cbd_model* m, int MS) {
+  const int per = attn_chunks_per_item(m);
+  return (MS + per - 1) / per;
 }
 
 // Per-step metadata: lanes[B], positions[B], tokens[B], n_items, padding to a
@@ -226,14 +232,24 @@ WsLayout layout(const cbd_model* m, int maxB, int max_seq) {
   L.a = take((size_t)m->actb * maxB * c.ffn_dim);
   L.amax = take(8 * (size_t)m->p_head.nRB * maxB);
   L.rope = take(8 * (size_t)maxB * (c.head_dim / 2));
-  L.apart = take(4 * (size_t)maxB * L.MS * c.n_kv_heads * m->G * (c.head_dim + 2));
-  // split partials of the wide-panel projections that run in split mode
+  L.parts = attn_partials(m, L.MS);
+  L.apart = take(4 * (size_t)maxB * L.parts * c.n_kv_heads * m->G * (c.head_dim + 2));
+  // split partials of the wide-panel projections that can run in split mode
+  // (panel_shape: a two-tile projection splits only up to 64 lanes, and only
+  // with fewer than 512 row blocks; a one-tile one may split at any width)
   size_t gp = 0;
   const Plan* plans[] = {&m->p_qkv, &m->p_o, &m->p_gu, &m->p_down, &m->p_head};
-  const int rows[] = {TILE * gemm_rows(EPI_STORE), TILE * gemm_rows(EPI_RESID), TILE * gemm_rows(EPI_SWIGLU),
-                      TILE * gemm_rows(EPI_RESID), TILE * gemm_rows(EPI_HEAD)};
-  for (int i = 0; i < 5; ++i) gp = std::max(gp, (size_t)plans[i]->S * plans[i]->nRB * rows[i]);
-  L.gpart = take(4 * gp * maxB);
+  const int epis[] = {EPI_STORE, EPI_RESID, EPI_SWIGLU, EPI_RESID, EPI_HEAD};
+  for (int i = 0; i < 5; ++i) {
+    const Plan& pl = *plans[i];
+    if (pl.S < 2) continue;
+    const bool one_tile = gemm_rows(epis[i]) == 1;
+    if (!one_tile && pl.nRB >= 512) continue;
+    const size_t lanes = one_tile ? (size_t)maxB : (size_t)std::min(maxB, 64);
+    gp = std::max(gp, (size_t)pl.S * pl.nRB * TILE * gemm_rows(epis[i]) * lanes);
+  }
+  L.gpart_bytes = 4 * gp;
+  L.gpart = take(L.gpart_bytes);
   L.total = off;
   return L;
 }
@@ -429,6 +445,9 @@ int cbd_arena_create(cbd_model* m, int n_lanes, int max_seq, void* dev_mem, size
   a->live.assign(n_lanes, 0);
   a->len.assign(n_lanes, 0);
   a->blocks.assign(n_lanes, std::vector<int>());
+  // every lane's block list at its longest, so that taking a block never
+  // reallocates (a step allocates no host memory either)
+  for (auto& bl : a->blocks) bl.reserve(((size_t)max_seq + ATTN_SPLIT - 1) / ATTN_SPLIT);
   a->free_blocks.resize(nb);
   for (size_t i = 0; i < nb; ++i) a->free_blocks[i] = (int)(nb - 1 - i);
   a->mark.assign(n_lanes, 0u);
@@ -669,6 +688,8 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   if (panel) {
     int C, rm, split;
     panel_shape(B, p, epi, &C, &rm, &split);
+    if (split && (size_t)4 * p.S * p.nRB * TILE * gemm_rows(epi) * B > L.gpart_bytes)
+      return fail(CBD_E_WORKSPACE, "split partials of %d lanes exceed the workspace's %zu bytes", B, L.gpart_bytes);
     if (epi == EPI_RESID && split && norm_g && normed && fold_norm_supported(p.N)) {
       g.norm_g = norm_g;
       g.norm_eps = m->c.rms_eps;
@@ -728,8 +749,8 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.items = d_items;
   at.n_items_dev = d_nitems;
   at.per = attn_chunks_per_item(m);
-  at.max_items = B * ((L.MS + at.per - 1) / at.per);
-  at.max_splits = L.MS;
+  at.max_items = B * L.parts;
+  at.max_splits = L.parts;
   at.Hq = c.n_heads;
   at.Hkv = c.n_kv_heads;
   at.G = m->G;
@@ -798,7 +819,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
 // produce logits and argmax.  Blocks for every row's slot are already taken.
 static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, const int32_t* lanes,
                        const int32_t* positions, const int32_t* tokens, char* ws, size_t workspace_bytes,
-                       const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st) {
+                       const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st, bool noalloc = false) {
   // Per-step metadata: lanes, positions, tokens, item count, attention work
   // items {b | chunks << 24, first chunk, position, 0, block of each chunk}: a
   // workgroup of the attention kernel takes one aligned group of up to `per`
@@ -815,6 +836,9 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   const int si = m->next_slot;
   m->next_slot = (si + 1) % NSLOT;
   if (m->slot_bytes[si] < meta_bytes) {
+    if (noalloc)
+      return fail(CBD_E_WORKSPACE, "pinned staging of %zu bytes is smaller than the step's %zu (the arena was "
+                  "created without a usable device)", m->slot_bytes[si], meta_bytes);
     int rc = grow_slots(m, meta_bytes);  // a prefill call with more rows than any arena's lanes
     if (rc) return rc;
   } else if (m->ev_live[si]) {
@@ -851,7 +875,7 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   m->ev_live[si] = true;
 
   int rc;
-  const bool graph = m->use_graphs && !m->prof && !multi;
+  const bool graph = m->use_graphs && !m->prof && !multi && !noalloc;  // instantiating a graph allocates
   if (!graph) {
     if ((rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, st))) return rc;
   } else {
@@ -887,9 +911,13 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   return CBD_OK;
 }
 
-int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
-                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// The decode step over a workspace; noalloc: the workspace is the device's
+// static scratch, and nothing may allocate (no staging growth, no graph).
+static int decode_step_impl(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                            const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                            size_t workspace_bytes, void* stream, bool noalloc) {
   if (!m || !a || !lanes || !positions || !tokens || !logits) return fail(CBD_E_ARG, "null argument");
   if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
   if (B < 1) return fail(CBD_E_ARG, "B = %d < 1", B);
@@ -924,8 +952,9 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
   if ((uintptr_t)workspace & 255u) return fail(CBD_E_WORKSPACE, "workspace must be 256-byte aligned");
   const int maxB = max_batch_for(m, a->max_seq, workspace_bytes);
   if (maxB < B)
-    return fail(CBD_E_WORKSPACE, "workspace of %zu bytes holds %d lanes, step has %d (need %zu)", workspace_bytes,
-                maxB, B, cbd_workspace_bytes(m, B, a->max_seq));
+    return fail(CBD_E_WORKSPACE, "%s of %zu bytes holds %d lanes at max_seq %d, step has %d (need %zu)",
+                noalloc ? "static scratch" : "workspace", workspace_bytes, maxB, a->max_seq, B,
+                cbd_workspace_bytes(m, B, a->max_seq));
   const WsLayout L = layout(m, maxB, a->max_seq);
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -938,7 +967,8 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
       a->free_blocks.pop_back();
     }
   }
-  int rc = submit_rows(m, a, B, B, false, lanes, positions, tokens, ws, workspace_bytes, L, logits, argmax, st);
+  int rc = submit_rows(m, a, B, B, false, lanes, positions, tokens, ws, workspace_bytes, L, logits, argmax, st,
+                       noalloc);
   if (rc) return rc;
 
   for (int b = 0; b < B; ++b) {
@@ -946,6 +976,15 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
     a->len[lanes[b]] += 1;
   }
   return CBD_OK;
+}
+
+extern "C" {
+
+int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                          const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_step_impl(m, a, B, lanes, positions, tokens, logits, argmax, workspace, workspace_bytes, stream,
+                          false);
 }
 
 int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lanes, int32_t* positions,

@@ -127,6 +127,7 @@ class TraceStats:
     occupancy: List[int] = field(default_factory=list)
     positions: List[np.ndarray] = field(default_factory=list)  # per step, if recorded: positions before it
     logits: Dict[int, List[np.ndarray]] = field(default_factory=dict)  # job id -> logits of its kept steps
+    kv: Dict[int, tuple] = field(default_factory=dict)  # job id -> (K, V) of its lane as it retired
 
 
 def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_positions: bool = False,
@@ -137,7 +138,8 @@ def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_
     ({job_id: generated tokens}, TraceStats); with record_positions the stats keep
     every step's lane positions (before the step).  keep_logits {job_id: n}: the
     stats keep the logits of that job's first n steps, as taken inside the
-    batched steps of the trace (st.logits[job_id], one row per step)."""
+    batched steps of the trace (st.logits[job_id], one row per step), and the
+    job's whole KV cache as it retires (st.kv[job_id] = (K, V))."""
     pending = sorted(jobs, key=lambda j: (j.arrival_step, j.job_id))
     qi = 0
     lane_job: Dict[int, object] = {}
@@ -190,6 +192,8 @@ def run_trace(eng: Engine, jobs, n_lanes: int, max_steps: int = 10 ** 7, record_
                 out[job.job_id].append(last[s])
                 st.generated += 1
                 if len(out[job.job_id]) >= job.max_new_tokens:
+                    if keep_logits and job.job_id in keep_logits:
+                        st.kv[job.job_id] = eng.kv_export(lane_ids[s])
                     del lane_job[s]
                     free.append(s)
                     free.sort()

@@ -12,19 +12,31 @@ this per-job equality).  Also checked: the arena's usage returns to zero, the
 trace used every lane, and lanes were reused.
 
 Against the oracle: two jobs' logits as taken inside the trace's batched
-steps (other lanes live at other positions), teacher-forced (the oracle is fed
-the tokens the GPU lane consumed): job 2 over all of its 66 steps (47-token
-prompt, 20 new tokens, so its last step too) and job 16 over its first 64
-steps (a 35-token prompt, then 29 steps that feed back generated tokens).
-Bar: 2e-2 max relative logit error at every step (bf16), and the greedy
-token equal to the oracle's at every decisive generation step.
+steps (other lanes live at other positions): job 2 over all of its 66 steps
+(47-token prompt, 20 new tokens, so its last step too) and job 16 over its
+first 64 steps (a 35-token prompt, then 29 steps that feed back generated
+tokens).  Each step is teacher-forced twice: with the token the GPU lane
+consumed and, as the oracle's cache, the K/V the GPU wrote at the earlier
+positions (the step alone); and with the token only, the oracle running the
+job on its own cache (the two caches drift apart step by step).  The greedy
+token must equal the oracle's at every decisive step.
+
+The bar.  At this depth a bf16 model turns any difference in f32 rounding
+into flipped bf16 roundings of activations that grow through the 32 layers:
+the oracle evaluated with f32 accumulators in any one place (the projections'
+dot products alone, or attention's sums alone, or the norms' sums of squares
+alone) already lands 1.5-2.2% from the exact-sum oracle on these steps.  So
+each check measures, on the same inputs, how far the oracle's own
+f32-accumulating build lands from the exact one (the floor of a correct f32
+evaluation), and holds the GPU to max(2e-2, 1.5 x that floor), for the logits
+and the appended K/V; the log reports how many steps are within 2e-2.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_helpers import TOL_BF16, compare_lane_teacher_forced, say
+from gpu_helpers import TOL_BF16, rel_err, say, top2_gap
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -98,14 +110,58 @@ def test_trace_job_teacher_forced_against_oracle(trace_run, weights_7b, job_id):
     job = next(j for j in jobs if j.job_id == job_id)
     n_steps = len(job.prompt) + job.max_new_tokens - 1
     lg = st.logits[job_id]
-    assert len(lg) == min(n_steps, ORACLE_JOBS[job_id])
+    n = len(lg)
+    assert n == min(n_steps, ORACLE_JOBS[job_id])
+    gk, gv = st.kv[job_id]
+    assert gk.shape[2] == n_steps
+    kf, vf = synth.bf16_to_f32(gk[:, :, :n]), synth.bf16_to_f32(gv[:, :, :n])
+    seq = (list(job.prompt) + list(out[job_id][:-1]))[:n]
     say("trace oracle: job %d (prompt %d, %d new), %d of its %d steps" % (
-        job_id, len(job.prompt), job.max_new_tokens, len(lg), n_steps))
+        job_id, len(job.prompt), job.max_new_tokens, n, n_steps))
     M = oracle.Model(weights_7b)
-    rep = compare_lane_teacher_forced(M, job.prompt, out[job_id], lg, TOL_BF16, max_seq=n_steps)
-    say("trace oracle: job %d max rel err %.4g over %d steps, %d generation steps: %d agree, %d near-ties, "
-        "%d decisive mismatches" % (job_id, rep.max_rel, rep.steps, rep.gen_steps, rep.top1_agree,
-                                    rep.near_ties, rep.mismatches))
-    assert rep.steps == len(lg)
-    assert rep.max_rel <= TOL_BF16
-    assert rep.mismatches == 0
+    F = oracle.Model(weights_7b, accumulate="f32")
+    # tokens and cache forced: the step alone, from the GPU's own state
+    lm, lf = M.lane(n), F.lane(n)
+    errs, kv_errs, floor, floor_kv, mism = [], [], 0.0, 0.0, 0
+    for s in range(n):
+        for ln in (lm, lf):
+            if s == 0:
+                ln.clear()
+            else:
+                ln.set_kv(kf[:, :, :s], vf[:, :, :s])
+        o, of = M.step(lm, int(seq[s])), F.step(lf, int(seq[s]))
+        errs.append(rel_err(lg[s], o))
+        floor = max(floor, rel_err(of, o))
+        ok, ov = lm.get_kv()
+        fk, fv = lf.get_kv()
+        kv_errs.append(max(rel_err(kf[:, :, s], ok[:, :, s]), rel_err(vf[:, :, s], ov[:, :, s])))
+        floor_kv = max(floor_kv, rel_err(fk[:, :, s], ok[:, :, s]), rel_err(fv[:, :, s], ov[:, :, s]))
+        if s >= len(job.prompt) - 1:  # a generation step: its token is out[s - (P - 1)]
+            ga, oa = int(out[job_id][s - (len(job.prompt) - 1)]), int(np.argmax(o))
+            if ga != oa and top2_gap(o) >= 4.0 * TOL_BF16 * np.max(np.abs(np.asarray(o, np.float64))):
+                mism += 1
+    within = sum(e <= TOL_BF16 for e in errs)
+    say("trace oracle: job %d, token and cache forced: logits max rel err %.4g (median %.4g, %d of %d steps within "
+        "2e-2; f32-accumulating oracle %.4g), appended K/V %.4g (f32-accumulating oracle %.4g), %d decisive "
+        "mismatches" % (job_id, max(errs), float(np.median(errs)), within, n, floor, max(kv_errs), floor_kv, mism))
+    assert max(errs) <= max(TOL_BF16, 1.5 * floor)
+    assert max(kv_errs) <= max(TOL_BF16, 1.5 * floor_kv)
+    assert mism == 0
+    # token only: the drift of the two caches, against the f32-accumulating oracle's on the same tokens
+    la, lf = M.lane(n), F.lane(n)
+    drift, floor, mism, near = 0.0, 0.0, 0, 0
+    for s in range(n):
+        o = M.step(la, int(seq[s]))
+        drift = max(drift, rel_err(lg[s], o))
+        floor = max(floor, rel_err(F.step(lf, int(seq[s])), o))
+        if s >= len(job.prompt) - 1:
+            ga, oa = int(out[job_id][s - (len(job.prompt) - 1)]), int(np.argmax(o))
+            if ga != oa:
+                if top2_gap(o) >= 4.0 * TOL_BF16 * np.max(np.abs(np.asarray(o, np.float64))):
+                    mism += 1
+                else:
+                    near += 1
+    say("trace oracle: job %d, token only: max rel err %.4g over %d steps (f32-accumulating oracle: %.4g); "
+        "%d near-ties, %d decisive mismatches" % (job_id, drift, n, floor, near, mism))
+    assert drift <= max(TOL_BF16, 1.5 * floor)
+    assert mism == 0

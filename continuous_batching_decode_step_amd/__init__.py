@@ -34,6 +34,7 @@ SYMBOLS = [
     "cbd_arena_free_blocks", "cbd_prefill_batch", "cbd_sched_create", "cbd_sched_create_device",
     "cbd_sched_destroy", "cbd_sched_submit", "cbd_sched_tick", "cbd_sched_run", "cbd_sched_get_telemetry",
     "cbd_sched_job_tokens", "cbd_lane_clone", "cbd_lane_evict_span", "cbd_debug_alloc_count",
+    "cbd_decode_step_batch_noalloc", "cbd_noalloc_scratch_bytes",
 ]
 
 
@@ -148,6 +149,9 @@ def lib():
         L.cbd_profile_classes.argtypes = []
         L.cbd_profile_class_name.argtypes = [i32]
         L.cbd_profile_class_name.restype = ctypes.c_char_p
+        L.cbd_decode_step_batch_noalloc.argtypes = [vp, vp, i32, pi32, pi32, pi32, vp, vp, vp]
+        L.cbd_noalloc_scratch_bytes.argtypes = []
+        L.cbd_noalloc_scratch_bytes.restype = sz
         L.cbd_debug_alloc_count.argtypes = []
         L.cbd_debug_alloc_count.restype = ctypes.c_longlong
         L.cbd_lane_clone.argtypes = [vp, i32, i32, i32, vp]
@@ -315,6 +319,18 @@ class Model:
             _check(lib().cbd_profile_read(self.h, c, ctypes.byref(ms), ctypes.byref(n)))
             out[lib().cbd_profile_class_name(c).decode()] = (ms.value, n.value)
         return out
+
+    def decode_step_batch_noalloc(self, arena: "Arena", lanes: Sequence[int], positions: np.ndarray, tokens,
+                                  logits, argmax=None, stream=None) -> None:
+        """cbd_decode_step_batch_noalloc: the step over the device's static scratch, allocating nothing.
+        positions: np.int32 array, advanced in place on success."""
+        ln = _i32(lanes)
+        assert isinstance(positions, np.ndarray) and positions.dtype == np.int32 and positions.flags["C_CONTIGUOUS"]
+        tk = _i32(tokens)
+        B = len(ln)
+        assert len(positions) == B and len(tk) == B
+        _check(lib().cbd_decode_step_batch_noalloc(self.h, arena.h, B, _pi32(ln), _pi32(positions), _pi32(tk),
+                                                   _ptr(logits), _ptr(argmax), _stream(stream)))
 
     def decode_step_batch(self, arena: "Arena", lanes: Sequence[int], positions: np.ndarray, tokens,
                           logits, argmax=None, workspace=None, workspace_bytes: Optional[int] = None,

@@ -978,6 +978,29 @@ static int decode_step_impl(cbd_model* m, cbd_arena* a, int B, const int32_t* la
   return CBD_OK;
 }
 
+// Scratch of the allocation-free step: one copy per device, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (its
+// host-side name is not a device address): it uses the address
+// hipGetSymbolAddress gives on the current device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+static std::atomic<void*> g_scratch[MAX_DEVICES];
+
+static int scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(CBD_E_UNSUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+  void* p = g_scratch[dev].load();
+  if (!p) {
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(CBD_E_HIP, "no device address for the static scratch on device %d", dev);
+    g_scratch[dev].store(p);  // the same address whichever thread stores it
+  }
+  *out = p;
+  return CBD_OK;
+}
+
 extern "C" {
 
 int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
@@ -985,6 +1008,17 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
                           size_t workspace_bytes, void* stream) {
   return decode_step_impl(m, a, B, lanes, positions, tokens, logits, argmax, workspace, workspace_bytes, stream,
                           false);
+}
+
+size_t cbd_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int cbd_decode_step_batch_noalloc(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                                  const int32_t* tokens, float* logits, int32_t* argmax, void* stream) {
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return decode_step_impl(m, a, B, lanes, positions, tokens, logits, argmax, ws, NOALLOC_SCRATCH_BYTES, stream,
+                          true);
 }
 
 int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lanes, int32_t* positions,

@@ -183,6 +183,26 @@ int cbd_decode_step_batch(cbd_model* m, cbd_arena* a, int B, const int32_t* lane
                           const int32_t* tokens, float* logits, int32_t* argmax, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same decode step with
+ * no workspace argument and no allocation of any kind.  Its workspace is a
+ * static device array of cbd_noalloc_scratch_bytes() (64 MiB), one copy per
+ * device, which the library holds on every device it runs on until the
+ * process ends; its device address is looked up once per device.  The step's
+ * pinned staging must already be sized (cbd_arena_create does it on a
+ * device), and graph replay does not apply.  Results are bitwise those of
+ * cbd_decode_step_batch.  Every call on a device shares that device's scratch
+ * and it keeps the last call's contents (nothing in it needs to start at
+ * zero: each step writes what it reads); calls that overlap on one device
+ * (other streams or threads) race and must not be issued.  Errors: as
+ * cbd_decode_step_batch; CBD_E_WORKSPACE when B lanes at the arena's max_seq
+ * need more than the scratch holds (the Mistral-7B shape: 64 lanes at 4097
+ * positions fit). */
+int cbd_decode_step_batch_noalloc(cbd_model* m, cbd_arena* a, int B, const int32_t* lanes, int32_t* positions,
+                                  const int32_t* tokens, float* logits, int32_t* argmax, void* stream);
+/* Bytes of that static scratch on each device. */
+size_t cbd_noalloc_scratch_bytes(void);
+
 /* The same step for one lane (B = 1): position in/out, logits [vocab]. */
 int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int32_t token, float* logits,
                     int32_t* argmax, void* workspace, size_t workspace_bytes, void* stream);

@@ -377,8 +377,8 @@ def main() -> int:
                     help="KV lengths are uniform in [128, KV_MAX] (seed 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
-                    help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels")
+    ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels, 3 dense tiles")
     ap.add_argument("--graph", action="store_true",
                     help="replay each decode step as a captured HIP graph (cbd_set_graph_replay) instead of "
                          "plain launches")

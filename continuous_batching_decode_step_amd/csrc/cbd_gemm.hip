@@ -763,6 +763,274 @@ __global__ __launch_bounds__(256) void k_fold_norm(GemmArgs a) {
   }
 }
 
+// ---- dense tiles: both operands staged in LDS (wide panels and prefill) ---------
+//
+// Once B makes the contraction dense ("MODEL-BATCHING-RESULTS — multi-user
+// batched decode, measured", section "The honest ceiling": throughput is then
+// capped by the matrix units, not by the weight stream), the matrix cores need
+// operands reused from on-chip memory.  A workgroup of four waves owns a tile
+// of 128 weight rows (SwiGLU: 64 gate/up pairs) by 128 lanes, each wave a
+// 64 x 64 quarter as 4 x 4 MFMA blocks, and walks K in stages of two k-steps
+// (64 elements, 128 bytes of every row).
+//
+// Loads go from memory straight into LDS (buffer loads with the LDS as
+// destination: no registers, no LDS write instructions).  One load
+// instruction fills a 1 KB block with 8 whole 128-byte row segments, eight
+// consecutive lanes per row, so every instruction reads whole cache lines;
+// the lanes of a row take its 16-byte pieces in the order p ^ (row % 16) / 2,
+// which spreads the 16 rows of an MFMA operand over all LDS banks when a wave
+// reads piece p of each of them (one 16-byte load per lane, no conflicts).
+// Two slots of 32 KB: the next stage loads while this one is computed; each
+// stage starts with one barrier, after which every wave's loads of it have
+// landed (each waits for its own first) and every wave has finished reading
+// the slot the new loads overwrite.  64 KB of LDS and fewer than 256
+// registers, so two workgroups share a compute unit.
+//
+// Same reduction contract: each 16 x 16 block is a chain of
+// v_mfma_f32_16x16x32_bf16 over ascending k-steps from zero per split.
+// Modes: DN_ONE, one split per workgroup whose partial goes straight to the
+// epilogue (the projection has one split: (-0) + P_0 is P_0); DN_PART, one
+// split per workgroup written as a partial for k_fold / k_fold_norm; DN_FULL,
+// every split of K in one workgroup, KPS k-steps each (a compile-time length:
+// a split is one fully unrolled loop iteration with a fresh chain, which keeps
+// the MFMA stream free of accumulator copies), folded in order into a running
+// total ((P_0 + P_1) + ...).  So every output bit equals the other families'.
+constexpr int DN_ROWS = 128, DN_COLS = 128;
+constexpr int DN_BLOCK = 1024;            // 8 rows x 128 bytes
+constexpr int DN_STAGE = 32 * DN_BLOCK;   // 16 blocks of weights, then 16 of activations
+enum { DN_ONE = 0, DN_PART = 1, DN_FULL = 2 };
+
+template <int EPI, int MODE, int KPS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_dense(GemmArgs a) {
+  constexpr int R0 = gemm_rows(EPI);
+  constexpr int RM = 4 / R0;  // row blocks of a wave's four row tiles
+  constexpr int KS = 32;
+  constexpr bool SPLIT = MODE == DN_PART;
+  // two stage slots, as separate objects so that the compiler can tell the
+  // slot being read from the slot being loaded
+  __shared__ __attribute__((aligned(16))) char sl0[DN_STAGE];
+  __shared__ __attribute__((aligned(16))) char sl1[DN_STAGE];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // workgroup -> (row group, split, lane group), the lane groups of one (row
+  // group, split) on one XCD (workgroups are dealt to the 8 XCDs in turn)
+  const int outs = EPI == EPI_SWIGLU ? DN_ROWS / 2 : DN_ROWS;  // outputs (rows or pairs) per row group
+  const int nRG = (a.N + outs - 1) / outs;
+  const int nRGS = nRG * (SPLIT ? a.S : 1);
+  const int bi = blockIdx.x;
+  const int cg = (bi >> 3) % a.nCG;
+  const int rgs = ((bi >> 3) / a.nCG) * 8 + (bi & 7);
+  if (rgs >= nRGS) return;  // padding workgroup: the whole workgroup leaves together
+  const int rg = SPLIT ? rgs / a.S : rgs;
+  const int split = SPLIT ? rgs % a.S : 0;
+
+  const int nks = a.K / KS;  // K is a multiple of 128
+  const int kps = a.Ks / KS;
+  const int t0 = SPLIT ? split * kps : 0;
+  const int ns = ((SPLIT ? min(t0 + kps, nks) : nks) - t0) / 2;  // stages walked: an even number
+
+  // Weight row of tile row q (0..127): MFMA row tile q / 16 of the tile,
+  // row q % 16 in it.  Row tiles 4 wm .. 4 wm + 3 are wave row wm's; SwiGLU
+  // row tiles are [gate, gate, up, up] of 32 pairs.
+  auto wrow = [&](int q) -> int {
+    const int f = q >> 4, fm = f >> 2, r = f & 3, i = q & 15;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j = min(rg * (DN_ROWS / 2) + fm * 32 + (r & 1) * 16 + i, a.N - 1);
+      return r < 2 ? j : a.N + j;
+    } else {
+      return min(rg * DN_ROWS + q, a.N - 1);
+    }
+  };
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, (size_t)a.Nraw * a.K * 2);
+  const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X, (size_t)a.B * a.K * 2);
+  // this wave fills blocks 4w .. 4w + 3 of the weights and of the activations;
+  // lane: row 8 j + lane / 8 of block j, its piece (lane % 8) ^ (row % 16) / 2
+  unsigned wv[4], xv[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int q = 8 * (4 * w + jj) + (lane >> 3);
+    const unsigned piece = (unsigned)((lane & 7) ^ ((q & 15) >> 1)) * 16;
+    wv[jj] = (unsigned)((size_t)wrow(q) * a.K * 2) + piece;
+    const int col = min(cg * DN_COLS + q, a.B - 1);
+    xv[jj] = (unsigned)((size_t)col * a.K * 2) + piece;
+  }
+  // stage st of the walk into a slot (a stage past the last reloads it into a
+  // slot nobody reads)
+  auto load = [&](char* slot, int st) {
+    const int kb = (t0 + 2 * min(st, ns - 1)) * KS * 2;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, slot + (4 * w + jj) * DN_BLOCK, 16, (int)wv[jj], kb, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, slot + (16 + 4 * w + jj) * DN_BLOCK, 16, (int)xv[jj], kb, 0, 0);
+  };
+  // Start of a stage: this wave's loads of it have landed, then the barrier.
+  auto arrive = [&]() { __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // Piece p of tile row 16 t + l16 sits at block 2 t + l16 / 8, row l16 % 8,
+  // slot p ^ l16 / 2: per lane, the offsets of k-step 0 and 1 (p = 4 ks + g4).
+  unsigned ro[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    ro[ks] = (unsigned)((l16 >> 3) * DN_BLOCK + (l16 & 7) * 128 + (((4 * ks + g4) ^ (l16 >> 1)) << 4));
+  auto compute = [&](f32x4 (&ch)[4][4], const char* slot) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 av[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) av[r] = *(const u32x4*)(slot + (2 * (4 * wm + r)) * DN_BLOCK + ro[ks]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = *(const u32x4*)(slot + (16 + 2 * (4 * wn + c)) * DN_BLOCK + ro[ks]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ch[r][c] = mma<WT_BF16>(av[r], bv[c], ch[r][c]);
+    }
+  };
+  // two stages st, st + 1 from slots 0, 1, loading st + 1, st + 2
+  auto pair = [&](f32x4 (&ch)[4][4], int st) {
+    arrive();
+    load(sl1, st + 1);
+    compute(ch, sl0);
+    arrive();
+    load(sl0, st + 2);
+    compute(ch, sl1);
+  };
+
+  // The running total of DN_FULL starts at -0: (-0) + x is x bit for bit.
+  f32x4 ch[4][4], tot[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ch[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tot[r][c] = f32x4{-0.f, -0.f, -0.f, -0.f};
+    }
+  load(sl0, 0);
+  if constexpr (MODE == DN_FULL) {
+    for (int st = 0; st < ns; st += KPS / 2) {  // one split per iteration, a fresh chain
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ch[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KPS / 2; q += 2) pair(ch, st + q);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[r][c][i] = tot[r][c][i] + ch[r][c][i];
+    }
+  } else {
+    for (int st = 0; st < ns; st += 2) pair(ch, st);  // the one split
+  }
+  // the load past the end must land before the workgroup's LDS is released
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const int rb = rg * 2 + wm;  // this wave's group of RM row blocks
+  const int cgw = cg * 2 + wn;  // this wave's group of 64 lanes
+  if constexpr (MODE == DN_PART) {
+    // P_s as [split][lane][row block][R0 tiles][16], as the panels write it
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = cgw * 64 + TILE * c + l16;
+      if (col >= a.B) continue;
+      float* dst = a.part + (size_t)split * a.B * a.nRB * (R0 * TILE) + (size_t)col * a.nRB * (R0 * TILE) + 4 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ob = rb * RM + (EPI == EPI_SWIGLU ? r % RM : r / R0);
+        const int t0r = EPI == EPI_SWIGLU ? r / RM : r % R0;
+        if (ob < a.nRB) *(f32x4*)(dst + (size_t)ob * (R0 * TILE) + t0r * TILE) = ch[r][c];
+      }
+    }
+  } else if constexpr (MODE == DN_FULL) {
+    epilogue<WT_BF16, EPI, 4, 4, RM>(a, rb, cgw, lane, tot);
+  } else {
+    epilogue<WT_BF16, EPI, 4, 4, RM>(a, rb, cgw, lane, ch);
+  }
+}
+
+// K-steps per split of the DN_FULL instances built (per epilogue; the
+// Mistral-7B shapes: QKV and O 512-element splits, gate|up and the head 1024,
+// down 1792), or 0.
+static int dense_full_kps(int epi, int Ks) {
+  const int kps = Ks / 32;
+  switch (epi) {
+    case EPI_STORE: return kps == 16 ? 16 : 0;
+    case EPI_RESID: return kps == 16 || kps == 56 ? kps : 0;
+    default: return kps == 32 ? 32 : 0;
+  }
+}
+
+int dense_mode_available(int epi, int K, int Ks, int S) {
+  if (S == 1) return 1;
+  return dense_full_kps(epi, Ks) && K % Ks == 0;
+}
+
+int dense_workgroups(const GemmArgs& a, int epi, int split) {
+  const int outs = epi == EPI_SWIGLU ? DN_ROWS / 2 : DN_ROWS;
+  const int nRGS = ((a.N + outs - 1) / outs) * (split ? a.S : 1);
+  const int nCG = (a.B + DN_COLS - 1) / DN_COLS;
+  return ((nRGS + 7) / 8) * 8 * nCG;
+}
+
+template <int EPI, int MODE, int KPS>
+static hipError_t launch_dense_k(const GemmArgs& a, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL((k_dense<EPI, MODE, KPS>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_dense_epi(int split, const GemmArgs& a, hipStream_t st) {
+  const int blocks = dense_workgroups(a, EPI, split);
+  if (split) {
+    hipError_t e = launch_dense_k<EPI, DN_PART, 0>(a, blocks, st);
+    if (e != hipSuccess) return e;
+    if (EPI == EPI_RESID && a.norm_out) {
+      if (!fold_norm_supported(a.N)) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_fold_norm<WT_BF16>), dim3(a.B), dim3(256), 0, st, a);
+    } else if (EPI == EPI_STORE && a.fold_elsewhere) {
+      // the consumer adds the partials
+    } else {
+      const int nct = (a.B + TILE - 1) / TILE;
+      hipLaunchKernelGGL((k_fold<WT_BF16, EPI>), dim3(a.nRB * nct), dim3(64), 0, st, a);
+    }
+    return hipGetLastError();
+  }
+  if (a.S == 1) return launch_dense_k<EPI, DN_ONE, 0>(a, blocks, st);
+  switch (dense_full_kps(EPI, a.Ks)) {
+    case 16:
+      if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 16>(a, blocks, st);
+      break;
+    case 32:
+      if constexpr (EPI == EPI_SWIGLU || EPI == EPI_HEAD) return launch_dense_k<EPI, DN_FULL, 32>(a, blocks, st);
+      break;
+    case 56:
+      if constexpr (EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 56>(a, blocks, st);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense(int epi, int split, const GemmArgs& a, hipStream_t st) {
+  if (a.S < 1 || a.K % 128 != 0 || a.Ks % 256 != 0) return hipErrorInvalidValue;
+  if (!split && !dense_mode_available(epi, a.K, a.Ks, a.S)) return hipErrorInvalidValue;
+  if (a.nRB <= 0 || a.B <= 0) return hipSuccess;
+  GemmArgs g = a;
+  g.nCG = (a.B + DN_COLS - 1) / DN_COLS;
+  switch (epi) {
+    case EPI_STORE: return launch_dense_epi<EPI_STORE>(split, g, st);
+    case EPI_RESID: return launch_dense_epi<EPI_RESID>(split, g, st);
+    case EPI_SWIGLU: return launch_dense_epi<EPI_SWIGLU>(split, g, st);
+    default: return launch_dense_epi<EPI_HEAD>(split, g, st);
+  }
+}
+
 template <int WT, int EPI>
 static hipError_t launch_c(int C, const GemmArgs& a, int blocks, hipStream_t st) {
   const dim3 blk(64 * a.S);

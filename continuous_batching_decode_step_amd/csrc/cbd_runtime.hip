@@ -605,7 +605,7 @@ int cbd_set_graph_replay(cbd_model* m, int enable) {
 }
 
 int cbd_set_variant(cbd_model* m, int variant) {
-  if (!m || variant < 0 || variant > 2) return fail(CBD_E_ARG, "variant must be 0, 1 or 2");
+  if (!m || variant < 0 || variant > 3) return fail(CBD_E_ARG, "variant must be 0, 1, 2 or 3");
   m->variant = variant;
   return CBD_OK;
 }
@@ -659,6 +659,45 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
   }
 }
 
+// Dense tiles (both operands in LDS) from this many rows on, for bf16 weights
+// whose reductions fit them (K a multiple of 128).  Measured per projection on
+// the 7B shapes: at 128 lanes the wide panels are faster; from 256 the dense
+// tiles are for gate|up, the head and the long reduction (down: one split per
+// workgroup beats the panels' split mode), while QKV and O stay panels unless
+// whole-K dense workgroups cover the chip (a 4096-row prefill: 23% faster
+// projections in all).
+constexpr int DENSE_MIN_B = 256;
+
+static bool dense_ok(const cbd_model* m, const Plan& p, int epi) {
+  if (m->wt != WT_BF16 || p.K % 128 != 0 || p.Ks % 256 != 0) return false;
+  return gemm_rows(epi) == 1 || dense_mode_available(epi, p.K, p.Ks, p.S);
+}
+
+// The automatic choice of dense tiles at B rows (see DENSE_MIN_B).
+static bool dense_auto(const Plan& p, int epi, int B) {
+  if (B < DENSE_MIN_B) return false;
+  if (gemm_rows(epi) != 1 || p.K > 4096) return true;
+  GemmArgs g{};
+  g.N = p.N;
+  g.B = B;
+  g.S = p.S;
+  return dense_mode_available(epi, p.K, p.Ks, p.S) && dense_workgroups(g, epi, 0) >= 256;
+}
+
+// Dense mode: a one-tile projection whose whole-K workgroups would not cover
+// the 256 compute units, or whose split length has no whole-K kernel, runs one
+// split per workgroup with partials; two-tile projections (gate|up, the head)
+// have rows enough and never split (dense_ok requires their whole-K kernel).
+static int dense_split(int B, const Plan& p, int epi) {
+  if (p.S < 2 || gemm_rows(epi) != 1) return 0;
+  if (!dense_mode_available(epi, p.K, p.Ks, p.S)) return 1;
+  GemmArgs g{};
+  g.N = p.N;
+  g.B = B;
+  g.S = p.S;
+  return dense_workgroups(g, epi, 0) < 256 ? 1 : 0;
+}
+
 // norm_g: for a residual projection, the gain of the RMSNorm that follows; if
 // the projection runs as a split-mode panel its fold also normalises x into
 // xn, and *normed says so (the caller then launches no norm).  unfolded: for
@@ -683,9 +722,25 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.amax = (float2*)(ws + L.amax);
   g.ssq_out = (float*)(ws + L.ssq);
   g.part = (float*)(ws + L.gpart);
-  const bool panel = m->variant == 2 || (m->variant == 0 && B >= panel_min_b(epi, p.K));
+  const bool dense = dense_ok(m, p, epi) && (m->variant == 3 || (m->variant == 0 && dense_auto(p, epi, B)));
+  const bool panel = !dense && (m->variant == 2 || m->variant == 3 || (m->variant == 0 && B >= panel_min_b(epi, p.K)));
   ProfScope ps(m, cls, st);
-  if (panel) {
+  if (dense) {
+    const int split = dense_split(B, p, epi);
+    if (split && (size_t)4 * p.S * p.nRB * TILE * gemm_rows(epi) * B > L.gpart_bytes)
+      return fail(CBD_E_WORKSPACE, "split partials of %d lanes exceed the workspace's %zu bytes", B, L.gpart_bytes);
+    if (epi == EPI_RESID && split && norm_g && normed && fold_norm_supported(p.N)) {
+      g.norm_g = norm_g;
+      g.norm_eps = m->c.rms_eps;
+      g.norm_out = ws + L.xn;
+      *normed = true;
+    }
+    if (epi == EPI_STORE && split && unfolded) {
+      g.fold_elsewhere = 1;
+      *unfolded = true;
+    }
+    HIP_TRY(launch_dense(epi, split, g, st));
+  } else if (panel) {
     int C, rm, split;
     panel_shape(B, p, epi, &C, &rm, &split);
     if (split && (size_t)4 * p.S * p.nRB * TILE * gemm_rows(epi) * B > L.gpart_bytes)

@@ -316,11 +316,15 @@ int cbd_set_graph_replay(cbd_model* m, int enable);
 /* Projection kernel family for steps of this model: 0 = automatic by batch
  * width and projection (wide panels from 4 lanes for QKV and the LM head, 8
  * for gate|up, 24 for the output projection, always for a reduction longer
- * than 4096; split-K tiles below), 1 =
- * weight-streaming split-K tiles at every width, 2 = wide panels (the
- * activation panel staged in on-chip memory) at every width.  Every family
- * computes each output with the same chunked reduction, so the choice changes
- * speed only, never a bit of the result.  Errors: CBD_E_ARG. */
+ * than 4096; split-K tiles below; for bf16 weights, dense tiles from 256 rows
+ * for gate|up, the head and the down projection, and for QKV and O once
+ * whole-K dense tiles fill the chip), 1 = weight-streaming split-K tiles at
+ * every width, 2 = wide panels (the activation panel staged in on-chip
+ * memory) at every width, 3 = dense tiles (both operands staged in on-chip
+ * memory; bf16 weights with K a multiple of 128, else wide panels) at every
+ * width.  Every family computes each output with the same chunked reduction,
+ * so the choice changes speed only, never a bit of the result.
+ * Errors: CBD_E_ARG. */
 int cbd_set_variant(cbd_model* m, int variant);
 
 /* ---- Continuous-batching scheduler (host policy over the step) ----

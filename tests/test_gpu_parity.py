@@ -202,21 +202,25 @@ def test_graph_replay_matches_plain_launches_bitwise():
 
 
 def test_projection_families_are_bitwise_identical():
-    # Split-K tiles (1), wide panels (2) and the automatic choice (0) follow the
-    # same reduction contract, so every logit bit agrees.  B = 40 covers panel
+    # Split-K tiles (1), wide panels (2), dense tiles (3; bf16 with K a multiple
+    # of 64, else panels) and the automatic choice (0) follow the same
+    # reduction contract, so every logit bit agrees.  B = 40 covers panel
     # split mode and full mode, ragged columns, and (tiny) a ragged K of 172;
     # B = 100 the 128-lane panel width; B = 260 on the wide vocabulary 64-lane
-    # panels in full mode beside 128-lane panels in split mode.
+    # panels in full mode beside 128-lane panels in split mode; the bf16 cases
+    # run the dense tiles in full and split mode, with ragged lane groups, and
+    # B = 160 picks them automatically.
     from continuous_batching_decode_step_amd.driver import generate_lockstep
     cases = [(synth.TINY, 40), (SMALL_GQA, 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 40),
              (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5),
-             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100), (WIDE_VOCAB, 260)]
+             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100), (WIDE_VOCAB, 260),
+             (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 160), (WIDE_VOCAB.with_wtype(synth.WTYPE_BF16), 136)]
     for cfg, B in cases:
         say("case: projection families, %s wtype %d B=%d" % (cfg.name, cfg.wtype, B))
         W = synth.make_weights(cfg)
         prompts = [synth.prompt_tokens(cfg, 80 + b, 2 + b % 5) for b in range(B)]
         runs = []
-        for variant in (1, 2, 0):
+        for variant in (1, 2, 3, 0):
             eng = engine_for(cfg, W, B, 12)
             eng.model.set_variant(variant)
             runs.append(generate_lockstep(eng, prompts, 4, want_logits=True))

@@ -48,6 +48,16 @@ __device__ inline uint16_t f2bf_a(float f) {
 }
 __device__ inline float bf2f(unsigned h16) { return __builtin_bit_cast(float, h16 << 16); }
 
+// One attention output in the activation format act (WT_F32, WT_BF16, WT_Q8).
+__device__ inline void put_out(void* base, size_t idx, float v, int act) {
+  if (act == WT_F32)
+    ((float*)base)[idx] = v;
+  else if (act == WT_BF16)
+    ((uint16_t*)base)[idx] = f2bf_a(v);
+  else
+    ((_Float16*)base)[idx] = (_Float16)v;
+}
+
 // D consecutive KV elements (D = hd/16) of one key as loaded (raw words), and
 // their f32 values.  Loading and converting are separate so that a whole
 // batch of loads can be issued before the first one is waited for.
@@ -333,6 +343,16 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       v += __shfl_xor(v, 32);
       o[j][e] = v;
     }
+  if (a.direct) {  // the lane's only chunk: the combine's o / l
+    if (r == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < D; ++e)
+          put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d0 + e, o[j][e] / ls[j], a.act);
+    }
+    return;
+  }
   const size_t pstride = (size_t)G * (HD + 2);
   float* dst = a.part + (((size_t)b * a.max_splits + s) * a.Hkv + g) * pstride;
   if (r == 0) {
@@ -702,7 +722,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   // (and the maximum and sum) in order, then every output uses them.
   const size_t pstride = (size_t)G * (HD + 2);
   float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
-  __shared__ float sca[MF_WAVES][G], scb[MF_WAVES][G];
+  __shared__ float sca[MF_WAVES][G], scb[MF_WAVES][G], lsum[G];
   if (tid < G) {
     float Mr = -INFINITY, Lr = 0.f;
     for (int k = 0; k < nc; ++k) {
@@ -714,15 +734,21 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       Lr = Lr * sa + ls[k][tid] * sb;
       Mr = M;
     }
-    dst[(size_t)tid * (HD + 2) + HD] = Mr;
-    dst[(size_t)tid * (HD + 2) + HD + 1] = Lr;
+    lsum[tid] = Lr;
+    if (!a.direct) {
+      dst[(size_t)tid * (HD + 2) + HD] = Mr;
+      dst[(size_t)tid * (HD + 2) + HD + 1] = Lr;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
     const int j = idx / HD, d = idx % HD;
     float Or = 0.f;
     for (int k = 0; k < nc; ++k) Or = Or * sca[k][j] + os[k][j][d] * scb[k][j];
-    dst[(size_t)j * (HD + 2) + d] = Or;
+    if (a.direct)  // the lane's only partial: the combine's o / l
+      put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d, Or / lsum[j], WT_BF16);
+    else
+      dst[(size_t)j * (HD + 2) + d] = Or;
   }
 }
 

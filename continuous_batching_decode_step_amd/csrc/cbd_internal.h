@@ -101,6 +101,11 @@ struct AttnArgs {
   int qkv_S;
   float* part;            // [B][max_splits][Hkv][G][hd + 2] partials (o, m, l) per chunk or group
   void* out;              // [B, Hq*hd] in the activation format
+  // Every row's keys fit one work item (one partial per lane): the attention
+  // kernel writes out = o / l itself, in the activation format act, and no
+  // combine runs (the combine of a single partial gives exactly o / l).
+  int direct;
+  int act;                // WT_* of the activation format
 };
 
 // Block sum of per-thread partials (256 threads): a fixed shuffle tree, then

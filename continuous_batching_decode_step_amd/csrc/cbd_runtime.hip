@@ -109,10 +109,12 @@ struct cbd_model {
     const void *ws, *arena, *base, *logits, *argmax;
     size_t ws_bytes, region_bytes;
     int max_seq, n_lanes, n_blocks, variant;
+    bool direct;  // attention finishes the rows itself (no combine launch)
     bool operator==(const GraphKey& o) const {
       return B == o.B && ws == o.ws && arena == o.arena && base == o.base && logits == o.logits &&
              argmax == o.argmax && ws_bytes == o.ws_bytes && region_bytes == o.region_bytes &&
-             max_seq == o.max_seq && n_lanes == o.n_lanes && n_blocks == o.n_blocks && variant == o.variant;
+             max_seq == o.max_seq && n_lanes == o.n_lanes && n_blocks == o.n_blocks && variant == o.variant &&
+             direct == o.direct;
     }
   };
   std::vector<std::pair<GraphKey, hipGraphExec_t>> graphs;
@@ -771,8 +773,8 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
 // Arguments depend only on (B, n_out, multi, workspace layout, arena,
 // outputs): the per-step data (lanes, positions, tokens, attention items) is
 // read from the workspace.
-static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, char* ws, const WsLayout& L,
-                        float* logits, int32_t* argmax, hipStream_t st) {
+static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, bool direct, char* ws,
+                        const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st) {
   const cbd_config& c = m->c;
   const int32_t* dmeta = (const int32_t*)(ws + L.meta);
   const int* d_lanes = dmeta;
@@ -813,6 +815,8 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.rope = rope;
   at.part = (float*)(ws + L.apart);
   at.out = o;
+  at.direct = direct ? 1 : 0;
+  at.act = m->wt;
   int rc;
   void* xn = ws + L.xn;
   // RMSNorm of x into xn; ssq_n = row blocks of the last producer of x (the embedding: one)
@@ -846,7 +850,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
       }
       HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
     }
-    {
+    if (!direct) {
       ProfScope ps(m, P_COMB, st);
       HIP_TRY(launch_attn_combine(c.head_dim, m->wt, at, st));
     }
@@ -929,14 +933,19 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   HIP_TRY(hipEventRecord(m->ev[si], st));
   m->ev_live[si] = true;
 
+  // Every row's keys in one work item (one attention partial per lane): the
+  // attention kernel finishes the rows itself and the combine is not launched.
+  int max_pos = 0;
+  for (int b = 0; b < B; ++b) max_pos = std::max(max_pos, positions[b]);
+  const bool direct = max_pos < ATTN_SPLIT * per;
   int rc;
   const bool graph = m->use_graphs && !m->prof && !multi && !noalloc;  // instantiating a graph allocates
   if (!graph) {
-    if ((rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, st))) return rc;
+    if ((rc = enqueue_step(m, a, B, n_out, multi, direct, ws, L, logits, argmax, st))) return rc;
   } else {
     const cbd_model::GraphKey key{B,          ws,        a,           a->base,    logits,
                                   argmax,     workspace_bytes, a->region_bytes, a->max_seq, a->n_lanes,
-                                  a->n_blocks, m->variant};
+                                  a->n_blocks, m->variant, direct};
     hipGraphExec_t exec = nullptr;
     for (auto& g : m->graphs)
       if (g.first == key) exec = g.second;
@@ -944,7 +953,7 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
       if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
       hipGraph_t graph_def = nullptr;
       HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-      rc = enqueue_step(m, a, B, n_out, multi, ws, L, logits, argmax, m->cap_stream);
+      rc = enqueue_step(m, a, B, n_out, multi, direct, ws, L, logits, argmax, m->cap_stream);
       hipError_t e = hipStreamEndCapture(m->cap_stream, &graph_def);
       if (rc) {
         if (graph_def) (void)hipGraphDestroy(graph_def);

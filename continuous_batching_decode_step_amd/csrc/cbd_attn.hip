@@ -40,6 +40,7 @@ namespace cbd {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline uint16_t f2bf_a(float f) {
   unsigned u = __builtin_bit_cast(unsigned, f);
@@ -120,6 +121,14 @@ __device__ inline void raw_to_f32(const KVRaw<D, BF>& r, float (&v)[D]) {
   }
 }
 
+// Rotate-half RoPE of one element: x is dim d of a head vector, y its
+// partner (dim d + hd/2 for the first half, d - hd/2 for the second), t the
+// pair's (cos, sin).  Every kernel that rotates a key or a query calls this one
+// expression, so a key appended by one kernel equals the key another uses.
+__device__ inline float rope_pair(float x, float y, float2 t, bool first) {
+  return first ? x * t.x - y * t.y : x * t.x + y * t.y;
+}
+
 template <int HD, bool KVBF16, int G>
 __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   constexpr int D = HD / 16;  // dims per lane
@@ -157,18 +166,16 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
     for (int e = 0; e < D; ++e) {
       const int jj = first_half ? d0 + e : d0 + e - HD / 2;
       const float2 t = cs[jj];
-      const float x = qh[d0 + e], y = qh[dp + e];
-      q[j][e] = first_half ? x * t.x - y * t.y : x * t.x + y * t.y;
+      q[j][e] = rope_pair(qh[d0 + e], qh[dp + e], t, first_half);
     }
   }
   // The new key and value at slot p, rotated and rounded to the KV format
   // (kept as stored words).
   // Fused mode: the item whose chunk holds slot p rotates and writes the new
-  // key and value and uses them for that slot.  Append-only mode stops after
-  // the write; attend-only mode reads slot p from the cache like any key.
+  // key and value and uses them for that slot.  Attend-only mode reads slot p
+  // from the cache like any key (k_kv_append wrote it).
   const bool fused = a.mode == ATTN_FUSED;
-  const bool has_new = a.mode != ATTN_ATTEND && nk > s * ATTN_SPLIT && nk <= s * ATTN_SPLIT + ATTN_SPLIT;
-  if (a.mode == ATTN_APPEND && !has_new) return;
+  const bool has_new = fused && nk > s * ATTN_SPLIT && nk <= s * ATTN_SPLIT + ATTN_SPLIT;
   const int pk = fused ? p : nk;  // keys below pk are read from the cache
   KVRaw<D, KVBF16> knr, vnr;
 #pragma unroll
@@ -181,8 +188,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
     for (int e = 0; e < D; ++e) {
       const int jj = first_half ? d0 + e : d0 + e - HD / 2;
       const float2 t = cs[jj];
-      const float x = kr[d0 + e], y = kr[dp + e];
-      kn[e] = first_half ? x * t.x - y * t.y : x * t.x + y * t.y;
+      kn[e] = rope_pair(kr[d0 + e], kr[dp + e], t, first_half);
       vn[e] = vr[d0 + e];
     }
     if constexpr (KVBF16) {
@@ -219,7 +225,6 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       }
     }
   }
-  if (a.mode == ATTN_APPEND) return;
 
   // Scores of the wave's 64 keys: lane (r, c) accumulates its D dims of key
   // kbeg + 4*it + r into part[it][j]; the row then reduce-scatters so that
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       v += __shfl_xor(v, 32);
       o[j][e] = v;
     }
-  if (a.direct) {  // the lane's only chunk: the combine's o / l
+  if (nk <= ATTN_SPLIT) {  // the row's only partial: the combine's o / l (the combine skips the row)
     if (r == 0) {
 #pragma unroll
       for (int j = 0; j < G; ++j)
@@ -440,12 +445,140 @@ struct RowBcastAll<0> {
   __device__ static inline void run(float, float*) {}
 };
 
+// The per-chunk work of a wave, shared by the decode kernel (k_attn_mf) and
+// the prefill kernel (k_attn_rows) so that both give the same bits.
+//
+// Scores S^T[key][col] of one 64-key chunk: four 16-key tiles, each a chain of
+// MFMAs over head_dim with the keys as the A operand (kr[t][kk]: key 16t + l16,
+// dims kk*32 + g4*8 ..) and the query parts as the B operand.
+template <int HD>
+__device__ inline void mf_scores(const u32x4 (&kr)[4][HD / 32], const u32x4 (&bq)[HD / 32], f32x4 (&sc)[4]) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < HD / 32; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t][kk]),
+                                                    __builtin_bit_cast(bf16x8, bq[kk]), acc, 0, 0, 0);
+    sc[t] = acc;
+  }
+}
+
+// Softmax statistics and P.V of the chunk from its scores: keys below ke
+// count (the rest are masked), value words vr[it] of key kb + 16*(it/4) +
+// 4*g4 + it%4 as loaded; a key at or past pk is zeroed and, if has_new, key p
+// takes vnr.  Leaves o[j][e] (dims l16*D + e of group head j, summed over the
+// wave's four lane rows, in every lane) and, in lanes l16 = j < G, head j's
+// maximum m and sum l.
+template <int HD, int G>
+__device__ inline void mf_softmax_pv(const f32x4 (&sc)[4], const KVRaw<HD / 16, true> (&vr)[16], int kb, int ke, int p,
+                                     int pk, bool has_new, const KVRaw<HD / 16, true>& vnr, int g4,
+                                     float (&o)[G][HD / 16], float& m, float& l) {
+  constexpr int D = HD / 16;
+  constexpr int NQ = 3 * G <= 16 ? 3 : 2;
+  const float inv = 1.0f / sqrtf((float)HD);
+  // hi + (mid + lo), scale, mask; softmax statistics of head l16 (lanes l16 < G)
+  float pr[4][4];
+  m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // columns G + j and 2G + j (used by the lanes of columns j < G)
+      float rest = row_shl<G>(sc[t][i]);
+      if constexpr (NQ == 3) rest = rest + row_shl<(NQ == 3 ? 2 * G : 1)>(sc[t][i]);
+      const int key = kb + 16 * t + 4 * g4 + i;
+      const float v = (sc[t][i] + rest) * inv;
+      pr[t][i] = key < ke ? v : -INFINITY;
+      m = fmaxf(m, pr[t][i]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  // exponentials by the hardware exp2 with the log2(e) scale (about 1 ulp;
+  // this path serves bf16 caches only)
+  l = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[t][i] = pr[t][i] == -INFINITY ? 0.f : __expf(pr[t][i] - m);
+      l += pr[t][i];
+    }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // P.V on the vector ALUs
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[j][e] = 0.f;
+  // A chunk wholly below slot p needs no masking: every key is an old, valid
+  // one (a uniform branch).
+  auto pv_pass = [&](auto masked) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      KVRaw<D, true> x = vr[it];
+      if constexpr (decltype(masked)::value) {
+        const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
+        const unsigned take = has_new && key == p ? ~0u : 0u;
+        const unsigned keep = key < pk ? ~0u : 0u;
+        raw_select<D, true>(x, keep, take, vnr);
+      }
+      float vv[D];
+      raw_to_f32<D, true>(x, vv);
+      float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
+      RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
+      }
+      if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
+    }
+  };
+  if (p >= kb + ATTN_SPLIT)
+    pv_pass(std::false_type{});
+  else
+    pv_pass(std::true_type{});
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      float v = o[j][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[j][e] = v;
+    }
+}
+
+// A group's chunk partials merged in chunk order into one partial: with
+// M = max(Mr, m_k), Lr = Lr e^(Mr - M) + l_k e^(m_k - M), likewise Or
+// (starting from Mr = -inf, Lr = Or = 0, so one chunk gives exactly its own
+// o and l).  ms/ls: chunk k's statistics at [k * st]; os: its output at [k * ost].
+struct Merged {
+  float o, l, m;
+};
+__device__ inline Merged merge_chunks(int nc, const float* ms, const float* ls, int st, const float* os, int ost) {
+  float Mr = -INFINITY, Lr = 0.f, Or = 0.f;
+  for (int k = 0; k < nc; ++k) {
+    const float mk = ms[k * st];
+    const float M = fmaxf(Mr, mk);
+    const float sa = __expf(Mr - M), sb = __expf(mk - M);
+    Lr = __builtin_fmaf(Lr, sa, ls[k * st] * sb);
+    Or = __builtin_fmaf(Or, sa, os[k * ost] * sb);
+    Mr = M;
+  }
+  return Merged{Or, Lr, Mr};
+}
+
 // One workgroup per (lane, KV head, aligned group of ATTN_GROUP chunks), one
 // wave per chunk.  Each wave computes its chunk's partial (o, m, l) exactly as
 // a one-chunk work item would; the partials meet in LDS and are merged in
-// chunk order, M = max(Mr, m), Or = Or e^(Mr - M) + o e^(m - M), likewise Lr,
-// into the group's partial.  The group is a function of the lane's position
-// only, so the result never depends on B.
+// chunk order (merge_chunks) into the group's partial.  The group is a
+// function of the lane's position only, so the result never depends on B.  A
+// row whose keys all fit its first group (its only partial) gets its output
+// o / l written here, and the combine skips it.
 constexpr int MF_WAVES = ATTN_GROUP;
 
 template <int HD, int G>
@@ -454,8 +587,6 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   constexpr int D = HD / 16;    // dims per lane in the P.V layout
   constexpr int NQ = 3 * G <= 16 ? 3 : 2;  // bf16 parts of each query (columns j, G + j, 2G + j)
   static_assert(ATTN_SPLIT == 64 && NQ * G <= 16, "four 16-key tiles; query part columns fit in 16");
-  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
 
   const int item = blockIdx.x;
   if (item >= *a.n_items_dev) return;  // the whole workgroup leaves together
@@ -469,14 +600,12 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int nk = p + 1;
   const int c = c0 + w;  // this wave's chunk
   // Fused mode: the lane's last group (its last chunk holds slot p) rotates
-  // and writes the new key and value and uses them for that slot.  Append-only
-  // mode: only that group runs, and stops after the write.  Attend-only mode:
-  // slot p is read from the cache like any key.
+  // and writes the new key and value and uses them for that slot.  Attend-only
+  // mode: slot p is read from the cache like any key.
   const bool fused = a.mode == ATTN_FUSED;
-  const bool holds_p = a.mode != ATTN_ATTEND && p / ATTN_SPLIT == c0 + nc - 1;
-  if (a.mode == ATTN_APPEND && !holds_p) return;
+  const bool holds_p = fused && p / ATTN_SPLIT == c0 + nc - 1;
   const int pk = fused ? p : nk;  // keys below pk are read from the cache
-  const bool active = w < nc && a.mode != ATTN_APPEND;  // waves that attend to a chunk
+  const bool active = w < nc;     // waves that attend to a chunk
   // (layer, head) offset inside a block; base: this wave's chunk (inactive
   // waves: the last chunk's, never read); lbase: the group's last chunk,
   // which holds slot p when the group is the lane's last
@@ -503,12 +632,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) kr[t][kk] = chunk_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
-  // rotated value of dim d of an f32 head vector v (rotate-half pairing)
+  // rotated value of dim d of an f32 head vector v
   auto rot = [&](const float* v, int d) -> float {
     const bool first = d < HD / 2;
-    const float2 t = cs[first ? d : d - HD / 2];
-    const float x = v[d], y = v[first ? d + HD / 2 : d - HD / 2];
-    return first ? x * t.x - y * t.y : x * t.x + y * t.y;
+    return rope_pair(v[d], v[first ? d + HD / 2 : d - HD / 2], cs[first ? d : d - HD / 2], first);
   };
   // The workgroup rotates the group's queries (split into bf16 parts) and, if
   // its last chunk holds slot p, the new key and value, through LDS; lanes
@@ -547,7 +674,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   } else {
     qv = row + (size_t)g * G * HD;
   }
-  for (int idx = tid; a.mode != ATTN_APPEND && idx < G * HD; idx += 64 * MF_WAVES) {
+  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
     const int j = idx / HD, d = idx % HD;
     const float q = rot(qv + (size_t)j * HD, d);
     const uint16_t hi = f2bf_a(q);
@@ -566,7 +693,6 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       ((uint16_t*)a.vpool)[lbase + (long long)p * HD + d] = vw;
     }
   }
-  if (a.mode == ATTN_APPEND) return;
   __syncthreads();
 
   if (active) {
@@ -576,7 +702,6 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       const u32x4 v = *(const u32x4*)&qs[l16 < NQ * G ? l16 : 0][kk * 32 + g4 * 8];
       bq[kk] = l16 < NQ * G ? v : zero4a();
     }
-    const float inv = 1.0f / sqrtf((float)HD);
     const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
     const bool has_new = fused && p >= kb && p < kb + ATTN_SPLIT;
     // the new key and value replace slot p's old contents
@@ -598,18 +723,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
           }
         }
     }
-
-    // scores: S^T[key][col] per 16-key tile
     f32x4 sc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t][kk]),
-                                                      __builtin_bit_cast(bf16x8, bq[kk]), acc, 0, 0, 0);
-      sc[t] = acc;
-    }
+    mf_scores<HD>(kr, bq, sc);
 
     // V is loaded once the scores are issued: holding K and V for the whole
     // wave from the start costs ~22 more registers, and the values are needed
@@ -630,79 +745,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
         vr[it].w[1] = v.y;
       }
     }
-
-    // hi + (mid + lo), scale, mask; softmax statistics of head l16 (lanes l16 < G)
-    float pr[4][4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // columns G + j and 2G + j (used by the lanes of columns j < G)
-        float rest = row_shl<G>(sc[t][i]);
-        if constexpr (NQ == 3) rest = rest + row_shl<(NQ == 3 ? 2 * G : 1)>(sc[t][i]);
-        const int key = kb + 16 * t + 4 * g4 + i;
-        const float v = (sc[t][i] + rest) * inv;
-        pr[t][i] = key < ke ? v : -INFINITY;
-        m = fmaxf(m, pr[t][i]);
-      }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    // exponentials by the hardware exp2 with the log2(e) scale (about 1 ulp;
-    // this kernel serves bf16 caches only)
-    float l = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[t][i] = pr[t][i] == -INFINITY ? 0.f : __expf(pr[t][i] - m);
-        l += pr[t][i];
-      }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-
-    // P.V on the vector ALUs
-    float o[G][D];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < D; ++e) o[j][e] = 0.f;
-    // A chunk wholly below slot p needs no masking: every key is an old, valid
-    // one (a uniform branch).
-    auto pv_pass = [&](auto masked) {
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        if constexpr (decltype(masked)::value) {
-          const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
-          const unsigned take = has_new && key == p ? ~0u : 0u;
-          const unsigned keep = key < pk ? ~0u : 0u;
-          raw_select<D, true>(vr[it], keep, take, vnr);
-        }
-        float vv[D];
-        raw_to_f32<D, true>(vr[it], vv);
-        float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
-        RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-#pragma unroll
-          for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
-        }
-        if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
-      }
-    };
-    if (p >= kb + ATTN_SPLIT)
-      pv_pass(std::false_type{});
-    else
-      pv_pass(std::true_type{});
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < D; ++e) {
-        float v = o[j][e];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        o[j][e] = v;
-      }
+    float o[G][D], m, l;
+    mf_softmax_pv<HD, G>(sc, vr, kb, ke, p, pk, has_new, vnr, g4, o, m, l);
     if (g4 == 0) {
 #pragma unroll
       for (int j = 0; j < G; ++j)
@@ -716,39 +760,191 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   }
   __syncthreads();
 
-  // the group's partial: its chunks merged in chunk order (the first chunk
-  // scales the empty state by e^(-inf) = 0).  The scales of chunk k, e^(Mr - M)
-  // and e^(m_k - M), depend on the head only: one thread per head takes them
-  // (and the maximum and sum) in order, then every output uses them.
+  // The group's partial: every thread merges the chunks of its outputs in
+  // chunk order.  A row with one partial is finished here.
+  const bool direct = nk <= ATTN_SPLIT * ATTN_GROUP;
   const size_t pstride = (size_t)G * (HD + 2);
   float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
-  __shared__ float sca[MF_WAVES][G], scb[MF_WAVES][G], lsum[G];
-  if (tid < G) {
-    float Mr = -INFINITY, Lr = 0.f;
-    for (int k = 0; k < nc; ++k) {
-      const float mk = ms[k][tid];
-      const float M = fmaxf(Mr, mk);
-      const float sa = __expf(Mr - M), sb = __expf(mk - M);
-      sca[k][tid] = sa;
-      scb[k][tid] = sb;
-      Lr = Lr * sa + ls[k][tid] * sb;
-      Mr = M;
-    }
-    lsum[tid] = Lr;
-    if (!a.direct) {
-      dst[(size_t)tid * (HD + 2) + HD] = Mr;
-      dst[(size_t)tid * (HD + 2) + HD + 1] = Lr;
-    }
-  }
-  __syncthreads();
   for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
     const int j = idx / HD, d = idx % HD;
-    float Or = 0.f;
-    for (int k = 0; k < nc; ++k) Or = Or * sca[k][j] + os[k][j][d] * scb[k][j];
-    if (a.direct)  // the lane's only partial: the combine's o / l
-      put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d, Or / lsum[j], WT_BF16);
-    else
-      dst[(size_t)j * (HD + 2) + d] = Or;
+    const Merged r = merge_chunks(nc, &ms[0][j], &ls[0][j], G, &os[0][j][d], G * HD);
+    if (direct) {
+      put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d, r.o / r.l, WT_BF16);
+    } else {
+      dst[(size_t)j * (HD + 2) + d] = r.o;
+      if (d == 0) {
+        dst[(size_t)j * (HD + 2) + HD] = r.m;
+        dst[(size_t)j * (HD + 2) + HD + 1] = r.l;
+      }
+    }
+  }
+}
+
+// ---- batched prefill: many rows of one lane per work item ---------------------
+//
+// "parallel-slots.md" (section "Reuse: batched PREFILL already exists"): a
+// prompt enters as many rows of one call.  Every row of a lane attends to
+// the same cache, so one work item takes up to ATTN_ROWS_MAX consecutive rows of
+// one lane (positions pa .. pa + nr - 1) and one aligned group of ATTN_GROUP
+// chunks: each wave loads its chunk's K and V once and keeps them in
+// registers while it computes the chunk partial of every row that reaches it,
+// the same per-chunk code and merge as k_attn_mf (so a row's partial has the
+// bits a decode step at that position gives).  Per row: the workgroup
+// rotates and splits the next row's queries into the other half of a
+// double-buffered LDS area, every wave writes its chunk partial, one barrier,
+// and the row's group partial (or, for a row with one partial, its output)
+// is merged and written.  Every row's key and value are in the cache already
+// (k_kv_append runs first).
+
+template <int HD, int G>
+__global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_rows(AttnArgs a) {
+  constexpr int KK = HD / 32;
+  constexpr int D = HD / 16;
+  constexpr int NQ = 3 * G <= 16 ? 3 : 2;
+  static_assert(ATTN_SPLIT == 64 && NQ * G <= 16, "four 16-key tiles; query part columns fit in 16");
+
+  const int item = blockIdx.x;
+  if (item >= *a.n_items_dev) return;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int4 it4 = *(const int4*)(a.items + ITEM_INTS * item);
+  const int4 bl4 = *(const int4*)(a.items + ITEM_INTS * item + 4);
+  const int first = it4.x & 0xffffff, nr = it4.x >> 24, c0 = it4.y, pa = it4.z, ncl = it4.w;
+  const int* rows = a.rowmap + first;
+  const int c = c0 + w;
+  const bool loaded = w < ncl;  // some row of the item reaches this wave's chunk
+  const long long hoff = a.layer_off + (long long)g * ATTN_SPLIT * HD;
+  const int myblk = w == 0 ? bl4.x : w == 1 ? bl4.y : w == 2 ? bl4.z : bl4.w;
+  const long long base = (long long)myblk * a.block_elems + hoff;
+  const unsigned chunk_bytes = (unsigned)ATTN_SPLIT * HD * 2;
+  const __amdgpu_buffer_rsrc_t krs = chunk_rsrc((const uint16_t*)a.kpool + base, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = chunk_rsrc((const uint16_t*)a.vpool + base, chunk_bytes);
+  const unsigned koff = loaded ? ((unsigned)l16 * HD + g4 * 8) * 2 : PAST_RANGE;
+  const unsigned voff = loaded ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : PAST_RANGE;
+  u32x4 kr[4][KK];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = chunk_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
+  KVRaw<D, true> vr[16];
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const unsigned oi = voff + (16 * (it / 4) + it % 4) * HD * 2;
+    if constexpr (D == 8) {
+      const u32x4 v = chunk_ld16(vrs, oi);
+      vr[it].w[0] = v.x;
+      vr[it].w[1] = v.y;
+      vr[it].w[2] = v.z;
+      vr[it].w[3] = v.w;
+    } else {
+      const u32x2 v = chunk_ld8(vrs, oi);
+      vr[it].w[0] = v.x;
+      vr[it].w[1] = v.y;
+    }
+  }
+
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][NQ * G][HD];
+  __shared__ float os[2][MF_WAVES][G][HD], ms[2][MF_WAVES][G], ls[2][MF_WAVES][G];
+  // rotated, split queries of row r of the item into qs[r & 1]
+  auto prep = [&](int r) {
+    const int b = rows[r];
+    const float* qv = a.qkv + (size_t)b * a.Nqkv + (size_t)g * G * HD;
+    const float2* cs = a.rope + (size_t)b * (HD / 2);
+    for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+      const int j = idx / HD, d = idx % HD;
+      const bool fh = d < HD / 2;
+      const float* v = qv + (size_t)j * HD;
+      const float q = rope_pair(v[d], v[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh);
+      const uint16_t hi = f2bf_a(q);
+      const float r1 = q - bf2f(hi);
+      const uint16_t mid = f2bf_a(r1);
+      qs[r & 1][j][d] = hi;
+      qs[r & 1][G + j][d] = mid;
+      if constexpr (NQ == 3) qs[r & 1][2 * G + j][d] = f2bf_a(r1 - bf2f(mid));
+    }
+  };
+  prep(0);
+  __syncthreads();
+  KVRaw<D, true> vnr;
+#pragma unroll
+  for (int i = 0; i < KVRaw<D, true>::NW; ++i) vnr.w[i] = 0u;
+  const size_t pstride = (size_t)G * (HD + 2);
+  for (int r = 0; r < nr; ++r) {
+    const int buf = r & 1;
+    const int p = pa + r, nk = p + 1;
+    const int ncr = min(ATTN_GROUP, p / ATTN_SPLIT + 1 - c0);  // the group's chunks this row reaches
+    u32x4 bq[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 v = *(const u32x4*)&qs[buf][l16 < NQ * G ? l16 : 0][kk * 32 + g4 * 8];
+      bq[kk] = l16 < NQ * G ? v : zero4a();
+    }
+    if (r + 1 < nr) prep(r + 1);
+    if (w < ncr) {
+      const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
+      f32x4 sc[4];
+      mf_scores<HD>(kr, bq, sc);
+      float o[G][D], m, l;
+      mf_softmax_pv<HD, G>(sc, vr, kb, ke, p, nk, false, vnr, g4, o, m, l);
+      if (g4 == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int e = 0; e < D; ++e) os[buf][w][j][l16 * D + e] = o[j][e];
+        if (l16 < G) {
+          ms[buf][w][l16] = m;
+          ls[buf][w][l16] = l;
+        }
+      }
+    }
+    __syncthreads();
+    const int b = rows[r];
+    const bool direct = nk <= ATTN_SPLIT * ATTN_GROUP;
+    float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
+    for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
+      const int j = idx / HD, d = idx % HD;
+      const Merged mr = merge_chunks(ncr, &ms[buf][0][j], &ls[buf][0][j], G, &os[buf][0][j][d], G * HD);
+      if (direct) {
+        put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d, mr.o / mr.l, WT_BF16);
+      } else {
+        dst[(size_t)j * (HD + 2) + d] = mr.o;
+        if (d == 0) {
+          dst[(size_t)j * (HD + 2) + HD] = mr.m;
+          dst[(size_t)j * (HD + 2) + HD + 1] = mr.l;
+        }
+      }
+    }
+  }
+}
+
+// Every row's new key (rotated at the row's position) and value, rounded to
+// the KV format, into slot pos[b] of its lane's block rowblk[b]; one
+// workgroup per row, all KV heads.  The same rotation and rounding as the
+// fused decode kernels.
+template <bool BF>
+__global__ __launch_bounds__(256) void k_kv_append(AttnArgs a, int hd) {
+  const int b = blockIdx.x;
+  const int p = a.pos[b];
+  const int h = hd / 2;
+  const long long base = (long long)a.rowblk[b] * a.block_elems + a.layer_off + (long long)(p % ATTN_SPLIT) * hd;
+  const float* row = a.qkv + (size_t)b * a.Nqkv;
+  const float2* cs = a.rope + (size_t)b * h;
+  for (int e = threadIdx.x; e < a.Hkv * hd; e += blockDim.x) {
+    const int g = e / hd, d = e % hd;
+    const bool fh = d < h;
+    const float* kn = row + (size_t)(a.Hq + g) * hd;
+    const float k = rope_pair(kn[d], kn[fh ? d + h : d - h], cs[fh ? d : d - h], fh);
+    const float v = row[(size_t)(a.Hq + a.Hkv + g) * hd + d];
+    const long long o = base + (long long)g * ATTN_SPLIT * hd + d;
+    if constexpr (BF) {
+      ((uint16_t*)a.kpool)[o] = f2bf_a(k);
+      ((uint16_t*)a.vpool)[o] = f2bf_a(v);
+    } else {
+      ((float*)a.kpool)[o] = k;
+      ((float*)a.vpool)[o] = v;
+    }
   }
 }
 
@@ -778,6 +974,7 @@ __global__ __launch_bounds__(COMB_THREADS) void k_attn_combine(AttnArgs a, int h
   const int j = e / hd, dim = e % hd;
   const int nchunk = (a.pos[b] + 1 + ATTN_SPLIT - 1) / ATTN_SPLIT;
   const int ns = (nchunk + a.per - 1) / a.per;
+  if (ns == 1) return;  // the attention kernel finished the row itself
   const size_t sstride = (size_t)a.Hkv * a.G * (hd + 2);
   const float* P = a.part + (((size_t)b * a.max_splits * a.Hkv + g) * a.G + j) * (hd + 2);
   float M = -INFINITY;
@@ -856,6 +1053,34 @@ hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
     case 128: return launch_hd<128>(kv_bf16, a.G, a, grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attn_rows(int hd, const AttnArgs& a, hipStream_t st) {
+  if (a.max_items <= 0) return hipSuccess;
+  if (!attn_mfma_supported(hd, true, a.G)) return hipErrorInvalidValue;
+  const dim3 grid(a.max_items, a.Hkv), blk(64 * MF_WAVES);
+  switch (hd * 16 + a.G) {
+    case 128 * 16 + 1: hipLaunchKernelGGL((k_attn_rows<128, 1>), grid, blk, 0, st, a); break;
+    case 128 * 16 + 2: hipLaunchKernelGGL((k_attn_rows<128, 2>), grid, blk, 0, st, a); break;
+    case 128 * 16 + 3: hipLaunchKernelGGL((k_attn_rows<128, 3>), grid, blk, 0, st, a); break;
+    case 128 * 16 + 4: hipLaunchKernelGGL((k_attn_rows<128, 4>), grid, blk, 0, st, a); break;
+    case 64 * 16 + 1: hipLaunchKernelGGL((k_attn_rows<64, 1>), grid, blk, 0, st, a); break;
+    case 64 * 16 + 2: hipLaunchKernelGGL((k_attn_rows<64, 2>), grid, blk, 0, st, a); break;
+    case 64 * 16 + 3: hipLaunchKernelGGL((k_attn_rows<64, 3>), grid, blk, 0, st, a); break;
+    case 64 * 16 + 4: hipLaunchKernelGGL((k_attn_rows<64, 4>), grid, blk, 0, st, a); break;
+    case 64 * 16 + 8: hipLaunchKernelGGL((k_attn_rows<64, 8>), grid, blk, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  if (kv_bf16)
+    hipLaunchKernelGGL(k_kv_append<true>, dim3(a.B), dim3(256), 0, st, a, hd);
+  else
+    hipLaunchKernelGGL(k_kv_append<false>, dim3(a.B), dim3(256), 0, st, a, hd);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st) {

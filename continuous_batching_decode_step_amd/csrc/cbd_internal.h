@@ -24,10 +24,12 @@ constexpr int ATTN_GROUP = 4;
 // position, padding, then the arena block of each of up to ATTN_GROUP chunks.
 constexpr int ITEM_INTS = 8;
 // Attention modes: fused (a decode step: each lane's new K/V is written and
-// used by the same launch), append only, attend only (several rows of a lane
-// in one call: all rows' K/V are written first, then every key is read from
-// the cache, so rows never read a slot another workgroup is writing).
-constexpr int ATTN_FUSED = 0, ATTN_APPEND = 1, ATTN_ATTEND = 2;
+// used by the same launch) and attend only (several rows of a lane in one
+// call: launch_kv_append writes every row's K/V first, then every key is read
+// from the cache, so rows never read a slot another workgroup is writing).
+constexpr int ATTN_FUSED = 0, ATTN_ATTEND = 2;
+// Rows of one lane per work item of the batched-prefill attention kernel.
+constexpr int ATTN_ROWS_MAX = 16;
 // Rows of one MFMA tile; 16-row tiles per wave in the projection kernels, by
 // epilogue (SwiGLU pairs a gate tile with an up tile; the LM head has the most
 // rows; the others take one tile so that d-row projections fill the chip).
@@ -84,7 +86,7 @@ struct AttnArgs {
   long long block_elems;  // Hkv * ATTN_SPLIT * hd
   long long layer_off;    // l * n_blocks * block_elems
   int B;
-  int mode;               // ATTN_FUSED, ATTN_APPEND or ATTN_ATTEND
+  int mode;               // ATTN_FUSED or ATTN_ATTEND
   const int* lanes;       // [B] arena lane ids
   const int* pos;         // [B] positions (slot written this step)
   const int* items;       // [n_items][ITEM_INTS] {b | chunks << 24, first chunk, position, 0, block of each chunk (up to 4)}, 16-byte aligned
@@ -101,11 +103,15 @@ struct AttnArgs {
   int qkv_S;
   float* part;            // [B][max_splits][Hkv][G][hd + 2] partials (o, m, l) per chunk or group
   void* out;              // [B, Hq*hd] in the activation format
-  // Every row's keys fit one work item (one partial per lane): the attention
-  // kernel writes out = o / l itself, in the activation format act, and no
-  // combine runs (the combine of a single partial gives exactly o / l).
-  int direct;
+  // A row whose keys fit one work item (one partial) gets out = o / l from the
+  // attention kernel itself, in the activation format act, and the combine
+  // skips it (the combine of a single partial gives exactly o / l).
   int act;                // WT_* of the activation format
+  // Batched prefill (attend mode): rowmap lists the rows of each lane in
+  // position order (work items of launch_attn_rows name a run of it);
+  // rowblk[b] is the block holding slot pos[b] of row b's lane (launch_kv_append).
+  const int* rowmap;
+  const int* rowblk;
 };
 
 // Block sum of per-thread partials (256 threads): a fixed shuffle tree, then
@@ -152,6 +158,14 @@ __host__ __device__ constexpr bool attn_mfma_supported(int hd, bool kv_bf16, int
 }
 // chunk partials of every (lane, KV head, 64-key chunk) item; RoPE and KV append
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
+// Batched-prefill attention (shapes attn_mfma_supported serves): a.max_items
+// work items {first rowmap index | rows << 24, first chunk of the group,
+// position of the first row, chunks of the group the last row reaches, block
+// of each of the group's chunks}, each up to ATTN_ROWS_MAX rows of one lane at
+// consecutive positions, all of which reach the group.
+hipError_t launch_attn_rows(int hd, const AttnArgs& a, hipStream_t st);
+// Every row's new K (rotated) and V into its slot (a.pos, a.rowblk), all heads.
+hipError_t launch_kv_append(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
 // combine a lane's chunks into the attention output (activation format act)
 hipError_t launch_attn_combine(int hd, int act, const AttnArgs& a, hipStream_t st);
 // x[b] = E[token_b]; ssq[b] = sum x[b]^2; rope table of pos_b.

@@ -128,6 +128,8 @@ struct cbd_model {
   hipEvent_t ev[NSLOT] = {};
   bool ev_live[NSLOT] = {};
   int next_slot = 0;
+  // rows of a multi-row call sorted by (lane, position), reused across calls
+  std::vector<int32_t> row_order;
   // per-kernel-class timing
   bool prof = false;
   std::vector<hipEvent_t> ev_pool;
@@ -187,10 +189,12 @@ int attn_partials(const cbd_model* m, int MS) {
   return (MS + per - 1) / per;
 }
 
-// Per-step metadata: lanes[B], positions[B], tokens[B], n_items, padding to a
-// multiple of 4 ints, then the attention work items {b | chunks << 24, first
-// chunk, position, arena lane}, 16-byte aligned (B is at most 65536).
-size_t meta_header(int B) { return ((size_t)3 * B + 1 + 3) & ~(size_t)3; }
+// Per-step metadata: lanes[B], positions[B], tokens[B], rowmap[B], rowblk[B]
+// (multi-row calls: the rows in (lane, position) order, and the block holding
+// each row's slot), n_items, padding to a multiple of 4 ints, then the
+// attention work items (ITEM_INTS ints each), 16-byte aligned (B is at most
+// 65536).
+size_t meta_header(int B) { return ((size_t)5 * B + 1 + 3) & ~(size_t)3; }
 
 // Bytes of the per-step metadata of B rows holding `chunks` 64-key chunks in all.
 size_t meta_bytes_for(int B, long long items) { return 4 * (meta_header(B) + (size_t)ITEM_INTS * items); }
@@ -773,14 +777,14 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
 // Arguments depend only on (B, n_out, multi, workspace layout, arena,
 // outputs): the per-step data (lanes, positions, tokens, attention items) is
 // read from the workspace.
-static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, bool direct, char* ws,
-                        const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st) {
+static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi, bool direct, int row_items,
+                        char* ws, const WsLayout& L, float* logits, int32_t* argmax, hipStream_t st) {
   const cbd_config& c = m->c;
   const int32_t* dmeta = (const int32_t*)(ws + L.meta);
   const int* d_lanes = dmeta;
   const int* d_pos = dmeta + B;
   const int* d_tok = dmeta + 2 * B;
-  const int* d_nitems = dmeta + 3 * B;
+  const int* d_nitems = dmeta + 5 * B;
   const int* d_items = dmeta + meta_header(B);
   float* x = (float*)(ws + L.x);
   float* ssq = (float*)(ws + L.ssq);
@@ -815,8 +819,9 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.rope = rope;
   at.part = (float*)(ws + L.apart);
   at.out = o;
-  at.direct = direct ? 1 : 0;
   at.act = m->wt;
+  at.rowmap = dmeta + 3 * B;
+  at.rowblk = dmeta + 4 * B;
   int rc;
   void* xn = ws + L.xn;
   // RMSNorm of x into xn; ssq_n = row blocks of the last producer of x (the embedding: one)
@@ -842,13 +847,21 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
     {
       ProfScope ps(m, P_ATTN, st);
       if (multi) {
-        at.mode = ATTN_APPEND;
-        HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
+        // every row's K/V first, then every row attends to its lane's cache:
+        // runs of one lane's rows per work item on the matrix-core shapes
+        HIP_TRY(launch_kv_append(c.head_dim, m->wt == WT_BF16, at, st));
         at.mode = ATTN_ATTEND;
+        if (row_items >= 0) {
+          AttnArgs ar = at;
+          ar.max_items = row_items;
+          HIP_TRY(launch_attn_rows(c.head_dim, ar, st));
+        } else {
+          HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
+        }
       } else {
         at.mode = ATTN_FUSED;
+        HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
       }
-      HIP_TRY(launch_attn(c.head_dim, m->wt == WT_BF16, at, st));
     }
     if (!direct) {
       ProfScope ps(m, P_COMB, st);
@@ -887,8 +900,39 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   // created, so a decode step allocates nothing), then one copy to the workspace.
   const size_t hdr = meta_header(B);
   const int per = attn_chunks_per_item(m);
+  // A multi-row call on the matrix-core shapes attends by runs of one lane's
+  // rows at consecutive positions (k_attn_rows): sort the rows by (lane,
+  // position); a run is cut where the lane changes or a position is skipped.
+  const bool by_runs = multi && per == ATTN_GROUP;
+  std::vector<int32_t>& ord = m->row_order;
   long long items = 0;
-  for (int b = 0; b < B; ++b) items += ((positions[b] + ATTN_SPLIT) / ATTN_SPLIT + per - 1) / per;
+  if (by_runs) {
+    ord.resize(B);
+    for (int b = 0; b < B; ++b) ord[b] = b;
+    std::sort(ord.begin(), ord.end(), [&](int x, int y) {
+      return lanes[x] != lanes[y] ? lanes[x] < lanes[y] : positions[x] < positions[y];
+    });
+  }
+  // visits each run [s, e) of ord with its first and last positions
+  auto for_runs = [&](auto&& fn) {
+    for (int s = 0; s < B;) {
+      int e = s + 1;
+      while (e < B && lanes[ord[e]] == lanes[ord[s]] && positions[ord[e]] == positions[ord[e - 1]] + 1) ++e;
+      fn(s, e, positions[ord[s]], positions[ord[e - 1]]);
+      s = e;
+    }
+  };
+  const int GROUP_KEYS = ATTN_SPLIT * ATTN_GROUP;
+  if (by_runs) {
+    for_runs([&](int, int, int P0, int P1) {
+      for (int k = 0; k * GROUP_KEYS <= P1; ++k) {
+        const int lo = std::max(P0, k * GROUP_KEYS);
+        items += (P1 - lo + ATTN_ROWS_MAX) / ATTN_ROWS_MAX;
+      }
+    });
+  } else {
+    for (int b = 0; b < B; ++b) items += ((positions[b] + ATTN_SPLIT) / ATTN_SPLIT + per - 1) / per;
+  }
   const size_t meta_bytes = meta_bytes_for(B, items);
   if (meta_bytes > L.meta_bytes)
     return fail(CBD_E_WORKSPACE, "step metadata of %zu bytes exceeds the workspace's %zu", meta_bytes, L.meta_bytes);
@@ -910,7 +954,32 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   for (size_t i = 3 * (size_t)B; i < hdr; ++i) meta[i] = 0;
   int32_t* it = meta + hdr;
   int n_items = 0;
-  for (int b = 0; b < B; ++b) {
+  if (multi) {
+    for (int b = 0; b < B; ++b) meta[4 * B + b] = a->blocks[lanes[b]][positions[b] / ATTN_SPLIT];
+  }
+  if (by_runs) {
+    // items of a run: for each group k its rows reach (positions from
+    // max(P0, first key of the group)), blocks of ATTN_ROWS_MAX rows
+    for (int b = 0; b < B; ++b) meta[3 * B + b] = ord[b];
+    for_runs([&](int s, int, int P0, int P1) {
+      const std::vector<int>& bl = a->blocks[lanes[ord[s]]];
+      const int nch = P1 / ATTN_SPLIT + 1;  // chunks the run's last row reaches
+      for (int k = 0; k * GROUP_KEYS <= P1; ++k) {
+        const int c0 = k * ATTN_GROUP;
+        for (int pa = std::max(P0, k * GROUP_KEYS); pa <= P1; pa += ATTN_ROWS_MAX) {
+          const int nr = std::min(ATTN_ROWS_MAX, P1 - pa + 1);
+          it[0] = (s + (pa - P0)) | (nr << 24);
+          it[1] = c0;
+          it[2] = pa;
+          it[3] = std::min(ATTN_GROUP, (pa + nr - 1) / ATTN_SPLIT + 1 - c0);
+          for (int q = 0; q < ATTN_GROUP; ++q) it[4 + q] = bl[std::min(c0 + q, nch - 1)];
+          it += ITEM_INTS;
+          ++n_items;
+        }
+      }
+    });
+  }
+  for (int b = 0; !by_runs && b < B; ++b) {
     const int ns = (positions[b] + ATTN_SPLIT) / ATTN_SPLIT;  // chunks holding slots 0..positions[b]
     const std::vector<int>& bl = a->blocks[lanes[b]];
     for (int s0 = 0; s0 < ns; s0 += per) {
@@ -924,7 +993,7 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
       ++n_items;
     }
   }
-  meta[3 * B] = n_items;
+  meta[5 * B] = n_items;
   int32_t* dmeta = (int32_t*)(ws + L.meta);
   {
     ProfScope ps(m, P_META, st);
@@ -941,7 +1010,8 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   int rc;
   const bool graph = m->use_graphs && !m->prof && !multi && !noalloc;  // instantiating a graph allocates
   if (!graph) {
-    if ((rc = enqueue_step(m, a, B, n_out, multi, direct, ws, L, logits, argmax, st))) return rc;
+    if ((rc = enqueue_step(m, a, B, n_out, multi, direct, by_runs ? n_items : -1, ws, L, logits, argmax, st)))
+      return rc;
   } else {
     const cbd_model::GraphKey key{B,          ws,        a,           a->base,    logits,
                                   argmax,     workspace_bytes, a->region_bytes, a->max_seq, a->n_lanes,
@@ -953,7 +1023,7 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
       if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
       hipGraph_t graph_def = nullptr;
       HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-      rc = enqueue_step(m, a, B, n_out, multi, direct, ws, L, logits, argmax, m->cap_stream);
+      rc = enqueue_step(m, a, B, n_out, multi, direct, -1, ws, L, logits, argmax, m->cap_stream);
       hipError_t e = hipStreamEndCapture(m->cap_stream, &graph_def);
       if (rc) {
         if (graph_def) (void)hipGraphDestroy(graph_def);

@@ -376,28 +376,35 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 }
 
 
-// ---- bf16 KV: scores on the matrix cores ---------------------------------------
+// ---- bf16 KV: scores and P.V on the matrix cores ---------------------------------
 //
 // Same work and the same per-chunk results contract as k_attn (chunk partials
-// (o, m, l) of 64 keys, combined in chunk order by k_attn_combine), with the
-// q.k products on MFMA: for each 16-key tile, S^T[key][col] over head_dim as a
-// chain of v_mfma_f32_16x16x32_bf16 with the keys (bf16, as stored) as the A
-// operand and, as the B operand, each query head's rotated f32 query split
-// into three bf16 parts, q = hi + mid + lo exactly (hi = bf16(q), mid =
-// bf16(q - hi), lo = q - hi - mid, which has at most 8 significant bits), in
-// columns j, G + j and 2G + j; the score is col j + (col G + j + col 2G + j).
-// Products of bf16 values are exact in f32, so each score is the f32 sum of
-// the exact products.  With more than five query heads per KV head (3G > 16)
-// the lo part is dropped (q = hi + mid + O(2^-18 |q|)).  P.V stays on the
-// vector ALUs.
+// (o, m, l) of 64 keys, combined in chunk order by k_attn_combine), with both
+// products on MFMA (v_mfma_f32_16x16x32_bf16).
 //
-// A wave takes `nc` consecutive chunks of one lane (an item); each chunk's
-// K and V are loaded one chunk ahead.  Lane mapping for the MFMA: row l16 =
-// key in the tile, lane group g4 holds head dims [g4*HD/4, (g4+1)*HD/4) over
-// the HD/32 k-steps; for P.V, lane (r, c) = (g4, l16) holds dims
-// [c*HD/16, (c+1)*HD/16) of keys 16*(it/4) + 4*r + it%4, it = 0..15, whose
-// probabilities sit in lane 16*r + j, register (it/4, it%4), of the score
-// layout.
+// Scores: for each 16-key tile, S^T[key][col] over head_dim with the keys (bf16,
+// as stored) as the A operand and, as the B operand, each query head's rotated
+// f32 query split into bf16 parts, q = hi + mid + lo exactly (hi = bf16(q),
+// mid = bf16(q - hi), lo = q - hi - mid, which has at most 8 significant bits),
+// in columns CPH*j, CPH*j + 1 and CPH*j + 2 of head j; the score is hi + (mid +
+// lo).  Products of bf16 values are exact in f32, so each score is the f32 sum
+// of the exact products.  With more than four query heads per KV head (CPH = 2)
+// the lo part is dropped (q = hi + mid + O(2^-18 |q|)).
+//
+// P.V: the probabilities p (f32) split the same way into bf16 parts, in the A
+// operand's rows CPH*j + part, against the values as the B operand; head j's
+// output is the f32 sum hi + (mid + lo) of its part rows.  Since p = hi + mid +
+// lo exactly, every product is exact and the sums are f32 sums of the exact
+// products, as the f32 vector path gives.
+//
+// Lane roles (l16 = lane % 16, g4 = lane / 16): the score tile leaves S[key
+// 16t + 4*g4 + i][col l16] in lane (l16, g4), register (t, i); the four lanes
+// of head j's columns combine its parts by quad-lane DPP and so all hold its
+// score, softmax statistics and p for those keys.  The P.V A operand of lane
+// (row l16, g4) over a 32-key block u is exactly those 8 keys (k = 8*g4 + e for
+// key 32u + 16*(e >> 2) + 4*g4 + (e & 3)), so the lane forms its part of p in
+// registers, and the values are stored in that key order (vfrag_off): one
+// 16-byte load per (dim tile, key block).
 __device__ inline u32x4 zero4a() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // Buffer-descriptor loads over one chunk of one (layer, KV head) in its block:
@@ -413,44 +420,48 @@ __device__ inline __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, unsigned b
 __device__ inline u32x4 chunk_ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-__device__ inline u32x2 chunk_ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+
+// Quad-lane DPP broadcast: every lane takes lane Q of its group of four (a
+// vector-ALU operand modifier, no trip through the LDS crossbar).
+template <int CTRL>
+__device__ inline float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
 }
 
-// Cross-lane moves within a row of 16 lanes by DPP (a vector-ALU operand modifier,
-// no trip through the LDS crossbar): every lane of row r takes lane 16r + J, or
-// lane i takes lane i + N of its row (the row's last N lanes keep their own value).
-template <int J>
-__device__ inline float row_bcast(float v) {
-  static_assert(J >= 0 && J < 16, "lane within a row");
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                                               0x150 + J, 0xF, 0xF, false));
-}
-template <int N>
-__device__ inline float row_shl(float v) {
-  static_assert(N >= 1 && N < 16, "shift within a row");
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                                               0x100 + N, 0xF, 0xF, false));
-}
-template <int J>
-struct RowBcastAll {
-  // out[j] = row_bcast<j>(v) for j < J
-  __device__ static inline void run(float v, float* out) {
-    RowBcastAll<J - 1>::run(v, out);
-    out[J - 1] = row_bcast<J - 1>(v);
-  }
+// Score columns per query head and bf16 parts of each query and probability.
+template <int G>
+struct MfCols {
+  static constexpr int CPH = G <= 4 ? 4 : 2;
+  static constexpr int NQ = CPH == 4 ? 3 : 2;
+  static_assert(G >= 1 && G * CPH <= 16, "query heads per KV head");
 };
-template <>
-struct RowBcastAll<0> {
-  __device__ static inline void run(float, float*) {}
-};
+
+// Two f32 values to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ inline unsigned pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// Part `part` (0 hi, 1 mid, 2 lo, else zero) of two probabilities, packed:
+// hi = bf16(p), mid = bf16(p - hi), lo = bf16(p - hi - mid); each difference
+// is exact, so hi + mid + lo = p exactly.
+__device__ inline unsigned p_part2(float a, float b, int part) {
+  const unsigned hi = pk_bf16(a, b);
+  const float ra = a - __builtin_bit_cast(float, hi << 16), rb = b - __builtin_bit_cast(float, hi & 0xffff0000u);
+  const unsigned mid = pk_bf16(ra, rb);
+  const float sa = ra - __builtin_bit_cast(float, mid << 16), sb = rb - __builtin_bit_cast(float, mid & 0xffff0000u);
+  const unsigned lo = pk_bf16(sa, sb);
+  return part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
+}
 
 // The per-chunk work of a wave, shared by the decode kernel (k_attn_mf) and
 // the prefill kernel (k_attn_rows) so that both give the same bits.
 //
-// Scores S^T[key][col] of one 64-key chunk: four 16-key tiles, each a chain of
-// MFMAs over head_dim with the keys as the A operand (kr[t][kk]: key 16t + l16,
-// dims kk*32 + g4*8 ..) and the query parts as the B operand.
+// Scores of one 64-key chunk: four 16-key tiles, each a chain of MFMAs over
+// head_dim with the keys as the A operand (kr[t][kk]: fragment (t, kk) of the
+// chunk) and the query parts as the B operand.
 template <int HD>
 __device__ inline void mf_scores(const u32x4 (&kr)[4][HD / 32], const u32x4 (&bq)[HD / 32], f32x4 (&sc)[4]) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -465,31 +476,58 @@ __device__ inline void mf_scores(const u32x4 (&kr)[4][HD / 32], const u32x4 (&bq
   }
 }
 
-// Softmax statistics and P.V of the chunk from its scores: keys below ke
-// count (the rest are masked), value words vr[it] of key kb + 16*(it/4) +
-// 4*g4 + it%4 as loaded; a key at or past pk is zeroed and, if has_new, key p
-// takes vnr.  Leaves o[j][e] (dims l16*D + e of group head j, summed over the
-// wave's four lane rows, in every lane) and, in lanes l16 = j < G, head j's
-// maximum m and sum l.
+// Value fragments vf[u][dt] of a chunk with the keys at or past pk zeroed and,
+// if has_new, key p (in this chunk) replaced by the new value vn (bf16 words,
+// dims 0..HD-1, in LDS).  kb: the chunk's first key.
+template <int HD>
+__device__ inline void mf_mask_v(u32x4 (&vf)[2][HD / 16], int kb, int pk, bool has_new, int p, int g4, int l16,
+                                 const uint16_t* vn) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // dword w holds keys e = 2w, 2w + 1: key 32u + 16*(w >> 1) + 4*g4 + 2*(w & 1) (+1)
+      const int k0 = kb + 32 * u + 16 * (w >> 1) + 4 * g4 + 2 * (w & 1);
+      const unsigned keep = (k0 < pk ? 0xffffu : 0u) | (k0 + 1 < pk ? 0xffff0000u : 0u);
+      const unsigned take = !has_new ? 0u : k0 == p ? 0xffffu : k0 + 1 == p ? 0xffff0000u : 0u;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        unsigned x = vf[u][dt][w] & keep;
+        if (take) {
+          const unsigned nv = vn[16 * dt + l16];
+          x = (x & ~take) | ((nv | (nv << 16)) & take);
+        }
+        vf[u][dt][w] = x;
+      }
+    }
+}
+
+// Softmax statistics and P.V of the chunk from its scores and its value
+// fragments (masked): keys below ke count.  Leaves, in lane (l16, g4), the
+// output o[r][dt] = dim 16*dt + l16 of the head of part row 4*g4 + r*CPH (r <
+// 4 / CPH; CPH = 4: head g4, CPH = 2: heads 2*g4 and 2*g4 + 1), and head
+// l16 / CPH's maximum m and sum l (every lane).
 template <int HD, int G>
-__device__ inline void mf_softmax_pv(const f32x4 (&sc)[4], const KVRaw<HD / 16, true> (&vr)[16], int kb, int ke, int p,
-                                     int pk, bool has_new, const KVRaw<HD / 16, true>& vnr, int g4,
-                                     float (&o)[G][HD / 16], float& m, float& l) {
-  constexpr int D = HD / 16;
-  constexpr int NQ = 3 * G <= 16 ? 3 : 2;
+__device__ inline void mf_softmax_pv(const f32x4 (&sc)[4], const u32x4 (&vf)[2][HD / 16], int kb, int ke, int g4,
+                                     int l16, float (&o)[4 / MfCols<G>::CPH][HD / 16], float& m, float& l) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int CPH = MfCols<G>::CPH;
+  constexpr int DT = HD / 16;
   const float inv = 1.0f / sqrtf((float)HD);
-  // hi + (mid + lo), scale, mask; softmax statistics of head l16 (lanes l16 < G)
+  // hi + (mid + lo) of the lane's head, scale, mask
   float pr[4][4];
   m = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // columns G + j and 2G + j (used by the lanes of columns j < G)
-      float rest = row_shl<G>(sc[t][i]);
-      if constexpr (NQ == 3) rest = rest + row_shl<(NQ == 3 ? 2 * G : 1)>(sc[t][i]);
+      float s;
+      if constexpr (CPH == 4)
+        s = quad_perm<0x00>(sc[t][i]) + (quad_perm<0x55>(sc[t][i]) + quad_perm<0xAA>(sc[t][i]));
+      else
+        s = quad_perm<0xA0>(sc[t][i]) + quad_perm<0xF5>(sc[t][i]);
       const int key = kb + 16 * t + 4 * g4 + i;
-      const float v = (sc[t][i] + rest) * inv;
+      const float v = s * inv;
       pr[t][i] = key < ke ? v : -INFINITY;
       m = fmaxf(m, pr[t][i]);
     }
@@ -508,48 +546,35 @@ __device__ inline void mf_softmax_pv(const f32x4 (&sc)[4], const KVRaw<HD / 16, 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // P.V on the vector ALUs
+  // A operand of key block u: this lane's part of p for keys 32u + 16*(e >> 2) + 4*g4 + (e & 3)
+  const int part = l16 % CPH;
+  u32x4 pa[2];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[j][e] = 0.f;
-  // A chunk wholly below slot p needs no masking: every key is an old, valid
-  // one (a uniform branch).
-  auto pv_pass = [&](auto masked) {
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      KVRaw<D, true> x = vr[it];
-      if constexpr (decltype(masked)::value) {
-        const int key = kb + 16 * (it / 4) + 4 * g4 + it % 4;
-        const unsigned take = has_new && key == p ? ~0u : 0u;
-        const unsigned keep = key < pk ? ~0u : 0u;
-        raw_select<D, true>(x, keep, take, vnr);
-      }
-      float vv[D];
-      raw_to_f32<D, true>(x, vv);
-      float pjs[G];  // the probability of this key for each group head, from lane 16*g4 + j
-      RowBcastAll<G>::run(pr[it / 4][it % 4], pjs);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-#pragma unroll
-        for (int e = 0; e < D; ++e) o[j][e] += pjs[j] * vv[e];
-      }
-      if (it % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live converted values
+    for (int w = 0; w < 4; ++w) {
+      const int t = 2 * u + (w >> 1), i = 2 * (w & 1);
+      pa[u][w] = p_part2(pr[t][i], pr[t][i + 1], part);
     }
-  };
-  if (p >= kb + ATTN_SPLIT)
-    pv_pass(std::false_type{});
-  else
-    pv_pass(std::true_type{});
+  f32x4 acc[DT];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < D; ++e) {
-      float v = o[j][e];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      o[j][e] = v;
+    for (int u = 0; u < 2; ++u)
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa[u]), __builtin_bit_cast(bf16x8, vf[u][dt]),
+                                                  a, 0, 0, 0);
+    acc[dt] = a;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    if constexpr (CPH == 4) {
+      o[0][dt] = acc[dt][0] + (acc[dt][1] + acc[dt][2]);
+    } else {
+      o[0][dt] = acc[dt][0] + acc[dt][1];
+      o[1][dt] = acc[dt][2] + acc[dt][3];
     }
+  }
 }
 
 // A group's chunk partials merged in chunk order into one partial: with
@@ -572,6 +597,75 @@ __device__ inline Merged merge_chunks(int nc, const float* ms, const float* ls, 
   return Merged{Or, Lr, Mr};
 }
 
+// Rotated query parts of the group's G heads (f32 head vectors at qv + j*HD,
+// rotation table cs) into the score B-operand rows qs[CPH*j + part].
+template <int HD, int G>
+__device__ inline void mf_prep_queries(const float* qv, const float2* cs, uint16_t (*qs)[HD], int tid, int nthr) {
+  constexpr int CPH = MfCols<G>::CPH;
+  for (int idx = tid; idx < G * HD; idx += nthr) {
+    const int j = idx / HD, d = idx % HD;
+    const bool fh = d < HD / 2;
+    const float* v = qv + (size_t)j * HD;
+    const float q = rope_pair(v[d], v[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh);
+    const uint16_t hi = f2bf_a(q);
+    const float r1 = q - bf2f(hi);  // exact
+    const uint16_t mid = f2bf_a(r1);
+    qs[CPH * j][d] = hi;
+    qs[CPH * j + 1][d] = mid;
+    if constexpr (MfCols<G>::NQ == 3) qs[CPH * j + 2][d] = f2bf_a(r1 - bf2f(mid));  // exact: at most 8 significant bits
+  }
+}
+
+// The score B operand of lane (col l16, g4) from the query rows in LDS (zero
+// for the columns no part uses).
+template <int HD, int G>
+__device__ inline void mf_load_bq(const uint16_t (*qs)[HD], int l16, int g4, u32x4 (&bq)[HD / 32]) {
+  constexpr int CPH = MfCols<G>::CPH;
+  const bool used = l16 < CPH * G && l16 % CPH < MfCols<G>::NQ;
+#pragma unroll
+  for (int kk = 0; kk < HD / 32; ++kk) {
+    const u32x4 v = *(const u32x4*)&qs[used ? l16 : 0][kk * 32 + g4 * 8];
+    bq[kk] = used ? v : zero4a();
+  }
+}
+
+// Chunk fragments of one wave: K (score A operand) and V (P.V B operand), one
+// 16-byte load per fragment and lane; 1 KB per wave-wide load.
+template <int HD>
+__device__ inline void mf_load_k(__amdgpu_buffer_rsrc_t krs, unsigned off, u32x4 (&kr)[4][HD / 32]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kk = 0; kk < HD / 32; ++kk) kr[t][kk] = chunk_ld16(krs, off + (t * (HD / 32) + kk) * 1024);
+}
+template <int HD>
+__device__ inline void mf_load_v(__amdgpu_buffer_rsrc_t vrs, unsigned off, u32x4 (&vf)[2][HD / 16]) {
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vf[u][dt] = chunk_ld16(vrs, off + (dt * 2 + u) * 1024);
+}
+
+// One wave's chunk partial to LDS: outputs of its heads, and the statistics
+// (lane l16 = CPH*j of lane row 0 holds head j's).
+template <int HD, int G>
+__device__ inline void mf_store_partial(const float (&o)[4 / MfCols<G>::CPH][HD / 16], float m, float l, int g4,
+                                        int l16, float (*os)[HD], float* ms, float* ls) {
+  constexpr int CPH = MfCols<G>::CPH;
+#pragma unroll
+  for (int r = 0; r < 4 / CPH; ++r) {
+    const int j = (4 / CPH) * g4 + r;
+    if (j < G) {
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) os[j][16 * dt + l16] = o[r][dt];
+    }
+  }
+  if (g4 == 0 && l16 % CPH == 0 && l16 / CPH < G) {
+    ms[l16 / CPH] = m;
+    ls[l16 / CPH] = l;
+  }
+}
+
 // One workgroup per (lane, KV head, aligned group of ATTN_GROUP chunks), one
 // wave per chunk.  Each wave computes its chunk's partial (o, m, l) exactly as
 // a one-chunk work item would; the partials meet in LDS and are merged in
@@ -584,9 +678,9 @@ constexpr int MF_WAVES = ATTN_GROUP;
 template <int HD, int G>
 __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mf(AttnArgs a) {
   constexpr int KK = HD / 32;   // MFMA k-steps over head_dim
-  constexpr int D = HD / 16;    // dims per lane in the P.V layout
-  constexpr int NQ = 3 * G <= 16 ? 3 : 2;  // bf16 parts of each query (columns j, G + j, 2G + j)
-  static_assert(ATTN_SPLIT == 64 && NQ * G <= 16, "four 16-key tiles; query part columns fit in 16");
+  constexpr int DT = HD / 16;   // 16-dim tiles of the output
+  constexpr int CPH = MfCols<G>::CPH;
+  static_assert(ATTN_SPLIT == 64, "four 16-key tiles, two 32-key blocks");
 
   const int item = blockIdx.x;
   if (item >= *a.n_items_dev) return;  // the whole workgroup leaves together
@@ -607,13 +701,13 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const int pk = fused ? p : nk;  // keys below pk are read from the cache
   const bool active = w < nc;     // waves that attend to a chunk
   // (layer, head) offset inside a block; base: this wave's chunk (inactive
-  // waves: the last chunk's, never read); lbase: the group's last chunk,
+  // waves: the last chunk's, never read); pbase: the group's last chunk,
   // which holds slot p when the group is the lane's last
   const long long hoff = a.layer_off + (long long)g * ATTN_SPLIT * HD;
   const int myblk = w == 0 ? bl4.x : w == 1 ? bl4.y : w == 2 ? bl4.z : bl4.w;
   const int lastblk = nc == 1 ? bl4.x : nc == 2 ? bl4.y : nc == 3 ? bl4.z : bl4.w;
   const long long base = (long long)(active ? myblk : lastblk) * a.block_elems + hoff;
-  const long long lbase = (long long)lastblk * a.block_elems + hoff - (long long)(c0 + nc - 1) * ATTN_SPLIT * HD;
+  const long long pbase = (long long)lastblk * a.block_elems + hoff;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * (HD / 2);
   const uint16_t* kpool = (const uint16_t*)a.kpool;
@@ -625,22 +719,13 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const unsigned chunk_bytes = (unsigned)ATTN_SPLIT * HD * 2;
   const __amdgpu_buffer_rsrc_t krs = chunk_rsrc(kpool + base, chunk_bytes);
   const __amdgpu_buffer_rsrc_t vrs = chunk_rsrc(vpool + base, chunk_bytes);
-  const unsigned koff = active ? ((unsigned)l16 * HD + g4 * 8) * 2 : PAST_RANGE;
-  const unsigned voff = active ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : PAST_RANGE;
+  const unsigned foff = active ? (unsigned)lane * 16 : PAST_RANGE;
   u32x4 kr[4][KK];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = chunk_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
-  // rotated value of dim d of an f32 head vector v
-  auto rot = [&](const float* v, int d) -> float {
-    const bool first = d < HD / 2;
-    return rope_pair(v[d], v[first ? d + HD / 2 : d - HD / 2], cs[first ? d : d - HD / 2], first);
-  };
+  mf_load_k<HD>(krs, foff, kr);
   // The workgroup rotates the group's queries (split into bf16 parts) and, if
   // its last chunk holds slot p, the new key and value, through LDS; lanes
   // then read their MFMA operand rows from there.
-  __shared__ __attribute__((aligned(16))) uint16_t qs[NQ * G][HD];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[16][HD];
   __shared__ __attribute__((aligned(16))) uint16_t kvn[2][HD];
   __shared__ float os[MF_WAVES][G][HD], ms[MF_WAVES][G], ls[MF_WAVES][G];
   // When the QKV projection ran in split mode without its fold, the workgroup
@@ -674,42 +759,28 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   } else {
     qv = row + (size_t)g * G * HD;
   }
-  for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
-    const int j = idx / HD, d = idx % HD;
-    const float q = rot(qv + (size_t)j * HD, d);
-    const uint16_t hi = f2bf_a(q);
-    const float r1 = q - bf2f(hi);  // exact
-    const uint16_t mid = f2bf_a(r1);
-    qs[j][d] = hi;
-    qs[G + j][d] = mid;
-    if constexpr (NQ == 3) qs[2 * G + j][d] = f2bf_a(r1 - bf2f(mid));  // exact: at most 8 significant bits
-  }
+  mf_prep_queries<HD, G>(qv, cs, qs, tid, 64 * MF_WAVES);
   if (holds_p) {
+    const int pc = p % ATTN_SPLIT;
     for (int d = tid; d < HD; d += 64 * MF_WAVES) {
-      const uint16_t kw = f2bf_a(rot(kn, d)), vw = f2bf_a(vn[d]);
+      const bool fh = d < HD / 2;
+      const uint16_t kw = f2bf_a(rope_pair(kn[d], kn[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh));
+      const uint16_t vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;
       kvn[1][d] = vw;
-      ((uint16_t*)a.kpool)[lbase + (long long)p * HD + d] = kw;
-      ((uint16_t*)a.vpool)[lbase + (long long)p * HD + d] = vw;
+      ((uint16_t*)a.kpool)[pbase + kfrag_off(pc, d, HD)] = kw;
+      ((uint16_t*)a.vpool)[pbase + vfrag_off(pc, d, HD)] = vw;
     }
   }
   __syncthreads();
 
   if (active) {
     u32x4 bq[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 v = *(const u32x4*)&qs[l16 < NQ * G ? l16 : 0][kk * 32 + g4 * 8];
-      bq[kk] = l16 < NQ * G ? v : zero4a();
-    }
+    mf_load_bq<HD, G>(qs, l16, g4, bq);
     const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
     const bool has_new = fused && p >= kb && p < kb + ATTN_SPLIT;
-    // the new key and value replace slot p's old contents
-    KVRaw<D, true> vnr;
-#pragma unroll
-    for (int i = 0; i < KVRaw<D, true>::NW; ++i) vnr.w[i] = 0u;
+    // the new key replaces slot p's old contents
     if (has_new) {
-      vnr = *(const KVRaw<D, true>*)&kvn[1][l16 * D];
       const int tp = (p - kb) >> 4, rp = (p - kb) & 15;
       const unsigned take = l16 == rp ? ~0u : 0u;
 #pragma unroll
@@ -726,37 +797,15 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     f32x4 sc[4];
     mf_scores<HD>(kr, bq, sc);
 
-    // V is loaded once the scores are issued: holding K and V for the whole
-    // wave from the start costs ~22 more registers, and the values are needed
-    // only after the softmax (B = 8: attention 26.3 -> 24.9 us; B = 64 unchanged)
-    KVRaw<D, true> vr[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const unsigned oi = voff + (16 * (it / 4) + it % 4) * HD * 2;
-      if constexpr (D == 8) {
-        const u32x4 v = chunk_ld16(vrs, oi);
-        vr[it].w[0] = v.x;
-        vr[it].w[1] = v.y;
-        vr[it].w[2] = v.z;
-        vr[it].w[3] = v.w;
-      } else {
-        const u32x2 v = chunk_ld8(vrs, oi);
-        vr[it].w[0] = v.x;
-        vr[it].w[1] = v.y;
-      }
-    }
-    float o[G][D], m, l;
-    mf_softmax_pv<HD, G>(sc, vr, kb, ke, p, pk, has_new, vnr, g4, o, m, l);
-    if (g4 == 0) {
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < D; ++e) os[w][j][l16 * D + e] = o[j][e];
-      if (l16 < G) {
-        ms[w][l16] = m;
-        ls[w][l16] = l;
-      }
-    }
+    // V is loaded once the scores are issued: the values are needed only
+    // after the softmax, and the K fragments' registers are free by then
+    u32x4 vf[2][DT];
+    mf_load_v<HD>(vrs, foff, vf);
+    // a chunk wholly below slot p needs no masking (a uniform branch)
+    if (p < kb + ATTN_SPLIT) mf_mask_v<HD>(vf, kb, pk, has_new, p, g4, l16, kvn[1]);
+    float o[4 / CPH][DT], m, l;
+    mf_softmax_pv<HD, G>(sc, vf, kb, ke, g4, l16, o, m, l);
+    mf_store_partial<HD, G>(o, m, l, g4, l16, os[w], ms[w], ls[w]);
   }
   __syncthreads();
 
@@ -786,22 +835,21 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
 // prompt enters as many rows of one call.  Every row of a lane attends to
 // the same cache, so one work item takes up to ATTN_ROWS_MAX consecutive rows of
 // one lane (positions pa .. pa + nr - 1) and one aligned group of ATTN_GROUP
-// chunks: each wave loads its chunk's K and V once and keeps them in
-// registers while it computes the chunk partial of every row that reaches it,
-// the same per-chunk code and merge as k_attn_mf (so a row's partial has the
-// bits a decode step at that position gives).  Per row: the workgroup
-// rotates and splits the next row's queries into the other half of a
-// double-buffered LDS area, every wave writes its chunk partial, one barrier,
-// and the row's group partial (or, for a row with one partial, its output)
-// is merged and written.  Every row's key and value are in the cache already
-// (k_kv_append runs first).
-
+// chunks: each wave loads its chunk's K and V fragments once and keeps them
+// in registers while it computes the chunk partial of every row that reaches
+// it, with the same per-chunk code and merge as k_attn_mf (so a row's
+// partial has the bits a decode step at that position gives).  Per row: the
+// workgroup rotates and splits the next row's queries into the other half of
+// a double-buffered LDS area, every wave writes its chunk partial, one
+// barrier, and the row's group partial (or, for a row with one partial, its
+// output) is merged and written.  Every row's key and value are in the cache
+// already (k_kv_append runs first).
 template <int HD, int G>
 __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_rows(AttnArgs a) {
   constexpr int KK = HD / 32;
-  constexpr int D = HD / 16;
-  constexpr int NQ = 3 * G <= 16 ? 3 : 2;
-  static_assert(ATTN_SPLIT == 64 && NQ * G <= 16, "four 16-key tiles; query part columns fit in 16");
+  constexpr int DT = HD / 16;
+  constexpr int CPH = MfCols<G>::CPH;
+  static_assert(ATTN_SPLIT == 64, "four 16-key tiles, two 32-key blocks");
 
   const int item = blockIdx.x;
   if (item >= *a.n_items_dev) return;
@@ -821,83 +869,45 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const unsigned chunk_bytes = (unsigned)ATTN_SPLIT * HD * 2;
   const __amdgpu_buffer_rsrc_t krs = chunk_rsrc((const uint16_t*)a.kpool + base, chunk_bytes);
   const __amdgpu_buffer_rsrc_t vrs = chunk_rsrc((const uint16_t*)a.vpool + base, chunk_bytes);
-  const unsigned koff = loaded ? ((unsigned)l16 * HD + g4 * 8) * 2 : PAST_RANGE;
-  const unsigned voff = loaded ? ((unsigned)(4 * g4) * HD + l16 * D) * 2 : PAST_RANGE;
-  u32x4 kr[4][KK];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[t][kk] = chunk_ld16(krs, koff + (16 * t * HD + kk * 32) * 2);
-  KVRaw<D, true> vr[16];
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const unsigned oi = voff + (16 * (it / 4) + it % 4) * HD * 2;
-    if constexpr (D == 8) {
-      const u32x4 v = chunk_ld16(vrs, oi);
-      vr[it].w[0] = v.x;
-      vr[it].w[1] = v.y;
-      vr[it].w[2] = v.z;
-      vr[it].w[3] = v.w;
-    } else {
-      const u32x2 v = chunk_ld8(vrs, oi);
-      vr[it].w[0] = v.x;
-      vr[it].w[1] = v.y;
-    }
-  }
+  const unsigned foff = loaded ? (unsigned)lane * 16 : PAST_RANGE;
+  u32x4 kr[4][KK], vf[2][DT];
+  mf_load_k<HD>(krs, foff, kr);
+  mf_load_v<HD>(vrs, foff, vf);
 
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][NQ * G][HD];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][16][HD];
   __shared__ float os[2][MF_WAVES][G][HD], ms[2][MF_WAVES][G], ls[2][MF_WAVES][G];
-  // rotated, split queries of row r of the item into qs[r & 1]
   auto prep = [&](int r) {
     const int b = rows[r];
-    const float* qv = a.qkv + (size_t)b * a.Nqkv + (size_t)g * G * HD;
-    const float2* cs = a.rope + (size_t)b * (HD / 2);
-    for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {
-      const int j = idx / HD, d = idx % HD;
-      const bool fh = d < HD / 2;
-      const float* v = qv + (size_t)j * HD;
-      const float q = rope_pair(v[d], v[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh);
-      const uint16_t hi = f2bf_a(q);
-      const float r1 = q - bf2f(hi);
-      const uint16_t mid = f2bf_a(r1);
-      qs[r & 1][j][d] = hi;
-      qs[r & 1][G + j][d] = mid;
-      if constexpr (NQ == 3) qs[r & 1][2 * G + j][d] = f2bf_a(r1 - bf2f(mid));
-    }
+    mf_prep_queries<HD, G>(a.qkv + (size_t)b * a.Nqkv + (size_t)g * G * HD, a.rope + (size_t)b * (HD / 2), qs[r & 1],
+                           tid, 64 * MF_WAVES);
   };
   prep(0);
   __syncthreads();
-  KVRaw<D, true> vnr;
-#pragma unroll
-  for (int i = 0; i < KVRaw<D, true>::NW; ++i) vnr.w[i] = 0u;
   const size_t pstride = (size_t)G * (HD + 2);
   for (int r = 0; r < nr; ++r) {
     const int buf = r & 1;
     const int p = pa + r, nk = p + 1;
     const int ncr = min(ATTN_GROUP, p / ATTN_SPLIT + 1 - c0);  // the group's chunks this row reaches
     u32x4 bq[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 v = *(const u32x4*)&qs[buf][l16 < NQ * G ? l16 : 0][kk * 32 + g4 * 8];
-      bq[kk] = l16 < NQ * G ? v : zero4a();
-    }
+    mf_load_bq<HD, G>(qs[buf], l16, g4, bq);
     if (r + 1 < nr) prep(r + 1);
     if (w < ncr) {
       const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
       f32x4 sc[4];
       mf_scores<HD>(kr, bq, sc);
-      float o[G][D], m, l;
-      mf_softmax_pv<HD, G>(sc, vr, kb, ke, p, nk, false, vnr, g4, o, m, l);
-      if (g4 == 0) {
+      float o[4 / CPH][DT], m, l;
+      if (p < kb + ATTN_SPLIT) {  // the row's last chunk: keys past p zeroed in a copy
+        u32x4 vm[2][DT];
 #pragma unroll
-        for (int j = 0; j < G; ++j)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int e = 0; e < D; ++e) os[buf][w][j][l16 * D + e] = o[j][e];
-        if (l16 < G) {
-          ms[buf][w][l16] = m;
-          ls[buf][w][l16] = l;
-        }
+          for (int dt = 0; dt < DT; ++dt) vm[u][dt] = vf[u][dt];
+        mf_mask_v<HD>(vm, kb, nk, false, p, g4, l16, nullptr);
+        mf_softmax_pv<HD, G>(sc, vm, kb, ke, g4, l16, o, m, l);
+      } else {
+        mf_softmax_pv<HD, G>(sc, vf, kb, ke, g4, l16, o, m, l);
       }
+      mf_store_partial<HD, G>(o, m, l, g4, l16, os[buf][w], ms[buf][w], ls[buf][w]);
     }
     __syncthreads();
     const int b = rows[r];
@@ -920,15 +930,15 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // Every row's new key (rotated at the row's position) and value, rounded to
-// the KV format, into slot pos[b] of its lane's block rowblk[b]; one
-// workgroup per row, all KV heads.  The same rotation and rounding as the
-// fused decode kernels.
+// the KV format, into slot pos[b] of its lane's block rowblk[b] (fragment
+// order when a.frag is set); one workgroup per row, all KV heads.  The same
+// rotation and rounding as the fused decode kernels.
 template <bool BF>
 __global__ __launch_bounds__(256) void k_kv_append(AttnArgs a, int hd) {
   const int b = blockIdx.x;
   const int p = a.pos[b];
-  const int h = hd / 2;
-  const long long base = (long long)a.rowblk[b] * a.block_elems + a.layer_off + (long long)(p % ATTN_SPLIT) * hd;
+  const int h = hd / 2, pc = p % ATTN_SPLIT;
+  const long long base = (long long)a.rowblk[b] * a.block_elems + a.layer_off;
   const float* row = a.qkv + (size_t)b * a.Nqkv;
   const float2* cs = a.rope + (size_t)b * h;
   for (int e = threadIdx.x; e < a.Hkv * hd; e += blockDim.x) {
@@ -937,13 +947,15 @@ __global__ __launch_bounds__(256) void k_kv_append(AttnArgs a, int hd) {
     const float* kn = row + (size_t)(a.Hq + g) * hd;
     const float k = rope_pair(kn[d], kn[fh ? d + h : d - h], cs[fh ? d : d - h], fh);
     const float v = row[(size_t)(a.Hq + a.Hkv + g) * hd + d];
-    const long long o = base + (long long)g * ATTN_SPLIT * hd + d;
+    const long long cb = base + (long long)g * ATTN_SPLIT * hd;
+    const long long ko = cb + (a.frag ? kfrag_off(pc, d, hd) : pc * hd + d);
+    const long long vo = cb + (a.frag ? vfrag_off(pc, d, hd) : pc * hd + d);
     if constexpr (BF) {
-      ((uint16_t*)a.kpool)[o] = f2bf_a(k);
-      ((uint16_t*)a.vpool)[o] = f2bf_a(v);
+      ((uint16_t*)a.kpool)[ko] = f2bf_a(k);
+      ((uint16_t*)a.vpool)[vo] = f2bf_a(v);
     } else {
-      ((float*)a.kpool)[o] = k;
-      ((float*)a.vpool)[o] = v;
+      ((float*)a.kpool)[ko] = k;
+      ((float*)a.vpool)[vo] = v;
     }
   }
 }
@@ -1026,14 +1038,18 @@ static hipError_t launch_hd(int kv_bf16, int G, const AttnArgs& a, dim3 grid, hi
 
 template <int HD>
 static hipError_t launch_mf(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  const dim3 blk(64 * MF_WAVES);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_mf<HD, 1>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_mf<HD, 2>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_mf<HD, 3>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_mf<HD, 4>), grid, dim3(64 * MF_WAVES), 0, st, a); break;
-    case 8:
+    case 1: hipLaunchKernelGGL((k_attn_mf<HD, 1>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_mf<HD, 2>), grid, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_mf<HD, 3>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_mf<HD, 4>), grid, blk, 0, st, a); break;
+    case 5: case 6: case 7: case 8:
       if constexpr (HD == 64) {
-        hipLaunchKernelGGL((k_attn_mf<HD, 8>), grid, dim3(64 * MF_WAVES), 0, st, a);
+        if (G == 5) hipLaunchKernelGGL((k_attn_mf<HD, 5>), grid, blk, 0, st, a);
+        if (G == 6) hipLaunchKernelGGL((k_attn_mf<HD, 6>), grid, blk, 0, st, a);
+        if (G == 7) hipLaunchKernelGGL((k_attn_mf<HD, 7>), grid, blk, 0, st, a);
+        if (G == 8) hipLaunchKernelGGL((k_attn_mf<HD, 8>), grid, blk, 0, st, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -1055,23 +1071,33 @@ hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_attn_rows(int hd, const AttnArgs& a, hipStream_t st) {
-  if (a.max_items <= 0) return hipSuccess;
-  if (!attn_mfma_supported(hd, true, a.G)) return hipErrorInvalidValue;
-  const dim3 grid(a.max_items, a.Hkv), blk(64 * MF_WAVES);
-  switch (hd * 16 + a.G) {
-    case 128 * 16 + 1: hipLaunchKernelGGL((k_attn_rows<128, 1>), grid, blk, 0, st, a); break;
-    case 128 * 16 + 2: hipLaunchKernelGGL((k_attn_rows<128, 2>), grid, blk, 0, st, a); break;
-    case 128 * 16 + 3: hipLaunchKernelGGL((k_attn_rows<128, 3>), grid, blk, 0, st, a); break;
-    case 128 * 16 + 4: hipLaunchKernelGGL((k_attn_rows<128, 4>), grid, blk, 0, st, a); break;
-    case 64 * 16 + 1: hipLaunchKernelGGL((k_attn_rows<64, 1>), grid, blk, 0, st, a); break;
-    case 64 * 16 + 2: hipLaunchKernelGGL((k_attn_rows<64, 2>), grid, blk, 0, st, a); break;
-    case 64 * 16 + 3: hipLaunchKernelGGL((k_attn_rows<64, 3>), grid, blk, 0, st, a); break;
-    case 64 * 16 + 4: hipLaunchKernelGGL((k_attn_rows<64, 4>), grid, blk, 0, st, a); break;
-    case 64 * 16 + 8: hipLaunchKernelGGL((k_attn_rows<64, 8>), grid, blk, 0, st, a); break;
+template <int HD>
+static hipError_t launch_rows_hd(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  const dim3 blk(64 * MF_WAVES);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn_rows<HD, 1>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_rows<HD, 2>), grid, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_rows<HD, 3>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_rows<HD, 4>), grid, blk, 0, st, a); break;
+    case 5: case 6: case 7: case 8:
+      if constexpr (HD == 64) {
+        if (G == 5) hipLaunchKernelGGL((k_attn_rows<HD, 5>), grid, blk, 0, st, a);
+        if (G == 6) hipLaunchKernelGGL((k_attn_rows<HD, 6>), grid, blk, 0, st, a);
+        if (G == 7) hipLaunchKernelGGL((k_attn_rows<HD, 7>), grid, blk, 0, st, a);
+        if (G == 8) hipLaunchKernelGGL((k_attn_rows<HD, 8>), grid, blk, 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_rows(int hd, const AttnArgs& a, hipStream_t st) {
+  if (a.max_items <= 0) return hipSuccess;
+  if (!attn_mfma_supported(hd, true, a.G)) return hipErrorInvalidValue;
+  const dim3 grid(a.max_items, a.Hkv);
+  return hd == 128 ? launch_rows_hd<128>(a.G, a, grid, st) : launch_rows_hd<64>(a.G, a, grid, st);
 }
 
 hipError_t launch_kv_append(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {

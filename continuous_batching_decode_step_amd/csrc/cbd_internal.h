@@ -112,6 +112,7 @@ struct AttnArgs {
   // rowblk[b] is the block holding slot pos[b] of row b's lane (launch_kv_append).
   const int* rowmap;
   const int* rowblk;
+  int frag;               // chunks in fragment order (kfrag_off / vfrag_off)
 };
 
 // Block sum of per-thread partials (256 threads): a fixed shuffle tree, then
@@ -158,6 +159,39 @@ __host__ __device__ constexpr bool attn_mfma_supported(int hd, bool kv_bf16, int
 }
 // chunk partials of every (lane, KV head, 64-key chunk) item; RoPE and KV append
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st);
+// Chunk layout of bf16 caches on the matrix-core shapes: within one (layer,
+// KV head) chunk of ATTN_SPLIT keys x hd dims, elements sit in the order the
+// attention kernels load their MFMA operand fragments, 16 bytes per lane and
+// 1 KB per wave-wide load:
+//  K: fragment (t, kk) = keys 16t..16t+15 x dims 32kk..32kk+31 (the score
+//     MFMA's A operand), lane 16*g4 + l16 holding key 16t + l16, dims
+//     32kk + 8*g4 .. + 7;
+//  V: fragment (dt, u) = keys 32u..32u+31 x dims 16dt..16dt+15 (the P.V
+//     MFMA's B operand), lane 16*kg + n holding dim 16dt + n of keys
+//     32u + 16*(e >> 2) + 4*kg + (e & 3), e = 0..7.
+// Other shapes keep row-major chunks (key * hd + dim).
+__host__ __device__ inline int kfrag_off(int key, int d, int hd) {
+  const int t = key >> 4, l16 = key & 15, kk = d >> 5, g4 = (d >> 3) & 3, e = d & 7;
+  return ((t * (hd / 32) + kk) * 64 + 16 * g4 + l16) * 8 + e;
+}
+__host__ __device__ inline int vfrag_off(int key, int d, int hd) {
+  const int dt = d >> 4, n = d & 15, u = key >> 5, h = (key >> 4) & 1, kg = (key >> 2) & 3, i = key & 3;
+  (void)hd;
+  return ((dt * 2 + u) * 64 + 16 * kg + n) * 8 + 4 * h + i;
+}
+// (key, dim) of element o of a fragment-ordered chunk (the inverses)
+__host__ __device__ inline void kfrag_at(int o, int hd, int* key, int* d) {
+  const int e = o & 7, lane = (o >> 3) & 63, tk = o >> 9, kk = tk % (hd / 32), t = tk / (hd / 32);
+  *key = 16 * t + (lane & 15);
+  *d = 32 * kk + 8 * (lane >> 4) + e;
+}
+__host__ __device__ inline void vfrag_at(int o, int hd, int* key, int* d) {
+  (void)hd;
+  const int e = o & 7, lane = (o >> 3) & 63, du = o >> 9, u = du & 1, dt = du >> 1;
+  *key = 32 * u + 16 * (e >> 2) + 4 * (lane >> 4) + (e & 3);
+  *d = 16 * dt + (lane & 15);
+}
+
 // Batched-prefill attention (shapes attn_mfma_supported serves): a.max_items
 // work items {first rowmap index | rows << 24, first chunk of the group,
 // position of the first row, chunks of the group the last row reaches, block
@@ -194,6 +228,11 @@ int workspace_rows(const cbd_model* m, int max_seq, size_t bytes);
 // on the device, one per 64 positions.
 hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
                           int row_bytes, long long lstride, long long bbytes, bool to_pool, hipStream_t st);
+// The same for fragment-ordered bf16 chunks (frag: 1 = K order, 2 = V order),
+// one workgroup per (row, chunk) through an LDS tile; chunks only partly in
+// [p0, p0 + len) keep their other keys.
+hipError_t launch_kv_rows_frag(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
+                               int hd, long long lstride, long long bbytes, bool to_pool, int frag, hipStream_t st);
 // Rotate n_vec key vectors of hd elements (bf16 or f32, device) in place by the
 // per-pair (cos, sin) table cs[hd/2] (rotate-half pairs; products and sums
 // rounded to f32 one by one), rounding to the KV format.

@@ -148,6 +148,70 @@ hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int p0, int
   return hipGetLastError();
 }
 
+// Fragment-ordered bf16 chunks (kfrag_off / vfrag_off) to or from rows: one
+// workgroup per (row (l, g), chunk c overlapping [p0, p0 + len)), through an
+// LDS tile of the chunk in row-major order.  A chunk only partly in range is
+// read first, so its other keys keep their contents.  Rows as in k_kv_rows.
+__global__ __launch_bounds__(256) void k_kv_rows_frag(uint16_t* pool, uint16_t* rows, const int* blocks, int p0,
+                                                      int len, int Hkv, int hd, long long lstride, long long bstride,
+                                                      int to_pool, int frag) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 128];
+  const int r = blockIdx.x, l = r / Hkv, g = r % Hkv;
+  const int c = p0 / 64 + (int)blockIdx.y;
+  const int kb = c * 64, lo = max(p0, kb), hi = min(p0 + len, kb + 64);
+  uint16_t* chunk = pool + l * lstride + (long long)blocks[c] * bstride + (long long)g * 64 * hd;
+  const int n = 64 * hd;
+  auto at = [&](int o, int* key, int* d) {
+    if (frag == 1)
+      kfrag_at(o, hd, key, d);
+    else
+      vfrag_at(o, hd, key, d);
+  };
+  if (!to_pool || lo > kb || hi < kb + 64) {
+    for (int q = threadIdx.x; q < n / 8; q += blockDim.x) {
+      const uint4 v = *(const uint4*)(chunk + 8 * q);
+      const unsigned wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int key, d;
+        at(8 * q + e, &key, &d);
+        tile[key * hd + d] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    __syncthreads();
+  }
+  const int pieces = (hi - lo) * (hd / 8);  // 16-byte pieces of the rows in range
+  uint16_t* rrow = rows + ((long long)r * len + (lo - p0)) * hd;
+  if (to_pool) {
+    for (int q = threadIdx.x; q < pieces; q += blockDim.x)
+      *(uint4*)(tile + (lo - kb) * hd + 8 * q) = *(const uint4*)(rrow + 8 * q);
+    __syncthreads();
+    for (int q = threadIdx.x; q < n / 8; q += blockDim.x) {
+      unsigned wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int key, d;
+        at(8 * q + e, &key, &d);
+        wv[e >> 1] |= (unsigned)tile[key * hd + d] << (16 * (e & 1));
+      }
+      *(uint4*)(chunk + 8 * q) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+  } else {
+    for (int q = threadIdx.x; q < pieces; q += blockDim.x)
+      *(uint4*)(rrow + 8 * q) = *(const uint4*)(tile + (lo - kb) * hd + 8 * q);
+  }
+}
+
+hipError_t launch_kv_rows_frag(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
+                               int hd, long long lstride, long long bbytes, bool to_pool, int frag, hipStream_t st) {
+  if (len <= 0 || n_rows <= 0) return hipSuccess;
+  if (hd > 128 || hd % 32 != 0 || (frag != 1 && frag != 2)) return hipErrorInvalidValue;
+  const int nch = (p0 + len - 1) / 64 - p0 / 64 + 1;
+  hipLaunchKernelGGL(k_kv_rows_frag, dim3(n_rows, nch), dim3(256), 0, st, (uint16_t*)pool, (uint16_t*)rows, blocks, p0,
+                     len, Hkv, hd, lstride / 2, bbytes / 2, (int)to_pool, frag);
+  return hipGetLastError();
+}
+
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   const unsigned u = __float_as_uint(f);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);

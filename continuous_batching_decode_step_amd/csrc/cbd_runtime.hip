@@ -183,6 +183,10 @@ int attn_chunks_per_item(const cbd_model* m) {
   return attn_mfma_supported(m->c.head_dim, m->wt == WT_BF16, m->G) ? ATTN_GROUP : 1;
 }
 
+// Whether the model's bf16 chunks are stored in the matrix-core kernels'
+// fragment order (kfrag_off / vfrag_off): exactly the shapes they serve.
+static bool kv_frag(const cbd_model* m) { return attn_chunks_per_item(m) == ATTN_GROUP; }
+
 // Attention partials per lane for MS chunks: one per work item.
 int attn_partials(const cbd_model* m, int MS) {
   const int per = attn_chunks_per_item(m);
@@ -822,6 +826,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.act = m->wt;
   at.rowmap = dmeta + 3 * B;
   at.rowblk = dmeta + 4 * B;
+  at.frag = kv_frag(m) ? 1 : 0;
   int rc;
   void* xn = ws + L.xn;
   // RMSNorm of x into xn; ssq_n = row blocks of the last producer of x (the embedding: one)
@@ -1242,6 +1247,21 @@ int cbd_decode_step(cbd_model* m, cbd_arena* a, int lane, int32_t* position, int
   return cbd_decode_step_batch(m, a, 1, &ln, position, &tok, logits, argmax, workspace, workspace_bytes, stream);
 }
 
+// Rows [n_rows][len][hd] of positions [p0, p0 + len) of a lane (block list on
+// the device) to or from the K (v = false) or V pool, in the pool's chunk order.
+static hipError_t kv_rows(cbd_arena* a, char* pool, char* rows, const int* dblk, int p0, int len, bool v, bool to_pool,
+                          hipStream_t st) {
+  const cbd_config& c = a->m->c;
+  const long long bbytes = a->block_elems * (long long)a->m->kvb;
+  const long long lstride = (long long)a->n_blocks * bbytes;
+  const int n_rows = c.n_layers * c.n_kv_heads;
+  if (kv_frag(a->m))
+    return launch_kv_rows_frag(pool, rows, dblk, p0, len, n_rows, c.n_kv_heads, c.head_dim, lstride, bbytes, to_pool,
+                               v ? 2 : 1, st);
+  return launch_kv_rows(pool, rows, dblk, p0, len, n_rows, c.n_kv_heads, c.head_dim * (int)a->m->kvb, lstride, bbytes,
+                        to_pool, st);
+}
+
 // Copy a lane's K or V between rows [L][Hkv][len][hd] (host or device) and its
 // blocks: one contiguous copy through the arena's device staging buffer, and
 // one kernel that moves the rows to or from the blocks.
@@ -1262,16 +1282,14 @@ static int copy_lane(cbd_arena* a, int lane, int len, char* rows, bool to_pool, 
     HIP_TRY(counted_malloc((void**)&a->stage, need));
     a->stage_bytes = need;
   }
-  const long long bbytes = a->block_elems * (long long)kvb;
-  const long long lstride = (long long)a->n_blocks * bbytes;
   char* pool = a->base + (v ? a->region_bytes : 0);
   int* dblk = (int*)(a->stage + boff);
   HIP_TRY(hipMemcpyAsync(dblk, bl.data(), bl.size() * sizeof(int), hipMemcpyHostToDevice, st));
   if (to_pool) {
     HIP_TRY(hipMemcpyAsync(a->stage, rows, bytes, hipMemcpyDefault, st));
-    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, 0, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true, st));
+    HIP_TRY(kv_rows(a, pool, a->stage, dblk, 0, len, v, true, st));
   } else {
-    HIP_TRY(launch_kv_rows(pool, a->stage, dblk, 0, len, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false, st));
+    HIP_TRY(kv_rows(a, pool, a->stage, dblk, 0, len, v, false, st));
     HIP_TRY(hipMemcpyAsync(rows, a->stage, bytes, hipMemcpyDefault, st));
   }
   // the staging buffer (and the block list) are reused by the next copy
@@ -1374,15 +1392,11 @@ int cbd_lane_evict_span(cbd_arena* a, int lane, int begin, int end, void* stream
     const float2* dcs = (const float2*)(a->stage + coff);
     HIP_TRY(hipMemcpyAsync(dblk, bl.data(), bl.size() * sizeof(int), hipMemcpyHostToDevice, st));
     HIP_TRY(hipMemcpyAsync(a->stage + coff, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, st));
-    const long long bbytes = a->block_elems * (long long)kvb;
-    const long long lstride = (long long)a->n_blocks * bbytes;
     for (int v = 0; v < 2; ++v) {
       char* pool = a->base + (v ? a->region_bytes : 0);
-      HIP_TRY(launch_kv_rows(pool, a->stage, dblk, end, n, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, false,
-                             st));
+      HIP_TRY(kv_rows(a, pool, a->stage, dblk, end, n, v != 0, false, st));
       if (!v) HIP_TRY(launch_kv_rot(a->stage, (long long)n_rows * n, c.head_dim, dcs, kvb == 2, st));
-      HIP_TRY(launch_kv_rows(pool, a->stage, dblk, begin, n, n_rows, c.n_kv_heads, row_bytes, lstride, bbytes, true,
-                             st));
+      HIP_TRY(kv_rows(a, pool, a->stage, dblk, begin, n, v != 0, true, st));
     }
     HIP_TRY(hipStreamSynchronize(st));
   }

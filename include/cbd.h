@@ -121,9 +121,15 @@ void cbd_model_destroy(cbd_model* m);
 
 /* The arena is a pool of KV blocks (paged KV): a block holds 64 positions (one
  * attention chunk) of one lane for every layer and KV head.  The pool is
- * layer-major: K [n_layers][n_blocks][n_kv_heads][64][head_dim], then V
+ * layer-major: K [n_layers][n_blocks][n_kv_heads][64 * head_dim], then V
  * alike, in the KV format of the model's wtype, so that block j of every
- * layer belongs to the same lane and one layer's blocks are contiguous.  A lane holds the blocks of its chunks, any
+ * layer belongs to the same lane and one layer's blocks are contiguous.  The
+ * 64 x head_dim elements of one (layer, block, KV head) are row-major
+ * [64][head_dim], except for bf16 caches whose attention runs on the matrix
+ * cores (head_dim 128 with at most 4, or 64 with at most 8, query heads per KV
+ * head): there they sit in the order the kernels load their matrix-core
+ * operands, so the pool is opaque; cbd_lane_kv_import / _export always take
+ * rows [len][head_dim].  A lane holds the blocks of its chunks, any
  * blocks of the pool in any order; a step takes a free block when a lane's new
  * slot opens a chunk (CBD_E_KV_FULL, changing nothing, if none is free), and
  * clear, evict and truncate return blocks to the pool.  Bytes of one block

@@ -8,16 +8,21 @@ token, same cache); the same lane's logits are bit-identical at every B; the
 GPU argmax equals the argmax of the GPU logits; the step writes the new K/V
 at slot len_b and leaves the older slots untouched.
 
-The bar: 2e-2 max relative error (||g - o||_inf / ||o||_inf) for the logits
-and for the K/V the step appends in every layer; layer 0's appended K/V
-depends on one projection only and is held to 2^-8 (a flipped bf16 rounding
-of single elements at most).  Eight lanes are checked against the oracle: the
-shortest (162 positions) and the longest (3997) of the 64, and six others
-spread over the range.  For reference the log also prints, where it is
-recorded, how far the same definition evaluated with f32 accumulators lands
-from the exact-sum oracle on that lane (tests/golden/bf16_7b_floor.json,
-written by tests/golden/make_bf16_7b_floor.py from the oracle alone): 1.5-2.1%
-at this depth, the noise floor any f32-accumulating evaluation sits near.
+The bar.  The logits are compared by max relative error (||g - o||_inf /
+||o||_inf).  At this depth bf16 activations turn any f32 rounding into flipped
+bf16 roundings that grow through the 32 layers, so an evaluation of the same
+definition with f32 accumulators (the oracle's own accumulate="f32" build,
+tests/golden/bf16_7b_floor.json, written by tests/golden/make_bf16_7b_floor.py
+from the oracle alone) lands 1.5-2.1% from the exact-sum oracle on these very
+lanes, above 2e-2 on three of the eight.  So each lane is held to
+max(2e-2, F), F the largest of those eight f32 distances (2.096%): no GPU lane
+may sit further from the exact oracle than an f32 evaluation's worst lane
+does; and the GPU must be at least as accurate as that evaluation on average
+(mean over the lanes of its error <= mean of the f32 distances).  The K/V the
+step appends in every layer is held to 2e-2, and layer 0's (one projection,
+no attention) to 2^-8 (a flipped bf16 rounding of single elements at most).
+Eight lanes are checked: the shortest (162 positions) and the longest (3997)
+of the 64, and six others spread over the range.
 """
 import json
 import os
@@ -37,6 +42,10 @@ SAMPLE = [0, 2, 4, 7, 14, 24, 40, 63]
 with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_7b_floor.json")) as _f:
     FLOOR = json.load(_f)["lanes"]
 LAYER0_TOL = 2.0 ** -8
+# the largest and the mean distance of the f32-accumulating evaluation from the exact one over the lanes
+FLOOR_MAX = max(FLOOR[str(b)]["max_rel"] for b in SAMPLE)
+FLOOR_MEAN = float(np.mean([FLOOR[str(b)]["max_rel"] for b in SAMPLE]))
+LOGIT_BAR = max(TOL_BF16, FLOOR_MAX)
 
 
 def _floor_note(b):
@@ -84,6 +93,7 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
                 else:
                     got[b] = lg[b].copy()
     M = oracle.Model(W)
+    errs = []
     for b in SAMPLE:
         k, v = kv[b]
         n = int(lens[b])
@@ -91,11 +101,11 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         lane.set_kv(synth.bf16_to_f32(k), synth.bf16_to_f32(v))
         say("7B: oracle lane %d (len %d)" % (b, n))
         ref = M.step(lane, int(toks[b]))
-        if str(b) in FLOOR:
-            assert FLOOR[str(b)]["kv_len"] == n and FLOOR[str(b)]["token"] == int(toks[b])
+        assert FLOOR[str(b)]["kv_len"] == n and FLOOR[str(b)]["token"] == int(toks[b])
         err = rel_err(got[b], ref)
-        say("7B: lane %d (len %d) max rel err %.4g, bar %.4g%s" % (b, n, err, TOL_BF16, _floor_note(b)))
-        assert err <= TOL_BF16
+        errs.append(err)
+        say("7B: lane %d (len %d) max rel err %.4g, bar %.4g%s" % (b, n, err, LOGIT_BAR, _floor_note(b)))
+        assert err <= LOGIT_BAR
         # KV: old slots untouched, new slot close to the oracle's
         gk, gv = eng.kv_export(lanes[b])
         assert gk.shape[2] == n + 1
@@ -107,6 +117,8 @@ def test_mistral7b_bf16_ragged_step_matches_oracle(setup7b):
         say("7B: lane %d new K/V rel err %.3g / %.3g, layer 0 %.3g / %.3g" % (b, ek, ev, ek0, ev0))
         assert ek <= TOL_BF16 and ev <= TOL_BF16
         assert ek0 <= LAYER0_TOL and ev0 <= LAYER0_TOL
+    say("7B: mean max rel err over the lanes %.4g (f32-accumulation mean %.4g)" % (float(np.mean(errs)), FLOOR_MEAN))
+    assert float(np.mean(errs)) <= FLOOR_MEAN
 
 
 WIDE_BATCHES = [128, 256, 512]

@@ -682,9 +682,12 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   constexpr int CPH = MfCols<G>::CPH;
   static_assert(ATTN_SPLIT == 64, "four 16-key tiles, two 32-key blocks");
 
-  const int item = blockIdx.x;
+  // workgroups in item-major order (the KV heads of one item adjacent), and
+  // the items in the order the host lists them: whole groups first, the
+  // shorter last groups after them, so the launch drains on the cheapest work
+  const int item = blockIdx.x / a.Hkv;
   if (item >= *a.n_items_dev) return;  // the whole workgroup leaves together
-  const int g = blockIdx.y;
+  const int g = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -851,9 +854,9 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   constexpr int CPH = MfCols<G>::CPH;
   static_assert(ATTN_SPLIT == 64, "four 16-key tiles, two 32-key blocks");
 
-  const int item = blockIdx.x;
+  const int item = blockIdx.x / a.Hkv;  // item-major, as k_attn_mf
   if (item >= *a.n_items_dev) return;
-  const int g = blockIdx.y;
+  const int g = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -1061,7 +1064,10 @@ static hipError_t launch_mf(int G, const AttnArgs& a, dim3 grid, hipStream_t st)
 hipError_t launch_attn(int hd, int kv_bf16, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
   const dim3 grid(a.max_items, a.Hkv);
-  if (attn_mfma_supported(hd, kv_bf16 != 0, a.G)) return hd == 128 ? launch_mf<128>(a.G, a, grid, st) : launch_mf<64>(a.G, a, grid, st);
+  if (attn_mfma_supported(hd, kv_bf16 != 0, a.G)) {
+    const dim3 flat((unsigned)a.max_items * a.Hkv);
+    return hd == 128 ? launch_mf<128>(a.G, a, flat, st) : launch_mf<64>(a.G, a, flat, st);
+  }
   switch (hd) {
     case 16: return launch_hd<16>(kv_bf16, a.G, a, grid, st);
     case 32: return launch_hd<32>(kv_bf16, a.G, a, grid, st);
@@ -1096,7 +1102,7 @@ static hipError_t launch_rows_hd(int G, const AttnArgs& a, dim3 grid, hipStream_
 hipError_t launch_attn_rows(int hd, const AttnArgs& a, hipStream_t st) {
   if (a.max_items <= 0) return hipSuccess;
   if (!attn_mfma_supported(hd, true, a.G)) return hipErrorInvalidValue;
-  const dim3 grid(a.max_items, a.Hkv);
+  const dim3 grid((unsigned)a.max_items * a.Hkv);
   return hd == 128 ? launch_rows_hd<128>(a.G, a, grid, st) : launch_rows_hd<64>(a.G, a, grid, st);
 }
 

@@ -984,20 +984,25 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
       }
     });
   }
-  for (int b = 0; !by_runs && b < B; ++b) {
-    const int ns = (positions[b] + ATTN_SPLIT) / ATTN_SPLIT;  // chunks holding slots 0..positions[b]
-    const std::vector<int>& bl = a->blocks[lanes[b]];
-    for (int s0 = 0; s0 < ns; s0 += per) {
-      const int n = std::min(per, ns - s0);
-      it[0] = b | (n << 24);
-      it[1] = s0;
-      it[2] = positions[b];
-      it[3] = 0;
-      for (int k = 0; k < ATTN_GROUP; ++k) it[4 + k] = k < n ? bl[s0 + k] : bl[s0 + n - 1];
-      it += ITEM_INTS;
-      ++n_items;
+  // Items by chunk count: groups of `per` chunks first (every lane's), then
+  // the lanes' shorter last groups, longest first, so that the launch drains
+  // on the cheapest items (the order changes no result).
+  for (int want = per; !by_runs && want >= 1; --want)
+    for (int b = 0; b < B; ++b) {
+      const int ns = (positions[b] + ATTN_SPLIT) / ATTN_SPLIT;  // chunks holding slots 0..positions[b]
+      const std::vector<int>& bl = a->blocks[lanes[b]];
+      for (int s0 = 0; s0 < ns; s0 += per) {
+        const int n = std::min(per, ns - s0);
+        if (n != want) continue;
+        it[0] = b | (n << 24);
+        it[1] = s0;
+        it[2] = positions[b];
+        it[3] = 0;
+        for (int k = 0; k < ATTN_GROUP; ++k) it[4 + k] = k < n ? bl[s0 + k] : bl[s0 + n - 1];
+        it += ITEM_INTS;
+        ++n_items;
+      }
     }
-  }
   meta[5 * B] = n_items;
   int32_t* dmeta = (int32_t*)(ws + L.meta);
   {

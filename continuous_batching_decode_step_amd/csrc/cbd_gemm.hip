@@ -816,15 +816,28 @@ void k_dense(GemmArgs a) {
   const int wm = w >> 1, wn = w & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // workgroup -> (row group, split, lane group), the lane groups of one (row
-  // group, split) on one XCD (workgroups are dealt to the 8 XCDs in turn)
+  // workgroup -> (row group with its split, lane group).  Workgroups are dealt
+  // to the 8 XCDs in turn; XCD x takes the row groups x, x + 8, ... (its
+  // weight rows come from HBM once, into its own L2), and walks them in blocks
+  // of DN_RB row groups, all row groups of a block for one lane group, then
+  // the next lane group: the 64 workgroups an XCD holds at a time then share
+  // 8 weight and 8 activation tiles instead of 2 and 32 (4096-row prefill:
+  // projections 32% -> 36% of MFMA peak; the activation tiles had been
+  // re-read from beyond L2 for every row group).
   const int outs = EPI == EPI_SWIGLU ? DN_ROWS / 2 : DN_ROWS;  // outputs (rows or pairs) per row group
   const int nRG = (a.N + outs - 1) / outs;
   const int nRGS = nRG * (SPLIT ? a.S : 1);
+  constexpr int DN_RB = 8;
   const int bi = blockIdx.x;
-  const int cg = (bi >> 3) % a.nCG;
-  const int rgs = ((bi >> 3) / a.nCG) * 8 + (bi & 7);
-  if (rgs >= nRGS) return;  // padding workgroup: the whole workgroup leaves together
+  const int xcd = bi & 7, li = bi >> 3;
+  const int rows_x = (nRGS - xcd + 7) / 8;  // row groups of this XCD
+  const int blk = li / (DN_RB * a.nCG);
+  const int within = li - blk * DN_RB * a.nCG;
+  const int rows_b = min(DN_RB, rows_x - blk * DN_RB);  // row groups of this block
+  if (rows_b <= 0) return;  // padding workgroup: the whole workgroup leaves together
+  const int cg = within / rows_b;
+  if (cg >= a.nCG) return;
+  const int rgs = xcd + 8 * (blk * DN_RB + within % rows_b);
   const int rg = SPLIT ? rgs / a.S : rgs;
   const int split = SPLIT ? rgs % a.S : 0;
 

@@ -444,6 +444,7 @@ def main() -> int:
         headline = (B, row["ms_per_step"], per, [int(x) for x in lens[:B]])
 
     B, ms, per, pos = headline
+    t_roof_step = rf.roofline_time_s(cfg, pos)
     dom = max((k for k in per if per[k]["alg_bytes"] > 0), key=lambda k: per[k]["total_ms"])
     d = per[dom]
     achieved = d["achieved_GBs"]
@@ -451,7 +452,9 @@ def main() -> int:
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / rf.HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
             "alg_bytes_per_launch": d["alg_bytes"], "avg_launch_us": round(d["avg_us"], 2),
-            "launches": d["launches"]}
+            "launches": d["launches"],
+            # the whole step against the same peak: (weight + KV bytes) / 8 TB/s over the step time
+            "step_frac": round(t_roof_step / (ms * 1e-3), 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

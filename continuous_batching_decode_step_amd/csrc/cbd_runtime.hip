@@ -626,13 +626,22 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // faster; above them their per-wave activation re-reads cost more than a
 // mostly idle 32-lane panel (at 16 lanes the four layer projections take
 // 116 us as split-K tiles, 97 us as panels).  The long reduction (down) is
-// faster as a panel even for one lane.
-static int panel_min_b(int epi, int K) {
+// faster as a panel even for one lane, and so are QKV and O once their
+// split-mode panels need no fold launch of their own: QKV's partials are
+// added by the matrix-core attention kernel up to 8 lanes (QKV 15.9 -> 13.2
+// us at one lane, attention +0.6), and O's fold runs the next RMSNorm in the
+// same kernel (O and norm 18.1 -> 16.7 us at one lane, 19.4 -> 16.5 at 8,
+// 20.6 -> 16.7 at 16; the split-K tiles' 384 and 256 workgroups also sit
+// unevenly on 256 compute units).  Other weight formats and attention shapes
+// keep the split-K tiles for QKV below 4 lanes and for O below 24 (not
+// measured otherwise; their fold would be a launch of its own).
+static int panel_min_b(const cbd_model* m, int epi, int K) {
+  const bool bf16_mf = m->wt == WT_BF16 && attn_chunks_per_item(m) == ATTN_GROUP;
   switch (epi) {
-    case EPI_STORE: return 4;               // QKV
-    case EPI_SWIGLU: return 8;              // gate|up
+    case EPI_STORE: return bf16_mf ? 1 : 4;                 // QKV
+    case EPI_SWIGLU: return 8;                              // gate|up
     case EPI_HEAD: return 4;
-    default: return K > 4096 ? 1 : 24;      // down; O
+    default: return K > 4096 || bf16_mf ? 1 : 24;           // down; O
   }
 }
 
@@ -733,7 +742,7 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.ssq_out = (float*)(ws + L.ssq);
   g.part = (float*)(ws + L.gpart);
   const bool dense = dense_ok(m, p, epi) && (m->variant == 3 || (m->variant == 0 && dense_auto(p, epi, B)));
-  const bool panel = !dense && (m->variant == 2 || m->variant == 3 || (m->variant == 0 && B >= panel_min_b(epi, p.K)));
+  const bool panel = !dense && (m->variant == 2 || m->variant == 3 || (m->variant == 0 && B >= panel_min_b(m, epi, p.K)));
   ProfScope ps(m, cls, st);
   if (dense) {
     const int split = dense_split(B, p, epi);

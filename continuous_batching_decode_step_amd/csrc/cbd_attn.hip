@@ -598,22 +598,35 @@ __device__ inline Merged merge_chunks(int nc, const float* ms, const float* ls, 
 }
 
 // Rotated query parts of the group's G heads (f32 head vectors at qv + j*HD,
-// rotation table cs) into the score B-operand rows qs[CPH*j + part].
+// rotation table cs) into the score B-operand rows qs[CPH*j + part], in two
+// stages so that a caller can load one row's inputs while it stores another's:
+// element idx = j*HD + d takes dim d of head j and its rotation partner.
+struct QIn {
+  float x, y;
+  float2 t;
+};
+template <int HD>
+__device__ inline QIn mf_query_in(const float* qv, const float2* cs, int idx) {
+  const int j = idx / HD, d = idx % HD;
+  const bool fh = d < HD / 2;
+  const float* v = qv + (size_t)j * HD;
+  return QIn{v[d], v[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2]};
+}
+template <int HD, int G>
+__device__ inline void mf_query_out(const QIn& in, int idx, uint16_t (*qs)[HD]) {
+  constexpr int CPH = MfCols<G>::CPH;
+  const int j = idx / HD, d = idx % HD;
+  const float q = rope_pair(in.x, in.y, in.t, d < HD / 2);
+  const uint16_t hi = f2bf_a(q);
+  const float r1 = q - bf2f(hi);  // exact
+  const uint16_t mid = f2bf_a(r1);
+  qs[CPH * j][d] = hi;
+  qs[CPH * j + 1][d] = mid;
+  if constexpr (MfCols<G>::NQ == 3) qs[CPH * j + 2][d] = f2bf_a(r1 - bf2f(mid));  // exact: at most 8 significant bits
+}
 template <int HD, int G>
 __device__ inline void mf_prep_queries(const float* qv, const float2* cs, uint16_t (*qs)[HD], int tid, int nthr) {
-  constexpr int CPH = MfCols<G>::CPH;
-  for (int idx = tid; idx < G * HD; idx += nthr) {
-    const int j = idx / HD, d = idx % HD;
-    const bool fh = d < HD / 2;
-    const float* v = qv + (size_t)j * HD;
-    const float q = rope_pair(v[d], v[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh);
-    const uint16_t hi = f2bf_a(q);
-    const float r1 = q - bf2f(hi);  // exact
-    const uint16_t mid = f2bf_a(r1);
-    qs[CPH * j][d] = hi;
-    qs[CPH * j + 1][d] = mid;
-    if constexpr (MfCols<G>::NQ == 3) qs[CPH * j + 2][d] = f2bf_a(r1 - bf2f(mid));  // exact: at most 8 significant bits
-  }
+  for (int idx = tid; idx < G * HD; idx += nthr) mf_query_out<HD, G>(mf_query_in<HD>(qv, cs, idx), idx, qs);
 }
 
 // The score B operand of lane (col l16, g4) from the query rows in LDS (zero
@@ -842,10 +855,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
 // in registers while it computes the chunk partial of every row that reaches
 // it, with the same per-chunk code and merge as k_attn_mf (so a row's
 // partial has the bits a decode step at that position gives).  Per row: the
-// workgroup rotates and splits the next row's queries into the other half of
-// a double-buffered LDS area, every wave writes its chunk partial, one
-// barrier, and the row's group partial (or, for a row with one partial, its
-// output) is merged and written.  Every row's key and value are in the cache
+// workgroup stores the next row's rotated, split queries into the other half
+// of a double-buffered LDS area (their inputs loaded a row earlier), every
+// wave writes its chunk partial, one barrier, and the row's group partial (or,
+// for a row with one partial, its output) is merged and written.  Every row's key and value are in the cache
 // already (k_kv_append runs first).
 template <int HD, int G>
 __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_rows(AttnArgs a) {
@@ -879,12 +892,34 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
 
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][16][HD];
   __shared__ float os[2][MF_WAVES][G][HD], ms[2][MF_WAVES][G], ls[2][MF_WAVES][G];
-  auto prep = [&](int r) {
-    const int b = rows[r];
-    mf_prep_queries<HD, G>(a.qkv + (size_t)b * a.Nqkv + (size_t)g * G * HD, a.rope + (size_t)b * (HD / 2), qs[r & 1],
-                           tid, 64 * MF_WAVES);
+  __shared__ int rws[ATTN_ROWS_MAX];
+  // The next row's query inputs are loaded one row ahead (registers) and
+  // rotated, split and stored to the other LDS half one row ahead, so no row
+  // waits on its own query loads.
+  constexpr int NE = (G * HD + 64 * MF_WAVES - 1) / (64 * MF_WAVES);  // query elements per thread
+  QIn qin[NE];
+  auto qload = [&](int r) {
+    const int b = rws[r];
+    const float* qv = a.qkv + (size_t)b * a.Nqkv + (size_t)g * G * HD;
+    const float2* cs = a.rope + (size_t)b * (HD / 2);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int idx = tid + e * 64 * MF_WAVES;
+      if (idx < G * HD) qin[e] = mf_query_in<HD>(qv, cs, idx);
+    }
   };
-  prep(0);
+  auto qstore = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int idx = tid + e * 64 * MF_WAVES;
+      if (idx < G * HD) mf_query_out<HD, G>(qin[e], idx, qs[buf]);
+    }
+  };
+  if (tid < nr) rws[tid] = rows[tid];
+  __syncthreads();
+  qload(0);
+  qstore(0);
+  if (nr > 1) qload(1);
   __syncthreads();
   const size_t pstride = (size_t)G * (HD + 2);
   for (int r = 0; r < nr; ++r) {
@@ -893,7 +928,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const int ncr = min(ATTN_GROUP, p / ATTN_SPLIT + 1 - c0);  // the group's chunks this row reaches
     u32x4 bq[KK];
     mf_load_bq<HD, G>(qs[buf], l16, g4, bq);
-    if (r + 1 < nr) prep(r + 1);
+    if (r + 1 < nr) qstore(buf ^ 1);
+    if (r + 2 < nr) qload(r + 2);
     if (w < ncr) {
       const int kb = c * ATTN_SPLIT, ke = min(kb + ATTN_SPLIT, nk);
       f32x4 sc[4];
@@ -913,7 +949,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
       mf_store_partial<HD, G>(o, m, l, g4, l16, os[buf][w], ms[buf][w], ls[buf][w]);
     }
     __syncthreads();
-    const int b = rows[r];
+    const int b = rws[r];
     const bool direct = nk <= ATTN_SPLIT * ATTN_GROUP;
     float* dst = a.part + (((size_t)b * a.max_splits + c0 / ATTN_GROUP) * a.Hkv + g) * pstride;
     for (int idx = tid; idx < G * HD; idx += 64 * MF_WAVES) {

@@ -768,10 +768,14 @@ __global__ __launch_bounds__(256) void k_fold_norm(GemmArgs a) {
 // Once B makes the contraction dense ("MODEL-BATCHING-RESULTS — multi-user
 // batched decode, measured", section "The honest ceiling": throughput is then
 // capped by the matrix units, not by the weight stream), the matrix cores need
-// operands reused from on-chip memory.  A workgroup of four waves owns a tile
-// of 128 weight rows (SwiGLU: 64 gate/up pairs) by 128 lanes, each wave a
-// 64 x 64 quarter as 4 x 4 MFMA blocks, and walks K in stages of two k-steps
-// (64 elements, 128 bytes of every row).
+// operands reused from on-chip memory.  A workgroup of eight waves owns a tile
+// of 256 weight rows (SwiGLU: 128 gate/up pairs) by 128 lanes, each wave a
+// 64 x 64 part as 4 x 4 MFMA blocks (four wave rows by two wave columns), and
+// walks K in stages of two k-steps (64 elements, 128 bytes of every row).  At
+// full MFMA rate the tile draws 48 bytes per clock per compute unit through
+// L2, against 64 for 128 x 128 tiles (4096-row prefill projections: 36% ->
+// 42% of MFMA peak; 256 and 512 lanes: 10-20% faster, though 256 lanes give
+// gate|up only 224 such workgroups).
 //
 // Loads go from memory straight into LDS (buffer loads with the LDS as
 // destination: no registers, no LDS write instructions).  One load
@@ -780,37 +784,42 @@ __global__ __launch_bounds__(256) void k_fold_norm(GemmArgs a) {
 // the lanes of a row take its 16-byte pieces in the order p ^ (row % 16) / 2,
 // which spreads the 16 rows of an MFMA operand over all LDS banks when a wave
 // reads piece p of each of them (one 16-byte load per lane, no conflicts).
-// Two slots of 32 KB: the next stage loads while this one is computed; each
-// stage starts with one barrier, after which every wave's loads of it have
-// landed (each waits for its own first) and every wave has finished reading
-// the slot the new loads overwrite.  64 KB of LDS and fewer than 256
-// registers, so two workgroups share a compute unit.
+// Three slots of 48 KB (one workgroup per compute unit, two waves per SIMD):
+// the loads run two stages ahead of the MFMAs.  Each stage starts with one
+// barrier, after which every wave's loads of it have landed (each waits for
+// its own first) and every wave has finished reading the slot the new loads
+// overwrite.
 //
 // Same reduction contract: each 16 x 16 block is a chain of
 // v_mfma_f32_16x16x32_bf16 over ascending k-steps from zero per split.
 // Modes: DN_ONE, one split per workgroup whose partial goes straight to the
 // epilogue (the projection has one split: (-0) + P_0 is P_0); DN_PART, one
 // split per workgroup written as a partial for k_fold / k_fold_norm; DN_FULL,
-// every split of K in one workgroup, KPS k-steps each (a compile-time length:
-// a split is one fully unrolled loop iteration with a fresh chain, which keeps
-// the MFMA stream free of accumulator copies), folded in order into a running
-// total ((P_0 + P_1) + ...).  So every output bit equals the other families'.
-constexpr int DN_ROWS = 128, DN_COLS = 128;
-constexpr int DN_BLOCK = 1024;            // 8 rows x 128 bytes
-constexpr int DN_STAGE = 32 * DN_BLOCK;   // 16 blocks of weights, then 16 of activations
+// every split of K in one workgroup, KPS k-steps each, each split's chain
+// folded in order into a running total ((P_0 + P_1) + ...) at the stage where
+// the next split starts.  So every output bit equals the other families'.
+constexpr int DN_ROWS = 256, DN_COLS = 128;
+constexpr int DN_WAVES = 8;
+constexpr int DN_BLOCK = 1024;             // 8 rows x 128 bytes
+constexpr int DN_WBLK = DN_ROWS / 8;       // weight blocks of a stage, then 16 activation blocks
+constexpr int DN_STAGE = (DN_WBLK + 16) * DN_BLOCK;
+constexpr int DN_WPW = DN_WBLK / DN_WAVES;  // weight blocks loaded per wave
+constexpr int DN_XPW = 16 / DN_WAVES;       // activation blocks loaded per wave
 enum { DN_ONE = 0, DN_PART = 1, DN_FULL = 2 };
 
 template <int EPI, int MODE, int KPS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(DN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_dense(GemmArgs a) {
   constexpr int R0 = gemm_rows(EPI);
   constexpr int RM = 4 / R0;  // row blocks of a wave's four row tiles
   constexpr int KS = 32;
   constexpr bool SPLIT = MODE == DN_PART;
-  // two stage slots, as separate objects so that the compiler can tell the
-  // slot being read from the slot being loaded
+  // stage slots, as separate objects so that the compiler can tell the slot
+  // being read from the slots being loaded (else it waits for every load
+  // before each LDS read)
   __shared__ __attribute__((aligned(16))) char sl0[DN_STAGE];
   __shared__ __attribute__((aligned(16))) char sl1[DN_STAGE];
+  __shared__ __attribute__((aligned(16))) char sl2[DN_STAGE];
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;
@@ -820,10 +829,9 @@ void k_dense(GemmArgs a) {
   // to the 8 XCDs in turn; XCD x takes the row groups x, x + 8, ... (its
   // weight rows come from HBM once, into its own L2), and walks them in blocks
   // of DN_RB row groups, all row groups of a block for one lane group, then
-  // the next lane group: the 64 workgroups an XCD holds at a time then share
-  // 8 weight and 8 activation tiles instead of 2 and 32 (4096-row prefill:
-  // projections 32% -> 36% of MFMA peak; the activation tiles had been
-  // re-read from beyond L2 for every row group).
+  // the next lane group: the workgroups an XCD holds at a time then share a
+  // few weight and activation tiles instead of re-reading the activation
+  // tiles from beyond L2 for every row group.
   const int outs = EPI == EPI_SWIGLU ? DN_ROWS / 2 : DN_ROWS;  // outputs (rows or pairs) per row group
   const int nRG = (a.N + outs - 1) / outs;
   const int nRGS = nRG * (SPLIT ? a.S : 1);
@@ -846,9 +854,9 @@ void k_dense(GemmArgs a) {
   const int t0 = SPLIT ? split * kps : 0;
   const int ns = ((SPLIT ? min(t0 + kps, nks) : nks) - t0) / 2;  // stages walked: an even number
 
-  // Weight row of tile row q (0..127): MFMA row tile q / 16 of the tile,
-  // row q % 16 in it.  Row tiles 4 wm .. 4 wm + 3 are wave row wm's; SwiGLU
-  // row tiles are [gate, gate, up, up] of 32 pairs.
+  // Weight row of tile row q: MFMA row tile q / 16 of the tile, row q % 16 in
+  // it.  Row tiles 4 wm .. 4 wm + 3 are wave row wm's; SwiGLU row tiles are
+  // [gate, gate, up, up] of 32 pairs.
   auto wrow = [&](int q) -> int {
     const int f = q >> 4, fm = f >> 2, r = f & 3, i = q & 15;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -860,58 +868,58 @@ void k_dense(GemmArgs a) {
   };
   const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, (size_t)a.Nraw * a.K * 2);
   const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X, (size_t)a.B * a.K * 2);
-  // this wave fills blocks 4w .. 4w + 3 of the weights and of the activations;
+  // this wave fills weight blocks DN_WPW w .. and activation blocks DN_XPW w ..;
   // lane: row 8 j + lane / 8 of block j, its piece (lane % 8) ^ (row % 16) / 2
-  unsigned wv[4], xv[4];
+  unsigned wv[DN_WPW], xv[DN_XPW];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int q = 8 * (4 * w + jj) + (lane >> 3);
+  for (int jj = 0; jj < DN_WPW; ++jj) {
+    const int q = 8 * (DN_WPW * w + jj) + (lane >> 3);
     const unsigned piece = (unsigned)((lane & 7) ^ ((q & 15) >> 1)) * 16;
     wv[jj] = (unsigned)((size_t)wrow(q) * a.K * 2) + piece;
+  }
+#pragma unroll
+  for (int jj = 0; jj < DN_XPW; ++jj) {
+    const int q = 8 * (DN_XPW * w + jj) + (lane >> 3);
+    const unsigned piece = (unsigned)((lane & 7) ^ ((q & 15) >> 1)) * 16;
     const int col = min(cg * DN_COLS + q, a.B - 1);
     xv[jj] = (unsigned)((size_t)col * a.K * 2) + piece;
   }
   // stage st of the walk into a slot (a stage past the last reloads it into a
-  // slot nobody reads)
+  // slot nobody reads, so every stage issues the same loads)
   auto load = [&](char* slot, int st) {
     const int kb = (t0 + 2 * min(st, ns - 1)) * KS * 2;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, slot + (4 * w + jj) * DN_BLOCK, 16, (int)wv[jj], kb, 0, 0);
+    for (int jj = 0; jj < DN_WPW; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, slot + (DN_WPW * w + jj) * DN_BLOCK, 16, (int)wv[jj], kb, 0, 0);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, slot + (16 + 4 * w + jj) * DN_BLOCK, 16, (int)xv[jj], kb, 0, 0);
+    for (int jj = 0; jj < DN_XPW; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, slot + (DN_WBLK + DN_XPW * w + jj) * DN_BLOCK, 16, (int)xv[jj],
+                                               kb, 0, 0);
   };
-  // Start of a stage: this wave's loads of it have landed, then the barrier.
-  auto arrive = [&]() { __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // Start of a stage: this wave's loads of it have landed (those of the next
+  // stage, issued after them, may still be in flight), then the barrier.
+  auto arrive = [&]() {
+    __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(DN_WPW + DN_XPW) : "memory");
+  };
   // Piece p of tile row 16 t + l16 sits at block 2 t + l16 / 8, row l16 % 8,
   // slot p ^ l16 / 2: per lane, the offsets of k-step 0 and 1 (p = 4 ks + g4).
   unsigned ro[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     ro[ks] = (unsigned)((l16 >> 3) * DN_BLOCK + (l16 & 7) * 128 + (((4 * ks + g4) ^ (l16 >> 1)) << 4));
-  auto compute = [&](f32x4 (&ch)[4][4], const char* slot) {
+  auto compute = [&](f32x4 (&acc)[4][4], const char* slot) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 av[4], bv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) av[r] = *(const u32x4*)(slot + (2 * (4 * wm + r)) * DN_BLOCK + ro[ks]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = *(const u32x4*)(slot + (16 + 2 * (4 * wn + c)) * DN_BLOCK + ro[ks]);
+      for (int c = 0; c < 4; ++c) bv[c] = *(const u32x4*)(slot + (DN_WBLK + 2 * (4 * wn + c)) * DN_BLOCK + ro[ks]);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ch[r][c] = mma<WT_BF16>(av[r], bv[c], ch[r][c]);
+        for (int c = 0; c < 4; ++c) acc[r][c] = mma<WT_BF16>(av[r], bv[c], acc[r][c]);
     }
-  };
-  // two stages st, st + 1 from slots 0, 1, loading st + 1, st + 2
-  auto pair = [&](f32x4 (&ch)[4][4], int st) {
-    arrive();
-    load(sl1, st + 1);
-    compute(ch, sl0);
-    arrive();
-    load(sl0, st + 2);
-    compute(ch, sl1);
   };
 
   // The running total of DN_FULL starts at -0: (-0) + x is x bit for bit.
@@ -923,30 +931,58 @@ void k_dense(GemmArgs a) {
       ch[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
       tot[r][c] = f32x4{-0.f, -0.f, -0.f, -0.f};
     }
-  load(sl0, 0);
-  if constexpr (MODE == DN_FULL) {
-    for (int st = 0; st < ns; st += KPS / 2) {  // one split per iteration, a fresh chain
+  auto fold = [](f32x4 (&acc)[4][4], f32x4 (&sum)[4][4]) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ch[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int q = 0; q < KPS / 2; q += 2) pair(ch, st + q);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tot[r][c][i] = tot[r][c][i] + ch[r][c][i];
+        for (int i = 0; i < 4; ++i) sum[r][c][i] = sum[r][c][i] + acc[r][c][i];
+        acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  };
+  // Stage st sits in slot (st - r) % 3, r = ns % 3, so that the loop walks
+  // whole triples of stages after r stages of prologue; at its start the
+  // loads of st + 2 go into the slot of st - 1.  DN_FULL folds at each split
+  // boundary (a uniform branch kept outside the MFMA stream).
+  int nf = KPS / 2;  // stage at which the next split starts
+  auto stage = [&](f32x4 (&acc)[4][4], f32x4 (&sum)[4][4], char* cur, char* nxt2, int st) {
+    if constexpr (MODE == DN_FULL) {
+      if (st == nf) {
+        __asm__ volatile("");
+        fold(acc, sum);
+        nf += KPS / 2;
+      }
     }
+    arrive();
+    load(nxt2, st + 2);
+    compute(acc, cur);
+  };
+  const int r = ns % 3;
+  if (r == 1) {
+    load(sl2, 0);
+    load(sl0, 1);
+    stage(ch, tot, sl2, sl1, 0);
+  } else if (r == 2) {
+    load(sl1, 0);
+    load(sl2, 1);
+    stage(ch, tot, sl1, sl0, 0);
+    stage(ch, tot, sl2, sl1, 1);
   } else {
-    for (int st = 0; st < ns; st += 2) pair(ch, st);  // the one split
+    load(sl0, 0);
+    load(sl1, 1);
   }
-  // the load past the end must land before the workgroup's LDS is released
+  for (int st = r; st < ns; st += 3) {
+    stage(ch, tot, sl0, sl2, st);
+    stage(ch, tot, sl1, sl0, st + 1);
+    stage(ch, tot, sl2, sl1, st + 2);
+  }
+  if constexpr (MODE == DN_FULL) fold(ch, tot);
+  // the loads past the end must land before the workgroup's LDS is released
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int rb = rg * 2 + wm;  // this wave's group of RM row blocks
-  const int cgw = cg * 2 + wn;  // this wave's group of 64 lanes
+  const int rb = rg * (DN_WAVES / 2) + wm;  // this wave's group of RM row blocks
+  const int cgw = cg * 2 + wn;              // this wave's group of 64 lanes
   if constexpr (MODE == DN_PART) {
     // P_s as [split][lane][row block][R0 tiles][16], as the panels write it
 #pragma unroll
@@ -993,16 +1029,15 @@ int dense_workgroups(const GemmArgs& a, int epi, int split) {
 }
 
 template <int EPI, int MODE, int KPS>
-static hipError_t launch_dense_k(const GemmArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((k_dense<EPI, MODE, KPS>), dim3(blocks), dim3(256), 0, st, a);
+static hipError_t launch_dense_k(const GemmArgs& a, int split, hipStream_t st) {
+  hipLaunchKernelGGL((k_dense<EPI, MODE, KPS>), dim3(dense_workgroups(a, EPI, split)), dim3(DN_WAVES * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int EPI>
 static hipError_t launch_dense_epi(int split, const GemmArgs& a, hipStream_t st) {
-  const int blocks = dense_workgroups(a, EPI, split);
   if (split) {
-    hipError_t e = launch_dense_k<EPI, DN_PART, 0>(a, blocks, st);
+    hipError_t e = launch_dense_k<EPI, DN_PART, 0>(a, 1, st);
     if (e != hipSuccess) return e;
     if (EPI == EPI_RESID && a.norm_out) {
       if (!fold_norm_supported(a.N)) return hipErrorInvalidValue;
@@ -1015,16 +1050,16 @@ static hipError_t launch_dense_epi(int split, const GemmArgs& a, hipStream_t st)
     }
     return hipGetLastError();
   }
-  if (a.S == 1) return launch_dense_k<EPI, DN_ONE, 0>(a, blocks, st);
+  if (a.S == 1) return launch_dense_k<EPI, DN_ONE, 0>(a, 0, st);
   switch (dense_full_kps(EPI, a.Ks)) {
     case 16:
-      if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 16>(a, blocks, st);
+      if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 16>(a, 0, st);
       break;
     case 32:
-      if constexpr (EPI == EPI_SWIGLU || EPI == EPI_HEAD) return launch_dense_k<EPI, DN_FULL, 32>(a, blocks, st);
+      if constexpr (EPI == EPI_SWIGLU || EPI == EPI_HEAD) return launch_dense_k<EPI, DN_FULL, 32>(a, 0, st);
       break;
     case 56:
-      if constexpr (EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 56>(a, blocks, st);
+      if constexpr (EPI == EPI_RESID) return launch_dense_k<EPI, DN_FULL, 56>(a, 0, st);
       break;
   }
   return hipErrorInvalidValue;

@@ -681,10 +681,11 @@ static void panel_shape(int B, const Plan& p, int epi, int* C, int* rm, int* spl
 // Dense tiles (both operands in LDS) from this many rows on, for bf16 weights
 // whose reductions fit them (K a multiple of 128).  Measured per projection on
 // the 7B shapes: at 128 lanes the wide panels are faster; from 256 the dense
-// tiles are for gate|up, the head and the long reduction (down: one split per
-// workgroup beats the panels' split mode), while QKV and O stay panels unless
-// whole-K dense workgroups cover the chip (a 4096-row prefill: 23% faster
-// projections in all).
+// tiles are for gate|up, the head and both residual projections (O and down:
+// one split per workgroup, its partials folded by the kernel that also runs
+// the next RMSNorm; O 38 -> 32 us at 256 lanes), while QKV, whose split
+// partials would need a fold launch of their own, stays a panel unless
+// whole-K dense workgroups cover the chip (a 4096-row prefill).
 constexpr int DENSE_MIN_B = 256;
 
 static bool dense_ok(const cbd_model* m, const Plan& p, int epi) {
@@ -695,7 +696,7 @@ static bool dense_ok(const cbd_model* m, const Plan& p, int epi) {
 // The automatic choice of dense tiles at B rows (see DENSE_MIN_B).
 static bool dense_auto(const Plan& p, int epi, int B) {
   if (B < DENSE_MIN_B) return false;
-  if (gemm_rows(epi) != 1 || p.K > 4096) return true;
+  if (gemm_rows(epi) != 1 || p.K > 4096 || epi == EPI_RESID) return true;
   GemmArgs g{};
   g.N = p.N;
   g.B = B;

@@ -1,7 +1,8 @@
 """Ragged attention at long contexts on shapes that take the matrix-core
 kernel (bf16 KV, head_dim 64 and 128, eight KV heads), two layers deep so the
 oracle comparison is sharp: 64 lanes with KV lengths uniform in [128, 4000]
-(seed 2) of synthetic post-rotary K/V (seed 3), one decode step.
+(seed 2) of synthetic post-rotary K/V (seed 3), one decode step.  The
+head_dim-64 shapes take every query-head group size up to eight (2, 5, 6, 7).
 
 At this size a wave takes several 64-key chunks of a lane, while a lane
 stepped alone gets one chunk per wave: the lane's logits must be bitwise the
@@ -23,6 +24,13 @@ SHAPES = [
     synth.ModelConfig("attn-hd64-bf16", d=1024, n_layers=2, n_heads=16, n_kv_heads=8, head_dim=64, ffn=256,
                       vocab=512, wtype=synth.WTYPE_BF16),
     synth.ModelConfig("attn-hd128-bf16", d=4096, n_layers=2, n_heads=32, n_kv_heads=8, head_dim=128, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+    # 5, 6 and 7 query heads per KV head: the head_dim-64 kernels' two-column query parts
+    synth.ModelConfig("attn-hd64-g5-bf16", d=1280, n_layers=2, n_heads=20, n_kv_heads=4, head_dim=64, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+    synth.ModelConfig("attn-hd64-g6-bf16", d=1536, n_layers=2, n_heads=24, n_kv_heads=4, head_dim=64, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+    synth.ModelConfig("attn-hd64-g7-bf16", d=1792, n_layers=2, n_heads=28, n_kv_heads=4, head_dim=64, ffn=256,
                       vocab=512, wtype=synth.WTYPE_BF16),
 ]
 N_LANES = 64

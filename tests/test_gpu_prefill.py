@@ -6,9 +6,9 @@ Feeding the same tokens one decode step at a time (lockstep over the lanes
 still feeding) must give bit-identical logits at the end of each chunk and a
 bit-identical cache afterwards: a row's result depends only on its own lane
 and position.  The last logits also match the oracle fed token by token.
-Both attention kernels are covered (bf16 head_dim 128, the matrix-core
-kernel; the tiny shape in f32, the general kernel), and the Q8_0 weight path
-(SmolLM2-135M shape, f32 cache).
+Both attention kernels are covered (bf16 head_dim 128, and 64 with six
+query heads per KV head: the matrix-core kernels; the tiny shape in f32: the
+general kernel), and the Q8_0 weight path (SmolLM2-135M shape, f32 cache).
 """
 import numpy as np
 import pytest
@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     synth.TINY,
     synth.ModelConfig("prefill-hd128-bf16", d=2048, n_layers=2, n_heads=16, n_kv_heads=4, head_dim=128, ffn=256,
+                      vocab=512, wtype=synth.WTYPE_BF16),
+    synth.ModelConfig("prefill-hd64-g6-bf16", d=1536, n_layers=2, n_heads=24, n_kv_heads=4, head_dim=64, ffn=256,
                       vocab=512, wtype=synth.WTYPE_BF16),
     synth.SMOL135M_Q8,
 ]

@@ -34,7 +34,7 @@ SYMBOLS = [
     "cbd_arena_free_blocks", "cbd_prefill_batch", "cbd_sched_create", "cbd_sched_create_device",
     "cbd_sched_destroy", "cbd_sched_submit", "cbd_sched_tick", "cbd_sched_run", "cbd_sched_get_telemetry",
     "cbd_sched_job_tokens", "cbd_lane_clone", "cbd_lane_evict_span", "cbd_debug_alloc_count",
-    "cbd_decode_step_batch_noalloc", "cbd_noalloc_scratch_bytes",
+    "cbd_decode_step_batch_noalloc", "cbd_noalloc_scratch_bytes", "cbd_packed_bytes", "cbd_pack_matrix",
 ]
 
 
@@ -49,7 +49,7 @@ class Config(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int), ("n_layers", ctypes.c_int), ("n_heads", ctypes.c_int),
                 ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("ffn_dim", ctypes.c_int),
                 ("vocab", ctypes.c_int), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("tied_embeddings", ctypes.c_int), ("wtype", ctypes.c_int)]
+                ("tied_embeddings", ctypes.c_int), ("wtype", ctypes.c_int), ("packed", ctypes.c_int)]
 
 
 class _Matrix(ctypes.Structure):
@@ -117,6 +117,9 @@ def lib():
         L.cbd_model_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Weights), ctypes.POINTER(vp)]
         L.cbd_model_destroy.argtypes = [vp]
         L.cbd_model_destroy.restype = None
+        L.cbd_packed_bytes.argtypes = [i32, i32, i32, i32]
+        L.cbd_packed_bytes.restype = sz
+        L.cbd_pack_matrix.argtypes = [i32, vp, vp, i32, i32, i32, vp]
         L.cbd_arena_bytes.argtypes = [ctypes.POINTER(Config), i32, i32]
         L.cbd_arena_bytes.restype = sz
         L.cbd_arena_block_bytes.argtypes = [ctypes.POINTER(Config)]
@@ -206,10 +209,11 @@ def _pi32(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def config_of(cfg) -> Config:
-    """C config from any object with the fields of a model shape (d, n_layers, ...)."""
+def config_of(cfg, packed: bool = False) -> Config:
+    """C config from any object with the fields of a model shape (d, n_layers, ...); packed: the
+    layer matrices (and an untied LM head) are in the packed tile layout."""
     return Config(cfg.d, cfg.n_layers, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab,
-                  cfg.rms_eps, cfg.rope_theta, int(cfg.tied), int(cfg.wtype))
+                  cfg.rms_eps, cfg.rope_theta, int(cfg.tied), int(cfg.wtype), int(packed))
 
 
 # ---- device weights -------------------------------------------------------------
@@ -231,6 +235,7 @@ class DeviceWeights:
     w_o: List[DeviceMatrix]
     w_gu: List[DeviceMatrix]
     w_down: List[DeviceMatrix]
+    packed: bool = False              # layer matrices and an untied head in the packed tile layout
 
     def nbytes(self) -> int:
         n = 0
@@ -242,8 +247,28 @@ class DeviceWeights:
         return n
 
 
-def upload_weights(W, device="cuda") -> DeviceWeights:
-    """Copy host weight arrays (numpy, in the layout of include/cbd.h) to device tensors."""
+def packable(cfg) -> bool:
+    """Whether a model shape's layer matrices have the packed tile layout (bf16, every K a multiple of 32)."""
+    return int(cfg.wtype) == CBD_BF16 and all(k % 32 == 0 for k in (cfg.d, cfg.ffn, cfg.n_heads * cfg.head_dim))
+
+
+def pack_matrix(data, rows: int, halves: int = 1, stream=None):
+    """The packed tile layout (cbd_pack_matrix) of a bf16 device matrix [halves * rows, K] (int16 bits),
+    as a new device tensor of int16 bits."""
+    import torch
+    K = int(data.shape[1])
+    nb = lib().cbd_packed_bytes(CBD_BF16, rows, K, halves)
+    if nb == 0:
+        raise CbdError(-10, "no packed layout for %d x %d rows, K %d" % (halves, rows, K))
+    out = torch.empty(nb // 2, dtype=torch.int16, device=data.device)
+    _check(lib().cbd_pack_matrix(CBD_BF16, _ptr(data), _ptr(out), rows, K, halves, _stream(stream)))
+    return out
+
+
+def upload_weights(W, device="cuda", pack: Optional[bool] = None) -> DeviceWeights:
+    """Copy host weight arrays (numpy, in the layout of include/cbd.h) to device tensors.  pack (default:
+    whenever the shape allows it, see packable): bf16 layer matrices and an untied LM head go to the
+    device in the packed tile layout, which the weight-streaming kernels load in whole kilobytes."""
     import torch
 
     def t(a):
@@ -254,10 +279,25 @@ def upload_weights(W, device="cuda") -> DeviceWeights:
     def m(x):
         return None if x is None else DeviceMatrix(t(x.data), None if x.scale is None else t(x.scale))
 
-    return DeviceWeights(embed=m(W.embed), lm_head=m(W.lm_head), final_norm=t(W.final_norm),
+    cfg = W.cfg
+    if pack is None:
+        pack = packable(cfg)
+    elif pack and not packable(cfg):
+        raise CbdError(-10, "model shape has no packed layout")
+
+    def mp(x, halves=1):
+        if x is None or not pack:
+            return m(x)
+        d = t(x.data)
+        p = pack_matrix(d, d.shape[0] // halves, halves)
+        torch.cuda.synchronize()
+        del d
+        return DeviceMatrix(p, None)
+
+    return DeviceWeights(embed=m(W.embed), lm_head=mp(W.lm_head), final_norm=t(W.final_norm),
                          attn_norm=[t(a) for a in W.attn_norm], ffn_norm=[t(a) for a in W.ffn_norm],
-                         w_qkv=[m(x) for x in W.w_qkv], w_o=[m(x) for x in W.w_o], w_gu=[m(x) for x in W.w_gu],
-                         w_down=[m(x) for x in W.w_down])
+                         w_qkv=[mp(x) for x in W.w_qkv], w_o=[mp(x) for x in W.w_o],
+                         w_gu=[mp(x, 2) for x in W.w_gu], w_down=[mp(x) for x in W.w_down], packed=bool(pack))
 
 
 # ---- objects ------------------------------------------------------------------------
@@ -268,7 +308,7 @@ class Model:
     def __init__(self, cfg, weights: DeviceWeights):
         self.cfg = cfg
         self.weights = weights
-        self._c = config_of(cfg)
+        self._c = config_of(cfg, weights.packed)
         L = cfg.n_layers
         mat = lambda x: _Matrix(_ptr(x.data), _ptr(x.scale)) if x is not None else _Matrix(None, None)
         self._attn = (ctypes.c_void_p * L)(*[_ptr(a) for a in weights.attn_norm])

@@ -232,20 +232,30 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
   const int koff = PL * g4;
 
   // Row pointers (A operand row = lane % 16).  A row past the end is clamped to
-  // the last row: it only feeds output rows that are never stored.
+  // the last row: it only feeds output rows that are never stored.  Packed
+  // bf16 weights: the lane's slot of the row tile's first k-step tile of the
+  // split (a tile past the end is clamped to the half's last tile), one tile
+  // (1 KB) per k-step.
   const char* ap[R];
   const uint16_t* sp[R];
+  const bool packed = WT == WT_BF16 && a.wpack;
+  const int wks = packed ? 1024 : KS * EB;  // weight bytes between k-steps
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    int row;
+    int row, tile;
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int H = R / 2;
       const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
       row = r < H ? j : a.N + j;
+      tile = min(rb * H + r % H, a.wtiles - 1) + (r < H ? 0 : a.wtiles);
     } else {
       row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
+      tile = min(rb * R + r, a.wtiles - 1);
     }
-    ap[r] = (const char*)a.W + ((size_t)row * a.K + kb + koff) * EB;
+    if (packed)
+      ap[r] = (const char*)a.W + ((size_t)tile * (a.K / KS + PACK_GAP) + kb / KS) * 1024 + lane * 16;
+    else
+      ap[r] = (const char*)a.W + ((size_t)row * a.K + kb + koff) * EB;
     if constexpr (WT == WT_Q8) sp[r] = a.Ws + (size_t)row * (a.K >> 5) + (kb >> 5);
   }
   // Column pointers (B operand column = lane % 16), clamped the same way.
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
         if constexpr (WT == WT_Q8)
           A[u][r] = ld_q8(ap[r] + k, sp[r] + (k >> 5));
         else
-          A[u][r] = ld16(ap[r] + (size_t)k * EB);
+          A[u][r] = ld16(ap[r] + (size_t)(step0 + u) * wks);
       }
 #pragma unroll
       for (int c = 0; c < C; ++c) Bv[u][c] = ld16(bp[c] + (size_t)k * XB);
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
       if constexpr (WT == WT_Q8)
         av[r] = q8_to_f16(ld_q8(ap[r] + (kok ? k : 0), sp[r] + (kok ? (k >> 5) : 0)));
       else
-        av[r] = ld16(ap[r] + (size_t)(kok ? k : 0) * EB);
+        av[r] = ld16(ap[r] + (size_t)(kok ? st : 0) * wks);
       if (!kok) av[r] = zero4();
     }
 #pragma unroll
@@ -476,21 +486,30 @@ __global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int tm = tail ? t1 - 1 : t1;  // end of the full k-steps
   const int nst = (tm - t0 + U - 1) / U;
 
-  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, (size_t)a.Nraw * a.K * EB);
+  // Packed bf16 weights: the lane's slot of the row tile's first tile, one
+  // tile (1 KB) per k-step (a tile past the end is clamped to the half's last).
+  const bool packed = WT == WT_BF16 && a.wpack;
+  const unsigned wks = packed ? 1024u : (unsigned)(KS * EB);  // weight bytes between k-steps
+  const size_t wbytes = packed ? (size_t)(EPI == EPI_SWIGLU ? 2 : 1) * a.wtiles * (a.K / KS + PACK_GAP) * 1024
+                               : (size_t)a.Nraw * a.K * EB;
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, wbytes);
   const __amdgpu_buffer_rsrc_t srs = buf_rsrc(a.Ws, WT == WT_Q8 ? (size_t)a.Nraw * (a.K >> 5) * 2 : 0);
   const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X, (size_t)a.B * a.K * XB);
   unsigned wv[R], sv[R];  // byte offsets of this lane's weight vector at k = 0 (and its Q8 scale)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    int row;
+    int row, tile;
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int H = R / 2;
       const int j = min(rb * TILE * H + TILE * (r % H) + r16, a.N - 1);
       row = r < H ? j : a.N + j;
+      tile = min(rb * H + r % H, a.wtiles - 1) + (r < H ? 0 : a.wtiles);
     } else {
       row = min(rb * TILE * R + TILE * r + r16, a.N - 1);
+      tile = min(rb * R + r, a.wtiles - 1);
     }
-    wv[r] = (unsigned)(((size_t)row * a.K + koff) * EB);
+    wv[r] = packed ? (unsigned)((size_t)tile * (a.K / KS + PACK_GAP) * 1024 + lane * 16)
+                   : (unsigned)(((size_t)row * a.K + koff) * EB);
     sv[r] = (unsigned)((size_t)row * (a.K >> 5) * 2);
   }
   auto ld_w = [&](int r, int t) -> u32x4 {
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const u32x2 q = buf_ld8(wrs, wv[r], (unsigned)t * KS);
       return u32x4{q.x, q.y, buf_ld2(srs, sv[r], (unsigned)t * 2), 0u};
     } else {
-      return buf_ld16(wrs, wv[r], (unsigned)t * KS * EB);
+      return buf_ld16(wrs, wv[r], (unsigned)t * wks);
     }
   };
 
@@ -866,17 +885,32 @@ void k_dense(GemmArgs a) {
       return min(rg * DN_ROWS + q, a.N - 1);
     }
   };
-  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, (size_t)a.Nraw * a.K * 2);
+  // Packed weights (1 KB tiles of 16 rows x one k-step): weight block j of a
+  // stage is row tile j / 2 of the tile at its k-step j % 2, loaded whole.
+  const bool packed = a.wpack != 0;
+  auto wtile = [&](int f) -> int {  // global tile of the tile's row tile f (0..15)
+    const int fm = f >> 2, r = f & 3;
+    if constexpr (EPI == EPI_SWIGLU)
+      return min(rg * (DN_ROWS / 32) + fm * 2 + (r & 1), a.wtiles - 1) + (r < 2 ? 0 : a.wtiles);
+    else
+      return min(rg * (DN_ROWS / 16) + f, a.wtiles - 1);
+  };
+  const size_t wbytes = packed ? (size_t)(EPI == EPI_SWIGLU ? 2 : 1) * a.wtiles * (a.K / KS + PACK_GAP) * 1024
+                               : (size_t)a.Nraw * a.K * 2;
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.W, wbytes);
   const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X, (size_t)a.B * a.K * 2);
   // this wave fills weight blocks DN_WPW w .. and activation blocks DN_XPW w ..;
-  // lane: row 8 j + lane / 8 of block j, its piece (lane % 8) ^ (row % 16) / 2
+  // row-major: lane row 8 j + lane / 8 of block j, its piece (lane % 8) ^ (row % 16) / 2
   unsigned wv[DN_WPW], xv[DN_XPW];
 #pragma unroll
   for (int jj = 0; jj < DN_WPW; ++jj) {
-    const int q = 8 * (DN_WPW * w + jj) + (lane >> 3);
+    const int jb = DN_WPW * w + jj;
+    const int q = 8 * jb + (lane >> 3);
     const unsigned piece = (unsigned)((lane & 7) ^ ((q & 15) >> 1)) * 16;
-    wv[jj] = (unsigned)((size_t)wrow(q) * a.K * 2) + piece;
+    wv[jj] = packed ? (unsigned)(((size_t)wtile(jb >> 1) * (a.K / KS + PACK_GAP) + (jb & 1)) * 1024 + lane * 16)
+                    : (unsigned)((size_t)wrow(q) * a.K * 2) + piece;
   }
+  const int wstep = packed ? 2048 : 128;  // weight bytes between stages
 #pragma unroll
   for (int jj = 0; jj < DN_XPW; ++jj) {
     const int q = 8 * (DN_XPW * w + jj) + (lane >> 3);
@@ -887,10 +921,11 @@ void k_dense(GemmArgs a) {
   // stage st of the walk into a slot (a stage past the last reloads it into a
   // slot nobody reads, so every stage issues the same loads)
   auto load = [&](char* slot, int st) {
-    const int kb = (t0 + 2 * min(st, ns - 1)) * KS * 2;
+    const int s2 = t0 / 2 + min(st, ns - 1);  // the stage's pair of k-steps
+    const int kb = s2 * 128, kbw = s2 * wstep;
 #pragma unroll
     for (int jj = 0; jj < DN_WPW; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, slot + (DN_WPW * w + jj) * DN_BLOCK, 16, (int)wv[jj], kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, slot + (DN_WPW * w + jj) * DN_BLOCK, 16, (int)wv[jj], kbw, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < DN_XPW; ++jj)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, slot + (DN_WBLK + DN_XPW * w + jj) * DN_BLOCK, 16, (int)xv[jj],
@@ -903,16 +938,19 @@ void k_dense(GemmArgs a) {
   };
   // Piece p of tile row 16 t + l16 sits at block 2 t + l16 / 8, row l16 % 8,
   // slot p ^ l16 / 2: per lane, the offsets of k-step 0 and 1 (p = 4 ks + g4).
-  unsigned ro[2];
+  // Packed weights: the lane's slot of block 2 t + ks.
+  unsigned ro[2], wo[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < 2; ++ks) {
     ro[ks] = (unsigned)((l16 >> 3) * DN_BLOCK + (l16 & 7) * 128 + (((4 * ks + g4) ^ (l16 >> 1)) << 4));
+    wo[ks] = packed ? (unsigned)(ks * DN_BLOCK + lane * 16) : ro[ks];
+  }
   auto compute = [&](f32x4 (&acc)[4][4], const char* slot) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 av[4], bv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = *(const u32x4*)(slot + (2 * (4 * wm + r)) * DN_BLOCK + ro[ks]);
+      for (int r = 0; r < 4; ++r) av[r] = *(const u32x4*)(slot + (2 * (4 * wm + r)) * DN_BLOCK + wo[ks]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) bv[c] = *(const u32x4*)(slot + (DN_WBLK + 2 * (4 * wn + c)) * DN_BLOCK + ro[ks]);
 #pragma unroll

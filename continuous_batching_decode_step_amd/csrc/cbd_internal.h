@@ -67,6 +67,12 @@ struct GemmArgs {
   float* ssq_out;       // EPI_RESID: [nRB][B] this tile's sum of x^2 per lane
   float* part;          // panel split mode: [S][B][nRB][rows per row block] split partials
   int fold_elsewhere;   // EPI_STORE split mode: leave the partials unfolded (the consumer adds them)
+  // bf16 weights in the packed tile layout (cbd_pack_matrix): W holds
+  // tiles of 16 rows x 32 k, 1 KB each, row tile i of half h from tile
+  // (h * wtiles + i) * (K / 32 + PACK_GAP); wtiles = row tiles per half
+  // (SWIGLU: the gate half, then the up half).  0: row-major.
+  int wpack;
+  int wtiles;
   // EPI_RESID in panel split mode only: if norm_out is set, the fold also runs
   // the next RMSNorm, xn = (x * r) * g into norm_out (activation format), and
   // writes no sums of squares.
@@ -226,6 +232,15 @@ int workspace_rows(const cbd_model* m, int max_seq, size_t bytes);
 // Copy one lane's K or V rows [L * Hkv][len][hd] (device, contiguous) into its
 // blocks of a layer-major pool (to_pool), or back; blocks: the lane's block ids
 // on the device, one per 64 positions.
+// The packed tile layout of a bf16 matrix (cbd_pack_matrix): its size (0 if
+// none) and the packing kernel.  Each row tile's run of K / 32 tiles is
+// followed by PACK_GAP unused tiles, so that the runs the waves stream at
+// once do not start 2^n kilobytes apart (two adjacent row tiles per wave, as
+// the LM head reads them, streamed at 5.0 TB/s with runs 128 KB apart and
+// at 5.85 TB/s with 136 KB).
+constexpr int PACK_GAP = 8;
+size_t packed_bytes_bf16(int rows, int K, int halves);
+hipError_t launch_pack_bf16(const void* src, void* dst, int rows, int K, int halves, hipStream_t st);
 hipError_t launch_kv_rows(char* pool, char* rows, const int* blocks, int p0, int len, int n_rows, int Hkv,
                           int row_bytes, long long lstride, long long bbytes, bool to_pool, hipStream_t st);
 // The same for fragment-ordered bf16 chunks (frag: 1 = K order, 2 = V order),

@@ -325,6 +325,40 @@ hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStr
   return hipGetLastError();
 }
 
+// Packed tile layout of a bf16 matrix (the layout the header documents at
+// cbd_pack_matrix): one thread per 16-byte slot of a tile, zeros for the
+// padding rows of a half's last tile and for the gap tiles.
+__global__ __launch_bounds__(256) void k_pack_bf16(const uint16_t* src, uint16_t* dst, int rows, int K, int T,
+                                                   long long n_slots) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_slots) return;
+  const int nks = K / 32, run = nks + PACK_GAP;
+  const int L = (int)(i & 63);
+  const long long tile = i >> 6;            // (h * T + ti) * run + t
+  const int t = (int)(tile % run);
+  const long long ht = tile / run;          // h * T + ti
+  const int ti = (int)(ht % T), h = (int)(ht / T);
+  const int row = ti * 16 + (L & 15);
+  const int k = t * 32 + 8 * (L >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < rows && t < nks) v = *(const uint4*)(src + ((size_t)h * rows + row) * K + k);
+  *(uint4*)(dst + (size_t)i * 8) = v;
+}
+
+size_t packed_bytes_bf16(int rows, int K, int halves) {
+  if (rows <= 0 || halves <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return (size_t)halves * ((rows + 15) / 16) * (K / 32 + PACK_GAP) * 1024;
+}
+
+hipError_t launch_pack_bf16(const void* src, void* dst, int rows, int K, int halves, hipStream_t st) {
+  const long long n_slots = (long long)(packed_bytes_bf16(rows, K, halves) / 16);
+  if (n_slots == 0) return hipSuccess;
+  const int T = (rows + 15) / 16;
+  hipLaunchKernelGGL(k_pack_bf16, dim3((unsigned)((n_slots + 255) / 256)), dim3(256), 0, st, (const uint16_t*)src,
+                     (uint16_t*)dst, rows, K, T, n_slots);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;

@@ -362,6 +362,8 @@ int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** ou
   const int qd = c.n_heads * c.head_dim;
   if (c.d_model % pl || c.ffn_dim % pl || qd % pl)
     return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and n_heads*head_dim must be multiples of %d", pl);
+  if (c.packed && (c.wtype != CBD_BF16 || c.d_model % 32 || c.ffn_dim % 32 || qd % 32))
+    return fail(CBD_E_UNSUPPORTED, "packed weights need bf16 and d_model, ffn_dim, n_heads*head_dim multiples of 32");
   if (!w->final_norm || !w->attn_norm || !w->ffn_norm || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down)
     return fail(CBD_E_ARG, "null weight pointer array");
   int rc;
@@ -419,6 +421,19 @@ void cbd_model_destroy(cbd_model* m) {
     if (m->slot[i]) (void)hipHostFree(m->slot[i]);
   }
   delete m;
+}
+
+size_t cbd_packed_bytes(int wtype, int rows, int K, int halves) {
+  return wtype == CBD_BF16 ? packed_bytes_bf16(rows, K, halves) : 0;
+}
+
+int cbd_pack_matrix(int wtype, const void* src, void* dst, int rows, int K, int halves, void* stream) {
+  if (!src || !dst) return fail(CBD_E_ARG, "null matrix pointer");
+  if (cbd_packed_bytes(wtype, rows, K, halves) == 0)
+    return fail(CBD_E_UNSUPPORTED, "no packed layout for wtype %d, %d x %d rows, K %d", wtype, halves, rows, K);
+  if (((uintptr_t)src | (uintptr_t)dst) & 15) return fail(CBD_E_ARG, "matrix pointers must be 16-byte aligned");
+  HIP_TRY(launch_pack_bf16(src, dst, rows, K, halves, (hipStream_t)stream));
+  return CBD_OK;
 }
 
 size_t cbd_arena_block_bytes(const cbd_config* cfg) {
@@ -742,6 +757,10 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.amax = (float2*)(ws + L.amax);
   g.ssq_out = (float*)(ws + L.ssq);
   g.part = (float*)(ws + L.gpart);
+  // packed tile layout: the layer matrices and an untied head (a tied head is
+  // the row-major embedding)
+  g.wpack = m->c.packed && (epi != EPI_HEAD || !m->c.tied_embeddings) ? 1 : 0;
+  g.wtiles = (p.N + TILE - 1) / TILE;
   const bool dense = dense_ok(m, p, epi) && (m->variant == 3 || (m->variant == 0 && dense_auto(p, epi, B)));
   const bool panel = !dense && (m->variant == 2 || m->variant == 3 || (m->variant == 0 && B >= panel_min_b(m, epi, p.K)));
   ProfScope ps(m, cls, st);

@@ -74,6 +74,10 @@ typedef struct {
   float rope_theta; /* rotary base, e.g. 10000 */
   int tied_embeddings; /* nonzero: the LM head is the embedding matrix */
   int wtype;           /* cbd_wtype */
+  int packed;          /* nonzero: w_qkv, w_o, w_gu, w_down and an untied lm_head are in
+                          the packed tile layout of cbd_pack_matrix (CBD_BF16, d_model,
+                          ffn_dim and n_heads*head_dim multiples of 32); the embedding
+                          stays row-major */
 } cbd_config;
 
 /* One weight matrix [N, K], row-major, K contiguous, rows 16-byte aligned.
@@ -107,6 +111,32 @@ typedef struct {
 
 typedef struct cbd_model cbd_model;
 typedef struct cbd_arena cbd_arena;
+
+/* Packed tile layout of a bf16 weight matrix.  The step reads every weight
+ * byte once for all lanes ("MODEL-BATCHING-RESULTS — multi-user batched
+ * decode, measured", section "The lever"); in this layout each 64-lane load
+ * of the weight stream is one contiguous kilobyte that is already a matrix-
+ * core operand, where row-major rows give 16 segments of 64 bytes (on
+ * MI355X the weight stream then runs about 12% faster).  The rows are
+ * taken as `halves` consecutive halves of `rows` rows each (w_gu: 2, the
+ * gate rows and the up rows; every other matrix 1); each half is cut into
+ * T = ceil(rows / 16) row tiles (the last padded with zero rows) and K / 32
+ * column steps; tile (h, i, t) is the 1024 bytes at offset
+ * ((h * T + i) * (K / 32 + 8) + t) * 1024 and holds, for slot L = 0 .. 63,
+ * the 8 elements of row 16 i + L % 16, columns 32 t + 8 (L / 16) .. + 7.
+ * The 8 tiles after each row tile's run are zeros (unused: they keep the
+ * runs the weight stream reads at once from starting 2^n kilobytes apart).
+ * Returns the packed size in bytes, or 0 when the matrix has no packed form
+ * (wtype other than CBD_BF16, K not a positive multiple of 32, rows or
+ * halves not positive). */
+size_t cbd_packed_bytes(int wtype, int rows, int K, int halves);
+
+/* Write the packed layout of src (device, [halves * rows, K] row-major) into
+ * dst (device, cbd_packed_bytes bytes, 16-byte aligned), on `stream` (a
+ * hipStream_t; NULL: the default stream).  src and dst must not overlap.
+ * Errors: CBD_E_ARG (null pointer), CBD_E_UNSUPPORTED (no packed form),
+ * CBD_E_HIP. */
+int cbd_pack_matrix(int wtype, const void* src, void* dst, int rows, int K, int halves, void* stream);
 
 /* Library version string. */
 const char* cbd_version(void);

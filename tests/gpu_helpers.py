@@ -39,10 +39,10 @@ def top2_gap(o) -> float:
     return float(s[-1] - s[-2])
 
 
-def engine_for(cfg, W, n_lanes, max_seq, max_batch=None):
+def engine_for(cfg, W, n_lanes, max_seq, max_batch=None, pack=None):
     import continuous_batching_decode_step_amd as cbd
     from continuous_batching_decode_step_amd.driver import Engine
-    dw = cbd.upload_weights(W)
+    dw = cbd.upload_weights(W, pack=pack)
     return Engine(cfg, dw, n_lanes, max_seq, max_batch)
 
 

@@ -209,8 +209,11 @@ def test_projection_families_are_bitwise_identical():
     # B = 100 the 128-lane panel width; B = 260 on the wide vocabulary 64-lane
     # panels in full mode beside 128-lane panels in split mode; the bf16 cases
     # run the dense tiles in full and split mode, with ragged lane groups, and
-    # B = 160 picks them automatically.
+    # B = 160 picks them automatically.  bf16 weights go to the device in the
+    # packed tile layout (partly padded tiles: FFN 96 rows per half, vocabulary
+    # 300); each bf16 case also runs the automatic choice on row-major weights.
     from continuous_batching_decode_step_amd.driver import generate_lockstep
+    import continuous_batching_decode_step_amd as cbd
     cases = [(synth.TINY, 40), (SMALL_GQA, 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 40),
              (SMALL_GQA.with_wtype(synth.WTYPE_Q8_0), 40), (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 5),
              (SMALL_GQA.with_wtype(synth.WTYPE_BF16), 100), (SMALL_GQA, 100), (WIDE_VOCAB, 260),
@@ -220,8 +223,12 @@ def test_projection_families_are_bitwise_identical():
         W = synth.make_weights(cfg)
         prompts = [synth.prompt_tokens(cfg, 80 + b, 2 + b % 5) for b in range(B)]
         runs = []
-        for variant in (1, 2, 3, 0):
-            eng = engine_for(cfg, W, B, 12)
+        layouts = [(v, None) for v in (1, 2, 3, 0)]
+        if cbd.packable(cfg):
+            layouts.append((0, False))
+        for variant, pack in layouts:
+            eng = engine_for(cfg, W, B, 12, pack=pack)
+            assert eng.model.weights.packed == (cbd.packable(cfg) and pack is None)
             eng.model.set_variant(variant)
             runs.append(generate_lockstep(eng, prompts, 4, want_logits=True))
             del eng
@@ -230,3 +237,27 @@ def test_projection_families_are_bitwise_identical():
             for la, lb in zip(runs[0][1], logs):
                 for x, y in zip(la, lb):
                     assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_packed_tile_layout():
+    # cbd_pack_matrix against the layout written out with numpy reshapes: per
+    # half, rows padded with zeros to whole 16-row tiles; tile (h, i, t) holds
+    # slot L = 16 g + r as row 16 i + r, columns 32 t + 8 g .. + 7; each row
+    # tile's run of K / 32 tiles is followed by 8 zero tiles.  Two halves
+    # of 40 rows (a partly padded last tile) by K = 96, and one half of 16 x 32.
+    import torch
+    import continuous_batching_decode_step_amd as cbd
+    for halves, rows, K in [(2, 40, 96), (1, 16, 32), (1, 300, 128)]:
+        say("case: packed layout, %d halves of %d rows, K %d" % (halves, rows, K))
+        rng = np.random.default_rng(7 + rows)
+        M = rng.integers(0, 1 << 16, size=(halves * rows, K), dtype=np.uint16)
+        T, nks = (rows + 15) // 16, K // 32
+        Mp = np.zeros((halves, T * 16, K + 8 * 32), np.uint16)   # + the 8 zero tiles after each run
+        Mp[:, :rows, :K] = M.reshape(halves, rows, K)
+        ref = Mp.reshape(halves, T, 16, nks + 8, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+        assert cbd.lib().cbd_packed_bytes(cbd.CBD_BF16, rows, K, halves) == ref.size * 2
+        d = torch.from_numpy(M.view(np.int16)).cuda()
+        got = cbd.pack_matrix(d, rows, halves).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref)
+    assert cbd.lib().cbd_packed_bytes(cbd.CBD_BF16, 16, 48, 1) == 0   # K not a multiple of 32
+    assert cbd.lib().cbd_packed_bytes(cbd.CBD_F32, 16, 64, 1) == 0

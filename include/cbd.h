@@ -117,7 +117,8 @@ typedef struct cbd_arena cbd_arena;
  * decode, measured", section "The lever"); in this layout each 64-lane load
  * of the weight stream is one contiguous kilobyte that is already a matrix-
  * core operand, where row-major rows give 16 segments of 64 bytes (on
- * MI355X the weight stream then runs about 12% faster).  The rows are
+ * MI355X a plain stream of such loads reads 5.85 TB/s against 5.4; the
+ * 7B gate|up projection at 64 lanes takes 46.5 us against 56.5).  The rows are
  * taken as `halves` consecutive halves of `rows` rows each (w_gu: 2, the
  * gate rows and the up rows; every other matrix 1); each half is cut into
  * T = ceil(rows / 16) row tiles (the last padded with zero rows) and K / 32

@@ -643,7 +643,7 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // 116 us as split-K tiles, 97 us as panels).  The long reduction (down) is
 // faster as a panel even for one lane, and so are QKV and O once their
 // split-mode panels need no fold launch of their own: QKV's partials are
-// added by the matrix-core attention kernel up to 8 lanes (QKV 15.9 -> 13.2
+// added by the matrix-core attention kernel up to 32 lanes (QKV 15.9 -> 13.2
 // us at one lane, attention +0.6), and O's fold runs the next RMSNorm in the
 // same kernel (O and norm 18.1 -> 16.7 us at one lane, 19.4 -> 16.5 at 8,
 // 20.6 -> 16.7 at 16; the split-K tiles' 384 and 256 workgroups also sit
@@ -866,12 +866,12 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   };
   if ((rc = norm(m->attn_norm[0], 1))) return rc;
   for (int l = 0; l < c.n_layers; ++l) {
-    // Up to 8 lanes the matrix-core attention kernel adds the QKV split partials
-    // itself (no fold launch); wider, each lane's partials would be re-read by
-    // all its attention workgroups from beyond L2 (at 64 lanes +36 MB per
-    // launch, more than the fold kernel costs).
+    // Up to 32 lanes the matrix-core attention kernel adds the QKV split
+    // partials itself (no fold launch: QKV 18.8 -> 14.7 us at 32 lanes,
+    // attention 51.9 -> 54.1); wider, each lane's partials are re-read by all
+    // its attention workgroups (at 64 lanes QKV -6.2 us, attention +7.1).
     bool unfolded = false;
-    const bool attn_folds = !multi && B <= 8 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
+    const bool attn_folds = !multi && B <= 32 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
     if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st, nullptr, nullptr,
                        attn_folds ? &unfolded : nullptr)))
       return rc;

@@ -640,23 +640,24 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // projection alone): below these widths the split-K tiles are as fast or
 // faster; above them their per-wave activation re-reads cost more than a
 // mostly idle 32-lane panel (at 16 lanes the four layer projections take
-// 116 us as split-K tiles, 97 us as panels).  The long reduction (down) is
-// faster as a panel even for one lane, and so are QKV and O once their
-// split-mode panels need no fold launch of their own: QKV's partials are
-// added by the matrix-core attention kernel up to 32 lanes (QKV 15.9 -> 13.2
-// us at one lane, attention +0.6), and O's fold runs the next RMSNorm in the
-// same kernel (O and norm 18.1 -> 16.7 us at one lane, 19.4 -> 16.5 at 8,
-// 20.6 -> 16.7 at 16; the split-K tiles' 384 and 256 workgroups also sit
-// unevenly on 256 compute units).  Other weight formats and attention shapes
-// keep the split-K tiles for QKV below 4 lanes and for O below 24 (not
-// measured otherwise; their fold would be a launch of its own).
+// 116 us as split-K tiles, 97 us as panels).  QKV on bf16 models with the
+// matrix-core attention shapes is a split-mode panel from one lane, its
+// partials added by the attention kernel up to 32 lanes (QKV 15.9 -> 13.2 us
+// at one lane, attention +0.6).  The residual projections (O, down) of those
+// models keep the split-K tiles below 8 lanes (their in-workgroup fold, then
+// the norm kernel: 277 -> 292 tok/s at one lane, 1047 -> 1094 at four, equal
+// at eight, on packed weights) and run as split-mode panels from 8, where the
+// fold also runs the next RMSNorm.  Other weight formats and attention shapes
+// keep the split-K tiles for QKV below 4 lanes and for O below 24, and run
+// the long reduction (down) as a panel at every width (not measured
+// otherwise).
 static int panel_min_b(const cbd_model* m, int epi, int K) {
   const bool bf16_mf = m->wt == WT_BF16 && attn_chunks_per_item(m) == ATTN_GROUP;
   switch (epi) {
     case EPI_STORE: return bf16_mf ? 1 : 4;                 // QKV
     case EPI_SWIGLU: return 8;                              // gate|up
     case EPI_HEAD: return 4;
-    default: return K > 4096 || bf16_mf ? 1 : 24;           // down; O
+    default: return bf16_mf ? 8 : (K > 4096 ? 1 : 24);      // down; O
   }
 }
 

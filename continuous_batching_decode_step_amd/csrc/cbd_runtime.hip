@@ -647,7 +647,9 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // models keep the split-K tiles below 8 lanes (their in-workgroup fold, then
 // the norm kernel: 277 -> 292 tok/s at one lane, 1047 -> 1094 at four, equal
 // at eight, on packed weights) and run as split-mode panels from 8, where the
-// fold also runs the next RMSNorm.  Other weight formats and attention shapes
+// fold also runs the next RMSNorm.  bf16 gate|up is a full-mode panel from one
+// lane (packed weights: 292 -> 297 tok/s at one lane, 1096 -> 1120 at four;
+// f32 and Q8_0 keep the split-K tiles below 8).  Other weight formats and attention shapes
 // keep the split-K tiles for QKV below 4 lanes and for O below 24, and run
 // the long reduction (down) as a panel at every width (not measured
 // otherwise).
@@ -655,7 +657,7 @@ static int panel_min_b(const cbd_model* m, int epi, int K) {
   const bool bf16_mf = m->wt == WT_BF16 && attn_chunks_per_item(m) == ATTN_GROUP;
   switch (epi) {
     case EPI_STORE: return bf16_mf ? 1 : 4;                 // QKV
-    case EPI_SWIGLU: return 8;                              // gate|up
+    case EPI_SWIGLU: return m->wt == WT_BF16 ? 1 : 8;       // gate|up
     case EPI_HEAD: return 4;
     default: return bf16_mf ? 8 : (K > 4096 ? 1 : 24);      // down; O
   }

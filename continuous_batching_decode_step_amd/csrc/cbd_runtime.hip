@@ -1204,15 +1204,20 @@ int cbd_prefill_batch(cbd_model* m, cbd_arena* a, int n_seq, const int32_t* lane
   if (a->m != m) return fail(CBD_E_ARG, "arena belongs to another model");
   if (n_seq < 1) return fail(CBD_E_ARG, "n_seq = %d < 1", n_seq);
   const cbd_config& c = m->c;
-  std::vector<uint8_t> seen(a->n_lanes, 0);
+  // distinct lanes: the arena's per-call marks, as the decode step checks them
+  // (no host allocation per call)
+  if (++a->epoch == 0) {
+    std::fill(a->mark.begin(), a->mark.end(), 0u);
+    a->epoch = 1;
+  }
   long long R = 0;
   int new_blocks = 0;
   bool multi = false;
   for (int i = 0; i < n_seq; ++i) {
     const int ln = lanes[i];
     if (ln < 0 || ln >= a->n_lanes) return fail(CBD_E_ARG, "lanes[%d] = %d outside [0, %d)", i, ln, a->n_lanes);
-    if (seen[ln]) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
-    seen[ln] = 1;
+    if (a->mark[ln] == a->epoch) return fail(CBD_E_DUP_LANE, "lane %d appears twice", ln);
+    a->mark[ln] = a->epoch;
     if (!a->live[ln]) return fail(CBD_E_LANE_NOT_LIVE, "lane %d is not live", ln);
     if (positions[i] != a->len[ln])
       return fail(CBD_E_POS_MISMATCH, "positions[%d] = %d but lane %d holds %d tokens", i, positions[i], ln,

@@ -148,9 +148,9 @@ hipError_t launch_panel(int wt, int epi, int C, int rm, int split, const GemmArg
 __host__ __device__ constexpr bool fold_norm_supported(int N) { return N % 16 == 0 && N <= 8192; }
 // workgroups of one panel launch (for sizing decisions)
 int panel_workgroups(const GemmArgs& a, int C, int rm, int split);
-// Dense-tile projection for bf16 weights (both operands staged in LDS, 128
-// weight rows x 128 lanes per workgroup); K a multiple of 128, split lengths
-// of 256.  split = 1: one split per workgroup, partials folded in order by a
+// Dense-tile projection for bf16 weights (both operands staged in LDS, 256
+// weight rows x 128 lanes per eight-wave workgroup); K a multiple of 128,
+// split lengths a multiple of 256.  split = 1: one split per workgroup, partials folded in order by a
 // second kernel (as launch_panel).  Same output bits as launch_gemm.
 hipError_t launch_dense(int epi, int split, const GemmArgs& a, hipStream_t st);
 int dense_workgroups(const GemmArgs& a, int epi, int split);

@@ -753,20 +753,29 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const float* kn = row + (size_t)(a.Hq + g) * HD;
   const float* vn = row + (size_t)(a.Hq + a.Hkv + g) * HD;
   if (a.qkv_S > 0) {
+    // every load first (one memory round trip), then the sums in split order
     const int nsum = (holds_p ? G + 2 : G) * HD;
     const size_t sstride = (size_t)a.B * a.Nqkv;
     const float* P = a.qkv_part + (size_t)b * a.Nqkv;
-    for (int idx = tid; idx < nsum; idx += 64 * MF_WAVES) {
+    constexpr int NT = 64 * MF_WAVES;
+    constexpr int IT = ((G + 2) * HD + NT - 1) / NT;  // values per thread at most
+    float pv[IT][GEMM_MAX_SPLIT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = min(tid + it * NT, nsum - 1);  // past nsum: a repeat, never stored
       const int hv = idx / HD, d = idx % HD;
       const int n = (hv < G ? (g * G + hv) : hv == G ? a.Hq + g : a.Hq + a.Hkv + g) * HD + d;
-      float pv[GEMM_MAX_SPLIT];
 #pragma unroll
-      for (int s2 = 0; s2 < GEMM_MAX_SPLIT; ++s2) pv[s2] = P[min(s2, a.qkv_S - 1) * sstride + n];
-      float v = pv[0];
+      for (int s2 = 0; s2 < GEMM_MAX_SPLIT; ++s2) pv[it][s2] = P[min(s2, a.qkv_S - 1) * sstride + n];
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * NT;
+      float v = pv[it][0];
 #pragma unroll
       for (int s2 = 1; s2 < GEMM_MAX_SPLIT; ++s2)
-        if (s2 < a.qkv_S) v = v + pv[s2];
-      qsum[idx] = v;
+        if (s2 < a.qkv_S) v = v + pv[it][s2];
+      if (idx < nsum) qsum[idx] = v;
     }
     __syncthreads();
     qv = qsum;

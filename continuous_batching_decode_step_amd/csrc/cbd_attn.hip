@@ -738,6 +738,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
   const unsigned foff = active ? (unsigned)lane * 16 : PAST_RANGE;
   u32x4 kr[4][KK];
   mf_load_k<HD>(krs, foff, kr);
+  // The lane's rotary table goes to LDS now, so its loads overlap the K loads
+  // and the query inputs' (the rotation below reads it from there).
+  __shared__ float2 css[HD / 2];
+  const float2 csv = cs[tid % (HD / 2)];
   // The workgroup rotates the group's queries (split into bf16 parts) and, if
   // its last chunk holds slot p, the new key and value, through LDS; lanes
   // then read their MFMA operand rows from there.
@@ -777,19 +781,20 @@ __global__ __launch_bounds__(64 * MF_WAVES) __attribute__((amdgpu_waves_per_eu(2
         if (s2 < a.qkv_S) v = v + pv[it][s2];
       if (idx < nsum) qsum[idx] = v;
     }
-    __syncthreads();
     qv = qsum;
     kn = qsum + G * HD;
     vn = qsum + (G + 1) * HD;
   } else {
     qv = row + (size_t)g * G * HD;
   }
-  mf_prep_queries<HD, G>(qv, cs, qs, tid, 64 * MF_WAVES);
+  if (tid < HD / 2) css[tid] = csv;
+  __syncthreads();
+  mf_prep_queries<HD, G>(qv, css, qs, tid, 64 * MF_WAVES);
   if (holds_p) {
     const int pc = p % ATTN_SPLIT;
     for (int d = tid; d < HD; d += 64 * MF_WAVES) {
       const bool fh = d < HD / 2;
-      const uint16_t kw = f2bf_a(rope_pair(kn[d], kn[fh ? d + HD / 2 : d - HD / 2], cs[fh ? d : d - HD / 2], fh));
+      const uint16_t kw = f2bf_a(rope_pair(kn[d], kn[fh ? d + HD / 2 : d - HD / 2], css[fh ? d : d - HD / 2], fh));
       const uint16_t vw = f2bf_a(vn[d]);
       kvn[0][d] = kw;
       kvn[1][d] = vw;

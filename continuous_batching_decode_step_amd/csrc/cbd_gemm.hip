@@ -213,8 +213,12 @@ __device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, con
   }
 }
 
-template <int WT, int EPI, int C>
+// NRM: the activations are the RMSNorm of a.in_x, computed by each wave for
+// its own split and staged in LDS (one column group of at most 16 lanes).
+template <int WT, int EPI, int C, bool NRM = false>
 __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
+  static_assert(!NRM || C == 1, "normalising split-K tiles take one column group");
+  extern __shared__ __attribute__((aligned(16))) char gsm[];  // [norm staging][split partials]
   constexpr int R = gemm_rows(EPI);
   constexpr int KS = KStep<WT>::v;
   constexpr int PL = KStep<WT>::per_lane;
@@ -259,12 +263,77 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
     if constexpr (WT == WT_Q8) sp[r] = a.Ws + (size_t)row * (a.K >> 5) + (kb >> 5);
   }
   // Column pointers (B operand column = lane % 16), clamped the same way.
+  // NRM: rows of this wave's LDS staging, one per lane of the step, Ks
+  // activations + 16 bytes each.
+  const int n_st = NRM ? a.B : 0;                    // staged lanes (B <= 16)
+  const int st_row = NRM ? a.Ks * XB + 16 : 0;       // bytes per staged lane
+  char* mine = gsm + (size_t)s * n_st * st_row;      // this wave's staging
   const char* bp[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int col = min(cg * TILE * C + TILE * c + r16, a.B - 1);
-    bp[c] = (const char*)a.X + ((size_t)col * a.K + kb + koff) * XB;
+    if constexpr (NRM)
+      bp[c] = mine + (size_t)col * st_row + koff * XB;
+    else
+      bp[c] = (const char*)a.X + ((size_t)col * a.K + kb + koff) * XB;
   }
+
+  // NRM: rows [0, B) of this wave's staging get xn = (x * r) * g over k in
+  // [kb, ke), as the norm kernel computes them: r from the sum of the
+  // producer's partials in its order (thread t of its 256 adds partial t; a
+  // shuffle tree per wave; then its four waves in order, three of them empty
+  // here), rounded to the activation format.
+  auto stage_norm = [&](char* dst, int row_bytes, int k0, int k1) {
+    if constexpr (NRM) {
+      float ssv[TILE];
+#pragma unroll
+      for (int j = 0; j < TILE; ++j) {
+        ssv[j] = 0.f;
+        if (j < a.B && lane < a.in_ssq_n) ssv[j] += a.in_ssq[(size_t)lane * a.B + j];
+      }
+      const int nq = (k1 - k0) / 4;  // float4 groups of the split
+#pragma unroll
+      for (int j = 0; j < TILE; ++j) {
+        if (j >= a.B) break;
+        float ss = ssv[j];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+        ss = ((ss + 0.f) + 0.f) + 0.f;
+        const float r = 1.0f / sqrtf(ss / (float)a.K + a.in_eps);
+        const float* xr = a.in_x + (size_t)j * a.K + k0;
+        const float* gr = a.in_g + k0;
+        char* row = dst + (size_t)j * row_bytes;
+        for (int q0 = 0; q0 < nq; q0 += 128) {
+          const int qa = q0 + lane, qb = q0 + 64 + lane;
+          const bool oka = qa < nq, okb = qb < nq;
+          const float4 xa = *(const float4*)(xr + 4 * (oka ? qa : 0));
+          const float4 ga = *(const float4*)(gr + 4 * (oka ? qa : 0));
+          const float4 xb = *(const float4*)(xr + 4 * (okb ? qb : 0));
+          const float4 gb = *(const float4*)(gr + 4 * (okb ? qb : 0));
+          auto put = [&](int q, const float4& xv, const float4& gv) {
+            const float v0 = (xv.x * r) * gv.x, v1 = (xv.y * r) * gv.y, v2 = (xv.z * r) * gv.z,
+                        v3 = (xv.w * r) * gv.w;
+            if constexpr (WT == WT_F32) {
+              *(float4*)(row + (size_t)q * 16) = make_float4(v0, v1, v2, v3);
+            } else if constexpr (WT == WT_BF16) {
+              *(u32x2*)(row + (size_t)q * 8) = u32x2{(unsigned)f2bf(v0) | ((unsigned)f2bf(v1) << 16),
+                                                     (unsigned)f2bf(v2) | ((unsigned)f2bf(v3) << 16)};
+            } else {
+              _Float16 h[4] = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+              *(u32x2*)(row + (size_t)q * 8) = __builtin_bit_cast(u32x2, h);
+            }
+          };
+          if (oka) put(qa, xa, ga);
+          if (okb) put(qb, xb, gb);
+        }
+      }
+    } else {
+      (void)dst;
+      (void)row_bytes;
+      (void)k0;
+      (void)k1;
+    }
+  };
 
   f32x4 acc[R][C];
 #pragma unroll
@@ -272,6 +341,27 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto load_stage_w = [&](u32x4 (&A)[U][R], int step0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (step0 + u) * KS;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if constexpr (WT == WT_Q8)
+          A[u][r] = ld_q8(ap[r] + k, sp[r] + (k >> 5));
+        else
+          A[u][r] = ld16(ap[r] + (size_t)(step0 + u) * wks);
+      }
+    }
+  };
+  auto load_stage_x = [&](u32x4 (&Bv)[U][C], int step0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (step0 + u) * KS;
+#pragma unroll
+      for (int c = 0; c < C; ++c) Bv[u][c] = ld16(bp[c] + (size_t)k * XB);
+    }
+  };
   auto load_stage = [&](u32x4 (&A)[U][R], u32x4 (&Bv)[U][C], int step0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -304,7 +394,15 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
   const int nst = nfull / U;
   {
     u32x4 A0[U][R], B0[U][C], A1[U][R], B1[U][C];
-    if (nst > 0) load_stage(A0, B0, 0);
+    if constexpr (NRM) {
+      // The first weights are in flight while the activations are normalised.
+      if (nst > 0) load_stage_w(A0, 0);
+      stage_norm(mine, st_row, kb, ke);
+      __syncthreads();
+      if (nst > 0) load_stage_x(B0, 0);
+    } else {
+      if (nst > 0) load_stage(A0, B0, 0);
+    }
     int st = 0;
     // steady state, no branches inside: stage st+1 (and st+2) load while st (st+1) computes
     for (; st + 2 < nst; st += 2) {
@@ -350,7 +448,8 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
     // Split partials through LDS, in rounds of `per_round` waves; wave 0 adds
     // them to its own partial P_0 in ascending split order.
     constexpr int E = R * C * 4;
-    extern __shared__ float red[];  // [per_round][E][64]
+    // [per_round][E][64], after the norm staging
+    float* red = (float*)(gsm + (NRM ? (size_t)a.S * n_st * st_row : 0));
     const int per_round = a.red_waves;
     for (int r0 = 1; r0 < a.S; r0 += per_round) {
       const int r1 = min(r0 + per_round, a.S);
@@ -1120,7 +1219,15 @@ hipError_t launch_dense(int epi, int split, const GemmArgs& a, hipStream_t st) {
 template <int WT, int EPI>
 static hipError_t launch_c(int C, const GemmArgs& a, int blocks, hipStream_t st) {
   const dim3 blk(64 * a.S);
-  const size_t lds = a.S > 1 ? (size_t)a.red_waves * gemm_rows(EPI) * C * 4 * 64 * sizeof(float) : 0;
+  size_t lds = a.S > 1 ? (size_t)a.red_waves * gemm_rows(EPI) * C * 4 * 64 * sizeof(float) : 0;
+  if (a.in_x) {
+    constexpr int XB = WT == WT_F32 ? 4 : 2;
+    if (C != 1 || EPI == EPI_RESID || !gemm_norm_in_supported(a.B, a.K, a.S, a.Ks, XB, a.in_ssq_n))
+      return hipErrorInvalidValue;
+    lds += (size_t)a.S * a.B * (a.Ks * XB + 16);
+    if constexpr (EPI != EPI_RESID) hipLaunchKernelGGL((k_gemm<WT, EPI, 1, true>), dim3(blocks), blk, lds, st, a);
+    return hipGetLastError();
+  }
   switch (C) {
     case 1: hipLaunchKernelGGL((k_gemm<WT, EPI, 1>), dim3(blocks), blk, lds, st, a); break;
     case 2: hipLaunchKernelGGL((k_gemm<WT, EPI, 2>), dim3(blocks), blk, lds, st, a); break;

@@ -79,7 +79,29 @@ struct GemmArgs {
   const float* norm_g;
   float norm_eps;
   void* norm_out;
+  // Split-K tiles only (launch_gemm, one column group of at most 16 lanes):
+  // if in_x is set, X is not read; each wave computes its split of the
+  // RMSNorm output itself, (x * r) * in_g rounded to the activation format,
+  // r = 1 / sqrt(sum of the in_ssq_n per-row-block sums of x^2 / K + in_eps)
+  // with the norm kernel's additions, and stages it in LDS (the norm kernel's
+  // bits, without its launch).  in_ssq_n at most NORM_IN_MAX_SSQ.
+  const float* in_x;
+  const float* in_ssq;
+  int in_ssq_n;
+  const float* in_g;
+  float in_eps;
 };
+// Producer row blocks (sums of x^2 per lane) a split-K tile that normalises its
+// own activations can add: one per lane of a wave.
+constexpr int NORM_IN_MAX_SSQ = 64;
+// Largest LDS staging of normalised activations per split-K workgroup.
+constexpr size_t NORM_IN_MAX_LDS = 32 * 1024;
+// Whether launch_gemm can normalise its own activations for a projection of K
+// inputs, S splits of Ks, over B lanes whose activation format has xb bytes.
+__host__ __device__ constexpr bool gemm_norm_in_supported(int B, int K, int S, int Ks, int xb, int ssq_n) {
+  return B >= 1 && B <= TILE && ssq_n >= 1 && ssq_n <= NORM_IN_MAX_SSQ && K % 4 == 0 &&
+         (size_t)S * B * ((size_t)Ks * xb + 16) <= NORM_IN_MAX_LDS;
+}
 
 struct AttnArgs {
   const float* qkv;       // [B, Nqkv] f32, before rotation

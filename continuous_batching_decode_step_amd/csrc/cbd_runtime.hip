@@ -741,9 +741,20 @@ static int dense_split(int B, const Plan& p, int epi) {
 // xn, and *normed says so (the caller then launches no norm).  unfolded: for
 // QKV, the consumer can add split partials itself; if the projection runs as
 // a split-mode panel its fold is skipped and *unfolded says so.
+// The RMSNorm of the residual stream that produces a projection's input, not
+// yet launched: its gain and the producer's row blocks of sums of x^2.
+struct PendingNorm {
+  const float* g;
+  int ssq_n;
+  int rows;  // rows of x (the step's B; the LM head reads only the first n_out)
+};
+
+// pre: the RMSNorm that produces X (xn), if not yet run; split-K tiles of one
+// column group run it themselves (no norm launch), otherwise it is launched
+// here first.
 static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_matrix& W, const void* X, int B, float* out,
                     void* act_out, char* ws, const WsLayout& L, hipStream_t st, const float* norm_g = nullptr,
-                    bool* normed = nullptr, bool* unfolded = nullptr) {
+                    bool* normed = nullptr, bool* unfolded = nullptr, const PendingNorm* pre = nullptr) {
   GemmArgs g{};
   g.W = W.data;
   g.Ws = (const uint16_t*)W.scale;
@@ -766,6 +777,21 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
   g.wtiles = (p.N + TILE - 1) / TILE;
   const bool dense = dense_ok(m, p, epi) && (m->variant == 3 || (m->variant == 0 && dense_auto(p, epi, B)));
   const bool panel = !dense && (m->variant == 2 || m->variant == 3 || (m->variant == 0 && B >= panel_min_b(m, epi, p.K)));
+  const int C1 = B <= 16 ? 1 : (B <= 32 ? 2 : 4);  // split-K tiles: column group width / 16
+  if (pre) {
+    if (!dense && !panel && C1 == 1 && epi != EPI_RESID && pre->rows == B &&
+        gemm_norm_in_supported(B, p.K, p.S, p.Ks, m->actb, pre->ssq_n)) {
+      g.in_x = (const float*)(ws + L.x);
+      g.in_ssq = (const float*)(ws + L.ssq);
+      g.in_ssq_n = pre->ssq_n;
+      g.in_g = pre->g;
+      g.in_eps = m->c.rms_eps;
+    } else {
+      ProfScope pn(m, P_NORM, st);
+      HIP_TRY(launch_norm(m->wt, (const float*)(ws + L.x), (const float*)(ws + L.ssq), pre->ssq_n, pre->g,
+                          pre->rows, m->c.d_model, m->c.rms_eps, ws + L.xn, st));
+    }
+  }
   ProfScope ps(m, cls, st);
   if (dense) {
     const int split = dense_split(B, p, epi);
@@ -799,9 +825,8 @@ static int run_gemm(cbd_model* m, int cls, const Plan& p, int epi, const cbd_mat
     }
     HIP_TRY(launch_panel(m->wt, epi, C, rm, split, g, st));
   } else {
-    const int C = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-    g.nCG = (B + TILE * C - 1) / (TILE * C);
-    HIP_TRY(launch_gemm(m->wt, epi, C, g, st));
+    g.nCG = (B + TILE * C1 - 1) / (TILE * C1);
+    HIP_TRY(launch_gemm(m->wt, epi, C1, g, st));
   }
   return CBD_OK;
 }
@@ -861,13 +886,15 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.frag = kv_frag(m) ? 1 : 0;
   int rc;
   void* xn = ws + L.xn;
-  // RMSNorm of x into xn; ssq_n = row blocks of the last producer of x (the embedding: one)
-  auto norm = [&](const float* g, int ssq_n) -> int {
-    ProfScope ps(m, P_NORM, st);
-    HIP_TRY(launch_norm(m->wt, x, ssq, ssq_n, g, B, d, c.rms_eps, xn, st));
-    return CBD_OK;
-  };
-  if ((rc = norm(m->attn_norm[0], 1))) return rc;
+  (void)x;
+  (void)ssq;
+  (void)d;
+  // The RMSNorm of x into xn that the next projection consumes, run by that
+  // projection (or launched just before it); ssq_n = row blocks of the last
+  // producer of x (the embedding: one).  None pending when a split-mode fold
+  // has already normalised x.
+  PendingNorm pn{m->attn_norm[0], 1, B};
+  const PendingNorm* pending = &pn;
   for (int l = 0; l < c.n_layers; ++l) {
     // Up to 32 lanes the matrix-core attention kernel adds the QKV split
     // partials itself (no fold launch: QKV 18.8 -> 14.7 us at 32 lanes,
@@ -876,7 +903,7 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
     bool unfolded = false;
     const bool attn_folds = !multi && B <= 32 && attn_mfma_supported(c.head_dim, m->wt == WT_BF16, m->G);
     if ((rc = run_gemm(m, P_QKV, m->p_qkv, EPI_STORE, m->qkv[l], xn, B, qkv, nullptr, ws, L, st, nullptr, nullptr,
-                       attn_folds ? &unfolded : nullptr)))
+                       attn_folds ? &unfolded : nullptr, pending)))
       return rc;
     at.qkv_part = unfolded ? (const float*)(ws + L.gpart) : nullptr;
     at.qkv_S = unfolded ? m->p_qkv.S : 0;
@@ -907,15 +934,21 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
     bool normed = false;
     if ((rc = run_gemm(m, P_O, m->p_o, EPI_RESID, m->o[l], o, B, x, nullptr, ws, L, st, m->ffn_norm[l], &normed)))
       return rc;
-    if (!normed && (rc = norm(m->ffn_norm[l], m->p_o.nRB))) return rc;
-    if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st))) return rc;
+    pn = PendingNorm{m->ffn_norm[l], m->p_o.nRB, B};
+    pending = normed ? nullptr : &pn;
+    if ((rc = run_gemm(m, P_GU, m->p_gu, EPI_SWIGLU, m->gu[l], xn, B, nullptr, act, ws, L, st, nullptr, nullptr,
+                       nullptr, pending)))
+      return rc;
     const float* gnext = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
     normed = false;
     if ((rc = run_gemm(m, P_DOWN, m->p_down, EPI_RESID, m->down[l], act, B, x, nullptr, ws, L, st, gnext, &normed)))
       return rc;
-    if (!normed && (rc = norm(gnext, m->p_down.nRB))) return rc;
+    pn = PendingNorm{gnext, m->p_down.nRB, B};
+    pending = normed ? nullptr : &pn;
   }
-  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, n_out, logits, nullptr, ws, L, st))) return rc;
+  if ((rc = run_gemm(m, P_HEAD, m->p_head, EPI_HEAD, m->head, xn, n_out, logits, nullptr, ws, L, st, nullptr, nullptr,
+                     nullptr, pending)))
+    return rc;
   if (argmax) {
     ProfScope ps(m, P_ARGMAX, st);
     HIP_TRY(launch_argmax((const float2*)(ws + L.amax), m->p_head.nRB, n_out, argmax, st));

@@ -285,7 +285,8 @@ def q8_leg(args, rf, log):
     from continuous_batching_decode_step_amd.driver import Engine
     cfg = synth.SMOL135M_Q8
     dw = cbd.upload_weights(synth.make_weights(cfg))
-    Bmax, ctx = 960, 16
+    batches = [int(x) for x in args.q8_batches.split(",")]
+    Bmax, ctx = max(batches), 16
     lens = np.full(Bmax, ctx, dtype=np.int64)
     toks = synth.step_tokens(cfg, Bmax)
     eng = Engine(cfg, dw, Bmax, ctx + 1, max_batch=Bmax)
@@ -296,7 +297,7 @@ def q8_leg(args, rf, log):
         eng.arena.kv_import(lanes[b], ctx, k, v, eng.stream)
     torch.cuda.synchronize()
     out = []
-    for B in (1, 64, 256, 512, 960):
+    for B in batches:
         row, _ = measure(eng, lanes, lens, toks, B, args.steps, args.warmup, cfg, rf, torch.cuda.current_stream())
         log("q8-135m B=%3d  %9.1f tok/s  %.3f ms/step" % (B, row["tok_s"], row["ms_per_step"]))
         out.append({"B": B, "tok_s": round(row["tok_s"], 1), "ms_per_step": round(row["ms_per_step"], 4),
@@ -384,6 +385,10 @@ def main() -> int:
                          "plain launches")
     ap.add_argument("--no-q8", action="store_true",
                     help="skip the SmolLM2-135M Q8_0 leg (decode steps at 16-position contexts, B = 1..960)")
+    ap.add_argument("--q8-only", action="store_true",
+                    help="run the SmolLM2-135M Q8_0 leg alone and print its rows as the JSON line (for profiling "
+                         "that leg; not the headline)")
+    ap.add_argument("--q8-batches", default="1,64,256,512,960", help="B values of the SmolLM2-135M Q8_0 leg")
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the wide-batch leg (B = 256 and 512 with KV U[128,4096], one paged pool) "
                          "that reports the projections' bf16 MFMA utilisation")
@@ -410,6 +415,9 @@ def main() -> int:
     from continuous_batching_decode_step_amd.driver import Engine
 
     cbd.lib()  # fail loudly if the HIP library is missing
+    if args.q8_only:
+        print(json.dumps({"context_q8_smollm135m": q8_leg(args, rf, log)}), flush=True)
+        return 0
     cfg = synth.MISTRAL7B
     batches = [int(x) for x in args.batches.split(",")]
     n_lanes = max(args.lanes, max(batches))

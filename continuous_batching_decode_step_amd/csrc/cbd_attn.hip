@@ -129,20 +129,37 @@ __device__ inline float rope_pair(float x, float y, float2 t, bool first) {
   return first ? x * t.x - y * t.y : x * t.x + y * t.y;
 }
 
+// G: query heads per wave, a divisor of the group size a.G; the a.G / G waves
+// of one (item, KV head) are numbered 8 apart, so they land on one XCD and
+// share the chunk's loads in its L2.
 template <int HD, bool KVBF16, int G>
 __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   constexpr int D = HD / 16;  // dims per lane
   static_assert(ATTN_SPLIT == 64, "one wave holds 4 keys x 16 iterations");
-  const int item = blockIdx.x;
-  if (item >= *a.n_items_dev) return;  // grid sized for the most items a step can have
+  const int nz = a.G / G;  // waves per (item, KV head)
+  const int zb = blockIdx.x >> 3;
+  const int item = (zb / nz) * 8 + (blockIdx.x & 7);
+  const int jz = (zb % nz) * G;  // this wave's first head of the group
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int4 it4 = *(const int4*)(a.items + ITEM_INTS * item);
-  const int blk = a.items[ITEM_INTS * item + 4];  // the chunk's block
-  const int b = it4.x & 0xffffff;
-  const int s = it4.y;  // one chunk per item for this kernel
-  const int p = a.pos[b];
+  // The item and the step's item count in one memory round trip, and the
+  // item carries the row's position, so the key loads wait on nothing else.
+  // The grid is sized for the most items a step can have: an item past the
+  // count reads lane 0's chunk 0 (in bounds, never used) and leaves before
+  // it writes anything.
+  const int n_items = *a.n_items_dev;
+  const int il = min(item, a.max_items - 1);  // the grid rounds items up to 8
+  int4 it4r = *(const int4*)(a.items + ITEM_INTS * il);
+  int blkr = a.items[ITEM_INTS * il + 4];  // the chunk's block
+  // an opaque use of the item here keeps its loads beside the count's (the
+  // compiler would otherwise load it only after testing the count)
+  __asm__ volatile("" : "+s"(it4r.x), "+s"(it4r.y), "+s"(it4r.z), "+s"(blkr));
+  const bool valid = item < n_items;
+  const int blk = valid ? blkr : 0;
+  const int b = valid ? (it4r.x & 0xffffff) : 0;
+  const int s = valid ? it4r.y : 0;  // one chunk per item for this kernel
+  const int p = valid ? it4r.z : 0;
   const int nk = p + 1;
   const int kbeg = s * ATTN_SPLIT;  // first key of the chunk
   const int kend = min(kbeg + ATTN_SPLIT, nk);
@@ -157,11 +174,43 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   const bool first_half = d0 < HD / 2;
   const int dp = first_half ? d0 + HD / 2 : d0 - HD / 2;
 
+  // Batches of KB keys (and values) are loaded before any is used
+  // (unconditional, from a key clamped into range; key p and keys past the
+  // end are replaced after the load, since slot p may be being written).  A
+  // one-head wave (a launch with few waves, bound by its serial chain) issues
+  // the first batch of keys and of values before anything waits on memory; a
+  // whole group's wave issues its keys after its queries and its values after
+  // its scores, as their registers would otherwise cut its occupancy (100 ->
+  // 192 VGPRs for three heads of 64 dims: 10-15% slower per step at 256-960
+  // lanes).
+  constexpr int KB = KVRaw<D, KVBF16>::BYTES > 16 ? 8 : 16;
+  constexpr bool EARLY = G == 1;
+  KVRaw<D, KVBF16> kr0[KB], vr[KB];
+  auto load_k0 = [&]() {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int key = kbeg + 4 * i + r;
+      kr0[i] = load_raw<D, KVBF16>(a.kpool, base + (long long)min(key, kend - 1) * HD + d0);
+    }
+  };
+  auto load_v0 = [&]() {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int key = kbeg + 4 * i + r;
+      vr[i] = load_raw<D, KVBF16>(a.vpool, base + (long long)min(key, kend - 1) * HD + d0);
+    }
+  };
+  if constexpr (EARLY) {
+    load_k0();
+    load_v0();
+  }
+  if (!valid) return;
+
   // Rotated queries of the group for this lane's dims (f32).
   float q[G][D];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float* qh = row + (size_t)(g * G + j) * HD;
+    const float* qh = row + (size_t)(g * a.G + jz + j) * HD;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
       const int jj = first_half ? d0 + e : d0 + e - HD / 2;
@@ -209,7 +258,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
         vnr.w[e] = __builtin_bit_cast(unsigned, vn[e]);
       }
     }
-    if (r == 0) {  // one row of lanes writes the slot
+    if (r == 0 && jz == 0) {  // one row of lanes of the group's first wave writes the slot
       const long long o = base + (long long)p * HD + d0;
 #pragma unroll
       for (int e = 0; e < D; ++e) {
@@ -229,23 +278,37 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
   // Scores of the wave's 64 keys: lane (r, c) accumulates its D dims of key
   // kbeg + 4*it + r into part[it][j]; the row then reduce-scatters so that
   // lane (r, c) ends with the full score of key kbeg + 4*c + r.  Loads are
-  // issued in batches of KB keys before any is used (unconditional, from a
-  // key clamped into range; key p and keys past the end are replaced after
-  // the load, since slot p may be being written).
-  constexpr int KB = KVRaw<D, KVBF16>::BYTES > 16 ? 8 : 16;
+  // issued in batches of KB keys before any is used (the first batch above).
+  if constexpr (!EARLY) load_k0();
   const float inv = 1.0f / sqrtf((float)HD);
+  // Keys of the chunk up to the row's end.  One-head waves skip groups of 16
+  // keys past it below: their probabilities are exactly 0 and their values
+  // 0, so their terms (+0) change no sum.  (In a whole group's wave the
+  // branches leave the compiler short of scalar registers: ~1000 spills to
+  // vector lanes, 25.5 -> 39.1 us per launch at 960 lanes.)
+  const int nlive = kend - kbeg;
   float part[16][G];
 #pragma unroll
   for (int i0 = 0; i0 < 16; i0 += KB) {
     KVRaw<D, KVBF16> kr[KB];
+    if (i0 == 0) {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int key = kbeg + 4 * (i0 + i) + r;
-      kr[i] = load_raw<D, KVBF16>(a.kpool, base + (long long)min(key, kend - 1) * HD + d0);
+      for (int i = 0; i < KB; ++i) kr[i] = kr0[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int key = kbeg + 4 * (i0 + i) + r;
+        kr[i] = load_raw<D, KVBF16>(a.kpool, base + (long long)min(key, kend - 1) * HD + d0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
+      if (EARLY && 4 * ((i0 + i) & ~3) >= nlive) {  // 16 keys all past the end: their scores are masked
+#pragma unroll
+        for (int j = 0; j < G; ++j) part[i0 + i][j] = 0.f;
+        continue;
+      }
       const int key = kbeg + 4 * (i0 + i) + r;
       const unsigned take = fused && key == p ? ~0u : 0u;
       const unsigned keep = key < pk ? ~0u : 0u;  // past the end: zero
@@ -261,14 +324,10 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       }
     }
   }
-  // Values of the first batch are loaded now, to be in flight during the softmax.
-  KVRaw<D, KVBF16> vr[KB];
-#pragma unroll
-  for (int i = 0; i < KB; ++i) {
-    const int key = kbeg + 4 * i + r;
-    vr[i] = load_raw<D, KVBF16>(a.vpool, base + (long long)min(key, kend - 1) * HD + d0);
+  if constexpr (!EARLY) {
+    load_v0();  // in flight during the softmax
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
   float sc[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -323,6 +382,7 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const int it = i0 + i;
+      if (EARLY && 4 * (it & ~3) >= nlive) continue;
       const int key = kbeg + 4 * it + r;
       const unsigned take = fused && key == p ? ~0u : 0u;
       const unsigned keep = key < pk ? ~0u : 0u;
@@ -354,12 +414,12 @@ __global__ __launch_bounds__(64) void k_attn(AttnArgs a) {
       for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int e = 0; e < D; ++e)
-          put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * G + j) * HD + d0 + e, o[j][e] / ls[j], a.act);
+          put_out(a.out, (size_t)b * a.Hq * HD + (size_t)(g * a.G + jz + j) * HD + d0 + e, o[j][e] / ls[j], a.act);
     }
     return;
   }
-  const size_t pstride = (size_t)G * (HD + 2);
-  float* dst = a.part + (((size_t)b * a.max_splits + s) * a.Hkv + g) * pstride;
+  const size_t pstride = (size_t)a.G * (HD + 2);
+  float* dst = a.part + (((size_t)b * a.max_splits + s) * a.Hkv + g) * pstride + (size_t)jz * (HD + 2);
   if (r == 0) {
 #pragma unroll
     for (int j = 0; j < G; ++j)
@@ -1071,14 +1131,33 @@ __global__ __launch_bounds__(COMB_THREADS) void k_attn_combine(AttnArgs a, int h
   put_act<ACT>(a.out, (size_t)b * a.Hq * hd + (size_t)(g * a.G + j) * hd + dim, O / L);
 }
 
+// Waves of (item, KV head) below this count take one query head each: a
+// wave's serial chain (scores, reduce-scatter, softmax, P.V of its heads)
+// bounds a launch with few waves (SmolLM2-135M shape, 16-key contexts: 11.6
+// -> 7.2 us at one lane, -6% per step at 64 lanes), while with more waves
+// the repeated chunk loads cost more (+3% and +5% per step at 512 and 960
+// lanes).  Splitting the group changes no result: each head is computed on
+// its own.
+constexpr long long ATTN_SPLIT_HEADS_BELOW = 512;
+
+template <int HD, bool BF, int G>
+static void launch_gk(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  const bool one = (long long)grid.x * grid.y < ATTN_SPLIT_HEADS_BELOW;
+  const dim3 g2((unsigned)(((long long)grid.x + 7) / 8 * 8 * (one ? G : 1)), grid.y);
+  if (one || G == 1)
+    hipLaunchKernelGGL((k_attn<HD, BF, 1>), g2, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn<HD, BF, G>), g2, dim3(64), 0, st, a);
+}
+
 template <int HD, bool BF>
 static hipError_t launch_g(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn<HD, BF, 1>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn<HD, BF, 2>), grid, dim3(64), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn<HD, BF, 3>), grid, dim3(64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn<HD, BF, 4>), grid, dim3(64), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_attn<HD, BF, 8>), grid, dim3(64), 0, st, a); break;
+    case 1: launch_gk<HD, BF, 1>(a, grid, st); break;
+    case 2: launch_gk<HD, BF, 2>(a, grid, st); break;
+    case 3: launch_gk<HD, BF, 3>(a, grid, st); break;
+    case 4: launch_gk<HD, BF, 4>(a, grid, st); break;
+    case 8: launch_gk<HD, BF, 8>(a, grid, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

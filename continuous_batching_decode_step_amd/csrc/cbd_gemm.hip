@@ -123,8 +123,11 @@ __device__ inline u32x4 q8_to_f16(u32x4 raw) {
 // and R = RM x the row tiles of one block).  Per-row-block side outputs (sums
 // of x^2, argmax candidates) are written per row block, exactly as a wave
 // owning one block writes them.
+// xpre (EPI_RESID, optional): the residual's values at the wave's outputs,
+// loaded earlier (the wave owns them: nobody else writes them meanwhile).
 template <int WT, int EPI, int R, int C, int RM = 1>
-__device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, const f32x4 (&acc)[R][C]) {
+__device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, const f32x4 (&acc)[R][C],
+                                const f32x4 (*xpre)[C] = nullptr) {
   constexpr int R0 = R / RM;  // row tiles of one row block
   const int r16 = lane & 15, g4 = lane >> 4;
   // Output coordinates of acc[r][c][i]: row (or gate/up pair) and lane column.
@@ -166,7 +169,7 @@ __device__ inline void epilogue(const GemmArgs& a, int rb, int cg, int lane, con
             const int n = out_row(r, i);
             if (!(cok && n < a.N)) continue;
             const size_t idx = (size_t)col * a.N + n;
-            const float xn = a.out[idx] + acc[r][c][i];
+            const float xn = (xpre ? xpre[r][c][i] : a.out[idx]) + acc[r][c][i];
             a.out[idx] = xn;
             ss = __builtin_fmaf(xn, xn, ss);  // the same operation in k_fold_norm
           }
@@ -340,6 +343,25 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Residual projections: wave 0, which runs the epilogue, loads the residual
+  // at its outputs now, beside its first weights, rather than after the
+  // reduction (one memory round trip less on the serial path).
+  f32x4 xpre[R][C];
+  if constexpr (EPI == EPI_RESID) {
+    if (s == 0) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int col = min(cg * TILE * C + TILE * c + r16, a.B - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = min(rb * TILE * R + TILE * r + 4 * g4 + i, a.N - 1);
+            xpre[r][c][i] = a.out[(size_t)col * a.N + n];
+          }
+      }
+    }
+  }
 
   auto load_stage_w = [&](u32x4 (&A)[U][R], int step0) {
 #pragma unroll
@@ -479,7 +501,10 @@ __global__ __launch_bounds__(GEMM_MAX_SPLIT * 64) void k_gemm(GemmArgs a) {
     if (s != 0) return;
   }
 
-  epilogue<WT, EPI, R, C>(a, rb, cg, lane, acc);
+  if constexpr (EPI == EPI_RESID)
+    epilogue<WT, EPI, R, C>(a, rb, cg, lane, acc, xpre);
+  else
+    epilogue<WT, EPI, R, C>(a, rb, cg, lane, acc);
 }
 
 

@@ -84,29 +84,47 @@ __global__ __launch_bounds__(256) void k_norm(const float* x, const float* ssq, 
 }
 
 // argmax[b]: largest value over the LM head's per-row-block candidates, the
-// lowest index on ties.  One wave per lane.
-__global__ __launch_bounds__(64) void k_argmax(const float2* amax, int nRB, int B, int* out) {
+// lowest index on ties.  "Larger value, then lower index" is a total order on
+// the (non-NaN) candidates, so the result does not depend on the order in
+// which they are compared.  One 256-thread workgroup per lane; each thread
+// keeps up to ARGMAX_PER candidates in flight (one memory round trip for the
+// LM heads here), then a shuffle tree per wave and the four waves in LDS.
+constexpr int ARGMAX_PER = 8;
+
+__device__ inline void argmax_take(float v, int i, float& best, int& bi) {
+  if (v > best || (v == best && i < bi)) {
+    best = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_argmax(const float2* amax, int nRB, int B, int* out) {
   const int b = blockIdx.x;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int rb = threadIdx.x; rb < nRB; rb += 64) {
-    const float2 e = amax[(size_t)rb * B + b];
-    const int i = __float_as_int(e.y);
-    if (e.x > best || (e.x == best && i < bi)) {
-      best = e.x;
-      bi = i;
+  for (int rb0 = 0; rb0 < nRB; rb0 += 256 * ARGMAX_PER) {
+    float2 e[ARGMAX_PER];
+#pragma unroll
+    for (int u = 0; u < ARGMAX_PER; ++u) {
+      const int rb = rb0 + u * 256 + threadIdx.x;
+      e[u] = rb < nRB ? amax[(size_t)rb * B + b] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
     }
+#pragma unroll
+    for (int u = 0; u < ARGMAX_PER; ++u) argmax_take(e[u].x, __float_as_int(e[u].y), best, bi);
   }
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float ov = __shfl_xor(best, off);
-    const int oi = __shfl_xor(bi, off);
-    if (ov > best || (ov == best && oi < bi)) {
-      best = ov;
-      bi = oi;
-    }
+  for (int off = 1; off < 64; off <<= 1) argmax_take(__shfl_xor(best, off), __shfl_xor(bi, off), best, bi);
+  __shared__ float vb[4];
+  __shared__ int ib[4];
+  if ((threadIdx.x & 63) == 0) {
+    vb[threadIdx.x >> 6] = best;
+    ib[threadIdx.x >> 6] = bi;
   }
-  if (threadIdx.x == 0) out[b] = bi;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) argmax_take(vb[w], ib[w], best, bi);
+    out[b] = bi;
+  }
 }
 
 __global__ void k_fill_u32(unsigned* p, size_t n, unsigned v) {
@@ -321,7 +339,7 @@ hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, cons
 }
 
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(B), dim3(64), 0, st, amax, nRB, B, argmax);
+  hipLaunchKernelGGL(k_argmax, dim3(B), dim3(256), 0, st, amax, nRB, B, argmax);
   return hipGetLastError();
 }
 

@@ -894,14 +894,39 @@ __global__ __launch_bounds__(256) void k_fold_norm(GemmArgs a) {
   }
   const float ss = block_sum(part);
   const float r = 1.0f / sqrtf(ss / (float)a.N + a.norm_eps);
+  // xn of the thread's rows in 16-byte stores (its 16 rows are consecutive)
 #pragma unroll
   for (int k = 0; k < MAXRB; ++k) {
     const int rb = t + 256 * k;
     if (rb >= a.nRB) break;
+    const size_t o = (size_t)b * a.N + rb * TILE;
+    float v[TILE];
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-      const int n = rb * TILE + i;
-      store_act<WT>(a.norm_out, (size_t)b * a.N + n, (xv[k][i] * r) * a.norm_g[n]);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 g = *(const f32x4*)(a.norm_g + rb * TILE + 4 * q);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * q + i] = (xv[k][4 * q + i] * r) * g[i];
+    }
+    if constexpr (WT == WT_F32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)((float*)a.norm_out + o + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = v[8 * h + 2 * e], hi = v[8 * h + 2 * e + 1];
+          if constexpr (WT == WT_BF16) {
+            w[e] = (unsigned)f2bf(lo) | ((unsigned)f2bf(hi) << 16);
+          } else {
+            w[e] = (unsigned)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                   ((unsigned)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+          }
+        }
+        *(u32x4*)((uint16_t*)a.norm_out + o + 8 * h) = w;
+      }
     }
   }
 }

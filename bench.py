@@ -377,6 +377,9 @@ def main() -> int:
     ap.add_argument("--kv-max", type=int, default=4096,
                     help="KV lengths are uniform in [128, KV_MAX] (seed 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="untimed decode steps at the widest B for this long before the sweep (a fresh "
+                         "process's first timed steps have shown one-off stalls of ~17 ms)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2, 3],
                     help="projection kernel family (cbd_set_variant): 0 automatic, 1 split-K, 2 wide panels, 3 dense tiles")
@@ -440,6 +443,15 @@ def main() -> int:
     log("KV of %d lanes generated and loaded in %.1fs" % (n_lanes, time.time() - t0))
 
     stream = torch.cuda.current_stream()
+    if args.prewarm_s > 0:
+        Bw = max(batches)
+        pw = lens[:Bw].astype(np.int32)
+        t_end = time.perf_counter() + args.prewarm_s
+        while time.perf_counter() < t_end:
+            for b in range(Bw):
+                eng.arena.lane_truncate(lanes[b], int(pw[b]))
+            eng.step(lanes[:Bw], pw.copy(), toks[:Bw])
+            torch.cuda.synchronize()
     sweep = []
     headline = None
     for B in batches:

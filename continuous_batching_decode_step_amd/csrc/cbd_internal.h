@@ -237,6 +237,9 @@ hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* to
 hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, const float* g, int B, int d, float eps,
                        void* xn, hipStream_t st);
 hipError_t launch_argmax(const float2* amax, int nRB, int B, int* argmax, hipStream_t st);
+// Copy `bytes` (a multiple of 4) from device-visible pinned host memory
+// (src_dev: its device address) to device memory, by a kernel.
+hipError_t launch_meta_copy(void* dst, const void* src_dev, size_t bytes, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t st);
 // Copy blocks src[j] -> dst[j] (j < n) of a layer-major pool in every layer,
 // K (at base) and V (at base + half); the block lists are on the device.

@@ -327,6 +327,25 @@ hipError_t launch_embed(int wt, const void* E, const uint16_t* Es, const int* to
   return hipGetLastError();
 }
 
+// The step's metadata from its pinned staging slot (host memory the device
+// reads over the bus) to the workspace, by a kernel: for the ~140 KB of items
+// of a 64-lane step the runtime's own copy goes through a DMA engine, whose
+// hand-off with the kernel queue left ~25 us idle before each step.  Loads at
+// system scope never see a stale cached copy of a slot written again by the
+// host four steps later.
+__global__ __launch_bounds__(256) void k_meta_copy(unsigned* dst, const unsigned* src, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_meta_copy(void* dst, const void* src_dev, size_t bytes, hipStream_t st) {
+  if (bytes % 4 != 0 || bytes / 4 > 0x7fffffffu) return hipErrorInvalidValue;
+  const int n = (int)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_meta_copy, dim3((n + 255) / 256), dim3(256), 0, st, (unsigned*)dst, (const unsigned*)src_dev, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm(int wt, const float* x, const float* ssq, int ssq_n, const float* g, int B, int d, float eps,
                        void* xn, hipStream_t st) {
   const dim3 grid((d + 1023) / 1024, B);

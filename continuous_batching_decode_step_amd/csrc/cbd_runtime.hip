@@ -124,6 +124,7 @@ struct cbd_model {
   // a decode step over all of its lanes (a decode step never allocates; a
   // prefill call with more rows may grow them)
   void* slot[NSLOT] = {};
+  void* slot_dev[NSLOT] = {};  // each slot's device address
   size_t slot_bytes[NSLOT] = {};
   hipEvent_t ev[NSLOT] = {};
   bool ev_live[NSLOT] = {};
@@ -211,9 +212,11 @@ int grow_slots(cbd_model* m, size_t bytes) {
     if (m->ev_live[i]) HIP_TRY(hipEventSynchronize(m->ev[i]));
     if (m->slot[i]) HIP_TRY(hipHostFree(m->slot[i]));
     m->slot[i] = nullptr;
+    m->slot_dev[i] = nullptr;
     m->slot_bytes[i] = 0;
     const size_t cap = std::max(bytes, (size_t)65536);
     HIP_TRY(counted_host_malloc(&m->slot[i], cap));
+    HIP_TRY(hipHostGetDevicePointer(&m->slot_dev[i], m->slot[i], 0));
     m->slot_bytes[i] = cap;
     if (!m->ev[i]) HIP_TRY(hipEventCreateWithFlags(&m->ev[i], hipEventDisableTiming));
   }
@@ -1072,7 +1075,7 @@ static int submit_rows(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi,
   int32_t* dmeta = (int32_t*)(ws + L.meta);
   {
     ProfScope ps(m, P_META, st);
-    HIP_TRY(hipMemcpyAsync(dmeta, m->slot[si], meta_bytes, hipMemcpyHostToDevice, st));
+    HIP_TRY(launch_meta_copy(dmeta, m->slot_dev[si], meta_bytes, st));
   }
   HIP_TRY(hipEventRecord(m->ev[si], st));
   m->ev_live[si] = true;

@@ -17,6 +17,7 @@ Prints ONE JSON line.  Only one GPU: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -93,6 +94,12 @@ def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Python's cyclic garbage collector off while steps are timed (as timeit
+    # does): a collection pass over this process's large heap has stalled the
+    # host for tens of ms, longer than the four steps it may run ahead, and the
+    # GPU then idles between steps.
+    gc_was = gc.isenabled()
+    gc.disable()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     e0, e1 = ev(), ev()
     per_step = [(ev(), ev()) for _ in range(steps)]
@@ -105,6 +112,8 @@ def measure(eng, lanes, lens, toks, B, steps, warmup, cfg, rf, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    if gc_was:
+        gc.enable()
     ms = e0.elapsed_time(e1) / steps
     each = sorted(a.elapsed_time(b) for a, b in per_step)
     pos = [int(x) for x in lens[:B]]

@@ -12,8 +12,9 @@
 // head_dim 64/128, k_attn_mf) takes one workgroup per (lane, KV head, aligned
 // group of ATTN_GROUP chunks of ATTN_SPLIT = 64 keys), one wave per chunk,
 // and merges the group's chunks in LDS into one partial.  The general kernel
-// (k_attn) takes one workgroup of one wave per (lane, KV head, chunk), so a
-// single lane's keys spread over many CUs.  Inside the general kernel's wave, 16
+// (k_attn) takes one workgroup of one wave per (lane, KV head, chunk), or, in
+// launches with few such waves, per (lane, query head, chunk), so a single
+// lane's keys spread over many CUs.  Inside the general kernel's wave, 16
 // lanes share one key row: lane
 // (r, c) = (lane / 16, lane % 16) holds dims [c*D, c*D + D) of key 4*it + r
 // for it = 0..15, D = hd / 16, so every load instruction reads 4 whole rows

@@ -18,9 +18,9 @@
 // lanes share one key row: lane
 // (r, c) = (lane / 16, lane % 16) holds dims [c*D, c*D + D) of key 4*it + r
 // for it = 0..15, D = hd / 16, so every load instruction reads 4 whole rows
-// (coalesced 16-byte loads for hd = 128 bf16 and hd = 64 f32).  The group's
-// query heads (all heads sharing the KV head) are scored together, so each K
-// and V row is read once per group.  Scores are f32 dot products of the
+// (coalesced 16-byte loads for hd = 128 bf16 and hd = 64 f32).  A whole-group
+// wave scores the group's query heads (all heads sharing the KV head)
+// together, so each K and V row is read once per group.  Scores are f32 dot products of the
 // rotated f32 query with the stored keys; a reduce-scatter across the 16
 // lanes of a row leaves lane (r, c) with the score of key 4c + r.  Softmax
 // statistics and the value sum are exact f32 per chunk; partials meet in a

@@ -561,6 +561,10 @@ def main() -> int:
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
         "context_q8_smollm135m": q8,
+        "context_q8_smollm135m_precision": None if q8 is None else (
+            "Q8_0 weights (int8 blocks of 32, binary16 scales) dequantised to binary16 in registers; "
+            "activations rounded to binary16 at the projections (the matrix cores' f16 operands), "
+            "f32 accumulation, residual stream and K/V in f32"),
         "wide": None if wide is None else [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                                            for r in wide],
         "prefill": prefill,

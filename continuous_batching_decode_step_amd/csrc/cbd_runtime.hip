@@ -372,8 +372,13 @@ int cbd_model_create(const cbd_config* cfg, const cbd_weights* w, cbd_model** ou
   int rc;
   if ((rc = check_matrix(w->embed, c.wtype, "embed"))) return rc;
   if (!c.tied_embeddings && (rc = check_matrix(w->lm_head, c.wtype, "lm_head"))) return rc;
+  // the norm kernels load the gains 16 bytes at a time
+  auto misaligned = [](const float* g) { return ((uintptr_t)g & 15) != 0; };
+  if (misaligned(w->final_norm)) return fail(CBD_E_ARG, "final_norm: gains must be 16-byte aligned");
   for (int l = 0; l < c.n_layers; ++l) {
     if (!w->attn_norm[l] || !w->ffn_norm[l]) return fail(CBD_E_ARG, "layer %d: null norm gain", l);
+    if (misaligned(w->attn_norm[l]) || misaligned(w->ffn_norm[l]))
+      return fail(CBD_E_ARG, "layer %d: norm gains must be 16-byte aligned", l);
     if ((rc = check_matrix(w->w_qkv[l], c.wtype, "w_qkv"))) return rc;
     if ((rc = check_matrix(w->w_o[l], c.wtype, "w_o"))) return rc;
     if ((rc = check_matrix(w->w_gu[l], c.wtype, "w_gu"))) return rc;

@@ -92,7 +92,7 @@ typedef struct {
  * arrays themselves are host arrays of n_layers entries, copied at create.
  *  embed      [vocab, d]
  *  lm_head    [vocab, d] (ignored when tied_embeddings)
- *  final_norm, attn_norm[l], ffn_norm[l]  f32 [d] RMSNorm gains
+ *  final_norm, attn_norm[l], ffn_norm[l]  f32 [d] RMSNorm gains, 16-byte aligned
  *  w_qkv[l]   [(n_heads + 2 n_kv_heads) * head_dim, d]: query rows, key rows, value rows
  *  w_o[l]     [d, n_heads * head_dim]
  *  w_gu[l]    [2 ffn, d]: gate rows, then up rows

@@ -67,6 +67,11 @@ def test_model_create_validates_shapes():
     with pytest.raises(cbd.CbdError) as e:
         cbd.Model(synth.TINY, w)
     assert e.value.name == "CBD_E_ARG"
+    w = fake_weights(synth.TINY)
+    w.ffn_norm[1] = FAKE + 4  # gains are loaded 16 bytes at a time
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Model(synth.TINY, w)
+    assert e.value.name == "CBD_E_ARG"
     wq = fake_weights(synth.SMOL135M_Q8)
     wq.w_gu[0] = cbd.DeviceMatrix(FAKE, None)  # Q8_0 without scales
     with pytest.raises(cbd.CbdError):

@@ -744,11 +744,6 @@ static int dense_split(int B, const Plan& p, int epi) {
   return dense_workgroups(g, epi, 0) < 256 ? 1 : 0;
 }
 
-// norm_g: for a residual projection, the gain of the RMSNorm that follows; if
-// the projection runs as a split-mode panel its fold also normalises x into
-// xn, and *normed says so (the caller then launches no norm).  unfolded: for
-// QKV, the consumer can add split partials itself; if the projection runs as
-// a split-mode panel its fold is skipped and *unfolded says so.
 // The RMSNorm of the residual stream that produces a projection's input, not
 // yet launched: its gain and the producer's row blocks of sums of x^2.
 struct PendingNorm {
@@ -757,6 +752,11 @@ struct PendingNorm {
   int rows;  // rows of x (the step's B; the LM head reads only the first n_out)
 };
 
+// norm_g: for a residual projection, the gain of the RMSNorm that follows; if
+// the projection runs as a split-mode panel its fold also normalises x into
+// xn, and *normed says so (the caller then launches no norm).  unfolded: for
+// QKV, the consumer can add split partials itself; if the projection runs as
+// a split-mode panel its fold is skipped and *unfolded says so.
 // pre: the RMSNorm that produces X (xn), if not yet run; split-K tiles of one
 // column group run it themselves (no norm launch), otherwise it is launched
 // here first.
@@ -894,9 +894,6 @@ static int enqueue_step(cbd_model* m, cbd_arena* a, int B, int n_out, bool multi
   at.frag = kv_frag(m) ? 1 : 0;
   int rc;
   void* xn = ws + L.xn;
-  (void)x;
-  (void)ssq;
-  (void)d;
   // The RMSNorm of x into xn that the next projection consumes, run by that
   // projection (or launched just before it); ssq_n = row blocks of the last
   // producer of x (the embedding: one).  None pending when a split-mode fold

@@ -652,10 +652,12 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // matrix-core attention shapes is a split-mode panel from one lane, its
 // partials added by the attention kernel up to 32 lanes (QKV 15.9 -> 13.2 us
 // at one lane, attention +0.6).  The residual projections (O, down) of those
-// models keep the split-K tiles below 8 lanes (their in-workgroup fold, then
-// the norm kernel: 277 -> 292 tok/s at one lane, 1047 -> 1094 at four, equal
-// at eight, on packed weights) and run as split-mode panels from 8, where the
-// fold also runs the next RMSNorm.  bf16 gate|up is a full-mode panel from one
+// models keep the split-K tiles (their in-workgroup fold, then the norm
+// kernel) up to 16 lanes, one column group: with the residual loaded at
+// kernel start they beat the split-mode panels there (8 lanes 2036 -> 2148
+// tok/s, 12 lanes 2900 -> 2993, 16 lanes 3680 -> 3718), and run as split-mode
+// panels from 17, where the fold also runs the next RMSNorm (tiles of two
+// column groups: 24 lanes -5%, 32 lanes -8%).  bf16 gate|up is a full-mode panel from one
 // lane (packed weights: 292 -> 297 tok/s at one lane, 1096 -> 1120 at four;
 // f32 and Q8_0 keep the split-K tiles below 8).  Other weight formats and attention shapes
 // keep the split-K tiles for QKV below 4 lanes and for O below 24, and run
@@ -667,7 +669,7 @@ static int panel_min_b(const cbd_model* m, int epi, int K) {
     case EPI_STORE: return bf16_mf ? 1 : 4;                 // QKV
     case EPI_SWIGLU: return m->wt == WT_BF16 ? 1 : 8;       // gate|up
     case EPI_HEAD: return 4;
-    default: return bf16_mf ? 8 : (K > 4096 ? 1 : 24);      // down; O
+    default: return bf16_mf ? 17 : (K > 4096 ? 1 : 24);     // down; O
   }
 }
 

@@ -96,10 +96,15 @@ struct GemmArgs {
 constexpr int NORM_IN_MAX_SSQ = 64;
 // Largest LDS staging of normalised activations per split-K workgroup.
 constexpr size_t NORM_IN_MAX_LDS = 32 * 1024;
+// Most lanes a split-K tile normalises for itself: a wave stages its lanes one
+// after another (a memory round trip each), so beyond two lanes the norm's own
+// launch costs less (SmolLM2-135M Q8_0 at 12 lanes: 1.37 ms per step with
+// normalising tiles, 0.97 at 16 with the norm launched).
+constexpr int NORM_IN_MAX_B = 2;
 // Whether launch_gemm can normalise its own activations for a projection of K
 // inputs, S splits of Ks, over B lanes whose activation format has xb bytes.
 __host__ __device__ constexpr bool gemm_norm_in_supported(int B, int K, int S, int Ks, int xb, int ssq_n) {
-  return B >= 1 && B <= TILE && ssq_n >= 1 && ssq_n <= NORM_IN_MAX_SSQ && K % 4 == 0 &&
+  return B >= 1 && B <= NORM_IN_MAX_B && ssq_n >= 1 && ssq_n <= NORM_IN_MAX_SSQ && K % 4 == 0 &&
          (size_t)S * B * ((size_t)Ks * xb + 16) <= NORM_IN_MAX_LDS;
 }
 

@@ -659,15 +659,18 @@ int cbd_set_variant(cbd_model* m, int variant) {
 // panels from 17, where the fold also runs the next RMSNorm (tiles of two
 // column groups: 24 lanes -5%, 32 lanes -8%).  bf16 gate|up is a full-mode panel from one
 // lane (packed weights: 292 -> 297 tok/s at one lane, 1096 -> 1120 at four;
-// f32 and Q8_0 keep the split-K tiles below 8).  Other weight formats and attention shapes
-// keep the split-K tiles for QKV below 4 lanes and for O below 24, and run
-// the long reduction (down) as a panel at every width (not measured
-// otherwise).
+// f32 and Q8_0 keep the split-K tiles up to 16 lanes, one column group).
+// Other weight formats and attention shapes keep the split-K tiles for QKV
+// and gate|up up to 16 lanes (the SmolLM2-135M shape, Q8_0: 4 lanes 1.065 ->
+// about 0.98 ms per step, 8 lanes 1.26 -> 1.17, 16 lanes 1.29 -> 0.97,
+// against split-mode panels from 4 and 8 lanes with their norm launches and
+// folds) and for O below 24, and run the long reduction (down) as a panel at
+// every width.
 static int panel_min_b(const cbd_model* m, int epi, int K) {
   const bool bf16_mf = m->wt == WT_BF16 && attn_chunks_per_item(m) == ATTN_GROUP;
   switch (epi) {
-    case EPI_STORE: return bf16_mf ? 1 : 4;                 // QKV
-    case EPI_SWIGLU: return m->wt == WT_BF16 ? 1 : 8;       // gate|up
+    case EPI_STORE: return bf16_mf ? 1 : 17;                // QKV
+    case EPI_SWIGLU: return m->wt == WT_BF16 ? 1 : 17;      // gate|up
     case EPI_HEAD: return 4;
     default: return bf16_mf ? 17 : (K > 4096 ? 1 : 24);     // down; O
   }
